@@ -1,0 +1,249 @@
+"""Benchmark of the MI355X Markov draft walk: microseconds per walk call (all draft steps).
+
+Headline workload: greedy walk, V = 151936, rank 256, 7 draft steps, bs = 1, bf16 W1 / W2 int8-
+quantised with one fp32 scale per row, fp32 base logits (the shape of the first row of the
+kernel table in vLLM PR #62958, Validation). Inputs are seeded synthetic tensors already
+resident in HBM when timing starts; W2 is quantised once, outside the timed region.
+
+Timing protocol (after that table's: CUDA graph, cold L2, median per call): before every
+timed call a 512 MiB read evicts W2 and the inputs from the 4 MiB L2 of each XCD and from the
+256 MiB MALL, leaving clean lines behind; a HIP event pair on the launch stream brackets each
+call; `value` is the median. Also reported: the same after a 512 MiB *write* (caches full of
+dirty lines, whose write-back the walk then pays), a warm back-to-back rate, and a sweep over
+the other shapes of that table.
+
+One JSON line on stdout; progress on stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import dspark_markov_draft_amd as dm  # noqa: E402
+from dspark_markov_draft_amd.synth import CASES, make_inputs, seeds_as_int64  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Walk:
+    """Device-resident inputs and outputs of one workload, plus a launcher for one mode."""
+
+    def __init__(self, case, mode, dev):
+        self.case, self.mode, self.dev = case, mode, dev
+        inp = make_inputs(case)
+        self.inp = inp
+        self.w1 = inp.w1.to(dev)
+        w2 = inp.w2.to(dev)
+        self.q, self.s = dm.dspark_quantize_w2(w2)
+        del w2
+        self.base = inp.base.to(dev)
+        self.start = inp.start.to(dev)
+        self.seeds = seeds_as_int64(inp.seeds).to(dev)
+        self.temps = inp.temperature.to(dev)
+        bs, T, V = self.base.shape
+        self.bs, self.T, self.V = bs, T, V
+        self.k = case.k
+        self.ws = dm.new_workspace(bs, T, V, self.k)
+        self.tokens = torch.empty((bs, T), dtype=torch.int32, device=dev)
+        self.draft_logits = (torch.empty((bs, T, V), dtype=torch.bfloat16, device=dev)
+                             if mode == "sample" else None)
+
+    def launch(self):
+        if self.k:
+            dm.dspark_walk_topk(self.q, self.s, self.w1, self.base, self.start, self.k, self.ws,
+                                sample=self.mode == "sample", seeds=self.seeds,
+                                temperature=self.temps, draft_tokens=self.tokens,
+                                draft_logits=self.draft_logits)
+        elif self.mode == "greedy":
+            dm.dspark_walk_greedy(self.q, self.s, self.w1, self.base, self.start, self.ws,
+                                  draft_tokens=self.tokens)
+        else:
+            dm.dspark_walk_sample(self.q, self.s, self.w1, self.base, self.start, self.seeds,
+                                  self.temps, self.ws, draft_tokens=self.tokens,
+                                  draft_logits=self.draft_logits)
+
+    def algorithmic_bytes(self):
+        """Bytes the method must move per call: W2 codes and scales once, every base logit,
+        the gathered W1 rows, and the outputs (tokens; bf16 draft logits when sampling)."""
+        bs, T, V, k = self.bs, self.T, self.V, self.k
+        w1_elem = self.w1.element_size()
+        n = bs * T * V * 4 + bs * T * 256 * w1_elem + bs * T * 4
+        if k:
+            n += bs * T * k * (256 + 4)               # gathered candidate rows and scales
+        else:
+            n += V * 256 + V * 4
+        if self.mode == "sample":
+            n += bs * T * V * 2
+        return n
+
+
+def _timed_calls(w, steps, flush_fn, stream):
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush_fn(i)
+        starts[i].record(stream)
+        w.launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([s.elapsed_time(e) * 1000.0 for s, e in zip(starts, ends)]), wall
+
+
+def time_walk(w, steps, warmup, flush, stream, dirty=False):
+    for _ in range(warmup):
+        w.launch()
+    torch.cuda.synchronize()
+    sink = torch.empty(1, dtype=torch.float32, device=flush.device)
+
+    def read_flush(i):
+        torch.sum(flush, out=sink)
+
+    us, wall = _timed_calls(w, steps, read_flush, stream)
+    dirty_us = None
+    if dirty:
+        dirty_us, _ = _timed_calls(w, steps, lambda i: flush.fill_(float(i)), stream)
+    # warm: back-to-back calls, no flush
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        w.launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1000.0 / steps
+    return us, wall, warm_us, dirty_us
+
+
+def cpu_baseline(case, budget_s=20.0):
+    """The CPU oracle on this host, same workload, whole walks, median of up to 3 calls
+    (fewer if one call exceeds the budget)."""
+    import oracle
+    inp = make_inputs(case)
+    q, s = oracle.quantize_w2(inp.w2.float().numpy())
+    w1 = inp.w1.float().numpy()
+    base = inp.base.numpy()
+    start = inp.start.numpy()
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < 3 and (time.perf_counter() - t_all) < budget_s:
+        t0 = time.perf_counter()
+        oracle.walk(q, s, w1, base, start)
+        times.append(time.perf_counter() - t0)
+    return {"value": float(np.median(times)) * 1e6, "unit": "us per walk call", "cores":
+            oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(times)} whole greedy walk(s) of {case.name} (all {case.T} steps, "
+                      f"all {case.bs} request(s)), wall clock per call, median"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None, help="time one case:mode only (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "walk's sharding across GPUs is a design, not an implementation.", file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    head_case, head_mode = CASES["v151936_t7_bs1"], "greedy"
+    if args.only:
+        name, mode = args.only.split(":")
+        head_case, head_mode = CASES[name], mode
+
+    log(f"[bench] headline {head_case.name} {head_mode}: steps={args.steps} warmup={args.warmup}")
+    w = Walk(head_case, head_mode, dev)
+    plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
+    us, wall, warm_us, dirty_us = time_walk(w, args.steps, args.warmup, flush, stream, dirty=True)
+    med = float(np.median(us))
+    nbytes = w.algorithmic_bytes()
+    achieved = nbytes / (float(np.mean(us)) * 1e-6) / 1e9
+    log(f"[bench] median {med:.2f} us  p10 {np.percentile(us, 10):.2f}  p90 "
+        f"{np.percentile(us, 90):.2f}  warm {warm_us:.2f} us")
+
+    sweep = []
+    if not args.no_sweep and not args.only:
+        for name, mode in [("v151936_t7_bs1", "sample"), ("v151936_t7_bs16", "greedy"),
+                           ("v151936_t7_bs16", "sample"), ("v151936_t7_bs64", "greedy"),
+                           ("v151936_t7_bs64", "sample"), ("v151936_t16_bs1", "greedy"),
+                           ("v151936_t16_bs1", "sample"), ("v129280_t5_bs1", "greedy"),
+                           ("v129280_t5_bs1", "sample"), ("v129280_t5_bs64", "greedy"),
+                           ("v129280_t5_bs64", "sample"), ("v248320_t16_bs1", "greedy"),
+                           ("v248320_t16_bs1", "sample")]:
+            del w
+            torch.cuda.empty_cache()
+            w = Walk(CASES[name], mode, dev)
+            try:
+                s_us, _, s_warm, _ = time_walk(w, max(10, args.steps // 2), 3, flush, stream)
+            except dm.DsparkError as e:
+                log(f"[bench] {name} {mode}: {e}")
+                continue
+            nb = w.algorithmic_bytes()
+            entry = {"workload": name, "mode": mode, "us_median": round(float(np.median(s_us)), 2),
+                     "us_p10": round(float(np.percentile(s_us, 10)), 2),
+                     "us_p90": round(float(np.percentile(s_us, 90)), 2),
+                     "us_warm": round(s_warm, 2),
+                     "hbm_frac": round(nb / (float(np.mean(s_us)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            sweep.append(entry)
+            log(f"[bench] {name} {mode}: {entry}")
+
+    cpu = None
+    if not args.no_cpu and not args.only:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(head_case)
+        log(f"[bench] oracle {cpu['value']:.0f} us/walk on {cpu['cores']} threads")
+
+    out = {
+        "metric": "us per Markov walk call (all draft steps), V=151936, 7 draft tokens, bs 1",
+        "value": round(med, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(us)) / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 x int8 -> int32 dot products, fp32 logits",
+        "data": "synthetic (seeded N(0, 0.02^2) bf16 W1/W2, N(0, 3^2) fp32 base logits)",
+        "config": {"workload": f"{head_case.name}:{head_mode}", "V": head_case.V, "draft_steps": head_case.T, "bs": head_case.bs, "rank": 256,
+                   "w_dtype": head_case.wdtype, "cache": "L2 and MALL evicted by a 512 MiB read before each call",
+                   "plan": plan},
+        "latency_us": {"median": round(med, 3), "p10": round(float(np.percentile(us, 10)), 3),
+                       "p90": round(float(np.percentile(us, 90)), 3), "warm": round(warm_us, 3),
+                       "after_dirty_flush_median": round(float(np.median(dirty_us)), 3),
+                       "wall_per_call_incl_flush": round(wall / args.steps * 1e6, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": "dense_walk_kernel"},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+"""Thin Python binding of libdspark.so, the gfx950 DSpark Markov draft walk.
+
+Every function has the name of the C entry point it calls and only marshals arguments: torch
+tensors in (device memory and the current stream come from PyTorch), status codes out as
+``DsparkError``. All arithmetic runs in the HIP kernels behind the C ABI (``include/dspark.h``).
+There is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark.so")
+
+F32, BF16, F16 = 0, 1, 2
+RANK = 256
+MAX_STEPS, MAX_BS, MAX_V, MAX_TOPK = 16, 64, 270336, 2048
+DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG = 1, 2, 3
+
+OK = 0
+ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NO_DEVICE = -1, -2, -3, -4
+ERR_LAUNCH, ERR_NONFINITE, ERR_TIMEOUT = -5, -6, -7
+
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class WalkPlan(ctypes.Structure):
+    _fields_ = [("device_cus", ctypes.c_int32), ("num_workgroups", ctypes.c_int32),
+                ("rows_per_workgroup", ctypes.c_int32), ("rows_in_registers", ctypes.c_int32),
+                ("rows_in_lds", ctypes.c_int32), ("rows_streamed", ctypes.c_int32),
+                ("resident_bytes", ctypes.c_int64), ("streamed_bytes", ctypes.c_int64),
+                ("lds_bytes", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """Load libdspark.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DsparkError(ERR_NO_DEVICE, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.dspark_status_string.argtypes = [i32]
+        L.dspark_status_string.restype = ctypes.c_char_p
+        L.dspark_quantize_w2.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+        L.dspark_walk_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.dspark_walk_workspace_bytes.restype = ctypes.c_size_t
+        L.dspark_walk_plan_query.argtypes = [i64, i64, i64, ctypes.POINTER(WalkPlan)]
+        L.dspark_walk_greedy.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
+        L.dspark_walk_sample.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, vp, vp, vp,
+                                         vp, vp, vp, ctypes.c_size_t, vp]
+        L.dspark_walk_topk.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i64, i32, vp,
+                                       vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dspark_walk_plan_for.argtypes = [ctypes.c_int32, i64, i64, i64, i64,
+                                           ctypes.POINTER(WalkPlan)]
+        L.dspark_workspace_status.argtypes = [vp, vp]
+        L.dspark_philox_words.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i64, i64, vp, vp]
+        L.dspark_debug_set.argtypes = [i32, i64]
+        for name in ["dspark_quantize_w2", "dspark_walk_plan_query", "dspark_walk_plan_for",
+                     "dspark_walk_greedy",
+                     "dspark_walk_sample", "dspark_walk_topk", "dspark_workspace_status",
+                     "dspark_philox_words", "dspark_debug_set"]:
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def dspark_status_string(status: int) -> str:
+    return lib().dspark_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise DsparkError(status, dspark_status_string(status))
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdspark must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE_CODE:
+        raise DsparkError(ERR_UNSUPPORTED, f"unsupported dtype {t.dtype}")
+    return _DTYPE_CODE[t.dtype]
+
+
+def dspark_quantize_w2(w2: torch.Tensor, q: Optional[torch.Tensor] = None,
+                       s: Optional[torch.Tensor] = None, stream=None):
+    """W2 [V, 256] (fp32 / bf16 / fp16, device) -> (q int8 [V, 256], s fp32 [V])."""
+    V, R = w2.shape
+    if q is None:
+        q = torch.empty((V, R), dtype=torch.int8, device=w2.device)
+    if s is None:
+        s = torch.empty((V,), dtype=torch.float32, device=w2.device)
+    _check(lib().dspark_quantize_w2(_p(w2), _dtype_code(w2), V, R, _p(q), _p(s), _stream(stream)))
+    return q, s
+
+
+def dspark_walk_workspace_bytes(bs: int, T: int, V: int, k: int = 0) -> int:
+    return int(lib().dspark_walk_workspace_bytes(bs, T, V, k))
+
+
+def new_workspace(bs: int, T: int, V: int, k: int = 0, device="cuda") -> torch.Tensor:
+    """A zeroed workspace of the size the walk needs (zeroed once; walks leave it zeroed)."""
+    n = dspark_walk_workspace_bytes(bs, T, V, k)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def dspark_walk_plan_query(bs: int, T: int, V: int) -> dict:
+    plan = WalkPlan()
+    _check(lib().dspark_walk_plan_query(bs, T, V, ctypes.byref(plan)))
+    return plan.as_dict()
+
+
+def dspark_walk_plan_for(cus: int, max_lds: int, bs: int, T: int, V: int) -> dict:
+    plan = WalkPlan()
+    _check(lib().dspark_walk_plan_for(cus, max_lds, bs, T, V, ctypes.byref(plan)))
+    return plan.as_dict()
+
+
+def dspark_walk_greedy(q, s, w1, base, start, workspace, draft_tokens=None, out_logits=None,
+                       stream=None):
+    """Greedy walk. base [bs, T, V] fp32; start [bs] int32. Returns draft_tokens [bs, T] int32."""
+    bs, T, V = base.shape
+    if draft_tokens is None:
+        draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
+    _check(lib().dspark_walk_greedy(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base), _p(start),
+                                    bs, T, V, q.shape[1], _p(draft_tokens), _p(out_logits),
+                                    _p(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+    return draft_tokens
+
+
+def dspark_walk_sample(q, s, w1, base, start, seeds, temperature, workspace, positions=None,
+                       draft_tokens=None, draft_logits=None, stream=None):
+    """Probabilistic walk. seeds [bs] int64 holding the uint64 bits; temperature [bs] fp32;
+    positions [bs] int64 or None. Returns (draft_tokens [bs, T] int32, draft_logits [bs, T, V]
+    bf16)."""
+    bs, T, V = base.shape
+    if draft_tokens is None:
+        draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
+    if draft_logits is None:
+        draft_logits = torch.empty((bs, T, V), dtype=torch.bfloat16, device=base.device)
+    _check(lib().dspark_walk_sample(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base), _p(start),
+                                    bs, T, V, q.shape[1], _p(seeds), _p(positions),
+                                    _p(temperature), _p(draft_tokens), _p(draft_logits),
+                                    _p(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+    return draft_tokens, draft_logits
+
+
+def dspark_walk_topk(q, s, w1, base, start, k, workspace, sample=False, seeds=None,
+                     temperature=None, positions=None, draft_tokens=None, draft_logits=None,
+                     stream=None):
+    """Top-k walk. Returns (draft_tokens, draft_logits): draft_logits is bf16 [bs, T, V] when
+    sampling, else the fp32 [bs, T, V] tensor passed in (or None)."""
+    bs, T, V = base.shape
+    if draft_tokens is None:
+        draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
+    if sample and draft_logits is None:
+        draft_logits = torch.empty((bs, T, V), dtype=torch.bfloat16, device=base.device)
+    _check(lib().dspark_walk_topk(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base), _p(start), bs,
+                                  T, V, q.shape[1], int(k), int(bool(sample)), _p(seeds),
+                                  _p(positions), _p(temperature), _p(draft_tokens),
+                                  _p(draft_logits), _p(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return draft_tokens, draft_logits
+
+
+def dspark_workspace_status(workspace, stream=None) -> int:
+    return int(lib().dspark_workspace_status(_p(workspace), _stream(stream)))
+
+
+def dspark_philox_words(seed: int, position: int, v0: int, n: int, device="cuda",
+                        stream=None) -> np.ndarray:
+    out = torch.empty(n, dtype=torch.int32, device=device)
+    _check(lib().dspark_philox_words(seed, position, v0, n, _p(out), _stream(stream)))
+    return out.cpu().numpy().view(np.uint32)
+
+
+def dspark_debug_set(key: int, value: int):
+    _check(lib().dspark_debug_set(key, value))

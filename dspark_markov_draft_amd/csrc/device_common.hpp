@@ -1,0 +1,132 @@
+// Device helpers of the gfx950 Markov-walk kernels: argmax keys, bf16 rounding, Philox4x32-10,
+// Gumbel noise and wave-wide reductions. GPU code only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int RANK = 256;
+constexpr int MAX_STEPS = 16;
+constexpr int MAX_BS = 64;
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------------------------------------
+// torch.argmax order as one unsigned 64-bit key (vLLM PR #64476, Claims: the first NaN wins,
+// otherwise the first maximum): the high word maps the float to an order-preserving u32 (every
+// NaN to the top, -0 onto +0), the low word is ~index so that at equal values the lower index
+// is the larger key. An atomic or wave-wide unsigned max then yields the torch.argmax winner.
+// Every real key is >= 0x007FFFFF00000000 (the key of -inf), so a zeroed slot is below all.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t argmax_key(float x, uint32_t idx) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t ord;
+    if (x != x) {
+        ord = 0xFFFFFFFFu;
+    } else {
+        if (x == 0.0f) u = 0u;
+        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    }
+    return ((uint64_t)ord << 32) | (uint64_t)(~idx);
+}
+
+__device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
+
+// ---------------------------------------------------------------------------------------------
+// bf16, round to nearest even; NaN stays a quiet NaN (vLLM PR #62958, Details: draft_logits
+// are the bf16 logits the sample was drawn from).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (x != x) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_value(uint32_t h) { return __uint_as_float(h << 16); }
+
+// ---------------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; a round takes the 64-bit
+// products of M0 * c0 and M1 * c2 and yields (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key
+// advances by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+// Noise word of vocabulary entry v at draft position P for a request keyed by `seed`
+// (vLLM PR #62958, Details: Philox keyed by request seed and draft position):
+// counter (v >> 2, lo32 P, hi32 P, 0), key (lo32 seed, hi32 seed), word v & 3.
+__device__ __forceinline__ uint32_t noise_word(uint64_t seed, uint64_t P, uint32_t v) {
+    const uint4 r = philox4x32_10(v >> 2, (uint32_t)P, (uint32_t)(P >> 32), 0u, (uint32_t)seed,
+                                  (uint32_t)(seed >> 32));
+    const uint32_t w = v & 3u;
+    return w == 0 ? r.x : w == 1 ? r.y : w == 2 ? r.z : r.w;
+}
+
+// u = (2 (x >> 9) + 1) 2^-24 is exact in fp32 and lies strictly inside (0, 1); the standard
+// Gumbel variate is g = -log(-log u).
+__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
+    const float u = (float)(2u * (x >> 9) + 1u) * 0x1p-24f;
+    return -logf(-logf(u));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wave-wide reductions over the 64 lanes.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = __shfl_xor(v, off, WAVE);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
+    return v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Loads of 4 consecutive W1 / W2 elements as fp32 (exact upcasts).
+// ---------------------------------------------------------------------------------------------
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+template <int DT>
+__device__ __forceinline__ float4 load4_as_f32(const void* base, int64_t elem) {
+    if constexpr (DT == DT_F32) {
+        return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+    } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + elem);
+        if constexpr (DT == DT_BF16) {
+            return make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                               __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u));
+        } else {
+            const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(raw.x & 0xFFFFu));
+            const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(raw.x >> 16));
+            const _Float16 h2 = __builtin_bit_cast(_Float16, (uint16_t)(raw.y & 0xFFFFu));
+            const _Float16 h3 = __builtin_bit_cast(_Float16, (uint16_t)(raw.y >> 16));
+            return make_float4((float)h0, (float)h1, (float)h2, (float)h3);
+        }
+    }
+}
+
+}  // namespace dspark

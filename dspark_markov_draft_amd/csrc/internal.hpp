@@ -1,0 +1,79 @@
+// Host-side declarations shared by the translation units of libdspark.so (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dspark.h"
+
+namespace dspark {
+
+// Workspace layout of a walk call (bytes from the start of the caller's workspace). A walk
+// leaves every word it uses at zero when it exits, so the caller zeroes the workspace once.
+constexpr size_t WS_ERR = 0;          // u32 error word (DSPARK_ERR_TIMEOUT / INVALID_ARG)
+constexpr size_t WS_RESULT = 256;     // u64 [16 steps][64 requests]: winning key of each step
+constexpr size_t WS_SLOTS = 16384;    // u64 [T][256 workgroups][slot stride]: per-workgroup keys
+constexpr size_t WS_TOPK = WS_SLOTS;  // top-k calls use the same region for candidate lists
+constexpr size_t WS_ALIGN = 256;
+constexpr int MAX_WORKGROUPS = 256;
+
+// keys per workgroup slot: whole 128-byte lines, so no two workgroups write the same line
+inline int slot_stride(int64_t bs) { return (int)((bs + 15) / 16 * 16); }
+inline size_t dense_slot_bytes(int64_t bs, int64_t T) {
+    return (size_t)T * MAX_WORKGROUPS * (size_t)slot_stride(bs) * 8;
+}
+inline size_t topk_bytes(int64_t bs, int64_t T, int64_t k) {
+    return k > 0 ? (size_t)bs * (size_t)T * ((size_t)k + 1) * 4 : 0;
+}
+
+// Process-wide test hooks (dspark_debug_set).
+struct DebugKnobs {
+    int max_workgroups = 0;
+    uint32_t spin_limit = 0;
+    uint32_t wait_unset = 0;
+};
+DebugKnobs& debug_knobs();
+
+struct DeviceInfo {
+    int device = -1;
+    int cus = 0;
+    size_t max_lds = 0;
+    bool cooperative = false;
+};
+// Query (cached per device) of the current device; returns a dspark_status.
+int current_device_info(DeviceInfo* info);
+
+int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, dspark_walk_plan* plan);
+
+struct WalkLaunch {
+    const int8_t* q;
+    const float* scale;
+    const void* w1;
+    int w1_dtype;
+    const float* base;
+    const int32_t* start;
+    int32_t* tokens;
+    float* out_logits;        // greedy, optional
+    uint16_t* draft_logits;   // sample, required
+    const uint64_t* seeds;
+    const int64_t* positions;
+    const float* temps;
+    void* workspace;
+    int bs, T, V;
+    int sample;
+};
+int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan, hipStream_t stream);
+
+int launch_quantize(const void* w2, int dtype, int64_t V, int8_t* q, float* s, hipStream_t stream);
+
+int launch_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n, uint32_t* out,
+                        hipStream_t stream);
+
+struct TopkLaunch {
+    WalkLaunch w;
+    int k;
+};
+int launch_topk_walk(const TopkLaunch& a, hipStream_t stream);
+
+}  // namespace dspark

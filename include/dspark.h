@@ -1,0 +1,198 @@
+/*
+ * dspark.h - C ABI of the MI355X (gfx950) DSpark Markov draft walk.
+ *
+ * The operation (vLLM PR #62958, int8 DSpark Markov walk, Overview): for each request the
+ * draft block is walked left to right; at step t
+ *
+ *     logits_t = base_logits[t] + dequant(W2) @ W1[prev],        W1, W2: V x 256
+ *
+ * then the step takes the first-maximum argmax (greedy) or a Gumbel-max sample, and the
+ * chosen token is prev for step t + 1 (prev at t = 0 is the request's start token). W2 is
+ * held as int8 with one fp32 scale per row (same page, Overview). Probabilistic drafting
+ * stores the bf16 logits it sampled from, and its noise is Philox keyed by the request seed
+ * and the draft position (same page, Details). Argmax follows torch.argmax: the first NaN
+ * wins, else the first maximum (vLLM PR #64476, Claims and Validation). The top-k variant
+ * takes the k best base logits once per draft position, biases only those, and scatters them
+ * into a row that is -inf elsewhere before the unchanged sampler runs (vLLM PR #49969
+ * "[Spec Decode] Add top-k DSpark Markov projection", Purpose).
+ *
+ * Conventions for every entry point:
+ *  - All tensors are row-major and contiguous, in device memory of the current HIP device,
+ *    owned by the caller. The library never frees caller memory and keeps no pointer after a
+ *    call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Walk calls only enqueue work on it
+ *    and return; they never wait on the device, so they may be captured into a HIP graph.
+ *  - A negative return value is an error from enum dspark_status. Argument errors are found on
+ *    the host before any device work: nothing is enqueued and no output is written.
+ *  - Supported envelope (PR #62958, Details): rank 256; 1 <= T <= 16 draft steps;
+ *    1 <= bs <= 64 requests; 1 <= V <= 270336; W1 and W2 in fp32, bf16 or fp16; base logits in
+ *    fp32. Larger inputs are rejected with DSPARK_ERR_UNSUPPORTED.
+ *  - Documented preconditions, not checked (checking would need a device sync): start tokens
+ *    lie in [0, V); W1 is finite; temperatures are finite and > 0; positions are >= 0.
+ *    NaN base logits are allowed in the dense walks and follow torch.argmax.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dspark_status {
+    DSPARK_OK = 0,
+    DSPARK_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer */
+    DSPARK_ERR_UNSUPPORTED = -2,  /* outside the supported envelope */
+    DSPARK_ERR_WORKSPACE = -3,    /* workspace missing or smaller than dspark_walk_workspace_bytes */
+    DSPARK_ERR_NO_DEVICE = -4,    /* no HIP device, or not a device this library was built for */
+    DSPARK_ERR_LAUNCH = -5,       /* a HIP launch or copy failed */
+    DSPARK_ERR_NONFINITE = -6,    /* dspark_quantize_w2 met a NaN or infinity in W2 */
+    DSPARK_ERR_TIMEOUT = -7       /* a walk's grid-wide wait hit its spin limit (see dspark_workspace_status) */
+};
+
+enum dspark_dtype { DSPARK_F32 = 0, DSPARK_BF16 = 1, DSPARK_F16 = 2 };
+
+#define DSPARK_RANK 256
+#define DSPARK_MAX_STEPS 16
+#define DSPARK_MAX_BS 64
+#define DSPARK_MAX_V 270336
+#define DSPARK_MAX_TOPK 2048
+
+/* Text for a status code. Never NULL; static storage. */
+const char* dspark_status_string(int status);
+
+/*
+ * Quantise W2 to int8 with one fp32 scale per row (PR #62958, Overview: "int8 with one fp32
+ * scale per row"). Reading of the unstated recipe: symmetric absmax, per row
+ *     s[v] = max_k |W2[v,k]| / 127            (IEEE fp32 division)
+ *     q[v,k] = clamp(rint(W2[v,k] / s[v]), -127, 127)   (IEEE division, round half to even)
+ * and an all-zero row gets s = 0, q = 0.
+ *   w2        [V, rank] in w2_dtype (DSPARK_F32 / BF16 / F16), 16-byte aligned
+ *   w2_q      [V, rank] int8 out, 16-byte aligned
+ *   w2_scale  [V] fp32 out
+ * Load-time call: it synchronises `stream` once to learn whether W2 held a NaN or infinity,
+ * and then returns DSPARK_ERR_NONFINITE with w2_q / w2_scale unspecified. Calls that overlap
+ * on one device must not run concurrently (they share the device-side flag).
+ */
+int dspark_quantize_w2(const void* w2, int w2_dtype, int64_t V, int64_t rank, int8_t* w2_q,
+                       float* w2_scale, void* stream);
+
+/*
+ * Bytes of workspace a walk call needs (k = 0 for the dense walks, else the top-k k).
+ * The caller allocates it on the device and zeroes it ONCE; every walk call leaves it zeroed
+ * again, so repeated calls need no memset. A workspace must not be used by two calls that can
+ * run at the same time.
+ */
+size_t dspark_walk_workspace_bytes(int64_t bs, int64_t T, int64_t V, int64_t k);
+
+/* How the dense walk will split W2 over the current device (for reports and tests). */
+typedef struct dspark_walk_plan {
+    int32_t device_cus;          /* compute units of the current device */
+    int32_t num_workgroups;      /* persistent workgroups, at most one per compute unit */
+    int32_t rows_per_workgroup;  /* contiguous W2 rows owned by each workgroup (last may own fewer) */
+    int32_t rows_in_registers;   /* per workgroup, held in the vector register file for the whole call */
+    int32_t rows_in_lds;         /* per workgroup, held in LDS for the whole call */
+    int32_t rows_streamed;       /* per workgroup, re-read from memory at every step */
+    int64_t resident_bytes;      /* int8 W2 bytes held on chip (whole grid) */
+    int64_t streamed_bytes;      /* int8 W2 bytes re-read per step (whole grid) */
+    int32_t lds_bytes;           /* dynamic LDS per workgroup */
+} dspark_walk_plan;
+
+int dspark_walk_plan_query(int64_t bs, int64_t T, int64_t V, dspark_walk_plan* plan);
+
+/* The same plan for a hypothetical gfx950 device with `cus` compute units and `max_lds` bytes of
+ * LDS per workgroup. Pure host logic (no HIP call); for tests and capacity planning. */
+int dspark_walk_plan_for(int32_t cus, int64_t max_lds, int64_t bs, int64_t T, int64_t V,
+                         dspark_walk_plan* plan);
+
+/*
+ * Greedy walk (PR #62958, Overview and Validation: greedy drafting, first-maximum argmax).
+ *   w2_q [V, 256] int8 and w2_scale [V] fp32 from dspark_quantize_w2 (w2_q 16-byte aligned)
+ *   w1 [V, 256] in w1_dtype, 16-byte aligned
+ *   base_logits [bs, T, V] fp32, 16-byte aligned
+ *   start_tokens [bs] int32: prev at step 0
+ *   draft_tokens [bs, T] int32 out
+ *   out_logits [bs, T, V] fp32 out, or NULL: the logits the argmax ran on
+ *   workspace of dspark_walk_workspace_bytes(bs, T, V, 0) bytes, zeroed once at allocation
+ * Numerics: the bias is (s[v] * s1) * sum_k q[v,k] * q1[k] with q1 = int8 codes of the gathered
+ * W1 row under its own absmax scale s1 (exact int32 sum); logits are fp32.
+ */
+int dspark_walk_greedy(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
+                       const float* base_logits, const int32_t* start_tokens, int64_t bs,
+                       int64_t T, int64_t V, int64_t rank, int32_t* draft_tokens,
+                       float* out_logits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Probabilistic walk (PR #62958, Details; PR #64476, Claims).
+ * Arguments as dspark_walk_greedy, plus
+ *   seeds [bs] uint64: per-request Philox key (lo32, hi32)
+ *   positions [bs] int64 or NULL: draft-position offset; step t uses P = positions[b] + t
+ *   temperature [bs] fp32 (> 0)
+ *   draft_logits [bs, T, V] bf16 bits out (required, 16-byte aligned): lb = bf16(logits), the
+ *       row the sample is drawn from
+ * Sample: x = Philox4x32-10(counter (v >> 2, lo32 P, hi32 P, 0), key seed)[v & 3],
+ * u = (2 (x >> 9) + 1) 2^-24, g = -log(-log u), token = argmax_v (lb[v] / temperature + g)
+ * with torch.argmax order; the divide is skipped at temperature 1.0.
+ */
+int dspark_walk_sample(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
+                       const float* base_logits, const int32_t* start_tokens, int64_t bs,
+                       int64_t T, int64_t V, int64_t rank, const uint64_t* seeds,
+                       const int64_t* positions, const float* temperature,
+                       int32_t* draft_tokens, uint16_t* draft_logits, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Top-k walk (PR #49969, Purpose). For each (request, step) the k largest base logits are the
+ * candidates (at equal values the lower index ranks first); the Markov bias is evaluated for
+ * candidates only; every other entry of the row is -inf; then greedy (sample = 0) or Gumbel
+ * (sample = 1, arguments as dspark_walk_sample) runs on the dense row, with noise keyed by the
+ * vocabulary index.
+ *   draft_logits: sample = 1: bf16 [bs, T, V] (required); sample = 0: fp32 [bs, T, V] or NULL
+ *   1 <= k <= min(V, DSPARK_MAX_TOPK); base logits must not hold NaN (result undefined)
+ */
+int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
+                     const float* base_logits, const int32_t* start_tokens, int64_t bs,
+                     int64_t T, int64_t V, int64_t rank, int64_t k, int sample,
+                     const uint64_t* seeds, const int64_t* positions, const float* temperature,
+                     int32_t* draft_tokens, void* draft_logits, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * Error word of a walk workspace: synchronises `stream`, returns DSPARK_OK or the error the
+ * last walk recorded, and clears it. Diagnostic call, not for hot loops.
+ *   DSPARK_ERR_TIMEOUT: a grid-wide wait hit its spin limit (the walk's workgroups were not all
+ *       resident at once, e.g. other work held compute units). The tokens of that call are
+ *       invalid, and the workspace must be zeroed again before the next call.
+ *   DSPARK_ERR_INVALID_ARG: a start token was outside [0, V) (it was replaced by 0).
+ */
+int dspark_workspace_status(void* workspace, void* stream);
+
+/*
+ * Test hook: out[i] = the Philox noise word the sampler uses for vocabulary entry v0 + i at
+ * draft position `position` of a request with this seed (see dspark_walk_sample), i < n.
+ */
+int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n, uint32_t* out,
+                        void* stream);
+
+/*
+ * Test hooks (process-wide, not thread-safe):
+ *   DSPARK_DEBUG_MAX_WORKGROUPS: cap the dense walk's grid (0 = one per compute unit);
+ *   DSPARK_DEBUG_SPIN_LIMIT: iterations of the grid-wide wait before DSPARK_ERR_TIMEOUT is
+ *       recorded (0 = default);
+ *   DSPARK_DEBUG_WAIT_UNSET_FLAG: non-zero makes the grid-wide waits also wait for a workspace
+ *       flag that nothing sets, so each runs into its spin limit (for the timeout test).
+ */
+enum dspark_debug_key {
+    DSPARK_DEBUG_MAX_WORKGROUPS = 1,
+    DSPARK_DEBUG_SPIN_LIMIT = 2,
+    DSPARK_DEBUG_WAIT_UNSET_FLAG = 3
+};
+int dspark_debug_set(int key, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

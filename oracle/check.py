@@ -1,0 +1,148 @@
+"""Teacher-forced comparison of a walk's outputs with the CPU oracle.
+
+TEST INFRASTRUCTURE ONLY (tests, ``__graft_entry__.smoke()``, the CPU leg of ``bench.py``).
+
+The walk is sequential, so one legitimate near-tie flip would change every later step. Each
+step is therefore re-run in the oracle with the previous token the walk under test actually
+chose (teacher forcing), and compared element by element:
+
+  * fp32 logits: |l_test - l_oracle| <= tol wherever the oracle is finite, and the -inf
+    entries of a top-k row match exactly;
+  * bf16 draft logits: equal, or the bf16 rounding of some value within tol of the oracle's
+    fp32 logit (the logit tolerance carried through the rounding; where |l| is small a bf16
+    step is far below tol, so a legitimate logit difference can move it by several steps);
+  * tokens: equal, or a near tie: the oracle's argmaxed quantity (logits for greedy, scores for
+    sampling) at the chosen token is within tol of its maximum; for sampling the allowance grows
+    by the stored bf16 difference / temperature at the two tokens.
+
+The tolerance 2e-3 (absolute, on logits) is the one the measured target names; the walk under
+test quantises the gathered W1 row to int8, which the oracle does not.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+from . import step as oracle_step
+from . import topk as oracle_topk
+
+TOL = 2e-3
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Report:
+    steps: int = 0
+    max_abs_logit_err: float = 0.0
+    lb_mismatch: int = 0            # bf16 entries that differ (each within the tolerance)
+    near_ties: List[tuple] = field(default_factory=list)   # (b, t, oracle tok, test tok, gap)
+    failures: List[str] = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> str:
+        return (f"steps={self.steps} max|dlogit|={self.max_abs_logit_err:.3g} "
+                f"bf16 diffs={self.lb_mismatch} near-ties={len(self.near_ties)} "
+                f"failures={len(self.failures)}" +
+                ("" if self.ok else "\n  " + "\n  ".join(self.failures[:10])))
+
+
+def _bf16_interval(h: np.ndarray):
+    """[lo, hi] of the fp32 values that round (nearest even) to each finite bf16 h: halfway to
+    the neighbouring bf16 values on either side."""
+    h = np.asarray(h, np.uint16).astype(np.int64)
+    v = bf16_bits_to_f32(h).astype(np.float64)
+    sign = np.where(h & 0x8000, -1, 1)
+    mag = h & 0x7FFF
+    up = bf16_bits_to_f32(((mag + 1) | (h & 0x8000)).astype(np.uint16)).astype(np.float64)
+    dn_mag = np.maximum(mag - 1, 0)
+    dn = bf16_bits_to_f32((dn_mag | (h & 0x8000)).astype(np.uint16)).astype(np.float64)
+    dn = np.where(mag == 0, -v - (up - v), dn)          # around zero the step is symmetric
+    a, b = (v + dn) / 2, (v + up) / 2                    # away-from-zero neighbour is `up`
+    lo = np.where(sign > 0, a, b)
+    hi = np.where(sign > 0, b, a)
+    return np.minimum(lo, hi), np.maximum(lo, hi)
+
+
+def _bf16_within_tol(l_orc: np.ndarray, lb_orc: np.ndarray, lb_test: np.ndarray, tol: float):
+    """Entries where lb_test != lb_orc are allowed if lb_test is the bf16 rounding of some value
+    within tol of the oracle's fp32 logit (its rounding interval meets [l - tol, l + tol])."""
+    diff = np.nonzero(lb_orc != lb_test)[0]
+    if diff.size == 0:
+        return diff, np.ones(0, bool)
+    l = l_orc[diff].astype(np.float64)
+    t = lb_test[diff]
+    tv = bf16_bits_to_f32(t).astype(np.float64)
+    lo, hi = _bf16_interval(t)
+    ok = np.isfinite(tv) & np.isfinite(l) & (lo <= l + tol) & (hi >= l - tol)
+    return diff, ok
+
+
+def check_walk(q, s, w1, base, start, tokens, *, sample=False, seeds=None, temps=None,
+               positions=None, k=0, logits=None, lb=None, requests=None, tol=TOL) -> Report:
+    """Compare a walk's outputs with the oracle, teacher-forced.
+
+    q, s: the ORACLE's own quantisation of W2; w1 fp32 [V, R]; base [bs, T, V] fp32; start [bs];
+    tokens [bs, T] from the walk under test; logits fp32 [bs, T, V] (greedy, optional);
+    lb uint16 [bs, T, V] (sample, optional); requests: subset of request indices to check.
+    """
+    bs, T, V = base.shape
+    rep = Report()
+    reqs = range(bs) if requests is None else requests
+    for b in reqs:
+        prev = int(start[b])
+        for t in range(T):
+            cand = oracle_topk(base[b, t], k) if k else None
+            P = (int(positions[b]) if positions is not None else 0) + t
+            seed = int(seeds[b]) if sample else 0
+            temp = float(temps[b]) if sample else 1.0
+            tok, l_o, lb_o, sc_o = oracle_step(q, s, w1, base[b, t], prev, cand=cand,
+                                               sample=sample, seed=seed, P=P, temp=temp)
+            got = int(tokens[b, t])
+            rep.steps += 1
+            where = f"b={b} t={t}"
+            if not (0 <= got < V):
+                rep.failures.append(f"{where}: token {got} out of range")
+                break
+            if logits is not None:
+                l_t = np.asarray(logits[b, t], np.float32)
+                fin = np.isfinite(l_o)
+                if not np.array_equal(np.isneginf(l_o), np.isneginf(l_t)):
+                    rep.failures.append(f"{where}: -inf pattern differs")
+                err = np.abs(l_t[fin].astype(np.float64) - l_o[fin].astype(np.float64))
+                m = float(err.max()) if err.size else 0.0
+                rep.max_abs_logit_err = max(rep.max_abs_logit_err, m)
+                if not m <= tol:
+                    rep.failures.append(f"{where}: max |dlogit| {m:.3g} > {tol}")
+            lb_t = None
+            if sample and lb is not None:
+                lb_t = np.asarray(lb[b, t], np.uint16)
+                diff, ok = _bf16_within_tol(l_o, lb_o, lb_t, tol)
+                rep.lb_mismatch += int(diff.size)
+                if diff.size and not ok.all():
+                    bad = diff[~ok][:3]
+                    rep.failures.append(
+                        f"{where}: bf16 draft logits differ at {bad.tolist()} "
+                        f"(oracle {bf16_bits_to_f32(lb_o[bad])}, test {bf16_bits_to_f32(lb_t[bad])},"
+                        f" l {l_o[bad]})")
+            if got != tok:
+                qty = sc_o if sample else l_o
+                gap = float(qty[tok]) - float(qty[got])
+                allow = tol
+                if sample and lb_t is not None:
+                    for v in (tok, got):
+                        allow += abs(float(bf16_bits_to_f32(lb_t[v:v + 1])[0]) -
+                                     float(bf16_bits_to_f32(lb_o[v:v + 1])[0])) / temp
+                if np.isnan(qty[tok]) or not (gap <= allow):
+                    rep.failures.append(f"{where}: token {got} vs oracle {tok} (gap {gap:.3g})")
+                else:
+                    rep.near_ties.append((b, t, tok, got, gap))
+            prev = got
+    return rep

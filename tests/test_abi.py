@@ -1,0 +1,198 @@
+"""The C ABI on the CPU: the library loads, exports every entry point its header declares, and
+rejects invalid arguments before any device work. No compute call is made here: every call
+below is invalid in at least one way that the host checks first, so it is safe on any machine.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import dspark_markov_draft_amd.binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+FAKE = 0x100000          # 16-byte aligned, never dereferenced: every call fails validation first
+VP = ctypes.c_void_p
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s+(dspark_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 10
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in dspark.h but not exported"
+
+
+def test_status_strings():
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, 99]:
+        s = B.dspark_status_string(code)
+        assert isinstance(s, str) and s
+
+
+def test_workspace_bytes():
+    # result words + per-workgroup slots of whole 128-byte lines (up to 256 workgroups)
+    one = B.dspark_walk_workspace_bytes(1, 1, 10, 0)
+    assert one >= 256 + 16 * 64 * 8 + 256 * 128 and one % 256 == 0
+    big = B.dspark_walk_workspace_bytes(64, 16, 270336, 0)
+    assert big >= 16 * 256 * 64 * 8 and big % 256 == 0
+    assert B.dspark_walk_workspace_bytes(64, 16, 4096, 0) == big      # independent of V
+    assert B.dspark_walk_workspace_bytes(17, 3, 10, 0) == B.dspark_walk_workspace_bytes(32, 3, 10, 0)
+    k = B.dspark_walk_workspace_bytes(64, 7, 151936, 512)
+    assert k >= 64 * 7 * 513 * 4 and k >= B.dspark_walk_workspace_bytes(64, 7, 151936, 0)
+
+
+@pytest.mark.parametrize("cus", [1, 8, 32, 80, 256, 304])
+@pytest.mark.parametrize("V", [1, 3, 255, 256, 257, 4096, 5000, 70000, 129280, 151936, 248320,
+                               270336])
+def test_plan_partition(cus, V):
+    try:
+        p = B.dspark_walk_plan_for(cus, 163840, 4, 7, V)
+    except B.DsparkError as e:
+        assert e.status == B.ERR_UNSUPPORTED
+        return
+    nwg, rpw = p["num_workgroups"], p["rows_per_workgroup"]
+    cus = min(cus, 256)                          # the grid is capped at 256 workgroups
+    assert 1 <= nwg <= cus
+    assert nwg * rpw >= V > (nwg - 1) * rpw          # every row owned exactly once
+    assert rpw % 4 == 0 or rpw >= V
+    assert p["rows_in_registers"] + p["rows_in_lds"] + p["rows_streamed"] == rpw
+    assert p["resident_bytes"] + p["streamed_bytes"] == V * 256
+    assert p["rows_in_registers"] <= 512 and p["rows_in_lds"] <= 512
+    assert 96 * 1024 <= p["lds_bytes"] <= 163840
+    if V >= 256 * cus:
+        # big vocabularies: the smallest multiple of 4 rows that covers V with every CU
+        assert (rpw - 4) * cus < V <= rpw * cus
+
+
+def test_plan_headline_fits_on_chip():
+    p = B.dspark_walk_plan_for(256, 163840, 1, 7, 151936)
+    assert p["streamed_bytes"] == 0 and p["resident_bytes"] == 151936 * 256
+    p = B.dspark_walk_plan_for(256, 163840, 1, 16, 248320)
+    assert p["streamed_bytes"] == 0
+
+
+def _greedy(**kw):
+    a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=1, T=7, V=151936,
+             rank=256, tokens=FAKE, logits=None, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return B.lib().dspark_walk_greedy(a["q"], a["s"], a["w1"], a["dt"], a["base"], a["start"],
+                                      a["bs"], a["T"], a["V"], a["rank"], a["tokens"],
+                                      a["logits"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), B.ERR_INVALID_ARG),
+    (dict(w1=None), B.ERR_INVALID_ARG),
+    (dict(base=None), B.ERR_INVALID_ARG),
+    (dict(tokens=None), B.ERR_INVALID_ARG),
+    (dict(ws=None), B.ERR_INVALID_ARG),
+    (dict(q=FAKE + 4), B.ERR_INVALID_ARG),
+    (dict(w1=FAKE + 8), B.ERR_INVALID_ARG),
+    (dict(bs=0), B.ERR_INVALID_ARG),
+    (dict(T=0), B.ERR_INVALID_ARG),
+    (dict(V=0), B.ERR_INVALID_ARG),
+    (dict(V=-5), B.ERR_INVALID_ARG),
+    (dict(rank=128), B.ERR_UNSUPPORTED),
+    (dict(T=17), B.ERR_UNSUPPORTED),
+    (dict(bs=65), B.ERR_UNSUPPORTED),
+    (dict(V=270337), B.ERR_UNSUPPORTED),
+    (dict(dt=7), B.ERR_UNSUPPORTED),
+    (dict(wsb=100), B.ERR_WORKSPACE),
+])
+def test_greedy_validation(kw, code):
+    assert _greedy(**kw) == code
+
+
+def _sample(**kw):
+    a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=1, T=7, V=151936,
+             rank=256, seeds=FAKE, pos=None, temp=FAKE, tokens=FAKE, lb=FAKE, ws=FAKE,
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    return B.lib().dspark_walk_sample(a["q"], a["s"], a["w1"], a["dt"], a["base"], a["start"],
+                                      a["bs"], a["T"], a["V"], a["rank"], a["seeds"], a["pos"],
+                                      a["temp"], a["tokens"], a["lb"], a["ws"], a["wsb"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seeds=None), B.ERR_INVALID_ARG),
+    (dict(temp=None), B.ERR_INVALID_ARG),
+    (dict(lb=None), B.ERR_INVALID_ARG),
+    (dict(seeds=FAKE + 4), B.ERR_INVALID_ARG),
+    (dict(pos=FAKE + 4), B.ERR_INVALID_ARG),
+    (dict(lb=FAKE + 1), B.ERR_INVALID_ARG),
+    (dict(T=99), B.ERR_UNSUPPORTED),
+    (dict(wsb=0), B.ERR_WORKSPACE),
+])
+def test_sample_validation(kw, code):
+    assert _sample(**kw) == code
+
+
+def _topk(**kw):
+    a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=64, T=7, V=151936,
+             rank=256, k=512, sample=1, seeds=FAKE, pos=None, temp=FAKE, tokens=FAKE, dl=FAKE,
+             ws=FAKE, wsb=1 << 24, stream=None)
+    a.update(kw)
+    return B.lib().dspark_walk_topk(a["q"], a["s"], a["w1"], a["dt"], a["base"], a["start"],
+                                    a["bs"], a["T"], a["V"], a["rank"], a["k"], a["sample"],
+                                    a["seeds"], a["pos"], a["temp"], a["tokens"], a["dl"],
+                                    a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), B.ERR_INVALID_ARG),
+    (dict(k=151937), B.ERR_INVALID_ARG),
+    (dict(k=4096), B.ERR_UNSUPPORTED),
+    (dict(sample=2), B.ERR_INVALID_ARG),
+    (dict(seeds=None), B.ERR_INVALID_ARG),
+    (dict(dl=None), B.ERR_INVALID_ARG),
+    (dict(dl=FAKE + 2), B.ERR_INVALID_ARG),
+    (dict(wsb=4096), B.ERR_WORKSPACE),
+    (dict(rank=255), B.ERR_UNSUPPORTED),
+])
+def test_topk_validation(kw, code):
+    assert _topk(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w2=None), B.ERR_INVALID_ARG),
+    (dict(V=0), B.ERR_INVALID_ARG),
+    (dict(rank=64), B.ERR_UNSUPPORTED),
+    (dict(dt=3), B.ERR_UNSUPPORTED),
+    (dict(q=FAKE + 2), B.ERR_INVALID_ARG),
+])
+def test_quantize_validation(kw, code):
+    a = dict(w2=FAKE, dt=B.BF16, V=10, rank=256, q=FAKE, s=FAKE)
+    a.update(kw)
+    assert B.lib().dspark_quantize_w2(a["w2"], a["dt"], a["V"], a["rank"], a["q"], a["s"],
+                                      None) == code
+
+
+def test_misc_validation():
+    L = B.lib()
+    assert L.dspark_philox_words(1, 2, 0, 10, None, None) == B.ERR_INVALID_ARG
+    assert L.dspark_philox_words(1, 2, -1, 10, FAKE, None) == B.ERR_INVALID_ARG
+    assert L.dspark_workspace_status(None, None) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(99, 1) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(B.DEBUG_SPIN_LIMIT, -1) == B.ERR_INVALID_ARG
+    assert L.dspark_walk_plan_query(1, 1, 10, None) == B.ERR_INVALID_ARG
+    assert L.dspark_walk_plan_for(0, 163840, 1, 1, 10, ctypes.byref(B.WalkPlan())) == \
+        B.ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible")
+def test_no_device_without_gpu():
+    """Valid arguments on a machine with no GPU: the device check refuses the call."""
+    assert _greedy() == B.ERR_NO_DEVICE
+    assert _sample() == B.ERR_NO_DEVICE
+    p = B.WalkPlan()
+    assert B.lib().dspark_walk_plan_query(1, 7, 151936, ctypes.byref(p)) == B.ERR_NO_DEVICE

@@ -1,0 +1,303 @@
+"""GPU parity of the dense walk, quantisation and Philox against the CPU oracle.
+
+All calls go through the C ABI (libdspark.so) via its thin binding. Bars: quantised W2 and
+Philox words bit-exact; logits within 2e-3; bf16 draft logits equal or a neighbour at a rounding
+midpoint; tokens teacher-forced, equal except at the oracle's near ties (oracle/check.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dspark_markov_draft_amd as dm
+import dspark_markov_draft_amd.binding as B
+import oracle
+from dspark_markov_draft_amd.synth import CASES, make_inputs
+from tests import structured
+from tests.gpu_helpers import DEV, Problem, lb_bits, random_problem
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset_knobs():
+    yield
+    for key in (B.DEBUG_MAX_WORKGROUPS, B.DEBUG_SPIN_LIMIT, B.DEBUG_WAIT_UNSET_FLAG):
+        dm.dspark_debug_set(key, 0)
+
+
+# ----------------------------------------------------------------------------------------------
+# quantisation and Philox: bit-exact
+# ----------------------------------------------------------------------------------------------
+def _special_rows(dtype):
+    w = torch.zeros(6, 256)
+    w[1, 0] = 127.0
+    w[1, 1:9] = torch.tensor([2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 126.5, -1.5])  # exact .5 ties
+    w[2, 3] = -1e-3                                                         # single element
+    w[3] = torch.linspace(-1, 1, 256)
+    w[4, :] = 7.0                                                           # constant row
+    return w.to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("V", [1, 4097, 151936])
+def test_quantize_bit_exact(dtype, V):
+    g = torch.Generator().manual_seed(V)
+    w2 = (torch.randn(V, 256, generator=g) * 0.02).to(dtype)
+    if V > 10:
+        w2[:6] = _special_rows(dtype)
+    q, s = dm.dspark_quantize_w2(w2.to(DEV))
+    q_o, s_o = oracle.quantize_w2(w2.float().numpy())
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_o)
+
+
+def test_quantize_rejects_nonfinite():
+    w2 = torch.zeros(10, 256)
+    w2[3, 7] = float("nan")
+    with pytest.raises(B.DsparkError) as e:
+        dm.dspark_quantize_w2(w2.to(DEV))
+    assert e.value.status == B.ERR_NONFINITE
+    q, s = dm.dspark_quantize_w2(torch.ones(10, 256, device=DEV))   # the flag is cleared again
+    assert float(s[0]) == np.float32(1.0) / np.float32(127.0)
+
+
+@pytest.mark.parametrize("seed,pos", [(0, 0), (1, 7), (2**64 - 1, 15), (0x0123456789ABCDEF, 2**33 + 5)])
+def test_philox_words_bit_exact(seed, pos):
+    v0, n = 151936 - 1000, 1200
+    got = dm.dspark_philox_words(seed, pos, v0, n)
+    want = np.array([oracle.noise_word(seed, pos, v0 + i) for i in range(n)], np.uint32)
+    assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------------------------
+# structured walks with exact answers
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_hand_worked_walk(dtype):
+    h = structured.hand_walk_v4()
+    g = h["golden"]
+    p = Problem(torch.from_numpy(h["w1"]).to(dtype), torch.from_numpy(h["w2"]).to(dtype),
+                h["base"], h["start"])
+    tok, logits = p.greedy()
+    assert tok[0].tolist() == g["tokens"]
+    assert logits[0].tolist() == g["logits"]
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_token_feedback_cycle(mode):
+    c = structured.feedback_cycle()
+    p = Problem(torch.from_numpy(c["w1"]).to(torch.bfloat16),
+                torch.from_numpy(c["w2"]).to(torch.bfloat16), c["base"], c["start"])
+    tok = p.greedy()[0] if mode == "greedy" else p.sample()[0]
+    assert np.array_equal(tok[0], c["expected"])
+
+
+# ----------------------------------------------------------------------------------------------
+# teacher-forced parity, oracle-sized problems spanning several workgroups and ragged tails
+# ----------------------------------------------------------------------------------------------
+SMALL = [  # V, T, bs, dtype, grid cap (0 = one workgroup per CU)
+    (4096, 4, 1, torch.float32, 0),
+    (5000, 3, 3, torch.bfloat16, 0),        # ragged last workgroup
+    (70001, 2, 2, torch.float16, 0),        # two register row sets, odd V
+    (20000, 3, 5, torch.bfloat16, 16),      # LDS-resident and streamed row sets
+    (3000, 5, 64, torch.bfloat16, 0),       # full batch
+    (257, 16, 2, torch.float32, 0),         # one workgroup, 16 steps
+    (1, 2, 1, torch.bfloat16, 0),           # a single-entry vocabulary
+]
+
+
+@pytest.mark.parametrize("V,T,bs,dtype,cap", SMALL)
+def test_greedy_parity_small(V, T, bs, dtype, cap):
+    dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+    p = random_problem(V, T, bs, dtype=dtype, w_std=0.05 if dtype == torch.float32 else 0.02,
+                       seed=V + T + bs)
+    tok, logits = p.greedy()
+    rep = p.check_greedy(tok, logits)
+    assert rep.ok, rep.summary()
+    print(rep.summary())
+
+
+@pytest.mark.parametrize("V,T,bs,dtype,cap", SMALL)
+def test_sample_parity_small(V, T, bs, dtype, cap):
+    dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+    temps = np.linspace(0.5, 2.0, bs).astype(np.float32) if bs > 1 else None
+    pos = np.arange(bs, dtype=np.int64) * 1000 + 3 if bs > 2 else None
+    p = random_problem(V, T, bs, dtype=dtype, seed=V * 7 + bs, temps=temps, positions=pos)
+    tok, lb = p.sample()
+    rep = p.check_sample(tok, lb)
+    assert rep.ok, rep.summary()
+    print(rep.summary())
+
+
+# ----------------------------------------------------------------------------------------------
+# full-size workloads (the pages' kernel-table shapes), sampled requests
+# ----------------------------------------------------------------------------------------------
+FULL = [
+    ("v151936_t7_bs1", "greedy", None),
+    ("v151936_t7_bs16", "greedy", [0, 7, 15]),
+    ("v151936_t7_bs16", "sample", [0, 9]),
+    ("v151936_t7_bs64", "greedy", [0, 33, 63]),
+    ("v151936_t7_bs64", "sample", [1, 62]),
+    ("v151936_t16_bs1", "sample", None),
+    ("v248320_t16_bs1", "sample", None),
+    ("v248320_t16_bs1", "greedy", None),
+    ("v129280_t5_bs64", "sample", [5, 40]),
+]
+
+
+@pytest.mark.parametrize("name,mode,reqs", FULL)
+def test_parity_full_size(name, mode, reqs):
+    inp = make_inputs(CASES[name])
+    p = Problem(inp.w1, inp.w2, inp.base, inp.start, seeds=inp.seeds,
+                temps=inp.temperature.numpy())
+    if mode == "greedy":
+        tok, logits = p.greedy()
+        rep = p.check_greedy(tok, logits, requests=reqs)
+    else:
+        tok, lb = p.sample()
+        rep = p.check_sample(tok, lb, requests=reqs)
+    print(name, mode, rep.summary())
+    assert rep.ok, rep.summary()
+
+
+def test_full_size_without_out_logits_same_tokens():
+    """The timed configuration (greedy, no logits output) emits the same tokens."""
+    inp = make_inputs(CASES["v151936_t7_bs1"])
+    p = Problem(inp.w1, inp.w2, inp.base, inp.start)
+    qs = p.quantize()
+    a, _ = p.greedy(want_logits=True, qs=qs)
+    b, _ = p.greedy(want_logits=False, qs=qs)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------------------------
+# torch.argmax order through the grid-wide combine (ties and NaN in different workgroups)
+# ----------------------------------------------------------------------------------------------
+def _zero_w2_problem(base_rows, start=0):
+    V = base_rows.shape[-1]
+    w = torch.zeros(V, 256, dtype=torch.bfloat16)
+    base = np.asarray(base_rows, np.float32)[None]
+    return Problem(w, w.clone(), base, np.array([start], np.int32))
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_argmax_order_across_workgroups(mode):
+    V = 151936      # 255 workgroups of 596 rows
+    rows = []
+    r = np.full(V, -1.0, np.float32); r[100000] = 5.0; r[3] = 5.0; rows.append((r, 3))
+    r = np.full(V, -1.0, np.float32); r[90000] = np.nan; r[150000] = np.nan; r[7] = 9.0
+    rows.append((r, 90000))
+    r = np.full(V, -np.inf, np.float32); rows.append((r, 0))
+    r = np.full(V, -1.0, np.float32); r[60000] = -0.0; r[120000] = 0.0; rows.append((r, 60000))
+    r = np.full(V, -1.0, np.float32); r[V - 1] = 2.0; rows.append((r, V - 1))
+    base = np.stack([x for x, _ in rows])
+    p = _zero_w2_problem(base)
+    if mode == "greedy":
+        tok, logits = p.greedy()
+        assert np.array_equal(logits[0], base, equal_nan=True)
+        for t, (_, want) in enumerate(rows):
+            assert tok[0, t] == want == int(torch.argmax(torch.from_numpy(base[t])))
+    else:
+        tok, lb = p.sample()
+        rep = p.check_sample(tok, lb)
+        assert rep.ok, rep.summary()
+        assert tok[0, 1] == 90000 and tok[0, 2] == 0
+
+
+# ----------------------------------------------------------------------------------------------
+# determinism, grid-size invariance, workspace hygiene, back-to-back calls
+# ----------------------------------------------------------------------------------------------
+def test_repeatable_and_grid_invariant():
+    p = random_problem(30000, 5, 4, seed=11)
+    qs = p.quantize()
+    ref_tok, ref_logits = p.greedy(qs=qs)
+    ws = dm.new_workspace(4, 5, 30000)
+    for _ in range(5):
+        tok, logits = p.greedy(qs=qs, ws=ws)
+        assert np.array_equal(tok, ref_tok)
+        assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32))
+    assert int(ws.count_nonzero()) == 0
+    for cap in (8, 37, 117, 0):
+        dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+        tok, logits = p.greedy(qs=qs, ws=ws)
+        assert np.array_equal(tok, ref_tok), cap
+        assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32)), cap
+        stok, slb = p.sample(qs=qs, ws=ws)
+        if cap == 8:
+            ref_s = (stok, slb)
+        else:
+            assert np.array_equal(stok, ref_s[0]) and np.array_equal(slb, ref_s[1])
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_back_to_back_calls_share_workspace():
+    a = random_problem(9000, 6, 8, seed=21)
+    b = random_problem(40000, 3, 2, seed=22)
+    ws = dm.new_workspace(64, 16, 1)
+    ra = a.greedy(ws=ws)
+    rb = b.sample(ws=ws)
+    ra2 = a.greedy(ws=ws)
+    rb2 = b.sample(ws=ws)
+    assert np.array_equal(ra[0], ra2[0]) and np.array_equal(ra[1], ra2[1])
+    assert np.array_equal(rb[0], rb2[0]) and np.array_equal(rb[1], rb2[1])
+    assert a.check_greedy(*ra).ok and b.check_sample(*rb).ok
+    assert dm.dspark_workspace_status(ws) == 0
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_timeout_is_reported_and_recovers():
+    """The host makes every grid-wide wait also wait for a flag it never sets; each wait runs
+    into its (small) spin limit, the kernel still completes, and the error word says so."""
+    p = random_problem(8192, 3, 2, seed=31)
+    qs = p.quantize()
+    ws = dm.new_workspace(2, 3, 8192)
+    dm.dspark_debug_set(B.DEBUG_SPIN_LIMIT, 200)
+    dm.dspark_debug_set(B.DEBUG_WAIT_UNSET_FLAG, 1)
+    p.greedy(qs=qs, ws=ws)
+    assert dm.dspark_workspace_status(ws) == B.ERR_TIMEOUT
+    dm.dspark_debug_set(B.DEBUG_WAIT_UNSET_FLAG, 0)
+    dm.dspark_debug_set(B.DEBUG_SPIN_LIMIT, 0)
+    ws.zero_()                      # after a timeout the workspace is zeroed again
+    tok, logits = p.greedy(qs=qs, ws=ws)
+    assert dm.dspark_workspace_status(ws) == 0
+    assert p.check_greedy(tok, logits).ok
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_out_of_range_start_token_is_contained():
+    p = random_problem(5000, 2, 2, seed=41)
+    p.start = torch.tensor([7, 5000], dtype=torch.int32, device=DEV)   # 5000 is out of range
+    ws = dm.new_workspace(2, 2, 5000)
+    p.greedy(ws=ws)
+    assert dm.dspark_workspace_status(ws) == B.ERR_INVALID_ARG
+
+
+def test_graph_capture_replay():
+    p = random_problem(20000, 4, 3, seed=51)
+    q, s = p.quantize()
+    bs, T, V = p.shape
+    ws = dm.new_workspace(bs, T, V)
+    tokens = torch.empty((bs, T), dtype=torch.int32, device=DEV)
+    logits = torch.empty((bs, T, V), dtype=torch.float32, device=DEV)
+    dm.dspark_walk_greedy(q, s, p.w1, p.base, p.start, ws, draft_tokens=tokens,
+                          out_logits=logits)
+    torch.cuda.synchronize()
+    ref_t, ref_l = tokens.clone(), logits.clone()
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        tokens.zero_()
+        with torch.cuda.graph(g, stream=stream):
+            dm.dspark_walk_greedy(q, s, p.w1, p.base, p.start, ws, draft_tokens=tokens,
+                                  out_logits=logits)
+    torch.cuda.synchronize()
+    for i in range(4):
+        tokens.fill_(-1)
+        logits.zero_()
+        scratch = torch.randn(1000, device=DEV) * 2          # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tokens, ref_t), i
+        assert torch.equal(logits, ref_l), i
+        assert float(scratch.abs().sum()) > 0
+    assert int(ws.count_nonzero()) == 0
