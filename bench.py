@@ -110,7 +110,7 @@ def time_walk(w, steps, warmup, flush, stream, dirty=False):
     sink = torch.empty(1, dtype=torch.float32, device=flush.device)
 
     def read_flush(i):
-        torch.sum(flush, out=sink)
+        torch.sum(flush, dim=0, keepdim=True, out=sink)
 
     us, wall = _timed_calls(w, steps, read_flush, stream)
     dirty_us = None

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libdspark.so")
 F32, BF16, F16 = 0, 1, 2
 RANK = 256
 MAX_STEPS, MAX_BS, MAX_V, MAX_TOPK = 16, 64, 270336, 2048
-DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG = 1, 2, 3
+DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG, DEBUG_STAMPS = 1, 2, 3, 4
+STAMPS_PER_WG = 82
 
 OK = 0
 ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NO_DEVICE = -1, -2, -3, -4

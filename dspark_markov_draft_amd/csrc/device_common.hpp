@@ -88,21 +88,60 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t x) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Wave-wide reductions over the 64 lanes.
+// Wave-wide maxima over the 64 lanes with DPP lane moves (a few cycles each, against ~100 for
+// an LDS-routed shuffle): swap within pairs and quads, mirror within 8 and 16 lanes, then
+// broadcast lane 15 of each 16-lane row into the next row and lane 31 into the upper half;
+// lane 63 ends with the maximum of all 64 lanes and is read back as a wave-uniform value.
+// Callers run them with all 64 lanes active.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t o = __shfl_xor(v, off, WAVE);
-        v = o > v ? o : v;
-    }
-    return v;
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
-    return v;
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    const uint32_t o = dpp_u32<CTRL, ROW_MASK>(v);
+    return o > v ? o : v;
+}
+
+constexpr int DPP_SWAP1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_SWAP2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // row_half_mirror
+constexpr int DPP_MIRROR = 0x140;      // row_mirror
+constexpr int DPP_BCAST15 = 0x142;     // row_bcast:15
+constexpr int DPP_BCAST31 = 0x143;     // row_bcast:31
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<DPP_SWAP1>(v);
+    v = dpp_max_u64<DPP_SWAP2>(v);
+    v = dpp_max_u64<DPP_HALF_MIRROR>(v);
+    v = dpp_max_u64<DPP_MIRROR>(v);
+    v = dpp_max_u64<DPP_BCAST15, 0xA>(v);
+    v = dpp_max_u64<DPP_BCAST31, 0xC>(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// maximum of non-negative floats (ordered like their bit patterns)
+__device__ __forceinline__ float wave_max_nonneg_f32(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = dpp_max_u32<DPP_SWAP1>(v);
+    v = dpp_max_u32<DPP_SWAP2>(v);
+    v = dpp_max_u32<DPP_HALF_MIRROR>(v);
+    v = dpp_max_u32<DPP_MIRROR>(v);
+    v = dpp_max_u32<DPP_BCAST15, 0xA>(v);
+    v = dpp_max_u32<DPP_BCAST31, 0xC>(v);
+    return __uint_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 
 // ---------------------------------------------------------------------------------------------

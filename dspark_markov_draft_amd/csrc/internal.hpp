@@ -32,6 +32,7 @@ struct DebugKnobs {
     int max_workgroups = 0;
     uint32_t spin_limit = 0;
     uint32_t wait_unset = 0;
+    uintptr_t stamps = 0;
 };
 DebugKnobs& debug_knobs();
 

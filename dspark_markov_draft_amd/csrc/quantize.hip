@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void quantize_w2_kernel(const void* __restrict
     const bool finite = isfinite(w.x) && isfinite(w.y) && isfinite(w.z) && isfinite(w.w);
     if (__any(!finite) && lane == 0) atomicOr(&g_quant_nonfinite, 1u);
     float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
-    a = wave_max_f32(a);
+    a = wave_max_nonneg_f32(a);
     uint32_t packed = 0;
     float sv = 0.0f;
     if (a > 0.0f) {

@@ -40,7 +40,7 @@ constexpr int REG_J = 2;                             // row sets held in VGPRs
 constexpr int LDS_J_MAX = 2;                         // row sets held in LDS
 constexpr int PF_J = REG_J + LDS_J_MAX;              // row sets whose base logits are prefetched
 constexpr int PF_DEPTH = 4;                          // requests of base logits in flight
-constexpr int GATHER_CHUNK = 4;                      // W1 rows in flight per wave
+constexpr int GATHER_CHUNK = 8;                      // W1 rows in flight per wave
 constexpr int ROW_CHUNKS = RANK / 16;                // 16-byte chunks per int8 row
 constexpr int LDS_ROWSET_BYTES = WALK_THREADS * RANK;  // one row per lane: 64 KiB
 constexpr int LDS_FIXED_BYTES = MAX_BS * RANK        // int8 codes of the gathered W1 rows
@@ -73,15 +73,34 @@ struct WalkParams {
     int stride;    // keys per workgroup slot
     uint32_t spin_limit;
     int wait_unset;
+    uint64_t* stamps;  // instrumented builds: [num workgroups][STAMPS_PER_WG] clock stamps
 };
 
-__device__ __forceinline__ int dot16(const int4 a, const int4 b, int acc) {
-    acc = __builtin_amdgcn_sdot4(a.x, b.x, acc, false);
-    acc = __builtin_amdgcn_sdot4(a.y, b.y, acc, false);
-    acc = __builtin_amdgcn_sdot4(a.z, b.z, acc, false);
-    acc = __builtin_amdgcn_sdot4(a.w, b.w, acc, false);
-    return acc;
+// Instrumented builds record the constant-rate device clock (s_memrealtime, 100 MHz) at these
+// points, per workgroup: kernel start, fill done, then per step: W1 codes ready, slice argmax
+// done, own slot stored, reductions done, result words seen.
+constexpr int STAMP_STEP0 = 2;
+constexpr int STAMPS_PER_STEP = 5;
+constexpr int STAMPS_PER_WG = STAMP_STEP0 + MAX_STEPS * STAMPS_PER_STEP;
+
+template <int TIMED>
+__device__ __forceinline__ void stamp(const WalkParams& p, int slot) {
+    if constexpr (TIMED) {
+        if (threadIdx.x == 0)
+            p.stamps[(size_t)blockIdx.x * STAMPS_PER_WG + slot] = __builtin_amdgcn_s_memrealtime();
+    }
 }
+
+// 16 int8 products of one 16-byte chunk into four independent int32 partial sums: v_dot4 has
+// ~20 cycles of latency against ~4-5 cycles of issue, so one wave per SIMD needs >= 5
+// independent accumulation chains to keep it busy.
+__device__ __forceinline__ void dot16x4(const int4 a, const int4 b, int4& acc) {
+    acc.x = __builtin_amdgcn_sdot4(a.x, b.x, acc.x, false);
+    acc.y = __builtin_amdgcn_sdot4(a.y, b.y, acc.y, false);
+    acc.z = __builtin_amdgcn_sdot4(a.z, b.z, acc.z, false);
+    acc.w = __builtin_amdgcn_sdot4(a.w, b.w, acc.w, false);
+}
+__device__ __forceinline__ int hsum(const int4 a) { return (a.x + a.y) + (a.z + a.w); }
 
 __device__ __forceinline__ uint32_t pack_codes(const float4 w, float inv) {
     const float v[4] = {w.x, w.y, w.z, w.w};
@@ -105,8 +124,9 @@ __device__ __forceinline__ void flag_error(uint32_t* err, int status) {
     __hip_atomic_store(err, (uint32_t)(-status), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int SAMPLE, int W1T>
+template <int SAMPLE, int W1T, int TIMED = 0>
 __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkParams p) {
+    stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
@@ -145,9 +165,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
             for (int c = 0; c < ROW_CHUNKS; ++c) dst[c ^ (tid & 15)] = src[c];
         }
     }
-    float sc[REG_J];
+    float sc[PF_J];  // scales of the register and LDS row sets
 #pragma unroll
-    for (int j = 0; j < REG_J; ++j) {
+    for (int j = 0; j < PF_J; ++j) {
         const int r = j * WALK_THREADS + tid;
         sc[j] = r < nrows ? p.scale[row0 + r] : 0.0f;
     }
@@ -174,6 +194,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
     for (int u = 0; u < PF_DEPTH; ++u)
         if (u < p.bs) load_base(pf[u], u, 0);
     __syncthreads();
+    stamp<TIMED>(p, 1);
 
     for (int t = 0; t < p.T; ++t) {
         // ---- gather W1[prev_b] (GATHER_CHUNK rows in flight per wave), int8 codes + scale ----
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
                 if (b < p.bs) {
                     const float4 w = wv[u];
                     float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
-                    a = wave_max_f32(a);
+                    a = wave_max_nonneg_f32(a);
                     const float inv = a > 0.0f ? 127.0f / a : 0.0f;
                     w1q[b * (RANK / 4) + lane] = pack_codes(w, inv);
                     if (lane == 0) s1[b] = a * (1.0f / 127.0f);
@@ -199,6 +220,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
             }
         }
         __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
         // ---- per request: int8 GEMV over the slice, logits, sampler, slice-local argmax -----
         for (int b0 = 0; b0 < p.bs; b0 += PF_DEPTH) {
@@ -237,21 +259,21 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
                     };
 
                     const int4* wq = reinterpret_cast<const int4*>(w1q + b * (RANK / 4));
-                    int acc[REG_J];
+                    int4 acc[REG_J];
 #pragma unroll
-                    for (int j = 0; j < REG_J; ++j) acc[j] = 0;
+                    for (int j = 0; j < REG_J; ++j) acc[j] = make_int4(0, 0, 0, 0);
 #pragma unroll
                     for (int c = 0; c < ROW_CHUNKS; ++c) {
                         const int4 w = wq[c];
 #pragma unroll
-                        for (int j = 0; j < REG_J; ++j) acc[j] = dot16(qr[j][c], w, acc[j]);
+                        for (int j = 0; j < REG_J; ++j) dot16x4(qr[j][c], w, acc[j]);
                     }
                     uint64_t best = 0;
 #pragma unroll
                     for (int j = 0; j < REG_J; ++j) {
                         const int r = j * WALK_THREADS + tid;
                         if (r < nrows) {
-                            const uint64_t key = finish(row0 + r, cur[j], sc[j], acc[j]);
+                            const uint64_t key = finish(row0 + r, cur[j], sc[j], hsum(acc[j]));
                             best = key > best ? key : best;
                         }
                     }
@@ -259,28 +281,38 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
                     for (int j = REG_J; j < p.nj; ++j) {
                         const int r = j * WALK_THREADS + tid;
                         if (r < nrows) {
-                            int a = 0;
+                            int4 a4 = make_int4(0, 0, 0, 0), b4 = make_int4(0, 0, 0, 0);
                             if (j < REG_J + p.lds_j) {
                                 const int4* src = reinterpret_cast<const int4*>(
                                     lds_rows + (size_t)((j - REG_J) * WALK_THREADS + tid) * RANK);
 #pragma unroll
-                                for (int c = 0; c < ROW_CHUNKS; ++c)
-                                    a = dot16(src[c ^ (tid & 15)], wq[c], a);
+                                for (int c = 0; c < ROW_CHUNKS; c += 2) {
+                                    dot16x4(src[c ^ (tid & 15)], wq[c], a4);
+                                    dot16x4(src[(c + 1) ^ (tid & 15)], wq[c + 1], b4);
+                                }
                             } else {
                                 const int4* src = reinterpret_cast<const int4*>(
                                     p.q + (int64_t)(row0 + r) * RANK);
 #pragma unroll 4
-                                for (int c = 0; c < ROW_CHUNKS; ++c) a = dot16(src[c], wq[c], a);
+                                for (int c = 0; c < ROW_CHUNKS; c += 2) {
+                                    dot16x4(src[c], wq[c], a4);
+                                    dot16x4(src[c + 1], wq[c + 1], b4);
+                                }
                             }
-                            float bv = 0.0f;
+                            const int a = hsum(a4) + hsum(b4);
+                            float bv = 0.0f, sv = 0.0f;
                             if (j < PF_J) {
 #pragma unroll
                                 for (int jj = REG_J; jj < PF_J; ++jj)
-                                    if (jj == j) bv = cur[jj];
+                                    if (jj == j) {
+                                        bv = cur[jj];
+                                        sv = sc[jj];
+                                    }
                             } else {
                                 bv = p.base[orow + row0 + r];
+                                sv = p.scale[row0 + r];
                             }
-                            const uint64_t key = finish(row0 + r, bv, p.scale[row0 + r], a);
+                            const uint64_t key = finish(row0 + r, bv, sv, a);
                             best = key > best ? key : best;
                         }
                     }
@@ -290,6 +322,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
             }
         }
         __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
 
         // the next step's first base logits load while the combine waits
         if (t + 1 < p.T) {
@@ -310,17 +343,25 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
                 }
                 st_dev(step_slots + (size_t)wg * p.stride + lane, k);
             }
+            stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 2);
             for (int b = wg; b < p.bs; b += nwg) {
                 uint64_t* col = step_slots + b;
                 uint64_t best = 0;
                 uint32_t spins = 0;
                 while (true) {
+                    // all slot loads of a round are in flight together (nwg <= 4 x 64)
+                    uint64_t v[MAX_WORKGROUPS / WAVE];
+#pragma unroll
+                    for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
+                        const int w = lane + k * WAVE;
+                        v[k] = w < nwg ? ld_dev(col + (size_t)w * p.stride) : 0;
+                    }
                     bool all = true;
                     best = 0;
-                    for (int w = lane; w < nwg; w += WAVE) {
-                        const uint64_t v = ld_dev(col + (size_t)w * p.stride);
-                        all = all && v != 0;
-                        best = v > best ? v : best;
+#pragma unroll
+                    for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
+                        all = all && (v[k] != 0 || lane + k * WAVE >= nwg);
+                        best = v[k] > best ? v[k] : best;
                     }
                     if (p.wait_unset)
                         all = all && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
@@ -341,8 +382,13 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
                     if (t + 1 < p.T) st_dev(p.result + t * MAX_BS + b, best);
                     if (t > 0) st_dev(p.result + (t - 1) * MAX_BS + b, 0);
                 }
-                for (int w = lane; w < nwg; w += WAVE) st_dev(col + (size_t)w * p.stride, 0);
+#pragma unroll
+                for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
+                    const int w = lane + k * WAVE;
+                    if (w < nwg) st_dev(col + (size_t)w * p.stride, 0);
+                }
             }
+            stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 3);
             if (t + 1 < p.T) {
                 uint64_t k = 0;
                 uint32_t spins = 0;
@@ -365,6 +411,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_kernel(const WalkP
                     tok[lane] = (int32_t)token;
                 }
             }
+            stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 4);
         }
         __syncthreads();
     }
@@ -417,7 +464,9 @@ int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, dspark_wa
 }
 
 template <int SAMPLE>
-static const void* pick_kernel(int w1_dtype) {
+static const void* pick_kernel(int w1_dtype, bool timed) {
+    if (timed)  // instrumented build: bf16 W1 only
+        return reinterpret_cast<const void*>(&dense_walk_kernel<SAMPLE, DT_BF16, 1>);
     switch (w1_dtype) {
         case DSPARK_F32: return reinterpret_cast<const void*>(&dense_walk_kernel<SAMPLE, DT_F32>);
         case DSPARK_BF16: return reinterpret_cast<const void*>(&dense_walk_kernel<SAMPLE, DT_BF16>);
@@ -459,8 +508,10 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan, hipStre
     const DebugKnobs& dbg = debug_knobs();
     p.spin_limit = dbg.spin_limit ? dbg.spin_limit : DEFAULT_SPIN_LIMIT;
     p.wait_unset = dbg.wait_unset ? 1 : 0;
+    p.stamps = reinterpret_cast<uint64_t*>(dbg.stamps);
+    const bool timed = p.stamps != nullptr && a.w1_dtype == DSPARK_BF16;
 
-    const void* fn = a.sample ? pick_kernel<1>(a.w1_dtype) : pick_kernel<0>(a.w1_dtype);
+    const void* fn = a.sample ? pick_kernel<1>(a.w1_dtype, timed) : pick_kernel<0>(a.w1_dtype, timed);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes) !=
         hipSuccess) {
         (void)hipGetLastError();

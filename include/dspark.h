@@ -182,12 +182,18 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *   DSPARK_DEBUG_SPIN_LIMIT: iterations of the grid-wide wait before DSPARK_ERR_TIMEOUT is
  *       recorded (0 = default);
  *   DSPARK_DEBUG_WAIT_UNSET_FLAG: non-zero makes the grid-wide waits also wait for a workspace
- *       flag that nothing sets, so each runs into its spin limit (for the timeout test).
+ *       flag that nothing sets, so each runs into its spin limit (for the timeout test);
+ *   DSPARK_DEBUG_STAMPS: a device address (8-byte aligned) of 256 x 82 uint64 words, or 0.
+ *       When set, dense walks with bf16 W1 run an instrumented build of the same kernel that
+ *       stores the 100 MHz device clock per workgroup: [0] start, [1] W2 resident, then per step
+ *       t at 2 + 5t: W1 codes ready, slice argmax done, own slot stored, reductions done,
+ *       result words seen. For profiling only.
  */
 enum dspark_debug_key {
     DSPARK_DEBUG_MAX_WORKGROUPS = 1,
     DSPARK_DEBUG_SPIN_LIMIT = 2,
-    DSPARK_DEBUG_WAIT_UNSET_FLAG = 3
+    DSPARK_DEBUG_WAIT_UNSET_FLAG = 3,
+    DSPARK_DEBUG_STAMPS = 4
 };
 int dspark_debug_set(int key, int64_t value);
 
