@@ -21,6 +21,8 @@ F32, BF16, F16 = 0, 1, 2
 RANK = 256
 MAX_STEPS, MAX_BS, MAX_V, MAX_TOPK = 16, 64, 270336, 2048
 DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG, DEBUG_STAMPS = 1, 2, 3, 4
+DEBUG_FORCE_PATH = 5
+PATH_DOT4, PATH_MFMA = 1, 2
 STAMPS_PER_WG = 82
 
 OK = 0
@@ -41,7 +43,10 @@ class WalkPlan(ctypes.Structure):
                 ("rows_per_workgroup", ctypes.c_int32), ("rows_in_registers", ctypes.c_int32),
                 ("rows_in_lds", ctypes.c_int32), ("rows_streamed", ctypes.c_int32),
                 ("resident_bytes", ctypes.c_int64), ("streamed_bytes", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int32)]
+                ("lds_bytes", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("reg_units", ctypes.c_int32), ("lds_units", ctypes.c_int32),
+                ("total_units", ctypes.c_int32), ("stage_bufs", ctypes.c_int32),
+                ("stage_stride", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

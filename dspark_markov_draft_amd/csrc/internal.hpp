@@ -33,6 +33,7 @@ struct DebugKnobs {
     uint32_t spin_limit = 0;
     uint32_t wait_unset = 0;
     uintptr_t stamps = 0;
+    int force_path = 0;
 };
 DebugKnobs& debug_knobs();
 

@@ -1,0 +1,264 @@
+// Pieces shared by the two dense-walk kernels (lane-per-row v_dot4 for one request, MFMA for
+// several): launch parameters, clock stamps, the per-step W1 gather, and the grid-wide combine.
+#pragma once
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace dspark {
+
+constexpr int WALK_THREADS = 256;
+constexpr int WALK_WAVES = WALK_THREADS / WAVE;  // 4: one wave per SIMD
+constexpr int W1Q_BYTES = MAX_BS * RANK;         // int8 codes of the gathered W1 rows (LDS)
+constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workgroup per CU
+constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;
+
+struct WalkParams {
+    const int8_t* q;
+    const float* scale;
+    const void* w1;
+    const float* base;
+    const int32_t* start;
+    int32_t* tokens;
+    float* out_logits;
+    uint16_t* draft_logits;
+    const uint64_t* seeds;
+    const int64_t* positions;
+    const float* temps;
+    uint64_t* result;       // [16][64] winning keys
+    uint64_t* slots;        // [T][num workgroups][stride] per-workgroup keys
+    uint32_t* err;
+    const uint32_t* never;  // a workspace word nothing writes (test hook)
+    uint64_t* stamps;       // instrumented builds: [num workgroups][STAMPS_PER_WG]
+    int bs, T, V;
+    int rows_per_wg;        // contiguous W2 rows per workgroup (the last may own fewer)
+    int reg_units;          // register-resident row sets (dot4) or tiles per wave (MFMA)
+    int lds_units;          // LDS-resident row sets (dot4) or tiles per wave (MFMA)
+    int total_units;        // all row sets / tiles per wave; the rest beyond reg+lds stream
+    int stride;             // keys per workgroup slot
+    int vec_ok;             // base / draft_logits rows allow float4 and 4 x bf16 accesses
+    int stage_bufs;         // MFMA: LDS buffers for the base logits of a 16-request tile (0-2)
+    int stage_stride;       // MFMA: floats per request row in a staging buffer
+    uint32_t spin_limit;
+    int wait_unset;
+};
+
+// Instrumented builds record the constant-rate device clock (s_memrealtime, 100 MHz) per
+// workgroup: kernel start, W2 resident, then per step: W1 codes ready, slice argmax done, own
+// slot stored, reductions done, result words seen.
+constexpr int STAMP_STEP0 = 2;
+constexpr int STAMPS_PER_STEP = 5;
+constexpr int STAMPS_PER_WG = STAMP_STEP0 + MAX_STEPS * STAMPS_PER_STEP;
+
+template <int TIMED>
+__device__ __forceinline__ void stamp(const WalkParams& p, int slot) {
+    if constexpr (TIMED) {
+        if (threadIdx.x == 0)
+            p.stamps[(size_t)blockIdx.x * STAMPS_PER_WG + slot] = __builtin_amdgcn_s_memrealtime();
+    }
+}
+
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_error(uint32_t* err, int status) {
+    __hip_atomic_store(err, (uint32_t)(-status), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The gathered W1 row of request b as int8 codes in LDS: 256 bytes, whose 16-byte chunk ch
+// sits at position ch ^ (b & 15). A broadcast read of one chunk is unaffected; a read of chunk
+// ch for 16 consecutive requests (the MFMA B operand) spreads over all LDS banks.
+__device__ __forceinline__ int w1q_chunk_dword(int b, int ch) { return b * (RANK / 4) + ((ch ^ (b & 15)) << 2); }
+
+__device__ __forceinline__ uint32_t pack_codes(const float4 w, float inv) {
+    const float v[4] = {w.x, w.y, w.z, w.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float r = rintf(v[i] * inv);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        packed |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * i);
+    }
+    return packed;
+}
+
+// maximum of non-negative floats over each 16-lane row of the wave (all 16 lanes get it)
+__device__ __forceinline__ float row16_max_nonneg_f32(float x) {
+    uint32_t v = __float_as_uint(x);
+    v = dpp_max_u32<DPP_SWAP1>(v);
+    v = dpp_max_u32<DPP_SWAP2>(v);
+    v = dpp_max_u32<DPP_HALF_MIRROR>(v);
+    v = dpp_max_u32<DPP_MIRROR>(v);
+    return __uint_as_float(v);
+}
+
+// Per step: W1[prev_b] for every request, as int8 codes with one absmax scale per row
+// (s1[b] = absmax / 127, codes = rint(w * 127 / absmax)). Up to 4 requests: one per wave, 64
+// lanes on the row. More: sixteen lanes share a row: lane
+// (quarter q, ql) holds elements 16 ql .. 16 ql + 15 of request 4 (iteration * 4 + wave) + q,
+// so one wave instruction serves 4 requests; all of a wave's rows are loaded before any is used.
+constexpr int GATHER_ITERS = MAX_BS / (WALK_WAVES * 4);   // 4 request groups per wave at bs 64
+
+template <int W1T>
+__device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32_t* tok,
+                                                uint32_t* w1q, float* s1, int wave, int lane) {
+    if (p.bs <= WALK_WAVES) {
+        // at most one request per wave: all 64 lanes on one row (elements 4l .. 4l+3)
+        const int b = wave;
+        if (b < p.bs) {
+            const float4 w = load4_as_f32<W1T>(p.w1, (int64_t)tok[b] * RANK + lane * 4);
+            float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+            a = wave_max_nonneg_f32(a);
+            const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+            w1q[w1q_chunk_dword(b, lane >> 2) + (lane & 3)] = pack_codes(w, inv);
+            if (lane == 0) s1[b] = a * (1.0f / 127.0f);
+        }
+        return;
+    }
+    const int q = lane >> 4, ql = lane & 15;
+    float4 wv[GATHER_ITERS][4];
+#pragma unroll
+    for (int it = 0; it < GATHER_ITERS; ++it) {
+        const int b = (it * WALK_WAVES + wave) * 4 + q;
+        if ((it * WALK_WAVES + wave) * 4 < p.bs && b < p.bs) {
+            const int64_t e = (int64_t)tok[b] * RANK + ql * 16;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wv[it][k] = load4_as_f32<W1T>(p.w1, e + 4 * k);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < GATHER_ITERS; ++it) {
+        if ((it * WALK_WAVES + wave) * 4 < p.bs) {    // wave-uniform: some request of it exists
+            const int b = (it * WALK_WAVES + wave) * 4 + q;
+            float a = 0.0f;
+            if (b < p.bs) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    a = fmaxf(a, fmaxf(fmaxf(fabsf(wv[it][k].x), fabsf(wv[it][k].y)),
+                                       fmaxf(fabsf(wv[it][k].z), fabsf(wv[it][k].w))));
+            }
+            a = row16_max_nonneg_f32(a);
+            if (b < p.bs) {
+                const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+                uint4 codes;
+                codes.x = pack_codes(wv[it][0], inv);
+                codes.y = pack_codes(wv[it][1], inv);
+                codes.z = pack_codes(wv[it][2], inv);
+                codes.w = pack_codes(wv[it][3], inv);
+                *reinterpret_cast<uint4*>(w1q + w1q_chunk_dword(b, ql)) = codes;
+                if (ql == 0) s1[b] = a * (1.0f / 127.0f);
+            }
+        }
+    }
+}
+
+// Start tokens into LDS, replacing any outside [0, V) by 0 (a documented precondition; this
+// keeps every later gather in bounds) and recording DSPARK_ERR_INVALID_ARG.
+__device__ __forceinline__ void load_start_tokens(const WalkParams& p, int32_t* tok) {
+    const int tid = threadIdx.x;
+    if (tid < p.bs) {
+        int s = p.start[tid];
+        if (s < 0 || s >= p.V) {
+            if (blockIdx.x == 0) flag_error(p.err, DSPARK_ERR_INVALID_ARG);
+            s = 0;
+        }
+        tok[tid] = s;
+    }
+}
+
+// Grid-wide combine of step t, run by wave 0 (all 64 lanes). `key` (lanes < bs) is this
+// workgroup's best key for request `lane`. Each workgroup stores its keys into its own slot;
+// the workgroup owning request b (b % num workgroups) waits for all slots of b, takes their
+// maximum, writes the token and publishes the winning key in result[t][b] (not for the last
+// step), clears the slots it read and its result word of step t-1 (every workgroup read that
+// before filling its slot of step t); then every workgroup waits for the result words of step
+// t and writes the new tokens into `tok`. All waits are bounded by the spin limit.
+template <int TIMED>
+__device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_t key,
+                                             int32_t* tok, int lane) {
+    const int nwg = gridDim.x;
+    const int wg = blockIdx.x;
+    uint64_t* step_slots = p.slots + (size_t)t * nwg * p.stride;
+    if (lane < p.bs) st_dev(step_slots + (size_t)wg * p.stride + lane, key);
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 2);
+
+    for (int b = wg; b < p.bs; b += nwg) {
+        uint64_t* col = step_slots + b;
+        uint64_t best = 0;
+        uint32_t spins = 0;
+        while (true) {
+            // all slot loads of a round are in flight together (nwg <= 4 x 64)
+            uint64_t v[MAX_WORKGROUPS / WAVE];
+#pragma unroll
+            for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
+                const int w = lane + k * WAVE;
+                v[k] = w < nwg ? ld_dev(col + (size_t)w * p.stride) : 0;
+            }
+            bool all = true;
+            best = 0;
+#pragma unroll
+            for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
+                all = all && (v[k] != 0 || lane + k * WAVE >= nwg);
+                best = v[k] > best ? v[k] : best;
+            }
+            if (p.wait_unset)
+                all = all && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) != 0;
+            if (__all(all)) break;
+            if (++spins > p.spin_limit) {
+                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        best = wave_max_u64(best);
+        if (best == 0) best = 1;  // only after a timeout: keep the result word non-zero
+        uint32_t token = key_index(best);
+        if (token >= (uint32_t)p.V) token = 0;
+        if (lane == 0) {
+            p.tokens[b * p.T + t] = (int32_t)token;
+            if (t + 1 < p.T) st_dev(p.result + t * MAX_BS + b, best);
+            if (t > 0) st_dev(p.result + (t - 1) * MAX_BS + b, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
+            const int w = lane + k * WAVE;
+            if (w < nwg) st_dev(col + (size_t)w * p.stride, 0);
+        }
+    }
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 3);
+
+    if (t + 1 < p.T) {
+        uint64_t k = 0;
+        uint32_t spins = 0;
+        while (true) {
+            bool ok = true;
+            if (lane < p.bs) {
+                k = ld_dev(p.result + t * MAX_BS + lane);
+                ok = k != 0;
+            }
+            if (__all(ok)) break;
+            if (++spins > p.spin_limit) {
+                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane < p.bs) {
+            uint32_t token = key_index(k);
+            if (token >= (uint32_t)p.V) token = 0;
+            tok[lane] = (int32_t)token;
+        }
+    }
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 4);
+}
+
+// Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0/1; w1t: DT_*).
+const void* dot4_walk_kernel(int sample, int w1t, bool timed);
+const void* mfma_walk_kernel(int sample, int w1t, bool timed);
+int mfma_fixed_lds_bytes(int rows_per_wg);
+
+}  // namespace dspark

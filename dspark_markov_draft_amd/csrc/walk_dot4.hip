@@ -1,0 +1,252 @@
+// Dense walk, lane-per-row v_dot4 kernel (used for a single request, where every row of W2 is
+// multiplied by one W1 row: a GEMV, which a matrix core would run at 1/16 use).
+//
+// What it computes (vLLM PR #62958, int8 DSpark Markov walk, Overview and Details; vLLM PR
+// #64476, Claims): for every request b and step t,
+//     l[v]  = base[b,t,v] + s[v] * s1 * sum_k q[v,k] * q1[k],   q1/s1 = int8 codes of W1[prev_b]
+//     greedy: token = argmax_v l[v];
+//     sample: lb = bf16(l), token = argmax_v (lb[v] / temp_b + Gumbel(Philox(seed_b, P, v)))
+// with torch.argmax order, and token becomes prev_b for step t+1.
+//
+// One workgroup of 4 waves (one wave per SIMD) per compute unit owns a contiguous slice of W2
+// rows for the whole call; each lane owns whole rows, so a row's 256-term dot product needs no
+// cross-lane reduction:
+//   * the first 2 x 256 rows of the slice live in VGPRs (2 rows x 64 dwords per lane),
+//   * the next up to 2 x 256 rows live in LDS (16-byte chunks XOR-swizzled by row, so the
+//     lanes of a wave reading one chunk index hit different banks),
+//   * rows beyond are re-read from memory at every step.
+// The W1 codes are LDS broadcasts; v_dot4_i32_i8 accumulates exact int32 sums in four
+// independent chains per row (its latency is ~20 cycles, its issue ~4); scale, base logit and
+// sampler finish each row; wave-wide and workgroup-wide maxima of 64-bit argmax keys give the
+// slice's best, and combine_step() combines the slices across the grid.
+#include "walk_common.hpp"
+
+namespace dspark {
+
+constexpr int REG_J = 2;                 // row sets held in VGPRs
+constexpr int LDS_J_MAX = 2;             // row sets held in LDS
+constexpr int PF_J = REG_J + LDS_J_MAX;  // row sets whose base logits are prefetched
+constexpr int PF_DEPTH = 4;              // requests of base logits in flight
+constexpr int ROW_CHUNKS = RANK / 16;    // 16-byte chunks per int8 row
+
+__device__ __forceinline__ void dot16x4(const int4 a, const int4 b, int4& acc) {
+    acc.x = __builtin_amdgcn_sdot4(a.x, b.x, acc.x, false);
+    acc.y = __builtin_amdgcn_sdot4(a.y, b.y, acc.y, false);
+    acc.z = __builtin_amdgcn_sdot4(a.z, b.z, acc.z, false);
+    acc.w = __builtin_amdgcn_sdot4(a.w, b.w, acc.w, false);
+}
+__device__ __forceinline__ int hsum(const int4 a) { return (a.x + a.y) + (a.z + a.w); }
+
+template <int SAMPLE, int W1T, int TIMED>
+__global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const WalkParams p) {
+    stamp<TIMED>(p, 0);
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wave = tid / WAVE;
+    const int row0 = blockIdx.x * p.rows_per_wg;
+    const int nrows = min(p.rows_per_wg, p.V - row0);
+    const int nj = p.total_units;
+    const int lds_j = p.lds_units;
+
+    unsigned char* lds_rows = smem;
+    uint32_t* w1q = reinterpret_cast<uint32_t*>(smem + (size_t)lds_j * WALK_THREADS * RANK);
+    float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
+    uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
+    int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
+
+    // ---- fill: this workgroup's W2 rows into VGPRs and LDS, their scales into VGPRs --------
+    int4 qr[REG_J][ROW_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < REG_J; ++j) {
+        const int r = j * WALK_THREADS + tid;
+        if (r < nrows) {
+            const int4* src = reinterpret_cast<const int4*>(p.q + (int64_t)(row0 + r) * RANK);
+#pragma unroll
+            for (int c = 0; c < ROW_CHUNKS; ++c) qr[j][c] = src[c];
+        } else {
+#pragma unroll
+            for (int c = 0; c < ROW_CHUNKS; ++c) qr[j][c] = make_int4(0, 0, 0, 0);
+        }
+    }
+    for (int j = 0; j < lds_j; ++j) {
+        const int r = (REG_J + j) * WALK_THREADS + tid;
+        if (r < nrows) {
+            const int4* src = reinterpret_cast<const int4*>(p.q + (int64_t)(row0 + r) * RANK);
+            int4* dst = reinterpret_cast<int4*>(lds_rows + (size_t)(j * WALK_THREADS + tid) * RANK);
+#pragma unroll
+            for (int c = 0; c < ROW_CHUNKS; ++c) dst[c ^ (tid & 15)] = src[c];
+        }
+    }
+    float sc[PF_J];  // scales of the register and LDS row sets
+#pragma unroll
+    for (int j = 0; j < PF_J; ++j) {
+        const int r = j * WALK_THREADS + tid;
+        sc[j] = r < nrows ? p.scale[row0 + r] : 0.0f;
+    }
+    load_start_tokens(p, tok);
+
+    // base logits of the first PF_J row sets, PF_DEPTH requests ahead of their use
+    float pf[PF_DEPTH][PF_J];
+    auto load_base = [&](float (&dst)[PF_J], int b, int t) {
+        const float* br = p.base + ((int64_t)b * p.T + t) * p.V + row0;
+#pragma unroll
+        for (int j = 0; j < PF_J; ++j) {
+            const int r = j * WALK_THREADS + tid;
+            dst[j] = r < nrows ? br[r] : 0.0f;
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < PF_DEPTH; ++u)
+        if (u < p.bs) load_base(pf[u], u, 0);
+    __syncthreads();
+    stamp<TIMED>(p, 1);
+
+    for (int t = 0; t < p.T; ++t) {
+        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane);
+        __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
+
+        for (int b0 = 0; b0 < p.bs; b0 += PF_DEPTH) {
+#pragma unroll
+            for (int u = 0; u < PF_DEPTH; ++u) {
+                const int b = b0 + u;
+                if (b < p.bs) {
+                    float cur[PF_J];
+#pragma unroll
+                    for (int j = 0; j < PF_J; ++j) cur[j] = pf[u][j];
+                    if (b + PF_DEPTH < p.bs) load_base(pf[u], b + PF_DEPTH, t);
+
+                    const float sb = s1[b];
+                    const int64_t orow = ((int64_t)b * p.T + t) * p.V;
+                    uint64_t seed = 0, P = 0;
+                    float temp = 1.0f;
+                    if constexpr (SAMPLE) {
+                        seed = p.seeds[b];
+                        P = (uint64_t)(p.positions ? p.positions[b] : 0) + (uint64_t)t;
+                        temp = p.temps[b];
+                    }
+                    // logit of row v -> output store and argmax key
+                    auto finish = [&](int v, float base_v, float scale_v, int acc) -> uint64_t {
+                        const float l = base_v + (scale_v * sb) * (float)acc;
+                        if constexpr (!SAMPLE) {
+                            if (p.out_logits) p.out_logits[orow + v] = l;
+                            return argmax_key(l, (uint32_t)v);
+                        } else {
+                            const uint32_t h = bf16_bits(l);
+                            p.draft_logits[orow + v] = (uint16_t)h;
+                            float x = bf16_value(h);
+                            if (temp != 1.0f) x = x / temp;
+                            const float g = gumbel_from_word(noise_word(seed, P, (uint32_t)v));
+                            return argmax_key(x + g, (uint32_t)v);
+                        }
+                    };
+
+                    const int4* wq = reinterpret_cast<const int4*>(w1q + b * (RANK / 4));
+                    const int sw = b & 15;  // chunk c of this request's codes is at c ^ sw
+                    int4 acc[REG_J];
+#pragma unroll
+                    for (int j = 0; j < REG_J; ++j) acc[j] = make_int4(0, 0, 0, 0);
+#pragma unroll
+                    for (int c = 0; c < ROW_CHUNKS; ++c) {
+                        const int4 w = wq[c ^ sw];
+#pragma unroll
+                        for (int j = 0; j < REG_J; ++j) dot16x4(qr[j][c], w, acc[j]);
+                    }
+                    uint64_t best = 0;
+#pragma unroll
+                    for (int j = 0; j < REG_J; ++j) {
+                        const int r = j * WALK_THREADS + tid;
+                        if (r < nrows) {
+                            const uint64_t key = finish(row0 + r, cur[j], sc[j], hsum(acc[j]));
+                            best = key > best ? key : best;
+                        }
+                    }
+                    // row sets beyond the registers: LDS-resident, then streamed from memory
+                    for (int j = REG_J; j < nj; ++j) {
+                        const int r = j * WALK_THREADS + tid;
+                        if (r < nrows) {
+                            int4 a4 = make_int4(0, 0, 0, 0), b4 = make_int4(0, 0, 0, 0);
+                            if (j < REG_J + lds_j) {
+                                const int4* src = reinterpret_cast<const int4*>(
+                                    lds_rows + (size_t)((j - REG_J) * WALK_THREADS + tid) * RANK);
+#pragma unroll
+                                for (int c = 0; c < ROW_CHUNKS; c += 2) {
+                                    dot16x4(src[c ^ (tid & 15)], wq[c ^ sw], a4);
+                                    dot16x4(src[(c + 1) ^ (tid & 15)], wq[(c + 1) ^ sw], b4);
+                                }
+                            } else {
+                                const int4* src = reinterpret_cast<const int4*>(
+                                    p.q + (int64_t)(row0 + r) * RANK);
+#pragma unroll 4
+                                for (int c = 0; c < ROW_CHUNKS; c += 2) {
+                                    dot16x4(src[c], wq[c ^ sw], a4);
+                                    dot16x4(src[c + 1], wq[(c + 1) ^ sw], b4);
+                                }
+                            }
+                            const int a = hsum(a4) + hsum(b4);
+                            float bv = 0.0f, sv = 0.0f;
+                            if (j < PF_J) {
+#pragma unroll
+                                for (int jj = REG_J; jj < PF_J; ++jj)
+                                    if (jj == j) {
+                                        bv = cur[jj];
+                                        sv = sc[jj];
+                                    }
+                            } else {
+                                bv = p.base[orow + row0 + r];
+                                sv = p.scale[row0 + r];
+                            }
+                            const uint64_t key = finish(row0 + r, bv, sv, a);
+                            best = key > best ? key : best;
+                        }
+                    }
+                    best = wave_max_u64(best);
+                    if (lane == 0) wkeys[wave * MAX_BS + b] = best;
+                }
+            }
+        }
+        __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
+
+        // the next step's first base logits load while the combine waits
+        if (t + 1 < p.T) {
+#pragma unroll
+            for (int u = 0; u < PF_DEPTH; ++u)
+                if (u < p.bs) load_base(pf[u], u, t + 1);
+        }
+        if (wave == 0) {
+            uint64_t k = 0;
+            if (lane < p.bs) {
+                k = wkeys[lane];
+#pragma unroll
+                for (int w = 1; w < WALK_WAVES; ++w) {
+                    const uint64_t o = wkeys[w * MAX_BS + lane];
+                    k = o > k ? o : k;
+                }
+            }
+            combine_step<TIMED>(p, t, k, tok, lane);
+        }
+        __syncthreads();
+    }
+}
+
+const void* dot4_walk_kernel(int sample, int w1t, bool timed) {
+#define DSPARK_DOT4(S, W, TI) reinterpret_cast<const void*>(&dense_walk_dot4_kernel<S, W, TI>)
+    if (timed) return sample ? DSPARK_DOT4(1, DT_BF16, 1) : DSPARK_DOT4(0, DT_BF16, 1);
+    if (sample) {
+        switch (w1t) {
+            case DT_F32: return DSPARK_DOT4(1, DT_F32, 0);
+            case DT_BF16: return DSPARK_DOT4(1, DT_BF16, 0);
+            default: return DSPARK_DOT4(1, DT_F16, 0);
+        }
+    }
+    switch (w1t) {
+        case DT_F32: return DSPARK_DOT4(0, DT_F32, 0);
+        case DT_BF16: return DSPARK_DOT4(0, DT_BF16, 0);
+        default: return DSPARK_DOT4(0, DT_F16, 0);
+    }
+#undef DSPARK_DOT4
+}
+
+}  // namespace dspark

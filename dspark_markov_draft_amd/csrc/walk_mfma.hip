@@ -1,0 +1,280 @@
+// Dense walk, matrix-core kernel (used for two or more requests, where each step is a GEMM of
+// W2 [V x 256] with the requests' W1 codes [256 x bs]).
+//
+// What it computes: as the v_dot4 kernel (vLLM PR #62958, int8 DSpark Markov walk, Overview
+// and Details; vLLM PR #64476, Claims): l[v] = base[b,t,v] + s[v] * s1_b * sum_k q[v,k] q1_b[k],
+// then the first-maximum argmax (greedy) or the Gumbel-max of bf16(l) / temp + noise (sample).
+//
+// v_mfma_i32_16x16x64_i8 multiplies a 16 x 64 int8 tile by a 64 x 16 int8 tile into 16 x 16
+// int32. Lane l supplies row l % 16 of A and column l % 16 of B, each for the k-chunk of lane
+// group l / 16, and receives D[(l / 16) * 4 + i][l % 16], i < 4. Here A = 16 rows of W2 and
+// B = the W1 codes of 16 requests; lane group g carries bytes g*64 + kb*16 .. +15 of the row in
+// K-block kb, so over the four K-blocks a lane holds one contiguous 64-byte quarter of its row.
+//
+// The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves: each wave keeps up
+// to 8 tiles (128 rows) in VGPRs as ready A operands, further tiles in LDS (laid out so a
+// K-block read is 64 consecutive 16-byte lane slots), and streams any rest from memory. Per
+// step and 16-request tile: 4 MFMAs per W2 tile; each lane then finishes 4 consecutive rows of
+// one request (one float4 of base logits, one Philox call for the 4 noise words), keeps its
+// best key, and the workgroup's best per request goes to combine_step().
+//
+// The base logits of a 16-request tile (16 rows of the workgroup's slice) are copied into LDS
+// by global_load_lds DMA before the tile is used (one latency per request tile instead of one
+// per W2 tile): with two staging buffers the next request tile's copy runs under the current
+// one's compute, and the first tile of step t+1 is fetched while the combine of step t waits.
+// Staging rows are padded to an odd number of 16-byte units, so the 16 requests a wave reads
+// at once fall into different LDS banks. The kernel needs V % 4 == 0 and 16-byte aligned rows
+// (the host runs the v_dot4 kernel otherwise): every 4-row group is then wholly inside or
+// wholly outside the slice, and its base logits, scales and outputs move as one vector.
+#include "walk_common.hpp"
+
+namespace dspark {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+constexpr int TILE_ROWS = 16;
+constexpr int NT_REG = 8;                       // W2 tiles per wave held in VGPRs
+constexpr int TILE_LDS_BYTES = 4 * WAVE * 16;   // one tile: 4 K-blocks x 64 lanes x 16 bytes
+constexpr int MAX_RT = MAX_BS / 16;             // 16-request tiles
+constexpr int LKEY_BYTES = WALK_WAVES * MAX_RT * WAVE * 8;
+
+// dynamic LDS besides the W2 tiles: W1 codes, their scales, row scales, lane keys, tokens
+__host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
+    return W1Q_BYTES + MAX_BS * 4 + ((rows_per_wg * 4 + 15) / 16) * 16 + LKEY_BYTES + MAX_BS * 4;
+}
+
+template <int SAMPLE, int W1T, int TIMED>
+__global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const WalkParams p) {
+    stamp<TIMED>(p, 0);
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wave = tid / WAVE;
+    const int c = lane & 15;   // A: row within the tile; B/D: request within the request tile
+    const int g = lane >> 4;   // k-chunk group; D: rows g*4 .. g*4+3
+    const int row0 = blockIdx.x * p.rows_per_wg;
+    const int nrows = min(p.rows_per_wg, p.V - row0);
+    const int vend = row0 + nrows;
+    const int ntiles = (nrows + TILE_ROWS - 1) / TILE_ROWS;   // tiles of this workgroup
+    const int ntw = p.total_units;                             // tile slots per wave
+    const int lds_tw = p.lds_units;
+
+    unsigned char* lds_tiles = smem;
+    float* stage = reinterpret_cast<float*>(smem + (size_t)lds_tw * WALK_WAVES * TILE_LDS_BYTES);
+    const int ss = p.stage_stride;
+    const int nbuf = p.stage_bufs;   // 1 or 2 (the host guarantees at least one)
+    uint32_t* w1q = reinterpret_cast<uint32_t*>(stage + (size_t)p.stage_bufs * 16 * ss);
+    float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
+    float* scl = s1 + MAX_BS;
+    uint64_t* lkeys = reinterpret_cast<uint64_t*>(scl + ((p.rows_per_wg * 4 + 15) / 16) * 4);
+    int32_t* tok = reinterpret_cast<int32_t*>(lkeys + WALK_WAVES * MAX_RT * WAVE);
+
+    // ---- fill: W2 tiles as A operands (VGPRs, then LDS), row scales into LDS ---------------
+    auto load_a = [&](int tl, int kb) -> v4i {
+        const int row = row0 + tl * TILE_ROWS + c;
+        if (row >= vend) return (v4i){0, 0, 0, 0};
+        return *reinterpret_cast<const v4i*>(p.q + (int64_t)row * RANK + g * 64 + kb * 16);
+    };
+    v4i qa[NT_REG][4];
+#pragma unroll
+    for (int tw = 0; tw < NT_REG; ++tw) {
+        const int tl = tw * WALK_WAVES + wave;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qa[tw][kb] = tl < ntiles ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
+    }
+    for (int tw = NT_REG; tw < NT_REG + lds_tw; ++tw) {
+        const int tl = tw * WALK_WAVES + wave;
+        if (tl < ntiles) {
+            v4i* dst = reinterpret_cast<v4i*>(
+                lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) * TILE_LDS_BYTES);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) dst[kb * WAVE + lane] = load_a(tl, kb);
+        }
+    }
+    for (int i = tid; i < ntiles * TILE_ROWS; i += WALK_THREADS)
+        scl[i] = i < nrows ? p.scale[row0 + i] : 0.0f;
+    load_start_tokens(p, tok);
+    __syncthreads();
+    stamp<TIMED>(p, 1);
+
+    const int nrt = (p.bs + 15) / 16;
+
+    // DMA of base[rt*16 .. rt*16+15, t, row0 .. vend) into staging buffer `buf`: each wave
+    // instruction moves 64 lanes x 16 bytes to consecutive LDS; row segments are whole 16-byte
+    // units (V and row0 are multiples of 4) and lanes past a segment's end stay idle.
+    const int units = nrows / 4;
+    auto stage_base = [&](int rt, int t, int buf) {
+        for (int r = 0; r < 16; ++r) {
+            const int b = rt * 16 + r;
+            if (b >= p.bs) break;
+            const float* src = p.base + ((int64_t)b * p.T + t) * p.V + row0;
+            float* dst = stage + (size_t)(buf * 16 + r) * ss;
+            for (int u0 = wave * WAVE; u0 < units; u0 += WALK_THREADS) {
+                if (u0 + lane < units)
+                    __builtin_amdgcn_global_load_lds((global_void_ptr)(src + 4 * (u0 + lane)),
+                                                     (lds_void_ptr)(dst + 4 * u0), 16, 0, 0);
+            }
+        }
+    };
+    stage_base(0, 0, 0);
+
+    for (int t = 0; t < p.T; ++t) {
+        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane);
+        __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
+
+        for (int rt = 0; rt < nrt; ++rt) {
+            const int buf = nbuf == 2 ? (rt & 1) : 0;
+            if (nbuf == 1 && rt > 0) {
+                __syncthreads();   // every wave is done with the previous request tile
+                stage_base(rt, t, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed ...
+            __syncthreads();                  // ... and every other wave's
+            if (nbuf == 2 && rt + 1 < nrt) stage_base(rt + 1, t, buf ^ 1);
+            const float* sbase = stage + (size_t)(buf * 16 + c) * ss;
+            const int b = rt * 16 + c;
+            const bool vb = b < p.bs;
+            v4i bop[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                bop[kb] = vb ? *reinterpret_cast<const v4i*>(w1q + w1q_chunk_dword(b, g * 4 + kb))
+                             : (v4i){0, 0, 0, 0};
+            const float sb = vb ? s1[b] : 0.0f;
+            const int64_t orow = ((int64_t)(vb ? b : 0) * p.T + t) * p.V;
+            uint64_t seed = 0, P = 0;
+            float temp = 1.0f;
+            if constexpr (SAMPLE) {
+                if (vb) {
+                    seed = p.seeds[b];
+                    P = (uint64_t)(p.positions ? p.positions[b] : 0) + (uint64_t)t;
+                    temp = p.temps[b];
+                }
+            }
+            uint64_t best = 0;
+
+            // Rows vt .. vt+3 of request b from the accumulator of one tile. The group is wholly
+            // inside the slice or wholly past its end (partial last tile); past-the-end groups and
+            // requests past bs read in-bounds LDS, are computed, and are dropped by a zero key.
+            auto finish4 = [&](const v4i acc, int vt) {
+                const int off = vt - row0;                       // < ntiles * 16 <= rows_per_wg
+                const float4 sv = *reinterpret_cast<const float4*>(scl + off);
+                const float4 bv = *reinterpret_cast<const float4*>(sbase + off);
+                const bool ok = vb && vt < vend;
+                float l[4];
+                l[0] = bv.x + (sv.x * sb) * (float)acc[0];
+                l[1] = bv.y + (sv.y * sb) * (float)acc[1];
+                l[2] = bv.z + (sv.z * sb) * (float)acc[2];
+                l[3] = bv.w + (sv.w * sb) * (float)acc[3];
+                uint64_t key[4];
+                if constexpr (!SAMPLE) {
+                    if (p.out_logits != nullptr && ok)
+                        *reinterpret_cast<float4*>(p.out_logits + orow + vt) =
+                            make_float4(l[0], l[1], l[2], l[3]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) key[i] = argmax_key(l[i], (uint32_t)(vt + i));
+                } else {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) h[i] = bf16_bits(l[i]);
+                    if (ok)
+                        *reinterpret_cast<uint2*>(p.draft_logits + orow + vt) =
+                            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                    // vt is a multiple of 4: one Philox call yields the words of all 4 rows
+                    const uint4 w = philox4x32_10((uint32_t)vt >> 2, (uint32_t)P, (uint32_t)(P >> 32),
+                                                  0u, (uint32_t)seed, (uint32_t)(seed >> 32));
+                    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = bf16_value(h[i]);
+                        if (temp != 1.0f) x = x / temp;
+                        key[i] = argmax_key(x + gumbel_from_word(words[i]), (uint32_t)(vt + i));
+                    }
+                }
+                const uint64_t keep = ok ? ~0ull : 0ull;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint64_t k = key[i] & keep;
+                    best = k > best ? k : best;
+                }
+            };
+
+#pragma unroll
+            for (int tw = 0; tw < NT_REG; ++tw) {
+                const int tl = tw * WALK_WAVES + wave;
+                if (tl < ntiles) {
+                    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb], acc, 0, 0, 0);
+                    finish4(acc, row0 + tl * TILE_ROWS + g * 4);
+                }
+            }
+            for (int tw = NT_REG; tw < ntw; ++tw) {
+                const int tl = tw * WALK_WAVES + wave;
+                if (tl < ntiles) {
+                    v4i acc = {0, 0, 0, 0};
+                    if (tw < NT_REG + lds_tw) {
+                        const v4i* src = reinterpret_cast<const v4i*>(
+                            lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) * TILE_LDS_BYTES);
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+                            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane], bop[kb],
+                                                                        acc, 0, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+                            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(load_a(tl, kb), bop[kb], acc,
+                                                                        0, 0, 0);
+                    }
+                    finish4(acc, row0 + tl * TILE_ROWS + g * 4);
+                }
+            }
+            lkeys[(wave * MAX_RT + rt) * WAVE + lane] = best;
+        }
+        __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
+        // the first request tile of step t+1 streams in while the combine of step t waits
+        if (nbuf && t + 1 < p.T) stage_base(0, t + 1, 0);
+
+        if (wave == 0) {
+            uint64_t k = 0;
+            if (lane < p.bs) {
+                const int rt = lane >> 4, cc = lane & 15;
+#pragma unroll
+                for (int w = 0; w < WALK_WAVES; ++w)
+#pragma unroll
+                    for (int gg = 0; gg < 4; ++gg) {
+                        const uint64_t o = lkeys[(w * MAX_RT + rt) * WAVE + gg * 16 + cc];
+                        k = o > k ? o : k;
+                    }
+            }
+            combine_step<TIMED>(p, t, k, tok, lane);
+        }
+        __syncthreads();
+    }
+}
+
+const void* mfma_walk_kernel(int sample, int w1t, bool timed) {
+#define DSPARK_MFMA(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI>)
+    if (timed) return sample ? DSPARK_MFMA(1, DT_BF16, 1) : DSPARK_MFMA(0, DT_BF16, 1);
+    if (sample) {
+        switch (w1t) {
+            case DT_F32: return DSPARK_MFMA(1, DT_F32, 0);
+            case DT_BF16: return DSPARK_MFMA(1, DT_BF16, 0);
+            default: return DSPARK_MFMA(1, DT_F16, 0);
+        }
+    }
+    switch (w1t) {
+        case DT_F32: return DSPARK_MFMA(0, DT_F32, 0);
+        case DT_BF16: return DSPARK_MFMA(0, DT_BF16, 0);
+        default: return DSPARK_MFMA(0, DT_F16, 0);
+    }
+#undef DSPARK_MFMA
+}
+
+int mfma_fixed_lds_bytes(int rows_per_wg) { return mfma_fixed_lds(rows_per_wg); }
+
+}  // namespace dspark

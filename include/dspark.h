@@ -98,7 +98,17 @@ typedef struct dspark_walk_plan {
     int64_t resident_bytes;      /* int8 W2 bytes held on chip (whole grid) */
     int64_t streamed_bytes;      /* int8 W2 bytes re-read per step (whole grid) */
     int32_t lds_bytes;           /* dynamic LDS per workgroup */
+    int32_t path;                /* DSPARK_PATH_DOT4 (one request) or DSPARK_PATH_MFMA */
+    int32_t reg_units;           /* register row sets (dot4) or 16-row tiles per wave (MFMA) */
+    int32_t lds_units;           /* LDS row sets (dot4) or tiles per wave (MFMA) */
+    int32_t total_units;         /* all row sets / tiles per wave (the rest are streamed) */
+    int32_t stage_bufs;          /* MFMA: LDS buffers staging a 16-request tile's base logits */
+    int32_t stage_stride;        /* MFMA: floats per request row in such a buffer */
 } dspark_walk_plan;
+
+/* Which kernel runs a dense walk: one request is a GEMV (lane-per-row v_dot4 kernel), two or
+ * more make every step a GEMM (int8 matrix cores, 16 requests per tile). */
+enum dspark_path { DSPARK_PATH_DOT4 = 1, DSPARK_PATH_MFMA = 2 };
 
 int dspark_walk_plan_query(int64_t bs, int64_t T, int64_t V, dspark_walk_plan* plan);
 
@@ -183,6 +193,8 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *       recorded (0 = default);
  *   DSPARK_DEBUG_WAIT_UNSET_FLAG: non-zero makes the grid-wide waits also wait for a workspace
  *       flag that nothing sets, so each runs into its spin limit (for the timeout test);
+ *   DSPARK_DEBUG_FORCE_PATH: 0 chooses by batch size; DSPARK_PATH_DOT4 / DSPARK_PATH_MFMA force
+ *       that kernel for every batch size (both compute the same results);
  *   DSPARK_DEBUG_STAMPS: a device address (8-byte aligned) of 256 x 82 uint64 words, or 0.
  *       When set, dense walks with bf16 W1 run an instrumented build of the same kernel that
  *       stores the 100 MHz device clock per workgroup: [0] start, [1] W2 resident, then per step
@@ -193,7 +205,8 @@ enum dspark_debug_key {
     DSPARK_DEBUG_MAX_WORKGROUPS = 1,
     DSPARK_DEBUG_SPIN_LIMIT = 2,
     DSPARK_DEBUG_WAIT_UNSET_FLAG = 3,
-    DSPARK_DEBUG_STAMPS = 4
+    DSPARK_DEBUG_STAMPS = 4,
+    DSPARK_DEBUG_FORCE_PATH = 5
 };
 int dspark_debug_set(int key, int64_t value);
 

@@ -50,34 +50,60 @@ def test_workspace_bytes():
     assert k >= 64 * 7 * 513 * 4 and k >= B.dspark_walk_workspace_bytes(64, 7, 151936, 0)
 
 
+@pytest.mark.parametrize("bs", [1, 4, 64])
 @pytest.mark.parametrize("cus", [1, 8, 32, 80, 256, 304])
 @pytest.mark.parametrize("V", [1, 3, 255, 256, 257, 4096, 5000, 70000, 129280, 151936, 248320,
                                270336])
-def test_plan_partition(cus, V):
+def test_plan_partition(bs, cus, V):
     try:
-        p = B.dspark_walk_plan_for(cus, 163840, 4, 7, V)
+        p = B.dspark_walk_plan_for(cus, 163840, bs, 7, V)
     except B.DsparkError as e:
         assert e.status == B.ERR_UNSUPPORTED
         return
+    mfma_ok = bs >= 2 and V % 4 == 0
+    if not mfma_ok:
+        assert p["path"] == B.PATH_DOT4
+    elif p["path"] == B.PATH_DOT4:
+        # the MFMA kernel was refused only because one staging buffer (16 request rows of the
+        # slice, padded) does not fit next to its fixed LDS
+        rpw16 = -(-max(-(-V // min(cus, 256)), min(V, 256)) // 16) * 16
+        u16 = rpw16 // 4 + (1 - (rpw16 // 4) % 2)
+        fixed = 64 * 256 + 64 * 4 + rpw16 * 4 + 4 * 4 * 64 * 8 + 64 * 4
+        assert fixed + 16 * u16 * 16 > 163840
+    mfma = p["path"] == B.PATH_MFMA
+    quantum = 16 if mfma else 4                      # rows: 16-row tiles vs lane-per-row sets
     nwg, rpw = p["num_workgroups"], p["rows_per_workgroup"]
     cus = min(cus, 256)                          # the grid is capped at 256 workgroups
     assert 1 <= nwg <= cus
     assert nwg * rpw >= V > (nwg - 1) * rpw          # every row owned exactly once
-    assert rpw % 4 == 0 or rpw >= V
+    assert rpw % quantum == 0
     assert p["rows_in_registers"] + p["rows_in_lds"] + p["rows_streamed"] == rpw
     assert p["resident_bytes"] + p["streamed_bytes"] == V * 256
-    assert p["rows_in_registers"] <= 512 and p["rows_in_lds"] <= 512
+    if not mfma:
+        assert p["rows_in_registers"] <= 512 and p["rows_in_lds"] <= 512
+        assert p["total_units"] == -(-rpw // 256)
+    else:
+        assert p["rows_in_registers"] <= 512         # 8 tiles x 16 rows x 4 waves
+        assert p["total_units"] == -(-(rpw // 16) // 4)
+        assert p["stage_bufs"] == (2 if bs > 16 else 1) or p["stage_bufs"] >= 1
+        assert p["stage_stride"] >= rpw and (p["stage_stride"] // 4) % 2 == 1
+    assert p["reg_units"] + p["lds_units"] <= p["total_units"]
     assert 96 * 1024 <= p["lds_bytes"] <= 163840
     if V >= 256 * cus:
-        # big vocabularies: the smallest multiple of 4 rows that covers V with every CU
-        assert (rpw - 4) * cus < V <= rpw * cus
+        # big vocabularies: the smallest multiple of the quantum that covers V with every CU
+        assert (rpw - quantum) * cus < V <= rpw * cus
 
 
-def test_plan_headline_fits_on_chip():
-    p = B.dspark_walk_plan_for(256, 163840, 1, 7, 151936)
-    assert p["streamed_bytes"] == 0 and p["resident_bytes"] == 151936 * 256
-    p = B.dspark_walk_plan_for(256, 163840, 1, 16, 248320)
-    assert p["streamed_bytes"] == 0
+@pytest.mark.parametrize("bs", [1, 16, 64])
+def test_plan_pages_shapes_fit_on_chip(bs):
+    """On a 256-CU MI355X the W2 of every shape in the pages' kernel table stays on chip (the
+    V = 248320 walks there are single-request; with several requests the MFMA kernel gives its
+    LDS to the base-logit staging first and streams part of that W2)."""
+    for V in (129280, 151936, 248320, 270336):
+        p = B.dspark_walk_plan_for(256, 163840, bs, 7, V)
+        if V <= 151936 or (bs == 1 and V <= 248320):
+            assert p["streamed_bytes"] == 0, (bs, V, p)
+        assert p["resident_bytes"] + p["streamed_bytes"] == V * 256
 
 
 def _greedy(**kw):
@@ -184,6 +210,8 @@ def test_misc_validation():
     assert L.dspark_workspace_status(None, None) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(99, 1) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_SPIN_LIMIT, -1) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(B.DEBUG_FORCE_PATH, 3) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(B.DEBUG_STAMPS, 12) == B.ERR_INVALID_ARG
     assert L.dspark_walk_plan_query(1, 1, 10, None) == B.ERR_INVALID_ARG
     assert L.dspark_walk_plan_for(0, 163840, 1, 1, 10, ctypes.byref(B.WalkPlan())) == \
         B.ERR_INVALID_ARG

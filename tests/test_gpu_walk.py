@@ -21,8 +21,12 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True)
 def _reset_knobs():
     yield
-    for key in (B.DEBUG_MAX_WORKGROUPS, B.DEBUG_SPIN_LIMIT, B.DEBUG_WAIT_UNSET_FLAG):
+    for key in (B.DEBUG_MAX_WORKGROUPS, B.DEBUG_SPIN_LIMIT, B.DEBUG_WAIT_UNSET_FLAG,
+                B.DEBUG_FORCE_PATH):
         dm.dspark_debug_set(key, 0)
+
+
+PATHS = [0, B.PATH_DOT4, B.PATH_MFMA]   # 0: chosen by batch size
 
 
 # ----------------------------------------------------------------------------------------------
@@ -103,12 +107,16 @@ SMALL = [  # V, T, bs, dtype, grid cap (0 = one workgroup per CU)
     (3000, 5, 64, torch.bfloat16, 0),       # full batch
     (257, 16, 2, torch.float32, 0),         # one workgroup, 16 steps
     (1, 2, 1, torch.bfloat16, 0),           # a single-entry vocabulary
+    (40001, 2, 17, torch.bfloat16, 8),      # MFMA: LDS and streamed tiles, ragged request tile
+    (4099, 3, 33, torch.float16, 0),        # V % 4 != 0: scalar base / draft-logit accesses
 ]
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("V,T,bs,dtype,cap", SMALL)
-def test_greedy_parity_small(V, T, bs, dtype, cap):
+def test_greedy_parity_small(V, T, bs, dtype, cap, path):
     dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
     p = random_problem(V, T, bs, dtype=dtype, w_std=0.05 if dtype == torch.float32 else 0.02,
                        seed=V + T + bs)
     tok, logits = p.greedy()
@@ -117,9 +125,11 @@ def test_greedy_parity_small(V, T, bs, dtype, cap):
     print(rep.summary())
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("V,T,bs,dtype,cap", SMALL)
-def test_sample_parity_small(V, T, bs, dtype, cap):
+def test_sample_parity_small(V, T, bs, dtype, cap, path):
     dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
     temps = np.linspace(0.5, 2.0, bs).astype(np.float32) if bs > 1 else None
     pos = np.arange(bs, dtype=np.int64) * 1000 + 3 if bs > 2 else None
     p = random_problem(V, T, bs, dtype=dtype, seed=V * 7 + bs, temps=temps, positions=pos)
@@ -157,6 +167,27 @@ def test_parity_full_size(name, mode, reqs):
         tok, lb = p.sample()
         rep = p.check_sample(tok, lb, requests=reqs)
     print(name, mode, rep.summary())
+    assert rep.ok, rep.summary()
+
+
+@pytest.mark.parametrize("name,mode,reqs", [("v151936_t7_bs1", "greedy", None),
+                                            ("v151936_t7_bs16", "sample", [3, 12])])
+def test_paths_agree_bitwise(name, mode, reqs):
+    """Both kernels form each logit with the same exact int32 sum and the same fp32 operations,
+    so they must agree bit for bit; each is also checked against the oracle."""
+    inp = make_inputs(CASES[name])
+    p = Problem(inp.w1, inp.w2, inp.base, inp.start, seeds=inp.seeds,
+                temps=inp.temperature.numpy())
+    qs = p.quantize()
+    outs = []
+    for path in (B.PATH_DOT4, B.PATH_MFMA):
+        dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
+        outs.append(p.greedy(qs=qs) if mode == "greedy" else p.sample(qs=qs))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32 if mode == "greedy" else np.uint16),
+                          outs[1][1].view(np.uint32 if mode == "greedy" else np.uint16))
+    rep = (p.check_greedy(*outs[1], requests=reqs) if mode == "greedy"
+           else p.check_sample(*outs[1], requests=reqs))
     assert rep.ok, rep.summary()
 
 
@@ -207,7 +238,9 @@ def test_argmax_order_across_workgroups(mode):
 # ----------------------------------------------------------------------------------------------
 # determinism, grid-size invariance, workspace hygiene, back-to-back calls
 # ----------------------------------------------------------------------------------------------
-def test_repeatable_and_grid_invariant():
+@pytest.mark.parametrize("path", [B.PATH_DOT4, B.PATH_MFMA])
+def test_repeatable_and_grid_invariant(path):
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
     p = random_problem(30000, 5, 4, seed=11)
     qs = p.quantize()
     ref_tok, ref_logits = p.greedy(qs=qs)
@@ -217,13 +250,13 @@ def test_repeatable_and_grid_invariant():
         assert np.array_equal(tok, ref_tok)
         assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32))
     assert int(ws.count_nonzero()) == 0
-    for cap in (8, 37, 117, 0):
+    for cap in (3, 8, 37, 117, 0):
         dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
         tok, logits = p.greedy(qs=qs, ws=ws)
         assert np.array_equal(tok, ref_tok), cap
         assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32)), cap
         stok, slb = p.sample(qs=qs, ws=ws)
-        if cap == 8:
+        if cap == 3:
             ref_s = (stok, slb)
         else:
             assert np.array_equal(stok, ref_s[0]) and np.array_equal(slb, ref_s[1])
