@@ -8,9 +8,15 @@ resident in HBM when timing starts; W2 is quantised once, outside the timed regi
 Timing protocol (after that table's: CUDA graph, cold L2, median per call): before every
 timed call a 512 MiB read evicts W2 and the inputs from the 4 MiB L2 of each XCD and from the
 256 MiB MALL, leaving clean lines behind; a HIP event pair on the launch stream brackets each
-call; `value` is the median. Also reported: the same after a 512 MiB *write* (caches full of
-dirty lines, whose write-back the walk then pays), a warm back-to-back rate, and a sweep over
-the other shapes of that table.
+call; `value` is the median. The roofline figures divide the algorithmic bytes by the mean
+duration of the kernel alone, taken in a second cold pass from events that the kernel's own
+dispatch records (hipExtLaunchKernel), so launch queueing is not charged to the kernel. Also
+reported: the same after a 512 MiB *write* (caches full of dirty lines, whose write-back the
+walk then pays), a warm back-to-back rate, and a sweep over the other shapes of that table.
+
+`roofline.traffic` is the HBM traffic per launch measured by the FETCH_SIZE / WRITE_SIZE
+counters (profiles/traffic.json, calibrated against a plain copy of known size); it is reported
+only while the library sources hash to what they were when the counters were taken.
 
 One JSON line on stdout; progress on stderr.
 """
@@ -31,6 +37,7 @@ from dspark_markov_draft_amd.synth import CASES, make_inputs, seeds_as_int64  # 
 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
+KERNEL_NAMES = {1: "dense_walk_dot4_kernel", 2: "dense_walk_mfma_kernel"}
 
 
 def log(*a):
@@ -103,6 +110,26 @@ def _timed_calls(w, steps, flush_fn, stream):
     return np.array([s.elapsed_time(e) * 1000.0 for s, e in zip(starts, ends)]), wall
 
 
+def kernel_times(w, steps, flush_fn):
+    """Dispatch-recorded durations of the walk's kernels alone (events written by each kernel's
+    own dispatch packet), same cold protocol as the call timing; summed per call (the top-k
+    walk runs two kernels)."""
+    from dspark_markov_draft_amd.binding import DEBUG_KERNEL_TIMING
+    dm.dspark_debug_set(DEBUG_KERNEL_TIMING, 4 * steps)
+    try:
+        for i in range(steps):
+            flush_fn(i)
+            w.launch()
+        torch.cuda.synchronize()
+        t = np.array(dm.dspark_kernel_times(4 * steps))
+        per_call = len(t) // steps
+        t = t[:per_call * steps].reshape(steps, per_call)
+        w.kernel_parts_us = [round(float(m), 2) for m in t.mean(axis=0)]
+        return t.sum(axis=1)
+    finally:
+        dm.dspark_debug_set(DEBUG_KERNEL_TIMING, 0)
+
+
 def time_walk(w, steps, warmup, flush, stream, dirty=False):
     for _ in range(warmup):
         w.launch()
@@ -113,6 +140,7 @@ def time_walk(w, steps, warmup, flush, stream, dirty=False):
         torch.sum(flush, dim=0, keepdim=True, out=sink)
 
     us, wall = _timed_calls(w, steps, read_flush, stream)
+    kus = kernel_times(w, steps, read_flush)
     dirty_us = None
     if dirty:
         dirty_us, _ = _timed_calls(w, steps, lambda i: flush.fill_(float(i)), stream)
@@ -125,7 +153,32 @@ def time_walk(w, steps, warmup, flush, stream, dirty=False):
     e1.record(stream)
     torch.cuda.synchronize()
     warm_us = e0.elapsed_time(e1) * 1000.0 / steps
-    return us, wall, warm_us, dirty_us
+    return us, wall, warm_us, dirty_us, kus
+
+
+def csrc_digest():
+    """sha256 over the library's sources (name and contents, sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "dspark_markov_draft_amd", "csrc")
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".hpp", ".h")):
+            h.update(n.encode())
+            h.update(open(os.path.join(d, n), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "dspark.h"), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """Counter-measured HBM bytes per launch for this workload, or None if not measured or the
+    sources changed since."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("csrc_sha256") != csrc_digest():
+        return None
+    return rec.get("workloads", {}).get(workload)
 
 
 def cpu_baseline(case, budget_s=20.0):
@@ -157,6 +210,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time one case:mode only (profiling)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB, whose "
+                         "known byte count calibrates the HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -167,6 +223,15 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB "
+            "written")
+        del src, dst
 
     head_case, head_mode = CASES["v151936_t7_bs1"], "greedy"
     if args.only:
@@ -176,12 +241,15 @@ def main():
     log(f"[bench] headline {head_case.name} {head_mode}: steps={args.steps} warmup={args.warmup}")
     w = Walk(head_case, head_mode, dev)
     plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
-    us, wall, warm_us, dirty_us = time_walk(w, args.steps, args.warmup, flush, stream, dirty=True)
+    us, wall, warm_us, dirty_us, kus = time_walk(w, args.steps, args.warmup, flush, stream,
+                                                 dirty=True)
     med = float(np.median(us))
     nbytes = w.algorithmic_bytes()
-    achieved = nbytes / (float(np.mean(us)) * 1e-6) / 1e9
+    kmean = float(np.mean(kus))
+    achieved = nbytes / (kmean * 1e-6) / 1e9
     log(f"[bench] median {med:.2f} us  p10 {np.percentile(us, 10):.2f}  p90 "
-        f"{np.percentile(us, 90):.2f}  warm {warm_us:.2f} us")
+        f"{np.percentile(us, 90):.2f}  warm {warm_us:.2f} us  kernel mean {kmean:.2f} us "
+        f"(per kernel {w.kernel_parts_us})")
 
     sweep = []
     if not args.no_sweep and not args.only:
@@ -191,12 +259,15 @@ def main():
                            ("v151936_t16_bs1", "sample"), ("v129280_t5_bs1", "greedy"),
                            ("v129280_t5_bs1", "sample"), ("v129280_t5_bs64", "greedy"),
                            ("v129280_t5_bs64", "sample"), ("v248320_t16_bs1", "greedy"),
-                           ("v248320_t16_bs1", "sample")]:
+                           ("v248320_t16_bs1", "sample"),
+                           ("topk512_v151936_t7_bs64", "greedy"),
+                           ("topk512_v151936_t7_bs64", "sample")]:
             del w
             torch.cuda.empty_cache()
             w = Walk(CASES[name], mode, dev)
             try:
-                s_us, _, s_warm, _ = time_walk(w, max(10, args.steps // 2), 3, flush, stream)
+                s_us, _, s_warm, _, s_kus = time_walk(w, max(10, args.steps // 2), 3, flush,
+                                                      stream)
             except dm.DsparkError as e:
                 log(f"[bench] {name} {mode}: {e}")
                 continue
@@ -205,7 +276,10 @@ def main():
                      "us_p10": round(float(np.percentile(s_us, 10)), 2),
                      "us_p90": round(float(np.percentile(s_us, 90)), 2),
                      "us_warm": round(s_warm, 2),
-                     "hbm_frac": round(nb / (float(np.mean(s_us)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                     "kernel_us_mean": round(float(np.mean(s_kus)), 2),
+                     "kernel_parts_us": w.kernel_parts_us,
+                     "hbm_frac": round(nb / (float(np.mean(s_kus)) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                       4)}
             sweep.append(entry)
             log(f"[bench] {name} {mode}: {entry}")
 
@@ -214,6 +288,9 @@ def main():
         log("[bench] CPU oracle baseline ...")
         cpu = cpu_baseline(head_case)
         log(f"[bench] oracle {cpu['value']:.0f} us/walk on {cpu['cores']} threads")
+
+    tr = measured_traffic(f"{head_case.name}:{head_mode}")
+    traffic = None if tr is None else tr["fetch_bytes"] + tr["write_bytes"]
 
     out = {
         "metric": "us per Markov walk call (all draft steps), V=151936, 7 draft tokens, bs 1",
@@ -234,11 +311,13 @@ def main():
         "latency_us": {"median": round(med, 3), "p10": round(float(np.percentile(us, 10)), 3),
                        "p90": round(float(np.percentile(us, 90)), 3), "warm": round(warm_us, 3),
                        "after_dirty_flush_median": round(float(np.median(dirty_us)), 3),
+                       "kernel_only_mean": round(kmean, 3),
+                       "kernel_only_median": round(float(np.median(kus)), 3),
                        "wall_per_call_incl_flush": round(wall / args.steps * 1e6, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
-                     "kernel": "dense_walk_kernel"},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": KERNEL_NAMES.get(plan["path"], "?")},
         "cpu_baseline": cpu,
         "sweep": sweep,
     }

@@ -22,6 +22,7 @@ RANK = 256
 MAX_STEPS, MAX_BS, MAX_V, MAX_TOPK = 16, 64, 270336, 2048
 DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG, DEBUG_STAMPS = 1, 2, 3, 4
 DEBUG_FORCE_PATH = 5
+DEBUG_KERNEL_TIMING = 6
 PATH_DOT4, PATH_MFMA = 1, 2
 STAMPS_PER_WG = 82
 
@@ -80,10 +81,12 @@ def lib():
         L.dspark_workspace_status.argtypes = [vp, vp]
         L.dspark_philox_words.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i64, i64, vp, vp]
         L.dspark_debug_set.argtypes = [i32, i64]
+        L.dspark_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
+                                          ctypes.POINTER(i32)]
         for name in ["dspark_quantize_w2", "dspark_walk_plan_query", "dspark_walk_plan_for",
                      "dspark_walk_greedy",
                      "dspark_walk_sample", "dspark_walk_topk", "dspark_workspace_status",
-                     "dspark_philox_words", "dspark_debug_set"]:
+                     "dspark_philox_words", "dspark_debug_set", "dspark_kernel_times"]:
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -213,3 +216,12 @@ def dspark_philox_words(seed: int, position: int, v0: int, n: int, device="cuda"
 
 def dspark_debug_set(key: int, value: int):
     _check(lib().dspark_debug_set(key, value))
+
+
+def dspark_kernel_times(max_count: int = 4096) -> list:
+    """Durations (us) of the walk kernels launched since kernel timing was switched on or last
+    read, oldest first (see DEBUG_KERNEL_TIMING)."""
+    buf = (ctypes.c_float * max_count)()
+    n = ctypes.c_int32(0)
+    _check(lib().dspark_kernel_times(buf, max_count, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]

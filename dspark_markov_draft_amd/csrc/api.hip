@@ -301,12 +301,18 @@ int dspark_debug_set(int key, int64_t value) {
                 return DSPARK_ERR_INVALID_ARG;
             k.force_path = (int)value;
             return DSPARK_OK;
+        case DSPARK_DEBUG_KERNEL_TIMING: return set_kernel_timing(value);
         case DSPARK_DEBUG_STAMPS:
             if (value & 7) return DSPARK_ERR_INVALID_ARG;
             k.stamps = (uintptr_t)value;
             return DSPARK_OK;
         default: return DSPARK_ERR_INVALID_ARG;
     }
+}
+
+int dspark_kernel_times(float* us, int max, int* count) {
+    if (us == nullptr || count == nullptr || max < 0) return DSPARK_ERR_INVALID_ARG;
+    return read_kernel_times(us, max, count);
 }
 
 }  // extern "C"

@@ -19,19 +19,27 @@ constexpr int WAVE = 64;
 // is the larger key. An atomic or wave-wide unsigned max then yields the torch.argmax winner.
 // Every real key is >= 0x007FFFFF00000000 (the key of -inf), so a zeroed slot is below all.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t argmax_key(float x, uint32_t idx) {
+__device__ __forceinline__ uint32_t order_key32(float x) {
     uint32_t u = __float_as_uint(x);
-    uint32_t ord;
-    if (x != x) {
-        ord = 0xFFFFFFFFu;
-    } else {
-        if (x == 0.0f) u = 0u;
-        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    return ((uint64_t)ord << 32) | (uint64_t)(~idx);
+    if (x != x) return 0xFFFFFFFFu;
+    if (x == 0.0f) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr uint32_t ORDER_KEY_NEG_INF = 0x007FFFFFu;  // order_key32(-inf), the smallest real key
+
+__device__ __forceinline__ uint64_t argmax_key(float x, uint32_t idx) {
+    return ((uint64_t)order_key32(x) << 32) | (uint64_t)(~idx);
 }
 
 __device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
+
+// The drafted logit of one vocabulary row: base + (s[v] * s1) * acc, where acc is the exact
+// int32 dot product of the row's int8 codes with the request's int8 W1 codes and s1 the W1
+// row's scale. Written as one explicit fused multiply-add so that every kernel (dense dot4,
+// MFMA, top-k) rounds it identically.
+__device__ __forceinline__ float walk_logit(float base, float s_row, float s1, int32_t acc) {
+    return __builtin_fmaf(s_row * s1, (float)acc, base);
+}
 
 // ---------------------------------------------------------------------------------------------
 // bf16, round to nearest even; NaN stays a quiet NaN (vLLM PR #62958, Details: draft_logits

@@ -78,4 +78,10 @@ struct TopkLaunch {
 };
 int launch_topk_walk(const TopkLaunch& a, hipStream_t stream);
 
+// Walk kernel launch: plain, or with dispatch-recorded events while kernel timing is on.
+hipError_t launch_walk_kernel(const void* fn, dim3 grid, dim3 block, void** args, size_t lds,
+                              hipStream_t stream);
+int set_kernel_timing(int64_t ring_size);
+int read_kernel_times(float* us, int max, int* count);
+
 }  // namespace dspark

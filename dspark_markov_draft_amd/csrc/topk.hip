@@ -1,12 +1,706 @@
-// K2 + K3: the top-k Markov walk (vLLM PR #49969, Purpose). Placeholder until the kernels land.
-#include "internal.hpp"
+// The top-k Markov walk (vLLM PR #49969, Purpose: the drafter's logits restricted to the k
+// best candidates of the target's base logits and scattered into a dense -inf row; vLLM PR
+// #62958, Details: the unchanged sampler over that row). Two kernels on the caller's stream.
+//
+// topk_select_kernel, one workgroup per (request, step) row of base logits: the k largest base
+// logits, ties toward the lower vocabulary index. Every element gets a unique 51-bit key (the
+// 32-bit order key of its value above 19 bits of reversed index), so "the k largest keys" is
+// exactly the wanted set, and an MSB-first radix select finds the k-th key. The row is read
+// from HBM once: its first 18432 elements stay in registers while their top-12-bit histogram
+// gives the bin L holding their k-th largest key; at least k keys of the row lie in bins >= L,
+// so the k-th key of the row does too. One pass over the rest of the row then appends every
+// element of a bin >= L to an LDS buffer, where 12- and 10-bit radix levels find the k-th key
+// and the winners are emitted. If the buffer overflows (rows sorted ascending, long plateaus),
+// an exact fallback takes two more passes: the histogram of the whole row, then the elements
+// above the k-th key's bin out directly and that bin to LDS (or, if that bin is itself too
+// large, its levels over the row in global memory). The first pass also writes -inf over the
+// dense output row when there is one.
+//
+// topk_walk_kernel, one workgroup per request, its steps in sequence (requests never wait for
+// each other): per step the wave-level int8 quantisation of W1[prev] used by the dense walk,
+// the v_dot4 logits of the step's k candidates with the dense walk's rounding, their values in
+// the dense output row, the sampler's noise keyed by vocabulary index, and the argmax over the
+// candidates, which equals the argmax of the dense row with -inf elsewhere. The candidates'
+// W2 rows, scales and base logits are loaded together with the step's W1 row, and the next
+// step's candidate indices one step ahead.
+#include "walk_common.hpp"
 
 namespace dspark {
 
+constexpr int SEL_THREADS = 512;
+constexpr int SEL_WAVES = SEL_THREADS / WAVE;
+constexpr int STASH_GROUPS = 9;                       // 4-element groups per thread in registers
+constexpr int STASH_ELEMS = SEL_THREADS * STASH_GROUPS * 4;   // 18432
+constexpr int MAIN_UNROLL = 8;                        // groups per thread per batch (2 in flight)
+constexpr int IDX_BITS = 19;                          // a vocabulary index fits in 19 bits
+constexpr uint64_t IDX_MASK = (1ull << IDX_BITS) - 1;
+constexpr int CK_BITS = 32 + IDX_BITS;                // 51-bit composite keys
+constexpr int L1_BITS = 12;                           // first level: the top 12 bits
+constexpr int L1_BINS = 1 << L1_BITS;
+constexpr int L1_SHIFT = CK_BITS - L1_BITS;           // 39
+constexpr int REGION_CAP = 992;                       // LDS keys per wave (8 waves: 7936 keys)
+constexpr int BUF_CAP = SEL_WAVES * REGION_CAP;       // fits two workgroups per CU
+constexpr int LDS_LEVEL_BITS = 10;                    // later levels over the LDS buffer
+constexpr int GLOBAL_LEVEL_BITS = 12;                 // later levels over the row (fallback)
+constexpr int SEL_LDS_BYTES = BUF_CAP * 8 + L1_BINS * 4 + 64;
+constexpr int TKW_THREADS = 512;
+constexpr int TKW_WAVES = TKW_THREADS / WAVE;
+static_assert(DSPARK_MAX_V <= (1 << IDX_BITS), "vocabulary index must fit the composite key");
+static_assert(DSPARK_MAX_TOPK <= STASH_ELEMS, "the register chunk must hold k keys");
+
+__device__ __forceinline__ uint64_t composite_key(float x, uint32_t idx) {
+    return ((uint64_t)order_key32(x) << IDX_BITS) | (IDX_MASK - idx);
+}
+__device__ __forceinline__ uint32_t composite_index(uint64_t ck) {
+    return (uint32_t)(IDX_MASK - (ck & IDX_MASK));
+}
+__device__ __forceinline__ uint32_t top_bin(float x) { return order_key32(x) >> (32 - L1_BITS); }
+
+// Instrumented builds: thread 0 records the 100 MHz device clock. Select rows use words
+// row * 8 + (0 start, 1 first bound known, 2 row scanned, 3 k-th key known, 4 done); walk
+// requests use TK_WALK_STAMPS0 + request * 40 + (0 start, then per step t: 1 + 2t W1 codes
+// ready, 2 + 2t token known).
+constexpr int TK_WALK_STAMPS0 = 8192;
+template <bool TIMED>
+__device__ __forceinline__ void tk_stamp(uint64_t* st, int64_t idx) {
+    if constexpr (TIMED) {
+        if (threadIdx.x == 0) st[idx] = __builtin_amdgcn_s_memrealtime();
+    }
+}
+
+// Lanes of this wave below the calling lane whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Positions for the lanes of a wave whose `pred` is set, reserved with one LDS atomic for the
+// whole wave (lanes in ascending order). Every write into a candidate row or into the LDS
+// buffer below is also checked against its capacity.
+__device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred, int lane) {
+    const uint64_t m = __ballot(pred);
+    if (m == 0) return 0;
+    const int leader = __ffsll((unsigned long long)m) - 1;
+    uint32_t base = 0;
+    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = (uint32_t)__shfl((int)base, leader);
+    return base + lanes_below(m);
+}
+
+// Inclusive suffix sum over the 64 lanes (lane l gets the sum of lanes l .. 63).
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_down((int)v, off);
+        if (lane + off < WAVE) v += o;
+    }
+    return v;
+}
+
+// Run by one whole wave: the bin d such that fewer than `need` counted keys lie in bins above d
+// and at least `need` in bins >= d (1 <= need <= total); `above` = the count above d. Lane l
+// sums bins [l * PER, l * PER + PER) in a lane-rotated order (no LDS bank conflicts); a suffix
+// scan over lanes finds the lane range holding d, and a second scan over that range's bins
+// (one per lane) finds d.
+template <int NBINS>
+__device__ __forceinline__ void select_digit(const uint32_t* hist, uint32_t need, int lane,
+                                             uint32_t& d, uint32_t& above) {
+    constexpr int PER = NBINS / WAVE;
+    static_assert(PER >= 1 && PER <= WAVE && (PER & (PER - 1)) == 0, "bins per lane");
+    uint32_t s = 0;
+#pragma unroll 8
+    for (int j = 0; j < PER; ++j) s += hist[lane * PER + ((j + lane) & (PER - 1))];
+    const uint32_t suf = wave_suffix_sum(s, lane);
+    const uint64_t m1 = __ballot(suf - s < need && need <= suf);
+    const int src = m1 ? __ffsll((unsigned long long)m1) - 1 : 0;
+    const uint32_t above_src = (uint32_t)__shfl((int)(suf - s), src);
+    const uint32_t c = lane < PER ? hist[src * PER + lane] : 0u;
+    const uint32_t suf2 = wave_suffix_sum(c, lane) + above_src;
+    const uint64_t m2 = __ballot(lane < PER && suf2 - c < need && need <= suf2);
+    const int j = m2 ? __ffsll((unsigned long long)m2) - 1 : 0;
+    d = (uint32_t)(src * PER + j);
+    above = (uint32_t)__shfl((int)(suf2 - c), j);
+}
+
+struct SelectParams {
+    const float* base;    // [rows][V]
+    int32_t* cand;        // [rows][k] (workspace)
+    uint16_t* fill_bf16;  // [rows][V] dense bf16 output to set to -inf, or null
+    float* fill_f32;      // [rows][V] dense fp32 output to set to -inf, or null
+    uint64_t* stamps;     // instrumented builds
+    int V, k;
+};
+
+// Group g of a row: elements 4g .. 4g+3 (those < V); absent elements read as -inf and are
+// excluded by the callers through the element count. VEC: the row allows float4 loads.
+template <bool VEC>
+__device__ __forceinline__ float4 load_group(const SelectParams& p, const float* x, int g) {
+    const int i = 4 * g;
+    if constexpr (VEC) {
+        return reinterpret_cast<const float4*>(x)[g];
+    } else {
+        float4 a;
+        a.x = i < p.V ? x[i] : -INFINITY;
+        a.y = i + 1 < p.V ? x[i + 1] : -INFINITY;
+        a.z = i + 2 < p.V ? x[i + 2] : -INFINITY;
+        a.w = i + 3 < p.V ? x[i + 3] : -INFINITY;
+        return a;
+    }
+}
+
+// The same, never branching around the load (so that the compiler can count loads in
+// flight): a group index past the end reads the last group, whose values the caller ignores.
+template <bool VEC>
+__device__ __forceinline__ float4 load_group_clamped(const SelectParams& p, const float* x, int g,
+                                                     int ngroups) {
+    const int gc = g < ngroups ? g : ngroups - 1;
+    if constexpr (VEC) {
+        return reinterpret_cast<const float4*>(x)[gc];
+    } else {
+        const int i = 4 * gc, last = p.V - 1;
+        return make_float4(x[min(i, last)], x[min(i + 1, last)], x[min(i + 2, last)],
+                           x[min(i + 3, last)]);
+    }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void fill_group(const SelectParams& p, int64_t row, int g) {
+    const int i = 4 * g;
+    if (p.fill_bf16) {
+        uint16_t* o = p.fill_bf16 + row * p.V + i;
+        if constexpr (VEC) {
+            *reinterpret_cast<uint2*>(o) = make_uint2(0xFF80FF80u, 0xFF80FF80u);
+        } else {
+            for (int u = 0; u < 4; ++u)
+                if (i + u < p.V) o[u] = 0xFF80u;
+        }
+    }
+    if (p.fill_f32) {
+        float* o = p.fill_f32 + row * p.V + i;
+        if constexpr (VEC) {
+            *reinterpret_cast<float4*>(o) = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        } else {
+            for (int u = 0; u < 4; ++u)
+                if (i + u < p.V) o[u] = -INFINITY;
+        }
+    }
+}
+
+// The LDS buffer is SEL_WAVES regions of REGION_CAP keys; region r holds cnt[r] keys.
+__device__ __forceinline__ bool buf_slot(const uint32_t* cnt, uint32_t e) {
+    return e % REGION_CAP < cnt[e / REGION_CAP];
+}
+
+// Radix levels over the keys in LDS (all threads): from bit `lo` down, among keys whose bits
+// above `lo` equal `prefix`, the need-th largest. The first level below bit 51 takes 12 bits,
+// later ones 10. Returns the full 51-bit key. cnt: per-region key counts.
+__device__ __forceinline__ uint64_t lds_select(const uint64_t* buf, const uint32_t* cnt,
+                                               uint32_t need, uint64_t prefix, int lo,
+                                               uint32_t* hist, uint32_t* sh, int tid, int lane) {
+    while (lo > 0) {
+        const int w = lo == CK_BITS ? L1_BITS : (lo < LDS_LEVEL_BITS ? lo : LDS_LEVEL_BITS);
+        lo -= w;
+        for (int i = tid; i < L1_BINS; i += SEL_THREADS) hist[i] = 0;
+        __syncthreads();
+        for (uint32_t e = tid; e < (uint32_t)BUF_CAP; e += SEL_THREADS) {
+            if (!buf_slot(cnt, e)) continue;
+            const uint64_t ck = buf[e];
+            if ((ck >> (lo + w)) == prefix) atomicAdd(&hist[(ck >> lo) & ((1u << w) - 1u)], 1u);
+        }
+        __syncthreads();
+        if (tid < WAVE) {
+            uint32_t d, above;
+            select_digit<L1_BINS>(hist, need, lane, d, above);
+            if (lane == 0) {
+                sh[0] = d;
+                sh[1] = above;
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << w) | sh[0];
+        need -= sh[1];
+    }
+    return prefix;
+}
+
+// Appends the keys >= kth of the buffer to the candidate row (all threads).
+__device__ __forceinline__ void emit_from_buffer(const uint64_t* buf, const uint32_t* cnt,
+                                                 uint64_t kth, int32_t* out, uint32_t* n_out,
+                                                 int k, int tid, int lane) {
+    for (uint32_t e0 = 0; e0 < (uint32_t)BUF_CAP; e0 += SEL_THREADS) {
+        const uint32_t e = e0 + tid;
+        const bool in = e < (uint32_t)BUF_CAP && buf_slot(cnt, e) && buf[e] >= kth;
+        const uint32_t po = wave_append(n_out, in, lane);
+        if (in && po < (uint32_t)k) out[po] = (int32_t)composite_index(buf[e]);
+    }
+}
+
+// The exact path for rows whose first bound lets too many keys through: see the file header.
+// Uses region 0's count for the whole buffer (one region of BUF_CAP keys).
+template <bool VEC>
+__device__ __forceinline__ void select_fallback(const SelectParams& p, const float* x, int32_t* out,
+                                                uint64_t* buf, uint32_t* hist, uint32_t* sh,
+                                                uint32_t* cnt, int tid, int lane) {
+    const int ngroups = (p.V + 3) / 4;
+    uint32_t* n_out = sh + 2;
+    uint32_t* n_buf = sh + 3;
+    for (int i = tid; i < L1_BINS; i += SEL_THREADS) hist[i] = 0;
+    if (tid == 0) {
+        *n_out = 0;
+        *n_buf = 0;
+    }
+    __syncthreads();
+    for (int g = tid; g < ngroups; g += SEL_THREADS) {
+        const float4 a = load_group<VEC>(p, x, g);
+        const float e[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (4 * g + u < p.V) atomicAdd(&hist[top_bin(e[u])], 1u);
+    }
+    __syncthreads();
+    if (tid < WAVE) {
+        uint32_t d, above;
+        select_digit<L1_BINS>(hist, (uint32_t)p.k, lane, d, above);
+        if (lane == 0) {
+            sh[0] = d;
+            sh[1] = above;
+        }
+    }
+    __syncthreads();
+    const uint32_t d1 = sh[0];
+    const uint32_t need = (uint32_t)p.k - sh[1];
+    const uint32_t bin_count = hist[d1];
+    for (int g0 = 0; g0 < ngroups; g0 += SEL_THREADS) {
+        const int g = g0 + tid;
+        const float4 a = g < ngroups ? load_group<VEC>(p, x, g) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float e[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = 4 * g + u;
+            const bool valid = g < ngroups && i < p.V;
+            const uint32_t bin = top_bin(e[u]);
+            const bool hi = valid && bin > d1, eq = valid && bin == d1;
+            const uint32_t po = wave_append(n_out, hi, lane);
+            if (hi && po < (uint32_t)p.k) out[po] = i;
+            const uint32_t pb = wave_append(n_buf, eq, lane);
+            if (eq && pb < (uint32_t)BUF_CAP) buf[pb] = composite_key(e[u], (uint32_t)i);
+        }
+    }
+    __syncthreads();
+    if (bin_count <= (uint32_t)BUF_CAP) {
+        // the whole buffer as consecutive regions: full ones, then the remainder
+        if (tid < SEL_WAVES) {
+            const int r = tid;
+            const int n = (int)bin_count - r * REGION_CAP;
+            cnt[r] = n <= 0 ? 0u : (n >= REGION_CAP ? (uint32_t)REGION_CAP : (uint32_t)n);
+        }
+        __syncthreads();
+        const uint64_t kth = lds_select(buf, cnt, need, d1, L1_SHIFT, hist, sh, tid, lane);
+        emit_from_buffer(buf, cnt, kth, out, n_out, p.k, tid, lane);
+        return;
+    }
+    uint64_t prefix = d1;
+    uint32_t nd = need;
+    int lo = L1_SHIFT;
+    while (lo > 0) {
+        const int w = lo < GLOBAL_LEVEL_BITS ? lo : GLOBAL_LEVEL_BITS;
+        lo -= w;
+        for (int i = tid; i < L1_BINS; i += SEL_THREADS) hist[i] = 0;
+        __syncthreads();
+        for (int g = tid; g < ngroups; g += SEL_THREADS) {
+            const float4 a = load_group<VEC>(p, x, g);
+            const float e[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = 4 * g + u;
+                if (i >= p.V) continue;
+                const uint64_t ck = composite_key(e[u], (uint32_t)i);
+                if ((ck >> (lo + w)) == prefix) atomicAdd(&hist[(ck >> lo) & ((1u << w) - 1u)], 1u);
+            }
+        }
+        __syncthreads();
+        if (tid < WAVE) {
+            uint32_t d, above;
+            select_digit<L1_BINS>(hist, nd, lane, d, above);
+            if (lane == 0) {
+                sh[0] = d;
+                sh[1] = above;
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << w) | sh[0];
+        nd -= sh[1];
+    }
+    const uint64_t kth = prefix;
+    for (int g0 = 0; g0 < ngroups; g0 += SEL_THREADS) {
+        const int g = g0 + tid;
+        const float4 a = g < ngroups ? load_group<VEC>(p, x, g) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float e[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = 4 * g + u;
+            const uint64_t ck = composite_key(e[u], (uint32_t)i);
+            const bool in = g < ngroups && i < p.V && (ck >> L1_SHIFT) == d1 && ck >= kth;
+            const uint32_t po = wave_append(n_out, in, lane);
+            if (in && po < (uint32_t)p.k) out[po] = i;
+        }
+    }
+}
+
+// (2 workgroups per CU: at most 128 VGPRs, i.e. 4 waves per SIMD)
+template <bool VEC, bool TIMED>
+__global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const SelectParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint64_t* buf = reinterpret_cast<uint64_t*>(smem);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + BUF_CAP * 8);
+    uint32_t* sh = hist + L1_BINS;  // [0] digit, [1] count above, [2] n_out, [3] n_buf,
+    uint32_t* cnt = sh + 4;         // [4 ..] keys per wave region
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+    const int64_t row = blockIdx.x;
+    const float* x = p.base + row * p.V;
+    int32_t* out = p.cand + row * p.k;
+    const int ngroups = (p.V + 3) / 4;
+    tk_stamp<TIMED>(p.stamps, row * 8 + 0);
+
+    for (int i = tid; i < L1_BINS; i += SEL_THREADS) hist[i] = 0;
+    if (tid == 0) {
+        sh[2] = 0;
+        sh[3] = 0;
+    }
+    // the first chunk into registers
+    float4 stash[STASH_GROUPS];
+#pragma unroll
+    for (int s = 0; s < STASH_GROUPS; ++s) {
+        const int g = s * SEL_THREADS + tid;
+        stash[s] = load_group_clamped<VEC>(p, x, g, ngroups);
+    }
+    __syncthreads();
+    // its top-12-bit histogram; -inf over the output
+#pragma unroll
+    for (int s = 0; s < STASH_GROUPS; ++s) {
+        const int g = s * SEL_THREADS + tid;
+        if (g < ngroups) {
+            const float e[4] = {stash[s].x, stash[s].y, stash[s].z, stash[s].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (VEC || 4 * g + u < p.V) atomicAdd(&hist[top_bin(e[u])], 1u);
+            fill_group<VEC>(p, row, g);
+        }
+    }
+    __syncthreads();
+    if (tid < WAVE) {
+        uint32_t d, above;
+        select_digit<L1_BINS>(hist, (uint32_t)p.k, lane, d, above);
+        if (lane == 0) sh[0] = d;
+    }
+    __syncthreads();
+    const uint32_t bin_lo = sh[0];
+    tk_stamp<TIMED>(p.stamps, row * 8 + 1);
+
+    // every key in a bin >= bin_lo into this wave's LDS region (wave-uniform count, no atomics)
+    uint64_t* region = buf + wave * REGION_CAP;
+    uint32_t n_region = 0;
+    auto offer = [&](const float4 a, int g, bool present) {
+        const float e[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = 4 * g + u;
+            const bool in = present && (VEC || i < p.V) && top_bin(e[u]) >= bin_lo;
+            const uint64_t m = __ballot(in);
+            if (m) {
+                const uint32_t pos = n_region + lanes_below(m);
+                if (in && pos < (uint32_t)REGION_CAP) region[pos] = composite_key(e[u], (uint32_t)i);
+                n_region += (uint32_t)__popcll(m);
+            }
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < STASH_GROUPS; ++s) {
+        const int g = s * SEL_THREADS + tid;
+        offer(stash[s], g, g < ngroups);
+    }
+    // the rest of the row, one batch in flight while the previous one is examined
+    constexpr int BATCH = MAIN_UNROLL * SEL_THREADS;
+    int g0 = STASH_GROUPS * SEL_THREADS;
+    float4 cur[MAIN_UNROLL];
+#pragma unroll
+    for (int u = 0; u < MAIN_UNROLL; ++u) {
+        const int g = g0 + u * SEL_THREADS + tid;
+        cur[u] = load_group_clamped<VEC>(p, x, g, ngroups);
+    }
+    for (; g0 < ngroups; g0 += BATCH) {
+        float4 nxt[MAIN_UNROLL];
+#pragma unroll
+        for (int u = 0; u < MAIN_UNROLL; ++u) {
+            const int g = g0 + BATCH + u * SEL_THREADS + tid;
+            nxt[u] = load_group_clamped<VEC>(p, x, g, ngroups);
+        }
+#pragma unroll
+        for (int u = 0; u < MAIN_UNROLL; ++u) {
+            const int g = g0 + u * SEL_THREADS + tid;
+            offer(cur[u], g, g < ngroups);
+            if (g < ngroups) fill_group<VEC>(p, row, g);
+        }
+#pragma unroll
+        for (int u = 0; u < MAIN_UNROLL; ++u) cur[u] = nxt[u];
+    }
+    if (lane == 0) cnt[wave] = n_region;
+    __syncthreads();
+    tk_stamp<TIMED>(p.stamps, row * 8 + 2);
+    bool overflow = false;
+#pragma unroll
+    for (int r = 0; r < SEL_WAVES; ++r) overflow = overflow || cnt[r] > (uint32_t)REGION_CAP;
+    if (!overflow) {
+        const uint64_t kth = lds_select(buf, cnt, (uint32_t)p.k, 0, CK_BITS, hist, sh, tid, lane);
+        tk_stamp<TIMED>(p.stamps, row * 8 + 3);
+        emit_from_buffer(buf, cnt, kth, out, sh + 2, p.k, tid, lane);
+    } else {
+        __syncthreads();
+        select_fallback<VEC>(p, x, out, buf, hist, sh, cnt, tid, lane);
+    }
+    tk_stamp<TIMED>(p.stamps, row * 8 + 4);
+}
+
+struct TopkWalkParams {
+    const int8_t* q;
+    const float* scale;
+    const void* w1;
+    const float* base;
+    const int32_t* start;
+    int32_t* tokens;
+    float* out_f32;        // greedy: dense fp32 logits row, or null
+    uint16_t* out_bf16;    // sample: dense bf16 logits row
+    const uint64_t* seeds;
+    const int64_t* positions;
+    const float* temps;
+    int32_t* cand;         // [bs][T][k] from topk_select_kernel; cleared at the end
+    uint32_t* err;
+    uint64_t* stamps;      // instrumented builds
+    int bs, T, V, k;
+};
+
+// The 64 candidates of one wave for one step. Rows are read cooperatively so that every load
+// instruction fetches whole cache lines: in load i (0..15) the 16 lanes of lane group r (lanes
+// 16r .. 16r+15) read the 16-byte chunks of the row of candidate 4i + r, lane 16r + c taking
+// chunk c. Lane 16r + i owns candidate 4i + r: its scale, base logit and vocabulary index.
+struct CandBlock {
+    int4 q[RANK / 16];  // q[i]: chunk (lane & 15) of the row of candidate 4i + (lane >> 4)
+    float s, base;
+    uint32_t v;
+};
+
+// Sum over each 16-lane row of the wave (every lane of the row gets it).
+__device__ __forceinline__ int row16_sum_i32(int x) {
+    x += (int)dpp_u32<DPP_SWAP1>((uint32_t)x);
+    x += (int)dpp_u32<DPP_SWAP2>((uint32_t)x);
+    x += (int)dpp_u32<DPP_HALF_MIRROR>((uint32_t)x);
+    x += (int)dpp_u32<DPP_MIRROR>((uint32_t)x);
+    return x;
+}
+
+// MULTI: k > TKW_THREADS, candidates in several chunks per step, loaded as they are scored;
+// otherwise one candidate per thread, the next step's loaded while this step is scored.
+template <int SAMPLE, int W1T, bool MULTI, bool TIMED>
+__global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkParams p) {
+    __shared__ __align__(16) uint32_t w1q[TKW_WAVES][RANK / 4];  // one copy per wave
+    __shared__ uint64_t wkeys[2][TKW_WAVES];                      // by step parity
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+    const int b = blockIdx.x;
+    const int64_t st0 = TK_WALK_STAMPS0 + (int64_t)b * 40;
+    tk_stamp<TIMED>(p.stamps, st0);
+
+    int prev = p.start[b];
+    if (prev < 0 || prev >= p.V) {
+        if (tid == 0) flag_error(p.err, DSPARK_ERR_INVALID_ARG);
+        prev = 0;
+    }
+    uint64_t seed = 0, P0 = 0;
+    float temp = 1.0f;
+    if constexpr (SAMPLE) {
+        seed = p.seeds[b];
+        P0 = p.positions ? (uint64_t)p.positions[b] : 0;
+        temp = p.temps[b];
+    }
+    const int32_t* req_cand = p.cand + (int64_t)b * p.T * p.k;
+    const int own = (lane & 15) * 4 + (lane >> 4);  // this lane's candidate within the wave's 64
+    // raw index of candidate j of step t (j clamped into the list; load_block bounds the value)
+    auto cand_index = [&](int t, int j) -> uint32_t {
+        return (uint32_t)req_cand[(int64_t)t * p.k + min(j, p.k - 1)];
+    };
+    auto load_block = [&](int t, uint32_t own_idx, CandBlock& blk) {
+        const uint32_t v = own_idx < (uint32_t)p.V ? own_idx : 0u;  // always: select emits rows
+        blk.v = v;
+        blk.s = p.scale[v];
+        blk.base = p.base[((int64_t)b * p.T + t) * p.V + v];
+        const int c = lane & 15;
+#pragma unroll
+        for (int i = 0; i < RANK / 16; ++i) {
+            const uint32_t vi = (uint32_t)__shfl((int)v, (lane & 48) | i);
+            blk.q[i] = reinterpret_cast<const int4*>(p.q + (int64_t)vi * RANK)[c];
+        }
+    };
+
+    // One step: this wave's copy of the W1 codes of the previous token (no workgroup barrier
+    // for it), the candidates' logits and keys, then one barrier for the step's argmax. The
+    // next step's rows load into `fill` (from `fill_idx`, loaded a step earlier) while the W1
+    // row is in flight, and the index two steps ahead into `next_idx`.
+    auto step = [&](int t, CandBlock& use, CandBlock& fill, uint32_t fill_idx, uint32_t& next_idx) {
+        const int64_t row = (int64_t)b * p.T + t;
+        const float4 w = load4_as_f32<W1T>(p.w1, (int64_t)prev * RANK + lane * 4);
+        if constexpr (!MULTI) {
+            // unconditional (past the last step they re-read the last step's rows), so that
+            // no branch keeps the compiler from counting the loads in flight
+            load_block(min(t + 1, p.T - 1), fill_idx, fill);
+            next_idx = cand_index(min(t + 2, p.T - 1), wave * WAVE + own);
+        }
+        float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+        a = wave_max_nonneg_f32(a);
+        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        const float sb = a * (1.0f / 127.0f);
+        w1q[wave][lane] = pack_codes(w, inv);
+        tk_stamp<TIMED>(p.stamps, st0 + 1 + 2 * t);
+        const int4 wc = reinterpret_cast<const int4*>(w1q[wave])[lane & 15];
+        uint64_t best = 0;
+        auto score = [&](const CandBlock& blk, bool has) {
+            int acc = 0;
+#pragma unroll
+            for (int i = 0; i < RANK / 16; ++i) {
+                int d = __builtin_amdgcn_sdot4(blk.q[i].x, wc.x, 0, false);
+                d = __builtin_amdgcn_sdot4(blk.q[i].y, wc.y, d, false);
+                d = __builtin_amdgcn_sdot4(blk.q[i].z, wc.z, d, false);
+                d = __builtin_amdgcn_sdot4(blk.q[i].w, wc.w, d, false);
+                d = row16_sum_i32(d);
+                acc = (lane & 15) == i ? d : acc;
+            }
+            const float l = walk_logit(blk.base, blk.s, sb, acc);
+            uint64_t key;
+            if constexpr (!SAMPLE) {
+                if (has && p.out_f32) p.out_f32[row * p.V + blk.v] = l;
+                key = argmax_key(l, blk.v);
+            } else {
+                const uint32_t h = bf16_bits(l);
+                if (has) p.out_bf16[row * p.V + blk.v] = (uint16_t)h;
+                float xs = bf16_value(h);
+                if (temp != 1.0f) xs = xs / temp;
+                const float g = gumbel_from_word(noise_word(seed, P0 + (uint64_t)t, blk.v));
+                key = argmax_key(xs + g, blk.v);
+            }
+            if (has) best = key > best ? key : best;
+        };
+        if constexpr (MULTI) {
+            for (int c0 = 0; c0 < p.k; c0 += TKW_THREADS) {
+                const int j = c0 + wave * WAVE + own;
+                load_block(t, cand_index(t, j), use);
+                score(use, j < p.k);
+            }
+        } else {
+            score(use, wave * WAVE + own < p.k);
+        }
+        best = wave_max_u64(best);
+        if (lane == 0) wkeys[t & 1][wave] = best;
+        __syncthreads();
+        uint64_t m = wkeys[t & 1][0];
+#pragma unroll
+        for (int w2 = 1; w2 < TKW_WAVES; ++w2) m = wkeys[t & 1][w2] > m ? wkeys[t & 1][w2] : m;
+        // every candidate at -inf: the dense row is -inf throughout, whose first max is 0
+        uint32_t token = (uint32_t)(m >> 32) <= ORDER_KEY_NEG_INF ? 0u : key_index(m);
+        if (token >= (uint32_t)p.V) token = 0;
+        if (tid == 0) p.tokens[b * p.T + t] = (int32_t)token;
+        prev = (int)token;
+        tk_stamp<TIMED>(p.stamps, st0 + 2 + 2 * t);
+    };
+
+    CandBlock ra, rb;  // alternate between steps: one is scored while the other fills
+    uint32_t ia = 0, ib = 0;
+    if (!MULTI) {
+        load_block(0, cand_index(0, wave * WAVE + own), ra);
+        ib = cand_index(min(1, p.T - 1), wave * WAVE + own);
+    }
+    for (int t = 0; t < p.T; t += 2) {
+        step(t, ra, rb, ib, ia);
+        if (t + 1 < p.T) step(t + 1, rb, ra, ia, ib);
+    }
+    // every candidate list of this request has been read before the last barrier: clear them,
+    // so that the workspace is all zero again for the dense walk
+    __syncthreads();
+    int32_t* clr = p.cand + (int64_t)b * p.T * p.k;
+    for (int i = tid; i < p.T * p.k; i += TKW_THREADS) clr[i] = 0;
+}
+
+template <bool MULTI>
+static const void* topk_walk_fn(int sample, int w1t, bool timed) {
+    if (timed && !MULTI && w1t == DT_BF16)
+        return sample ? reinterpret_cast<const void*>(&topk_walk_kernel<1, DT_BF16, false, true>)
+                      : reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_BF16, false, true>);
+    if (sample) {
+        if (w1t == DT_F32) return reinterpret_cast<const void*>(&topk_walk_kernel<1, DT_F32, MULTI, false>);
+        if (w1t == DT_BF16) return reinterpret_cast<const void*>(&topk_walk_kernel<1, DT_BF16, MULTI, false>);
+        return reinterpret_cast<const void*>(&topk_walk_kernel<1, DT_F16, MULTI, false>);
+    }
+    if (w1t == DT_F32) return reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_F32, MULTI, false>);
+    if (w1t == DT_BF16) return reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_BF16, MULTI, false>);
+    return reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_F16, MULTI, false>);
+}
+
 int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
-    (void)a;
-    (void)stream;
-    return DSPARK_ERR_UNSUPPORTED;
+    const WalkLaunch& w = a.w;
+    unsigned char* ws = static_cast<unsigned char*>(w.workspace);
+    int32_t* cand = reinterpret_cast<int32_t*>(ws + WS_TOPK);
+
+    SelectParams sp = {};
+    sp.base = w.base;
+    sp.cand = cand;
+    sp.fill_bf16 = w.sample ? w.draft_logits : nullptr;
+    sp.fill_f32 = w.sample ? nullptr : w.out_logits;
+    sp.V = w.V;
+    sp.k = a.k;
+    const bool vec = (w.V % 4 == 0) && ((uintptr_t)w.base % 16 == 0);
+    sp.stamps = reinterpret_cast<uint64_t*>(debug_knobs().stamps);
+    const bool timed = sp.stamps != nullptr;
+    void* sargs[] = {&sp};
+    const void* sel = vec ? (timed ? reinterpret_cast<const void*>(&topk_select_kernel<true, true>)
+                                   : reinterpret_cast<const void*>(&topk_select_kernel<true, false>))
+                          : reinterpret_cast<const void*>(&topk_select_kernel<false, false>);
+    if (hipFuncSetAttribute(sel, hipFuncAttributeMaxDynamicSharedMemorySize, SEL_LDS_BYTES) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+    }
+    hipError_t e = launch_walk_kernel(sel, dim3((unsigned)(w.bs * w.T)), dim3(SEL_THREADS), sargs,
+                                      (size_t)SEL_LDS_BYTES, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return DSPARK_ERR_LAUNCH;
+    }
+
+    TopkWalkParams kp = {};
+    kp.q = w.q;
+    kp.scale = w.scale;
+    kp.w1 = w.w1;
+    kp.base = w.base;
+    kp.start = w.start;
+    kp.tokens = w.tokens;
+    kp.out_f32 = w.sample ? nullptr : w.out_logits;
+    kp.out_bf16 = w.sample ? w.draft_logits : nullptr;
+    kp.seeds = w.seeds;
+    kp.positions = w.positions;
+    kp.temps = w.temps;
+    kp.cand = cand;
+    kp.err = reinterpret_cast<uint32_t*>(ws + WS_ERR);
+    kp.stamps = sp.stamps;
+    kp.bs = w.bs;
+    kp.T = w.T;
+    kp.V = w.V;
+    kp.k = a.k;
+    const int w1t = w.w1_dtype == DSPARK_F32 ? DT_F32 : w.w1_dtype == DSPARK_BF16 ? DT_BF16 : DT_F16;
+    void* kargs[] = {&kp};
+    const void* fn = a.k > TKW_THREADS ? topk_walk_fn<true>(w.sample, w1t, timed)
+                                       : topk_walk_fn<false>(w.sample, w1t, timed);
+    e = launch_walk_kernel(fn, dim3((unsigned)w.bs), dim3(TKW_THREADS),
+                           kargs, 0, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return DSPARK_ERR_LAUNCH;
+    }
+    return DSPARK_OK;
 }
 
 }  // namespace dspark

@@ -173,8 +173,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
         (void)hipGetLastError();
     }
     void* args[] = {&p};
-    const hipError_t e = hipLaunchKernel(fn, dim3(plan.num_workgroups), dim3(WALK_THREADS), args,
-                                         (size_t)plan.lds_bytes, stream);
+    const hipError_t e = launch_walk_kernel(fn, dim3(plan.num_workgroups), dim3(WALK_THREADS),
+                                            args, (size_t)plan.lds_bytes, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return DSPARK_ERR_LAUNCH;

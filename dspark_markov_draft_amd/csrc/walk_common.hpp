@@ -95,6 +95,27 @@ __device__ __forceinline__ float row16_max_nonneg_f32(float x) {
     return __uint_as_float(v);
 }
 
+// 16 int8 x int8 products added into 4 independent int32 chains (v_dot4_i32_i8), and their sum.
+__device__ __forceinline__ void dot16x4(const int4 a, const int4 b, int4& acc) {
+    acc.x = __builtin_amdgcn_sdot4(a.x, b.x, acc.x, false);
+    acc.y = __builtin_amdgcn_sdot4(a.y, b.y, acc.y, false);
+    acc.z = __builtin_amdgcn_sdot4(a.z, b.z, acc.z, false);
+    acc.w = __builtin_amdgcn_sdot4(a.w, b.w, acc.w, false);
+}
+__device__ __forceinline__ int hsum(const int4 a) { return (a.x + a.y) + (a.z + a.w); }
+
+// One W1 row quantised by one wave (lane l holds elements 4l .. 4l+3): returns lane l's four
+// codes and sets s1 = absmax / 127 (codes = rint(w * 127 / absmax), zero for a zero row).
+template <int W1T>
+__device__ __forceinline__ uint32_t w1_row_codes(const void* w1, int32_t row, int lane, float& s1) {
+    const float4 w = load4_as_f32<W1T>(w1, (int64_t)row * RANK + lane * 4);
+    float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+    a = wave_max_nonneg_f32(a);
+    const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+    s1 = a * (1.0f / 127.0f);
+    return pack_codes(w, inv);
+}
+
 // Per step: W1[prev_b] for every request, as int8 codes with one absmax scale per row
 // (s1[b] = absmax / 127, codes = rint(w * 127 / absmax)). Up to 4 requests: one per wave, 64
 // lanes on the row. More: sixteen lanes share a row: lane
@@ -109,12 +130,9 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
         // at most one request per wave: all 64 lanes on one row (elements 4l .. 4l+3)
         const int b = wave;
         if (b < p.bs) {
-            const float4 w = load4_as_f32<W1T>(p.w1, (int64_t)tok[b] * RANK + lane * 4);
-            float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
-            a = wave_max_nonneg_f32(a);
-            const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-            w1q[w1q_chunk_dword(b, lane >> 2) + (lane & 3)] = pack_codes(w, inv);
-            if (lane == 0) s1[b] = a * (1.0f / 127.0f);
+            float sb;
+            w1q[w1q_chunk_dword(b, lane >> 2) + (lane & 3)] = w1_row_codes<W1T>(p.w1, tok[b], lane, sb);
+            if (lane == 0) s1[b] = sb;
         }
         return;
     }

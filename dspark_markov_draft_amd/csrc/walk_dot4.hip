@@ -29,13 +29,6 @@ constexpr int PF_J = REG_J + LDS_J_MAX;  // row sets whose base logits are prefe
 constexpr int PF_DEPTH = 4;              // requests of base logits in flight
 constexpr int ROW_CHUNKS = RANK / 16;    // 16-byte chunks per int8 row
 
-__device__ __forceinline__ void dot16x4(const int4 a, const int4 b, int4& acc) {
-    acc.x = __builtin_amdgcn_sdot4(a.x, b.x, acc.x, false);
-    acc.y = __builtin_amdgcn_sdot4(a.y, b.y, acc.y, false);
-    acc.z = __builtin_amdgcn_sdot4(a.z, b.z, acc.z, false);
-    acc.w = __builtin_amdgcn_sdot4(a.w, b.w, acc.w, false);
-}
-__device__ __forceinline__ int hsum(const int4 a) { return (a.x + a.y) + (a.z + a.w); }
 
 template <int SAMPLE, int W1T, int TIMED>
 __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const WalkParams p) {
@@ -128,7 +121,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                     }
                     // logit of row v -> output store and argmax key
                     auto finish = [&](int v, float base_v, float scale_v, int acc) -> uint64_t {
-                        const float l = base_v + (scale_v * sb) * (float)acc;
+                        const float l = walk_logit(base_v, scale_v, sb, acc);
                         if constexpr (!SAMPLE) {
                             if (p.out_logits) p.out_logits[orow + v] = l;
                             return argmax_key(l, (uint32_t)v);

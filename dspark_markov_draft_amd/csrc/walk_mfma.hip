@@ -164,10 +164,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 const float4 bv = *reinterpret_cast<const float4*>(sbase + off);
                 const bool ok = vb && vt < vend;
                 float l[4];
-                l[0] = bv.x + (sv.x * sb) * (float)acc[0];
-                l[1] = bv.y + (sv.y * sb) * (float)acc[1];
-                l[2] = bv.z + (sv.z * sb) * (float)acc[2];
-                l[3] = bv.w + (sv.w * sb) * (float)acc[3];
+                l[0] = walk_logit(bv.x, sv.x, sb, acc[0]);
+                l[1] = walk_logit(bv.y, sv.y, sb, acc[1]);
+                l[2] = walk_logit(bv.z, sv.z, sb, acc[2]);
+                l[3] = walk_logit(bv.w, sv.w, sb, acc[3]);
                 uint64_t key[4];
                 if constexpr (!SAMPLE) {
                     if (p.out_logits != nullptr && ok)
@@ -201,16 +201,23 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 }
             };
 
+            // all register tiles' MFMAs first, each into its own accumulator, so the matrix
+            // core runs ahead while the VALU finishes tile after tile
+            v4i accs[NT_REG];
+#pragma unroll
+            for (int tw = 0; tw < NT_REG; ++tw) {
+                accs[tw] = (v4i){0, 0, 0, 0};
+                if (tw * WALK_WAVES + wave < ntiles) {
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb],
+                                                                         accs[tw], 0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int tw = 0; tw < NT_REG; ++tw) {
                 const int tl = tw * WALK_WAVES + wave;
-                if (tl < ntiles) {
-                    v4i acc = {0, 0, 0, 0};
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
-                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb], acc, 0, 0, 0);
-                    finish4(acc, row0 + tl * TILE_ROWS + g * 4);
-                }
+                if (tl < ntiles) finish4(accs[tw], row0 + tl * TILE_ROWS + g * 4);
             }
             for (int tw = NT_REG; tw < ntw; ++tw) {
                 const int tl = tw * WALK_WAVES + wave;

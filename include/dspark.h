@@ -199,16 +199,31 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *       When set, dense walks with bf16 W1 run an instrumented build of the same kernel that
  *       stores the 100 MHz device clock per workgroup: [0] start, [1] W2 resident, then per step
  *       t at 2 + 5t: W1 codes ready, slice argmax done, own slot stored, reductions done,
- *       result words seen. For profiling only.
+ *       result words seen. Top-k walks with bf16 W1 (k <= 512, V % 4 == 0) use words
+ *       row * 8 + (0 start, 1 first bound, 2 row scanned, 3 k-th key, 4 done) for each
+ *       (request, step) row of the candidate select, and 8192 + request * 40 + (0 start, then
+ *       per step t: 1 + 2t W1 codes ready, 2 + 2t token known) for the walk. For profiling only;
+ *   DSPARK_DEBUG_KERNEL_TIMING: n in 1..4096 launches every later walk kernel on the current
+ *       device with hipExtLaunchKernel and one of a ring of n HIP event pairs, which the dispatch
+ *       records at the kernel's start and end (read them with dspark_kernel_times); 0 frees the
+ *       ring. For benchmarks; do not enable it around graph capture.
  */
 enum dspark_debug_key {
     DSPARK_DEBUG_MAX_WORKGROUPS = 1,
     DSPARK_DEBUG_SPIN_LIMIT = 2,
     DSPARK_DEBUG_WAIT_UNSET_FLAG = 3,
     DSPARK_DEBUG_STAMPS = 4,
-    DSPARK_DEBUG_FORCE_PATH = 5
+    DSPARK_DEBUG_FORCE_PATH = 5,
+    DSPARK_DEBUG_KERNEL_TIMING = 6
 };
 int dspark_debug_set(int key, int64_t value);
+
+/* Durations in microseconds of the walk kernels launched while DSPARK_DEBUG_KERNEL_TIMING was on,
+ * since it was switched on or last read: at most the ring size and `max` of the most recent,
+ * oldest first, into `us`; their number into *count. Blocks until those kernels have finished.
+ * Returns DSPARK_ERR_INVALID_ARG for null pointers or max < 0, DSPARK_ERR_LAUNCH if an event
+ * query fails; with timing off, *count = 0. */
+int dspark_kernel_times(float* us, int max, int* count);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,32 @@ class Problem:
         torch.cuda.synchronize()
         return tok.cpu().numpy(), lb_bits(lb)
 
+    def topk(self, k, sample=False, want_logits=True, ws=None, qs=None):
+        """Top-k walk: (tokens, dense fp32 logits or None) greedy; (tokens, bf16 bits) sample."""
+        bs, T, V = self.shape
+        q, s = qs if qs is not None else self.quantize()
+        ws = dm.new_workspace(bs, T, V, k) if ws is None else ws
+        if sample:
+            tok, lb = dm.dspark_walk_topk(q, s, self.w1, self.base, self.start, k, ws,
+                                          sample=True, seeds=self.seeds,
+                                          temperature=self.temps, positions=self.pos)
+            torch.cuda.synchronize()
+            return tok.cpu().numpy(), lb_bits(lb)
+        logits = torch.empty((bs, T, V), dtype=torch.float32, device=DEV) if want_logits else None
+        tok, _ = dm.dspark_walk_topk(q, s, self.w1, self.base, self.start, k, ws,
+                                     draft_logits=logits)
+        torch.cuda.synchronize()
+        return tok.cpu().numpy(), (None if logits is None else logits.cpu().numpy())
+
+    def check_topk(self, k, tokens, out, sample=False, requests=None):
+        q, s = self.oracle_q()
+        if sample:
+            return check_walk(q, s, self.w1_np(), self.base_np, self.start_np, tokens,
+                              sample=True, seeds=self.seeds_np, temps=self.temps_np,
+                              positions=self.pos_np, lb=out, k=k, requests=requests)
+        return check_walk(q, s, self.w1_np(), self.base_np, self.start_np, tokens, logits=out,
+                          k=k, requests=requests)
+
     def check_greedy(self, tokens, logits, requests=None):
         q, s = self.oracle_q()
         return check_walk(q, s, self.w1_np(), self.base_np, self.start_np, tokens, logits=logits,

@@ -212,6 +212,13 @@ def test_misc_validation():
     assert L.dspark_debug_set(B.DEBUG_SPIN_LIMIT, -1) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_FORCE_PATH, 3) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_STAMPS, 12) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(B.DEBUG_KERNEL_TIMING, 4097) == B.ERR_INVALID_ARG
+    n = ctypes.c_int32(-1)
+    buf = (ctypes.c_float * 4)()
+    assert L.dspark_kernel_times(None, 4, ctypes.byref(n)) == B.ERR_INVALID_ARG
+    assert L.dspark_kernel_times(buf, -1, ctypes.byref(n)) == B.ERR_INVALID_ARG
+    assert L.dspark_kernel_times(buf, 4, None) == B.ERR_INVALID_ARG
+    assert L.dspark_kernel_times(buf, 4, ctypes.byref(n)) == B.OK and n.value == 0
     assert L.dspark_walk_plan_query(1, 1, 10, None) == B.ERR_INVALID_ARG
     assert L.dspark_walk_plan_for(0, 163840, 1, 1, 10, ctypes.byref(B.WalkPlan())) == \
         B.ERR_INVALID_ARG

@@ -1,0 +1,170 @@
+"""GPU parity of the top-k walk (candidate selection + walk over the candidates) against the
+CPU oracle, through the C ABI.
+
+The oracle's candidates are the k largest base logits ordered by (value desc, index asc); its
+step fills -inf outside them and runs the unchanged greedy / Gumbel-max rule over the dense row.
+Checked: the -inf pattern of the dense output (the candidate set, exactly), candidate logits
+within 2e-3, bf16 rows under the dense walk's rule, tokens teacher-forced; k = V against the
+dense walk bit for bit; boundary ties, +-0, -inf rows and the large-bin path of the select.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dspark_markov_draft_amd as dm
+import dspark_markov_draft_amd.binding as B
+from dspark_markov_draft_amd.synth import CASES, make_inputs
+from tests.gpu_helpers import DEV, Problem, random_problem
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_check(p, k, mode, requests=None):
+    sample = mode == "sample"
+    tok, out = p.topk(k, sample=sample)
+    rep = p.check_topk(k, tok, out, sample=sample, requests=requests)
+    return tok, out, rep
+
+
+SMALL = [  # V, T, bs, dtype, k
+    (4096, 4, 1, torch.float32, 64),
+    (5001, 3, 3, torch.bfloat16, 100),      # V % 4 != 0: element-wise select path
+    (20000, 3, 5, torch.bfloat16, 512),
+    (3000, 5, 16, torch.float16, 2048),
+    (257, 4, 2, torch.float32, 257),        # k = V
+    (1, 2, 1, torch.bfloat16, 1),
+    (9000, 2, 64, torch.bfloat16, 1),
+    (12345, 3, 7, torch.bfloat16, 777),
+]
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+@pytest.mark.parametrize("V,T,bs,dtype,k", SMALL)
+def test_topk_parity_small(V, T, bs, dtype, k, mode):
+    p = random_problem(V, T, bs, dtype=dtype, seed=V + 7 * k + bs,
+                       temps=np.linspace(0.5, 1.5, bs).astype(np.float32),
+                       positions=np.arange(bs, dtype=np.int64) * 3)
+    _, _, rep = _run_check(p, k, mode)
+    print(V, T, bs, k, mode, rep.summary())
+    assert rep.ok, rep.summary()
+
+
+def test_topk_candidate_set_is_exact():
+    """Finite entries of the greedy dense output are exactly the k best base logits
+    (lexicographic: value desc, index asc), for every row."""
+    V, T, bs, k = 30000, 3, 4, 700
+    p = random_problem(V, T, bs, seed=3)
+    _, dense = p.topk(k)
+    for b in range(bs):
+        for t in range(T):
+            row = p.base_np[b, t]
+            want = np.lexsort((np.arange(V), -row))[:k]
+            got = np.flatnonzero(np.isfinite(dense[b, t]))
+            assert np.array_equal(np.sort(want), got), (b, t)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_topk_k_equals_V_is_the_dense_walk(mode):
+    """k = V selects every entry: tokens and dense outputs equal the dense walk's bit for bit
+    (V = 2048, the largest k the library takes)."""
+    p = random_problem(2048, 4, 3, seed=11, temps=np.array([1.0, 0.7, 1.3], np.float32))
+    qs = p.quantize()
+    V = p.shape[2]
+    if mode == "greedy":
+        d_tok, d_out = p.greedy(qs=qs)
+        k_tok, k_out = p.topk(V, qs=qs)
+        assert np.array_equal(d_out.view(np.uint32), k_out.view(np.uint32))
+    else:
+        d_tok, d_out = p.sample(qs=qs)
+        k_tok, k_out = p.topk(V, sample=True, qs=qs)
+        assert np.array_equal(d_out, k_out)
+    assert np.array_equal(d_tok, k_tok)
+
+
+def _zero_w_problem(base, start=None):
+    base = np.asarray(base, np.float32)
+    bs, T, V = base.shape
+    w = torch.zeros(V, 256, dtype=torch.bfloat16)
+    start = np.zeros(bs, np.int32) if start is None else np.asarray(start, np.int32)
+    return Problem(w, w.clone(), base, start)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_topk_boundary_ties_take_lower_indices(mode):
+    """Rows of few distinct values (many equal keys across the k-th position, +0 and -0 mixed):
+    the lower indices win at the boundary."""
+    rng = np.random.default_rng(5)
+    V, T = 3000, 3
+    base = rng.integers(-3, 4, size=(2, T, V)).astype(np.float32)
+    base[base == 0] = np.where(rng.random(int((base == 0).sum())) < 0.5, 0.0, -0.0)
+    p = _zero_w_problem(base)
+    for k in (1, 5, 400, 1234):
+        tok, out = p.topk(k, sample=mode == "sample")
+        rep = p.check_topk(k, tok, out, sample=mode == "sample")
+        assert rep.ok, (k, rep.summary())
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_topk_large_bin_path(mode):
+    """A row whose k-th key shares its top bits with more elements than the select keeps in LDS
+    (constant rows; a narrow band) takes the global-memory levels; the result is unchanged."""
+    V, T, k = 20000, 3, 300
+    base = np.zeros((1, T, V), np.float32)
+    base[0, 1] = 1.0 + np.arange(V, dtype=np.float32) * 1e-7   # ~20000 keys in one top bin
+    base[0, 2, ::7] = 2.0                                        # ties above a constant floor
+    p = _zero_w_problem(base)
+    tok, out = p.topk(k, sample=mode == "sample")
+    rep = p.check_topk(k, tok, out, sample=mode == "sample")
+    assert rep.ok, rep.summary()
+    if mode == "greedy":
+        assert np.array_equal(np.flatnonzero(np.isfinite(out[0, 0])), np.arange(k))
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_topk_all_candidates_neg_inf_gives_token_zero(mode):
+    """A step whose candidates are all -inf: the dense row is -inf everywhere, and torch.argmax
+    of such a row is 0 (the first maximum), whether or not 0 is a candidate."""
+    V, T, k = 4096, 2, 16
+    base = np.full((1, T, V), -np.inf, np.float32)
+    base[0, 1, 100:200] = np.linspace(-1, 1, 100)
+    p = _zero_w_problem(base, start=[7])
+    tok, out = p.topk(k, sample=mode == "sample")
+    assert tok[0, 0] == 0
+    rep = p.check_topk(k, tok, out, sample=mode == "sample")
+    assert rep.ok, rep.summary()
+
+
+@pytest.mark.parametrize("mode,reqs", [("greedy", [0, 21, 63]), ("sample", [2, 50])])
+def test_topk_full_size(mode, reqs):
+    case = CASES["topk512_v151936_t7_bs64"]
+    inp = make_inputs(case)
+    p = Problem(inp.w1, inp.w2, inp.base, inp.start, seeds=inp.seeds,
+                temps=inp.temperature.numpy())
+    _, _, rep = _run_check(p, case.k, mode, requests=reqs)
+    print(case.name, mode, rep.summary())
+    assert rep.ok, rep.summary()
+
+
+def test_topk_leaves_workspace_zeroed_for_dense_walks():
+    """The candidate lists live in the workspace; the walk clears them, so a dense walk on the
+    same workspace afterwards is unaffected."""
+    p = random_problem(10000, 4, 8, seed=17)
+    qs = p.quantize()
+    bs, T, V = p.shape
+    ws = dm.new_workspace(bs, T, V, 1000)
+    tk = p.topk(1000, ws=ws, qs=qs)
+    assert int(ws.count_nonzero()) == 0
+    dense = p.greedy(ws=ws, qs=qs)
+    assert p.check_greedy(*dense).ok
+    tk2 = p.topk(1000, ws=ws, qs=qs)
+    assert np.array_equal(tk[0], tk2[0]) and np.array_equal(tk[1].view(np.uint32),
+                                                            tk2[1].view(np.uint32))
+    assert dm.dspark_workspace_status(ws) == 0
+
+
+def test_topk_out_of_range_start_is_contained():
+    p = random_problem(5000, 2, 2, seed=19)
+    p.start = torch.tensor([3, 5000], dtype=torch.int32, device=DEV)
+    ws = dm.new_workspace(2, 2, 5000, 50)
+    p.topk(50, ws=ws)
+    assert dm.dspark_workspace_status(ws) == B.ERR_INVALID_ARG

@@ -278,6 +278,25 @@ def test_back_to_back_calls_share_workspace():
     assert int(ws.count_nonzero()) == 0
 
 
+def test_kernel_timing_hook():
+    """Dispatch-recorded kernel times: one positive duration per launch, results unchanged."""
+    p = random_problem(30000, 4, 2, seed=23)
+    qs = p.quantize()
+    ws = dm.new_workspace(2, 4, 30000)
+    ref = p.greedy(qs=qs, ws=ws)
+    dm.dspark_debug_set(B.DEBUG_KERNEL_TIMING, 3)
+    try:
+        outs = [p.greedy(qs=qs, ws=ws) for _ in range(5)]
+        times = dm.dspark_kernel_times()
+    finally:
+        dm.dspark_debug_set(B.DEBUG_KERNEL_TIMING, 0)
+    assert len(times) == 3 and all(0.0 < t < 1e5 for t in times)
+    assert dm.dspark_kernel_times() == []
+    for tok, logits in outs:
+        assert np.array_equal(tok, ref[0]) and np.array_equal(logits, ref[1])
+    assert dm.dspark_workspace_status(ws) == 0
+
+
 def test_timeout_is_reported_and_recovers():
     """The host makes every grid-wide wait also wait for a flag it never sets; each wait runs
     into its (small) spin limit, the kernel still completes, and the error word says so."""
