@@ -42,7 +42,7 @@ constexpr int REGION_CAP = 992;                       // LDS keys per wave (8 wa
 constexpr int BUF_CAP = SEL_WAVES * REGION_CAP;       // fits two workgroups per CU
 constexpr int LDS_LEVEL_BITS = 10;                    // later levels over the LDS buffer
 constexpr int GLOBAL_LEVEL_BITS = 12;                 // later levels over the row (fallback)
-constexpr int SEL_LDS_BYTES = BUF_CAP * 8 + L1_BINS * 4 + 64;
+constexpr int SEL_LDS_BYTES = BUF_CAP * 8 + L1_BINS * 4 + 128;
 constexpr int TKW_THREADS = 512;
 constexpr int TKW_WAVES = TKW_THREADS / WAVE;
 static_assert(DSPARK_MAX_V <= (1 << IDX_BITS), "vocabulary index must fit the composite key");
@@ -57,7 +57,8 @@ __device__ __forceinline__ uint32_t composite_index(uint64_t ck) {
 __device__ __forceinline__ uint32_t top_bin(float x) { return order_key32(x) >> (32 - L1_BITS); }
 
 // Instrumented builds: thread 0 records the 100 MHz device clock. Select rows use words
-// row * 8 + (0 start, 1 first bound known, 2 row scanned, 3 k-th key known, 4 done); walk
+// row * 8 + (0 start, 1 first bound known, 2 row scanned, 3 k-th key known, 4 done, 5 bin of
+// the k-th key known, 6 bins above it emitted); walk
 // requests use TK_WALK_STAMPS0 + request * 40 + (0 start, then per step t: 1 + 2t W1 codes
 // ready, 2 + 2t token known).
 constexpr int TK_WALK_STAMPS0 = 8192;
@@ -192,24 +193,28 @@ __device__ __forceinline__ bool buf_slot(const uint32_t* cnt, uint32_t e) {
 
 // Radix levels over the keys in LDS (all threads): from bit `lo` down, among keys whose bits
 // above `lo` equal `prefix`, the need-th largest. The first level below bit 51 takes 12 bits,
-// later ones 10. Returns the full 51-bit key. cnt: per-region key counts.
+// later ones 10 (NBINS = 1024 takes only 10-bit levels). Returns the full 51-bit key. The keys
+// are buf[e] for e < n_linear, or, with n_linear < 0, the wave regions of counts cnt.
+template <int NBINS = L1_BINS>
 __device__ __forceinline__ uint64_t lds_select(const uint64_t* buf, const uint32_t* cnt,
-                                               uint32_t need, uint64_t prefix, int lo,
-                                               uint32_t* hist, uint32_t* sh, int tid, int lane) {
+                                               int n_linear, uint32_t need, uint64_t prefix,
+                                               int lo, uint32_t* hist, uint32_t* sh, int tid,
+                                               int lane) {
+    const uint32_t n_slots = n_linear < 0 ? (uint32_t)BUF_CAP : (uint32_t)n_linear;
     while (lo > 0) {
         const int w = lo == CK_BITS ? L1_BITS : (lo < LDS_LEVEL_BITS ? lo : LDS_LEVEL_BITS);
         lo -= w;
-        for (int i = tid; i < L1_BINS; i += SEL_THREADS) hist[i] = 0;
+        for (int i = tid; i < NBINS; i += SEL_THREADS) hist[i] = 0;
         __syncthreads();
-        for (uint32_t e = tid; e < (uint32_t)BUF_CAP; e += SEL_THREADS) {
-            if (!buf_slot(cnt, e)) continue;
+        for (uint32_t e = tid; e < n_slots; e += SEL_THREADS) {
+            if (n_linear < 0 && !buf_slot(cnt, e)) continue;
             const uint64_t ck = buf[e];
             if ((ck >> (lo + w)) == prefix) atomicAdd(&hist[(ck >> lo) & ((1u << w) - 1u)], 1u);
         }
         __syncthreads();
         if (tid < WAVE) {
             uint32_t d, above;
-            select_digit<L1_BINS>(hist, need, lane, d, above);
+            select_digit<NBINS>(hist, need, lane, d, above);
             if (lane == 0) {
                 sh[0] = d;
                 sh[1] = above;
@@ -222,13 +227,15 @@ __device__ __forceinline__ uint64_t lds_select(const uint64_t* buf, const uint32
     return prefix;
 }
 
-// Appends the keys >= kth of the buffer to the candidate row (all threads).
+// Appends the keys >= kth of the buffer whose top 12 bits are `bin` to the candidate row (all
+// threads).
 __device__ __forceinline__ void emit_from_buffer(const uint64_t* buf, const uint32_t* cnt,
-                                                 uint64_t kth, int32_t* out, uint32_t* n_out,
-                                                 int k, int tid, int lane) {
+                                                 uint64_t kth, uint32_t bin, int32_t* out,
+                                                 uint32_t* n_out, int k, int tid, int lane) {
     for (uint32_t e0 = 0; e0 < (uint32_t)BUF_CAP; e0 += SEL_THREADS) {
         const uint32_t e = e0 + tid;
-        const bool in = e < (uint32_t)BUF_CAP && buf_slot(cnt, e) && buf[e] >= kth;
+        const bool in = e < (uint32_t)BUF_CAP && buf_slot(cnt, e) && buf[e] >= kth &&
+                        (buf[e] >> L1_SHIFT) == bin;
         const uint32_t po = wave_append(n_out, in, lane);
         if (in && po < (uint32_t)k) out[po] = (int32_t)composite_index(buf[e]);
     }
@@ -294,8 +301,8 @@ __device__ __forceinline__ void select_fallback(const SelectParams& p, const flo
             cnt[r] = n <= 0 ? 0u : (n >= REGION_CAP ? (uint32_t)REGION_CAP : (uint32_t)n);
         }
         __syncthreads();
-        const uint64_t kth = lds_select(buf, cnt, need, d1, L1_SHIFT, hist, sh, tid, lane);
-        emit_from_buffer(buf, cnt, kth, out, n_out, p.k, tid, lane);
+        const uint64_t kth = lds_select(buf, cnt, -1, need, d1, L1_SHIFT, hist, sh, tid, lane);
+        emit_from_buffer(buf, cnt, kth, d1, out, n_out, p.k, tid, lane);
         return;
     }
     uint64_t prefix = d1;
@@ -353,7 +360,9 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     uint64_t* buf = reinterpret_cast<uint64_t*>(smem);
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + BUF_CAP * 8);
     uint32_t* sh = hist + L1_BINS;  // [0] digit, [1] count above, [2] n_out, [3] n_buf,
-    uint32_t* cnt = sh + 4;         // [4 ..] keys per wave region
+                                    // [4] keys of the k-th key's bin, [16 .. 31] per-wave
+                                    // counts of the compaction
+    uint32_t* cnt = sh + 8;         // [8 .. 15] keys per wave region
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
     const int64_t row = blockIdx.x;
     const float* x = p.base + row * p.V;
@@ -395,8 +404,11 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     __syncthreads();
     const uint32_t bin_lo = sh[0];
     tk_stamp<TIMED>(p.stamps, row * 8 + 1);
+    for (int i = tid; i < L1_BINS; i += SEL_THREADS) hist[i] = 0;  // now: the offered keys
+    __syncthreads();
 
-    // every key in a bin >= bin_lo into this wave's LDS region (wave-uniform count, no atomics)
+    // every key in a bin >= bin_lo into this wave's LDS region (wave-uniform count, no atomics
+    // for the position) and into the histogram
     uint64_t* region = buf + wave * REGION_CAP;
     uint32_t n_region = 0;
     auto offer = [&](const float4 a, int g, bool present) {
@@ -404,11 +416,15 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = 4 * g + u;
-            const bool in = present && (VEC || i < p.V) && top_bin(e[u]) >= bin_lo;
+            const uint32_t bin = top_bin(e[u]);
+            const bool in = present && (VEC || i < p.V) && bin >= bin_lo;
             const uint64_t m = __ballot(in);
             if (m) {
                 const uint32_t pos = n_region + lanes_below(m);
-                if (in && pos < (uint32_t)REGION_CAP) region[pos] = composite_key(e[u], (uint32_t)i);
+                if (in) {
+                    atomicAdd(&hist[bin], 1u);
+                    if (pos < (uint32_t)REGION_CAP) region[pos] = composite_key(e[u], (uint32_t)i);
+                }
                 n_region += (uint32_t)__popcll(m);
             }
         }
@@ -449,13 +465,86 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     bool overflow = false;
 #pragma unroll
     for (int r = 0; r < SEL_WAVES; ++r) overflow = overflow || cnt[r] > (uint32_t)REGION_CAP;
-    if (!overflow) {
-        const uint64_t kth = lds_select(buf, cnt, (uint32_t)p.k, 0, CK_BITS, hist, sh, tid, lane);
-        tk_stamp<TIMED>(p.stamps, row * 8 + 3);
-        emit_from_buffer(buf, cnt, kth, out, sh + 2, p.k, tid, lane);
-    } else {
-        __syncthreads();
+    if (overflow) {
         select_fallback<VEC>(p, x, out, buf, hist, sh, cnt, tid, lane);
+        tk_stamp<TIMED>(p.stamps, row * 8 + 4);
+        return;
+    }
+    // the bin d1 of the k-th key, from the histogram of the offered keys
+    if (tid < WAVE) {
+        uint32_t d, above;
+        select_digit<L1_BINS>(hist, (uint32_t)p.k, lane, d, above);
+        if (lane == 0) {
+            sh[0] = d;
+            sh[1] = above;
+            sh[4] = 0;  // keys of bin d1 collected below
+        }
+    }
+    __syncthreads();
+    tk_stamp<TIMED>(p.stamps, row * 8 + 5);
+    const uint32_t d1 = sh[0];
+    const uint32_t need = (uint32_t)p.k - sh[1];
+    // Keys above bin d1 are in; those of bin d1 go to a small list in the first half of the
+    // histogram's memory (no longer needed). Each wave counts its own region's keys of both
+    // kinds, the waves take consecutive ranges of the outputs, then each writes its keys: no
+    // atomics. (A bin too large for the list takes radix levels over the whole buffer.)
+    constexpr uint32_t SMALL_CAP = 1024;
+    uint64_t* small = reinterpret_cast<uint64_t*>(hist);
+    uint32_t* hist2 = hist + 2 * SMALL_CAP;          // 1024 bins after the small list
+    const uint64_t* mine = buf + wave * REGION_CAP;
+    const uint32_t n_mine = cnt[wave];
+    uint32_t n_hi = 0, n_eq = 0;
+    for (uint32_t e0 = 0; e0 < n_mine; e0 += WAVE) {
+        const uint32_t e = e0 + lane;
+        const uint64_t ck = e < n_mine ? mine[e] : 0ull;
+        const uint32_t bin = (uint32_t)(ck >> L1_SHIFT);
+        n_hi += (uint32_t)__popcll(__ballot(e < n_mine && bin > d1));
+        n_eq += (uint32_t)__popcll(__ballot(e < n_mine && bin == d1));
+    }
+    __syncthreads();  // every wave is past select_digit's reads of the histogram
+    uint32_t* wc = sh + 16;  // [16 + w] keys above d1, [24 + w] keys of d1, per wave
+    if (lane == 0) {
+        wc[wave] = n_hi;
+        wc[SEL_WAVES + wave] = n_eq;
+    }
+    __syncthreads();
+    uint32_t off_hi = 0, off_eq = 0, m = 0;
+#pragma unroll
+    for (int w = 0; w < SEL_WAVES; ++w) {
+        off_hi += w < wave ? wc[w] : 0u;
+        off_eq += w < wave ? wc[SEL_WAVES + w] : 0u;
+        m += wc[SEL_WAVES + w];
+    }
+    for (uint32_t e0 = 0; e0 < n_mine; e0 += WAVE) {
+        const uint32_t e = e0 + lane;
+        const uint64_t ck = e < n_mine ? mine[e] : 0ull;
+        const uint32_t bin = (uint32_t)(ck >> L1_SHIFT);
+        const bool hi = e < n_mine && bin > d1, eq = e < n_mine && bin == d1;
+        const uint64_t mh = __ballot(hi), me = __ballot(eq);
+        const uint32_t ph = off_hi + lanes_below(mh), pe = off_eq + lanes_below(me);
+        if (hi && ph < (uint32_t)p.k) out[ph] = (int32_t)composite_index(ck);
+        if (eq && pe < SMALL_CAP) small[pe] = ck;
+        off_hi += (uint32_t)__popcll(mh);
+        off_eq += (uint32_t)__popcll(me);
+    }
+    if (tid == 0) sh[2] = (uint32_t)p.k - need;  // keys emitted so far (all above bin d1)
+    __syncthreads();
+    tk_stamp<TIMED>(p.stamps, row * 8 + 6);
+    if (m <= SMALL_CAP) {
+        const uint64_t kth = lds_select<1024>(small, cnt, (int)m, need, d1, L1_SHIFT, hist2, sh,
+                                              tid, lane);
+        tk_stamp<TIMED>(p.stamps, row * 8 + 3);
+        for (uint32_t e0 = 0; e0 < m; e0 += SEL_THREADS) {
+            const uint32_t e = e0 + tid;
+            const bool in = e < m && small[e] >= kth;
+            const uint32_t po = wave_append(sh + 2, in, lane);
+            if (in && po < (uint32_t)p.k) out[po] = (int32_t)composite_index(small[e]);
+        }
+    } else {
+        // radix levels over the whole buffer (still intact)
+        const uint64_t kth = lds_select(buf, cnt, -1, need, d1, L1_SHIFT, hist, sh, tid, lane);
+        tk_stamp<TIMED>(p.stamps, row * 8 + 3);
+        emit_from_buffer(buf, cnt, kth, d1, out, sh + 2, p.k, tid, lane);
     }
     tk_stamp<TIMED>(p.stamps, row * 8 + 4);
 }

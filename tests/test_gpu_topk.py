@@ -120,6 +120,29 @@ def test_topk_large_bin_path(mode):
         assert np.array_equal(np.flatnonzero(np.isfinite(out[0, 0])), np.arange(k))
 
 
+@pytest.mark.parametrize("n_bin", [40, 1500, 5000])
+@pytest.mark.parametrize("k", [17, 300])
+def test_topk_select_kth_bin_sizes(n_bin, k):
+    """Rows whose k-th key shares its top 12 bits with n_bin keys spread along the row (distinct
+    values 1 + j 2^-20 in [1, 1.125)): a small bin is ranked directly, a medium one takes radix
+    levels over a compacted list, a large one radix levels over the whole buffer."""
+    V, T = 24000, 2
+    base = np.zeros((1, T, V), np.float32)
+    rng = np.random.default_rng(n_bin + k)
+    for t in range(T):
+        pos = np.sort(rng.choice(V, n_bin, replace=False))
+        base[0, t, pos] = 1.0 + rng.permutation(n_bin).astype(np.float32) * 2.0 ** -20
+        base[0, t, rng.choice(V, 5, replace=False)] = 3.0 + t   # a few keys above the bin
+    p = _zero_w_problem(base)
+    tok, dense = p.topk(k)
+    rep = p.check_topk(k, tok, dense)
+    assert rep.ok, rep.summary()
+    for t in range(T):
+        row = base[0, t]
+        want = np.sort(np.lexsort((np.arange(V), -row))[:k])
+        assert np.array_equal(np.flatnonzero(np.isfinite(dense[0, t])), want), t
+
+
 @pytest.mark.parametrize("mode", ["greedy", "sample"])
 def test_topk_all_candidates_neg_inf_gives_token_zero(mode):
     """A step whose candidates are all -inf: the dense row is -inf everywhere, and torch.argmax
