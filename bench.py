@@ -38,6 +38,7 @@ from dspark_markov_draft_amd.synth import CASES, make_inputs, seeds_as_int64  # 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
 KERNEL_NAMES = {1: "dense_walk_dot4_kernel", 2: "dense_walk_mfma_kernel"}
+TOPK_KERNELS = "topk_select_kernel+topk_walk_kernel"
 
 
 def log(*a):
@@ -156,29 +157,36 @@ def time_walk(w, steps, warmup, flush, stream, dirty=False):
     return us, wall, warm_us, dirty_us, kus
 
 
-def csrc_digest():
-    """sha256 over the library's sources (name and contents, sorted by name)."""
+COMMON_SOURCES = ["device_common.hpp", "internal.hpp", "walk_common.hpp", "walk.hip", "api.hip"]
+KERNEL_SOURCES = {
+    "dense_walk_dot4_kernel": COMMON_SOURCES + ["walk_dot4.hip"],
+    "dense_walk_mfma_kernel": COMMON_SOURCES + ["walk_mfma.hip"],
+    "topk_select_kernel+topk_walk_kernel": COMMON_SOURCES + ["topk.hip"],
+}
+
+
+def sources_digest(kernel):
+    """sha256 over the sources that define `kernel` (name and contents) and the C header."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "dspark_markov_draft_amd", "csrc")
-    for n in sorted(os.listdir(d)):
-        if n.endswith((".hip", ".hpp", ".h")):
-            h.update(n.encode())
-            h.update(open(os.path.join(d, n), "rb").read())
+    for n in sorted(KERNEL_SOURCES[kernel]):
+        h.update(n.encode())
+        h.update(open(os.path.join(d, n), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "dspark.h"), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, kernel):
     """Counter-measured HBM bytes per launch for this workload, or None if not measured or the
-    sources changed since."""
+    kernel's sources changed since."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(p):
+    if not os.path.exists(p) or kernel not in KERNEL_SOURCES:
         return None
-    rec = json.load(open(p))
-    if rec.get("csrc_sha256") != csrc_digest():
+    rec = json.load(open(p)).get("workloads", {}).get(workload)
+    if rec is None or rec.get("kernel") != kernel or rec.get("sources_sha256") != sources_digest(kernel):
         return None
-    return rec.get("workloads", {}).get(workload)
+    return rec
 
 
 def cpu_baseline(case, budget_s=20.0):
@@ -210,10 +218,15 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time one case:mode only (profiling)")
+    ap.add_argument("--print-digest", default=None, metavar="KERNEL",
+                    help="print the source digest of a kernel (for the traffic record) and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB, whose "
                          "known byte count calibrates the HBM traffic counters")
     args = ap.parse_args()
+    if args.print_digest:
+        print(sources_digest(args.print_digest))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "walk's sharding across GPUs is a design, not an implementation.", file=sys.stderr)
@@ -289,7 +302,8 @@ def main():
         cpu = cpu_baseline(head_case)
         log(f"[bench] oracle {cpu['value']:.0f} us/walk on {cpu['cores']} threads")
 
-    tr = measured_traffic(f"{head_case.name}:{head_mode}")
+    kernel = TOPK_KERNELS if head_case.k else KERNEL_NAMES.get(plan["path"], "?")
+    tr = measured_traffic(f"{head_case.name}:{head_mode}", kernel)
     traffic = None if tr is None else tr["fetch_bytes"] + tr["write_bytes"]
 
     out = {
@@ -317,7 +331,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
-                     "kernel": KERNEL_NAMES.get(plan["path"], "?")},
+                     "kernel": kernel},
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
