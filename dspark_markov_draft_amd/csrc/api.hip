@@ -116,7 +116,7 @@ int dspark_walk_plan_query(int64_t bs, int64_t T, int64_t V, dspark_walk_plan* p
     DeviceInfo dev;
     const int d = current_device_info(&dev);
     if (d != DSPARK_OK) return d;
-    return plan_walk(dev, bs, T, V, plan);
+    return plan_walk(dev, bs, T, V, 0, plan);
 }
 
 int dspark_walk_plan_for(int32_t cus, int64_t max_lds, int64_t bs, int64_t T, int64_t V,
@@ -129,7 +129,7 @@ int dspark_walk_plan_for(int32_t cus, int64_t max_lds, int64_t bs, int64_t T, in
     dev.cus = cus;
     dev.max_lds = (size_t)max_lds;
     dev.cooperative = true;
-    return plan_walk(dev, bs, T, V, plan);
+    return plan_walk(dev, bs, T, V, 0, plan);
 }
 
 static int dense_walk(const WalkLaunch& a, int64_t rank, size_t ws_bytes, void* stream) {
@@ -150,7 +150,7 @@ static int dense_walk(const WalkLaunch& a, int64_t rank, size_t ws_bytes, void* 
     st = current_device_info(&dev);
     if (st != DSPARK_OK) return st;
     dspark_walk_plan plan;
-    st = plan_walk(dev, a.bs, a.T, a.V, &plan);
+    st = plan_walk(dev, a.bs, a.T, a.V, a.sample, &plan);
     if (st != DSPARK_OK) return st;
     return launch_dense_walk(a, plan, static_cast<hipStream_t>(stream));
 }

@@ -46,7 +46,8 @@ struct DeviceInfo {
 // Query (cached per device) of the current device; returns a dspark_status.
 int current_device_info(DeviceInfo* info);
 
-int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, dspark_walk_plan* plan);
+int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, int sample,
+              dspark_walk_plan* plan);
 
 struct WalkLaunch {
     const int8_t* q;

@@ -18,7 +18,11 @@ constexpr int DOT4_LDS_SETS_MAX = 2;    // row sets in LDS
 constexpr int DOT4_FIXED_LDS = W1Q_BYTES + MAX_BS * 4 + WALK_WAVES * MAX_BS * 8 + MAX_BS * 4;
 constexpr int MFMA_REG_TILES = 8;       // 16-row tiles per wave in VGPRs
 constexpr int MFMA_TILE_LDS = 4 * WAVE * 16;
-constexpr int MFMA_MIN_BS = 2;
+// Smallest batch run on the MFMA kernel: below it the lane-per-row kernel is faster (measured at
+// V = 151936, 7 steps: 48 vs 63 us greedy at bs 1, 60 vs 64 at bs 2, 85 vs 67 at bs 4; sampling
+// moves the crossover up by one request, its finish costing more per MFMA tile).
+constexpr int MFMA_MIN_BS_GREEDY = 3;
+constexpr int MFMA_MIN_BS_SAMPLE = 4;
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -95,16 +99,18 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
     return DSPARK_OK;
 }
 
-// The MFMA kernel runs for two or more requests when V % 4 == 0 (and, at launch, the rows it
+// The MFMA kernel runs from MFMA_MIN_BS_* requests when V % 4 == 0 (and, at launch, the rows it
 // moves as vectors are 16-byte aligned) and its staging buffer fits in LDS; otherwise, or when
 // forced by the test hook, the v_dot4 kernel runs.
-int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, dspark_walk_plan* plan) {
+int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, int sample,
+              dspark_walk_plan* plan) {
     (void)T;
     int cap = dev.cus < MAX_WORKGROUPS ? dev.cus : MAX_WORKGROUPS;
     const DebugKnobs& dbg = debug_knobs();
     if (dbg.max_workgroups > 0 && dbg.max_workgroups < cap) cap = dbg.max_workgroups;
     if (cap < 1) return DSPARK_ERR_NO_DEVICE;
-    int path = (bs >= MFMA_MIN_BS && V % 4 == 0) ? DSPARK_PATH_MFMA : DSPARK_PATH_DOT4;
+    const int min_bs = sample ? MFMA_MIN_BS_SAMPLE : MFMA_MIN_BS_GREEDY;
+    int path = (bs >= min_bs && V % 4 == 0) ? DSPARK_PATH_MFMA : DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_DOT4) path = DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_MFMA && V % 4 == 0) path = DSPARK_PATH_MFMA;
     if (path == DSPARK_PATH_MFMA && plan_path(dev, cap, bs, V, path, plan) == DSPARK_OK)

@@ -98,7 +98,7 @@ typedef struct dspark_walk_plan {
     int64_t resident_bytes;      /* int8 W2 bytes held on chip (whole grid) */
     int64_t streamed_bytes;      /* int8 W2 bytes re-read per step (whole grid) */
     int32_t lds_bytes;           /* dynamic LDS per workgroup */
-    int32_t path;                /* DSPARK_PATH_DOT4 (one request) or DSPARK_PATH_MFMA */
+    int32_t path;                /* DSPARK_PATH_DOT4 (few requests) or DSPARK_PATH_MFMA */
     int32_t reg_units;           /* register row sets (dot4) or 16-row tiles per wave (MFMA) */
     int32_t lds_units;           /* LDS row sets (dot4) or tiles per wave (MFMA) */
     int32_t total_units;         /* all row sets / tiles per wave (the rest are streamed) */
@@ -106,8 +106,9 @@ typedef struct dspark_walk_plan {
     int32_t stage_stride;        /* MFMA: floats per request row in such a buffer */
 } dspark_walk_plan;
 
-/* Which kernel runs a dense walk: one request is a GEMV (lane-per-row v_dot4 kernel), two or
- * more make every step a GEMM (int8 matrix cores, 16 requests per tile). */
+/* Which kernel runs a dense walk: a few requests are GEMVs (lane-per-row v_dot4 kernel, up to 2
+ * requests greedy, 3 sampling), more make every step a GEMM (int8 matrix cores, 16 requests per
+ * tile). The plan queries below report the greedy walk's plan. */
 enum dspark_path { DSPARK_PATH_DOT4 = 1, DSPARK_PATH_MFMA = 2 };
 
 int dspark_walk_plan_query(int64_t bs, int64_t T, int64_t V, dspark_walk_plan* plan);

@@ -60,7 +60,7 @@ def test_plan_partition(bs, cus, V):
     except B.DsparkError as e:
         assert e.status == B.ERR_UNSUPPORTED
         return
-    mfma_ok = bs >= 2 and V % 4 == 0
+    mfma_ok = bs >= 3 and V % 4 == 0                 # the greedy plan
     if not mfma_ok:
         assert p["path"] == B.PATH_DOT4
     elif p["path"] == B.PATH_DOT4:
