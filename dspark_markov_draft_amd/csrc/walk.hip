@@ -13,7 +13,6 @@
 
 namespace dspark {
 
-constexpr int DOT4_REG_SETS = 2;        // row sets (256 rows each) in VGPRs
 constexpr int DOT4_LDS_SETS_MAX = 2;    // row sets in LDS
 constexpr int DOT4_FIXED_LDS = W1Q_BYTES + MAX_BS * 4 + WALK_WAVES * MAX_BS * 8 + MAX_BS * 4;
 constexpr int MFMA_REG_TILES = 8;       // 16-row tiles per wave in VGPRs

@@ -12,6 +12,7 @@ constexpr int WALK_WAVES = WALK_THREADS / WAVE;  // 4: one wave per SIMD
 constexpr int W1Q_BYTES = MAX_BS * RANK;         // int8 codes of the gathered W1 rows (LDS)
 constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workgroup per CU
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;
+constexpr int DOT4_REG_SETS = 3;  // lane-per-row kernel: row sets of 256 rows held in registers
 
 struct WalkParams {
     const int8_t* q;

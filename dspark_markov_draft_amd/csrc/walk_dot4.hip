@@ -23,10 +23,10 @@
 
 namespace dspark {
 
-constexpr int REG_J = 2;                 // row sets held in VGPRs
+constexpr int REG_J = DOT4_REG_SETS;     // row sets held in registers
 constexpr int LDS_J_MAX = 2;             // row sets held in LDS
 constexpr int PF_J = REG_J + LDS_J_MAX;  // row sets whose base logits are prefetched
-constexpr int PF_DEPTH = 4;              // requests of base logits in flight
+constexpr int PF_DEPTH = 2;              // requests of base logits in flight
 constexpr int ROW_CHUNKS = RANK / 16;    // 16-byte chunks per int8 row
 
 
@@ -142,6 +142,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                     for (int j = 0; j < REG_J; ++j) acc[j] = make_int4(0, 0, 0, 0);
 #pragma unroll
                     for (int c = 0; c < ROW_CHUNKS; ++c) {
+                        // a compiler-only barrier every 4 chunks: the W1 chunks are read from
+                        // LDS 4 at a time instead of all 16 up front, which keeps the register
+                        // rows in VGPRs
+                        if (c % 4 == 0) asm volatile("" ::: "memory");
                         const int4 w = wq[c ^ sw];
 #pragma unroll
                         for (int j = 0; j < REG_J; ++j) dot16x4(qr[j][c], w, acc[j]);
