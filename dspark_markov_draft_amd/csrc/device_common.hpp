@@ -33,6 +33,26 @@ __device__ __forceinline__ uint64_t argmax_key(float x, uint32_t idx) {
 
 __device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
 
+// Running torch.argmax of one lane's values, offered in increasing index order: a value
+// replaces the best so far if it is larger (so the first of equal values stays, and -0 and +0
+// are equal), if it is a NaN and the best is not (the first NaN stays), or if there is no best
+// yet. Three compares and two selects per value, instead of building and comparing a 64-bit
+// key for each; key() gives the argmax_key of the element it holds (0 if none).
+struct RunningArgmax {
+    float v = 0.0f;
+    uint32_t i = 0xFFFFFFFFu;
+    __device__ __forceinline__ void offer(float x, uint32_t idx, bool ok) {
+        const bool better = x > v || i == 0xFFFFFFFFu || (x != x && v == v);
+        if (ok && better) {
+            v = x;
+            i = idx;
+        }
+    }
+    __device__ __forceinline__ uint64_t key() const {
+        return i == 0xFFFFFFFFu ? 0ull : argmax_key(v, i);
+    }
+};
+
 // The drafted logit of one vocabulary row: base + (s[v] * s1) * acc, where acc is the exact
 // int32 dot product of the row's int8 codes with the request's int8 W1 codes and s1 the W1
 // row's scale. Written as one explicit fused multiply-add so that every kernel (dense dot4,

@@ -119,19 +119,21 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                         P = (uint64_t)(p.positions ? p.positions[b] : 0) + (uint64_t)t;
                         temp = p.temps[b];
                     }
-                    // logit of row v -> output store and argmax key
-                    auto finish = [&](int v, float base_v, float scale_v, int acc) -> uint64_t {
+                    // logit of row v -> output store, offered to this lane's running argmax (its
+                    // rows come in increasing index order)
+                    RunningArgmax run;
+                    auto finish = [&](int v, float base_v, float scale_v, int acc) {
                         const float l = walk_logit(base_v, scale_v, sb, acc);
                         if constexpr (!SAMPLE) {
                             if (p.out_logits) p.out_logits[orow + v] = l;
-                            return argmax_key(l, (uint32_t)v);
+                            run.offer(l, (uint32_t)v, true);
                         } else {
                             const uint32_t h = bf16_bits(l);
                             p.draft_logits[orow + v] = (uint16_t)h;
                             float x = bf16_value(h);
                             if (temp != 1.0f) x = x / temp;
                             const float g = gumbel_from_word(noise_word(seed, P, (uint32_t)v));
-                            return argmax_key(x + g, (uint32_t)v);
+                            run.offer(x + g, (uint32_t)v, true);
                         }
                     };
 
@@ -150,14 +152,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
 #pragma unroll
                         for (int j = 0; j < REG_J; ++j) dot16x4(qr[j][c], w, acc[j]);
                     }
-                    uint64_t best = 0;
 #pragma unroll
                     for (int j = 0; j < REG_J; ++j) {
                         const int r = j * WALK_THREADS + tid;
-                        if (r < nrows) {
-                            const uint64_t key = finish(row0 + r, cur[j], sc[j], hsum(acc[j]));
-                            best = key > best ? key : best;
-                        }
+                        if (r < nrows) finish(row0 + r, cur[j], sc[j], hsum(acc[j]));
                     }
                     // row sets beyond the registers: LDS-resident, then streamed from memory
                     for (int j = REG_J; j < nj; ++j) {
@@ -194,11 +192,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                                 bv = p.base[orow + row0 + r];
                                 sv = p.scale[row0 + r];
                             }
-                            const uint64_t key = finish(row0 + r, bv, sv, a);
-                            best = key > best ? key : best;
+                            finish(row0 + r, bv, sv, a);
                         }
                     }
-                    best = wave_max_u64(best);
+                    const uint64_t best = wave_max_u64(run.key());
                     if (lane == 0) wkeys[wave * MAX_BS + b] = best;
                 }
             }
