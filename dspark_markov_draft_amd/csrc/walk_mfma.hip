@@ -153,12 +153,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     temp = p.temps[b];
                 }
             }
-            uint64_t best = 0;
-
-            // Rows vt .. vt+3 of request b from the accumulator of one tile. The group is wholly
-            // inside the slice or wholly past its end (partial last tile); past-the-end groups and
-            // requests past bs read in-bounds LDS, are computed, and are dropped by a zero key.
-            auto finish4 = [&](const v4i acc, int vt) {
+            // Rows vt .. vt+3 of request b from the accumulator of one tile: their logits (and
+            // bf16 rows and noise when sampling) and the quantity the argmax compares. The group
+            // is wholly inside the slice or wholly past its end (partial last tile); past-the-end
+            // groups and requests past bs read in-bounds LDS, are computed, and are dropped.
+            auto scores4 = [&](const v4i acc, int vt, bool store, float (&sc)[4]) {
                 const int off = vt - row0;                       // < ntiles * 16 <= rows_per_wg
                 const float4 sv = *reinterpret_cast<const float4*>(scl + off);
                 const float4 bv = *reinterpret_cast<const float4*>(sbase + off);
@@ -168,18 +167,17 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 l[1] = walk_logit(bv.y, sv.y, sb, acc[1]);
                 l[2] = walk_logit(bv.z, sv.z, sb, acc[2]);
                 l[3] = walk_logit(bv.w, sv.w, sb, acc[3]);
-                uint64_t key[4];
                 if constexpr (!SAMPLE) {
-                    if (p.out_logits != nullptr && ok)
+                    if (store && p.out_logits != nullptr && ok)
                         *reinterpret_cast<float4*>(p.out_logits + orow + vt) =
                             make_float4(l[0], l[1], l[2], l[3]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) key[i] = argmax_key(l[i], (uint32_t)(vt + i));
+                    for (int i = 0; i < 4; ++i) sc[i] = l[i];
                 } else {
                     uint32_t h[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) h[i] = bf16_bits(l[i]);
-                    if (ok)
+                    if (store && ok)
                         *reinterpret_cast<uint2*>(p.draft_logits + orow + vt) =
                             make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
                     // vt is a multiple of 4: one Philox call yields the words of all 4 rows
@@ -190,54 +188,97 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     for (int i = 0; i < 4; ++i) {
                         float x = bf16_value(h[i]);
                         if (temp != 1.0f) x = x / temp;
-                        key[i] = argmax_key(x + gumbel_from_word(words[i]), (uint32_t)(vt + i));
+                        sc[i] = x + gumbel_from_word(words[i]);
                     }
                 }
-                const uint64_t keep = ok ? ~0ull : 0ull;
+                return ok;
+            };
+
+            // Every tile of this wave in increasing row order: register tiles (all their MFMAs
+            // first, each into its own accumulator, so the matrix core runs ahead while the VALU
+            // finishes tile after tile), then LDS tiles, then streamed ones.
+            auto for_tiles = [&](auto&& fin) {
+                v4i accs[NT_REG];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint64_t k = key[i] & keep;
-                    best = k > best ? k : best;
+                for (int tw = 0; tw < NT_REG; ++tw) {
+                    accs[tw] = (v4i){0, 0, 0, 0};
+                    if (tw * WALK_WAVES + wave < ntiles) {
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+                            accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb],
+                                                                             accs[tw], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int tw = 0; tw < NT_REG; ++tw) {
+                    const int tl = tw * WALK_WAVES + wave;
+                    if (tl < ntiles) fin(accs[tw], row0 + tl * TILE_ROWS + g * 4);
+                }
+                for (int tw = NT_REG; tw < ntw; ++tw) {
+                    const int tl = tw * WALK_WAVES + wave;
+                    if (tl < ntiles) {
+                        v4i acc = {0, 0, 0, 0};
+                        if (tw < NT_REG + lds_tw) {
+                            const v4i* src = reinterpret_cast<const v4i*>(
+                                lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) * TILE_LDS_BYTES);
+#pragma unroll
+                            for (int kb = 0; kb < 4; ++kb)
+                                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane],
+                                                                            bop[kb], acc, 0, 0, 0);
+                        } else {
+#pragma unroll
+                            for (int kb = 0; kb < 4; ++kb)
+                                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(load_a(tl, kb), bop[kb],
+                                                                            acc, 0, 0, 0);
+                        }
+                        fin(acc, row0 + tl * TILE_ROWS + g * 4);
+                    }
                 }
             };
 
-            // all register tiles' MFMAs first, each into its own accumulator, so the matrix
-            // core runs ahead while the VALU finishes tile after tile
-            v4i accs[NT_REG];
+            // Fast pass: a running (value, row) maximum per lane with plain float compares. A
+            // lane meets its rows in increasing order, so a strictly larger value replacing the
+            // best keeps the first of equal values (and -0 equals +0), as torch.argmax does.
+            // NaN is the one case a float compare cannot order; a lane that meets one (or a
+            // false alarm such as inf - inf in its check sum) sends its wave through the exact
+            // pass below, which builds the order-preserving key of every value.
+            float run_v = -INFINITY;
+            uint32_t run_i = 0xFFFFFFFFu;
+            bool nan_seen = false;
+            for_tiles([&](const v4i acc, int vt) {
+                float sc[4];
+                const bool ok = scores4(acc, vt, true, sc);
+                const float chk = ok ? (sc[0] + sc[1]) + (sc[2] + sc[3]) : 0.0f;
+                nan_seen = nan_seen || chk != chk;
 #pragma unroll
-            for (int tw = 0; tw < NT_REG; ++tw) {
-                accs[tw] = (v4i){0, 0, 0, 0};
-                if (tw * WALK_WAVES + wave < ntiles) {
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
-                        accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb],
-                                                                         accs[tw], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int tw = 0; tw < NT_REG; ++tw) {
-                const int tl = tw * WALK_WAVES + wave;
-                if (tl < ntiles) finish4(accs[tw], row0 + tl * TILE_ROWS + g * 4);
-            }
-            for (int tw = NT_REG; tw < ntw; ++tw) {
-                const int tl = tw * WALK_WAVES + wave;
-                if (tl < ntiles) {
-                    v4i acc = {0, 0, 0, 0};
-                    if (tw < NT_REG + lds_tw) {
-                        const v4i* src = reinterpret_cast<const v4i*>(
-                            lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) * TILE_LDS_BYTES);
-#pragma unroll
-                        for (int kb = 0; kb < 4; ++kb)
-                            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane], bop[kb],
-                                                                        acc, 0, 0, 0);
-                    } else {
-#pragma unroll
-                        for (int kb = 0; kb < 4; ++kb)
-                            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(load_a(tl, kb), bop[kb], acc,
-                                                                        0, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    const float x = ok ? sc[i] : -INFINITY;
+                    if (x > run_v) {
+                        run_v = x;
+                        run_i = (uint32_t)(vt + i);
                     }
-                    finish4(acc, row0 + tl * TILE_ROWS + g * 4);
                 }
+            });
+            uint64_t best;
+            if (run_i != 0xFFFFFFFFu) {
+                best = argmax_key(run_v, run_i);
+            } else {
+                // every row of this lane was -inf (or it had none): its first row wins
+                const int vt0 = row0 + wave * TILE_ROWS + g * 4;
+                best = (vb && wave < ntiles && vt0 < vend) ? argmax_key(-INFINITY, (uint32_t)vt0) : 0ull;
+            }
+            if (__any(nan_seen)) {
+                best = 0;
+                for_tiles([&](const v4i acc, int vt) {
+                    float sc[4];
+                    const bool ok = scores4(acc, vt, false, sc);
+                    const uint64_t keep = ok ? ~0ull : 0ull;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint64_t k = argmax_key(sc[i], (uint32_t)(vt + i)) & keep;
+                        best = k > best ? k : best;
+                    }
+                });
             }
             lkeys[(wave * MAX_RT + rt) * WAVE + lane] = best;
         }

@@ -191,6 +191,39 @@ def test_paths_agree_bitwise(name, mode, reqs):
     assert rep.ok, rep.summary()
 
 
+@pytest.mark.parametrize("path", [B.PATH_DOT4, B.PATH_MFMA])
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_special_values_both_paths(mode, path):
+    """W2 = 0 makes every logit its base logit exactly, so special values reach the argmax as
+    planted: NaN (the first NaN wins), rows that are -inf throughout (row 0 wins), +inf next to
+    -inf, all-zero rows with -0 and +0 mixed (ties: the first index), a NaN after a +inf. Both
+    kernels, 20 requests (two 16-request tiles on the MFMA path)."""
+    V, T, bs = 4096, 3, 20
+    rng = np.random.default_rng(77)
+    base = rng.normal(0.0, 3.0, (bs, T, V)).astype(np.float32)
+    base[0, 0, [100, 2000, 3000]] = np.nan
+    base[1, 1, :] = -np.inf
+    base[2, 0, 50], base[2, 0, 51] = np.inf, -np.inf
+    base[3, 0, :] = np.where(rng.random(V) < 0.5, 0.0, -0.0)
+    base[4, 2, 7], base[4, 2, 8], base[4, 2, 3] = np.nan, np.inf, np.inf
+    base[17, 1, :] = -np.inf
+    base[17, 1, 4095] = np.nan
+    base[19, 2, 1000:1010] = np.inf
+    w = torch.zeros(V, 256, dtype=torch.bfloat16)
+    p = Problem(w, w.clone(), base, np.zeros(bs, np.int32))
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
+    if mode == "greedy":
+        tok, logits = p.greedy()
+        rep = p.check_greedy(tok, logits)
+        assert tok[0, 0] == 100 and tok[1, 1] == 0 and tok[2, 0] == 50 and tok[3, 0] == 0
+        assert tok[4, 2] == 7 and tok[17, 1] == 4095 and tok[19, 2] == 1000
+    else:
+        tok, lb = p.sample()
+        rep = p.check_sample(tok, lb)
+        assert tok[0, 0] == 100 and tok[1, 1] == 0 and tok[4, 2] == 7 and tok[17, 1] == 4095
+    assert rep.ok, rep.summary()
+
+
 def test_full_size_without_out_logits_same_tokens():
     """The timed configuration (greedy, no logits output) emits the same tokens."""
     inp = make_inputs(CASES["v151936_t7_bs1"])
