@@ -12,8 +12,10 @@ namespace dspark {
 // Workspace layout of a walk call (bytes from the start of the caller's workspace). A walk
 // leaves every word it uses at zero when it exits, so the caller zeroes the workspace once.
 constexpr size_t WS_ERR = 0;          // u32 error word (DSPARK_ERR_TIMEOUT / INVALID_ARG)
-constexpr size_t WS_RESULT = 256;     // u64 [16 steps][64 requests]: winning key of each step
-constexpr size_t WS_SLOTS = 16384;    // u64 [T][256 workgroups][slot stride]: per-workgroup keys
+constexpr int RESULT_REPLICAS = 8;    // copies of the result words, read by disjoint workgroups
+constexpr size_t WS_RESULT = 4096;    // u64 [8 copies][16 steps][64 requests]: each step's winner
+constexpr size_t WS_SLOTS = WS_RESULT + (size_t)RESULT_REPLICAS * 16 * 64 * 8;  // then
+                                      // u64 [T][256 workgroups][slot stride]: per-workgroup keys
 constexpr size_t WS_TOPK = WS_SLOTS;  // top-k calls use the same region for candidate lists
 constexpr size_t WS_ALIGN = 256;
 constexpr int MAX_WORKGROUPS = 256;

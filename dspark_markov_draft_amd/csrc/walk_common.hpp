@@ -192,9 +192,16 @@ __device__ __forceinline__ void load_start_tokens(const WalkParams& p, int32_t* 
 // workgroup's best key for request `lane`. Each workgroup stores its keys into its own slot;
 // the workgroup owning request b (b % num workgroups) waits for all slots of b, takes their
 // maximum, writes the token and publishes the winning key in result[t][b] (not for the last
-// step), clears the slots it read and its result word of step t-1 (every workgroup read that
-// before filling its slot of step t); then every workgroup waits for the result words of step
-// t and writes the new tokens into `tok`. All waits are bounded by the spin limit.
+// step) in RESULT_REPLICAS copies on separate cache lines, clears the slots it read and its
+// result words of step t-1 (every workgroup read those before filling its slot of step t); then
+// every workgroup waits for its copy (workgroup w reads copy w % RESULT_REPLICAS) of the result
+// words of step t and writes the new tokens into `tok`. Both waits keep two rounds of loads in
+// flight: a store that becomes visible is seen about one load latency later, not one and a half.
+// All waits are bounded by the spin limit.
+__device__ __forceinline__ uint64_t* result_word(const WalkParams& p, int rep, int t, int b) {
+    return p.result + ((size_t)rep * MAX_STEPS + t) * MAX_BS + b;
+}
+
 template <int TIMED>
 __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_t key,
                                              int32_t* tok, int lane) {
@@ -204,67 +211,91 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
     if (lane < p.bs) st_dev(step_slots + (size_t)wg * p.stride + lane, key);
     stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 2);
 
+    constexpr int NL = MAX_WORKGROUPS / WAVE;  // slot loads per lane per round
     for (int b = wg; b < p.bs; b += nwg) {
-        uint64_t* col = step_slots + b;
-        uint64_t best = 0;
-        uint32_t spins = 0;
-        while (true) {
-            // all slot loads of a round are in flight together (nwg <= 4 x 64)
-            uint64_t v[MAX_WORKGROUPS / WAVE];
+        const uint64_t* col = step_slots + b;
+        // unconditional loads (lanes past the grid re-read the last slot), so that the compiler
+        // can count the loads in flight
+        auto issue = [&](uint64_t (&v)[NL]) {
 #pragma unroll
-            for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
-                const int w = lane + k * WAVE;
-                v[k] = w < nwg ? ld_dev(col + (size_t)w * p.stride) : 0;
+            for (int k = 0; k < NL; ++k) {
+                const int w = min(lane + k * WAVE, nwg - 1);
+                v[k] = ld_dev(col + (size_t)w * p.stride);
             }
+        };
+        auto complete = [&](const uint64_t (&v)[NL], uint64_t& best) {
             bool all = true;
             best = 0;
 #pragma unroll
-            for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
-                all = all && (v[k] != 0 || lane + k * WAVE >= nwg);
+            for (int k = 0; k < NL; ++k) {
+                all = all && v[k] != 0;
                 best = v[k] > best ? v[k] : best;
             }
             if (p.wait_unset)
                 all = all && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT) != 0;
-            if (__all(all)) break;
+            return __all(all);
+        };
+        uint64_t va[NL], vb[NL];
+        uint64_t best = 0;
+        uint32_t spins = 0;
+        issue(va);
+        while (true) {
+            issue(vb);
+            if (complete(va, best)) break;
+            issue(va);
+            if (complete(vb, best)) break;
             if (++spins > p.spin_limit) {
                 if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
         }
         best = wave_max_u64(best);
-        if (best == 0) best = 1;  // only after a timeout: keep the result word non-zero
+        if (best == 0) best = 1;  // only after a timeout: keep the result words non-zero
         uint32_t token = key_index(best);
         if (token >= (uint32_t)p.V) token = 0;
-        if (lane == 0) {
-            p.tokens[b * p.T + t] = (int32_t)token;
-            if (t + 1 < p.T) st_dev(p.result + t * MAX_BS + b, best);
-            if (t > 0) st_dev(p.result + (t - 1) * MAX_BS + b, 0);
+        if (lane == 0) p.tokens[b * p.T + t] = (int32_t)token;
+        if (lane < RESULT_REPLICAS) {
+            if (t + 1 < p.T) st_dev(result_word(p, lane, t, b), best);
+            if (t > 0) st_dev(result_word(p, lane, t - 1, b), 0);
         }
 #pragma unroll
-        for (int k = 0; k < MAX_WORKGROUPS / WAVE; ++k) {
+        for (int k = 0; k < NL; ++k) {
             const int w = lane + k * WAVE;
-            if (w < nwg) st_dev(col + (size_t)w * p.stride, 0);
+            if (w < nwg) st_dev(step_slots + (size_t)w * p.stride + b, 0);
         }
     }
     stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 3);
 
     if (t + 1 < p.T) {
-        uint64_t k = 0;
+        const uint64_t* mine = result_word(p, wg % RESULT_REPLICAS, t, lane < p.bs ? lane : 0);
+        uint64_t ka, kb;
         uint32_t spins = 0;
+        auto seen = [&](uint64_t k) {
+            bool ok = lane >= p.bs || k != 0;
+            if (p.wait_unset)
+                ok = ok && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) != 0;
+            return __all(ok);
+        };
+        uint64_t k = 0;
+        ka = ld_dev(mine);
         while (true) {
-            bool ok = true;
-            if (lane < p.bs) {
-                k = ld_dev(p.result + t * MAX_BS + lane);
-                ok = k != 0;
-            }
-            if (__all(ok)) break;
-            if (++spins > p.spin_limit) {
-                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+            kb = ld_dev(mine);
+            if (seen(ka)) {
+                k = ka;
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
+            ka = ld_dev(mine);
+            if (seen(kb)) {
+                k = kb;
+                break;
+            }
+            if (++spins > p.spin_limit) {
+                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                k = kb;
+                break;
+            }
         }
         if (lane < p.bs) {
             uint32_t token = key_index(k);
