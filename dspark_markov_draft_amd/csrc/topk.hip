@@ -643,7 +643,7 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         }
         float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
         a = wave_max_nonneg_f32(a);
-        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        const float inv = w1_code_scale(a);
         const float sb = a * (1.0f / 127.0f);
         w1q[wave][lane] = pack_codes(w, inv);
         tk_stamp<TIMED>(p.stamps, st0 + 1 + 2 * t);

@@ -74,16 +74,22 @@ __device__ __forceinline__ void flag_error(uint32_t* err, int status) {
 // ch for 16 consecutive requests (the MFMA B operand) spreads over all LDS banks.
 __device__ __forceinline__ int w1q_chunk_dword(int b, int ch) { return b * (RANK / 4) + ((ch ^ (b & 15)) << 2); }
 
+// 127 / absmax, the factor that maps a W1 row onto int8 codes; 0 for rows whose absmax is at
+// most 2^-100 (zero rows, and denormal ones whose 127 / absmax would overflow): their codes are
+// 0, dropping a bias below 2^-90.
+__device__ __forceinline__ float w1_code_scale(float absmax) {
+    return absmax > 0x1p-100f ? 127.0f / absmax : 0.0f;
+}
+
+// Four int8 codes rint(w * inv) (round half to even) in one dword. With inv = 127 / absmax of
+// the row, |w * inv| <= 127 * (1 + 2^-23)^2 < 127.5, so every code lies in [-127, 127] without
+// a clamp.
 __device__ __forceinline__ uint32_t pack_codes(const float4 w, float inv) {
-    const float v[4] = {w.x, w.y, w.z, w.w};
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float r = rintf(v[i] * inv);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        packed |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * i);
-    }
-    return packed;
+    const uint32_t c0 = (uint32_t)(int32_t)rintf(w.x * inv) & 0xFFu;
+    const uint32_t c1 = (uint32_t)(int32_t)rintf(w.y * inv) & 0xFFu;
+    const uint32_t c2 = (uint32_t)(int32_t)rintf(w.z * inv) & 0xFFu;
+    const uint32_t c3 = (uint32_t)(int32_t)rintf(w.w * inv);
+    return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
 // maximum of non-negative floats over each 16-lane row of the wave (all 16 lanes get it)
@@ -112,7 +118,7 @@ __device__ __forceinline__ uint32_t w1_row_codes(const void* w1, int32_t row, in
     const float4 w = load4_as_f32<W1T>(w1, (int64_t)row * RANK + lane * 4);
     float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
     a = wave_max_nonneg_f32(a);
-    const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+    const float inv = w1_code_scale(a);
     s1 = a * (1.0f / 127.0f);
     return pack_codes(w, inv);
 }
@@ -161,7 +167,7 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
             }
             a = row16_max_nonneg_f32(a);
             if (b < p.bs) {
-                const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+                const float inv = w1_code_scale(a);
                 uint4 codes;
                 codes.x = pack_codes(wv[it][0], inv);
                 codes.y = pack_codes(wv[it][1], inv);
