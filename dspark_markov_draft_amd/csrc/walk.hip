@@ -50,24 +50,33 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         int64_t u16 = rpw / 4;
         if (u16 % 2 == 0) u16 += 1;
         stage_stride = u16 * 4;
-        const int64_t buf_bytes = 16 * stage_stride * 4;
+        int64_t buf_bytes = 16 * stage_stride * 4;
         const int64_t fixed = mfma_fixed_lds_bytes((int)rpw);
         const int64_t want = bs > 16 ? 2 : 1;
-        stage_bufs = ((int64_t)dev.max_lds - fixed) / buf_bytes;
-        if (stage_bufs > want) stage_bufs = want;
-        if (stage_bufs < 1) return DSPARK_ERR_UNSUPPORTED;        // the caller falls back
+        const bool stat = rpw <= MFMA_STATIC_ROWS && stage_stride <= MFMA_STATIC_STRIDE;
+        if (stat) {
+            // all LDS is static and of fixed size (both staging buffers exist for any batch)
+            stage_bufs = want;
+            if (MFMA_STATIC_LDS_BYTES > (int64_t)dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
+        } else {
+            stage_bufs = ((int64_t)dev.max_lds - fixed) / buf_bytes;
+            if (stage_bufs > want) stage_bufs = want;
+            if (stage_bufs < 1) return DSPARK_ERR_UNSUPPORTED;    // the caller falls back
+        }
+        const int64_t stage_lds = stage_bufs * buf_bytes;
         const int64_t tiles = rpw / 16;
         units = (tiles + WALK_WAVES - 1) / WALK_WAVES;              // tile slots per wave
         reg_units = units < MFMA_REG_TILES ? units : MFMA_REG_TILES;
-        int64_t room = ((int64_t)dev.max_lds - fixed - stage_bufs * buf_bytes) /
-                       (WALK_WAVES * MFMA_TILE_LDS);
+        int64_t room = stat ? MFMA_STATIC_LDS_SLOTS
+                            : ((int64_t)dev.max_lds - fixed - stage_lds) / (WALK_WAVES * MFMA_TILE_LDS);
         if (room < 0) room = 0;
         lds_units = units - reg_units;
         if (lds_units > room) lds_units = room;
         reg_rows = rpw < reg_units * WALK_WAVES * 16 ? rpw : reg_units * WALK_WAVES * 16;
         lds_rows = rpw - reg_rows;
         if (lds_rows > lds_units * WALK_WAVES * 16) lds_rows = lds_units * WALK_WAVES * 16;
-        lds_bytes = lds_units * WALK_WAVES * MFMA_TILE_LDS + fixed + stage_bufs * buf_bytes;
+        lds_bytes = stat ? MFMA_STATIC_LDS_BYTES
+                         : lds_units * WALK_WAVES * MFMA_TILE_LDS + fixed + stage_lds;
     }
     if (lds_bytes < LDS_MIN_BYTES) lds_bytes = LDS_MIN_BYTES;
     if ((size_t)lds_bytes > dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
@@ -171,15 +180,21 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     const bool timed = p.stamps != nullptr && a.w1_dtype == DSPARK_BF16;
 
     const int w1t = a.w1_dtype == DSPARK_F32 ? DT_F32 : a.w1_dtype == DSPARK_BF16 ? DT_BF16 : DT_F16;
-    const void* fn = plan.path == DSPARK_PATH_MFMA ? mfma_walk_kernel(a.sample, w1t, timed)
-                                                   : dot4_walk_kernel(a.sample, w1t, timed);
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, plan.lds_bytes) !=
+    // the MFMA kernel for small slices keeps all its LDS in static arrays (no dynamic LDS)
+    const bool static_stage = plan.path == DSPARK_PATH_MFMA &&
+                              plan.rows_per_workgroup <= MFMA_STATIC_ROWS &&
+                              plan.stage_stride <= MFMA_STATIC_STRIDE;
+    const int dyn_lds = static_stage ? 0 : plan.lds_bytes;
+    const void* fn = plan.path == DSPARK_PATH_MFMA
+                         ? mfma_walk_kernel(a.sample, w1t, timed, static_stage)
+                         : dot4_walk_kernel(a.sample, w1t, timed);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_lds) !=
         hipSuccess) {
         (void)hipGetLastError();
     }
     void* args[] = {&p};
     const hipError_t e = launch_walk_kernel(fn, dim3(plan.num_workgroups), dim3(WALK_THREADS),
-                                            args, (size_t)plan.lds_bytes, stream);
+                                            args, (size_t)dyn_lds, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return DSPARK_ERR_LAUNCH;

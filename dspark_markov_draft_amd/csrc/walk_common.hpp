@@ -13,6 +13,16 @@ constexpr int W1Q_BYTES = MAX_BS * RANK;         // int8 codes of the gathered W
 constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workgroup per CU
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;
 constexpr int DOT4_REG_SETS = 3;  // lane-per-row kernel: row sets of 256 rows held in registers
+// MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
+// two staging buffers of 16 rows of MFMA_STATIC_STRIDE floats (157 odd 16-byte units), up to
+// MFMA_STATIC_LDS_SLOTS LDS tiles per wave, W1 codes and scales, row scales, lane keys, tokens
+constexpr int MFMA_STATIC_ROWS = 624;
+constexpr int MFMA_STATIC_STRIDE = 628;
+constexpr int MFMA_STATIC_LDS_SLOTS = 2;
+constexpr int MFMA_STATIC_LDS_BYTES =
+    2 * 16 * MFMA_STATIC_STRIDE * 4 + MFMA_STATIC_LDS_SLOTS * WALK_WAVES * 4 * WAVE * 16 +
+    W1Q_BYTES + MAX_BS * 4 + MFMA_STATIC_ROWS * 4 + WALK_WAVES * (MAX_BS / 16) * WAVE * 8 +
+    MAX_BS * 4;
 
 struct WalkParams {
     const int8_t* q;
@@ -314,7 +324,7 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
 
 // Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0/1; w1t: DT_*).
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
-const void* mfma_walk_kernel(int sample, int w1t, bool timed);
+const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage);
 int mfma_fixed_lds_bytes(int rows_per_wg);
 
 }  // namespace dspark

@@ -38,6 +38,13 @@ constexpr int TILE_ROWS = 16;
 constexpr int NT_REG = 8;                       // W2 tiles per wave held in VGPRs
 constexpr int TILE_LDS_BYTES = 4 * WAVE * 16;   // one tile: 4 K-blocks x 64 lanes x 16 bytes
 constexpr int MAX_RT = MAX_BS / 16;             // 16-request tiles
+constexpr int NT_STAT = NT_REG + MFMA_STATIC_LDS_SLOTS;   // tile slots per wave with STAT
+constexpr int STAT_SLOT_ROWS = NT_STAT * WALK_WAVES * TILE_ROWS;   // rows the slots cover
+static_assert(STAT_SLOT_ROWS >= MFMA_STATIC_ROWS, "STAT slices fit on chip");
+// Row c of a staging buffer is read at c * stride + [0, STAT_SLOT_ROWS): the last row runs past
+// the buffer's 16 rows by at most this many floats (the slots past the slice's end)
+constexpr int STAT_PAD = STAT_SLOT_ROWS - MFMA_STATIC_STRIDE;
+static_assert(STAT_PAD >= 0 && STAT_PAD % 4 == 0, "STAT staging pad");
 constexpr int LKEY_BYTES = WALK_WAVES * MAX_RT * WAVE * 8;
 
 // dynamic LDS besides the W2 tiles: W1 codes, their scales, row scales, lane keys, tokens
@@ -45,13 +52,30 @@ __host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
     return W1Q_BYTES + MAX_BS * 4 + ((rows_per_wg * 4 + 15) / 16) * 16 + LKEY_BYTES + MAX_BS * 4;
 }
 
-template <int SAMPLE, int W1T, int TIMED>
+// STAT (slices of up to MFMA_STATIC_ROWS rows): every LDS buffer is a static array of its own
+// (two staging buffers, the LDS tiles, W1 codes, scales, lane keys, tokens) and there is no
+// dynamic LDS. The compiler then knows that the DMA into one staging buffer cannot touch the
+// other one or any other LDS data, and reads them while the DMA runs. With dynamic LDS it has
+// to assume that any LDS read may alias the DMA's target, and waits for every DMA in flight
+// before each LDS read, which serialises the next request tile's copy with the current tile's
+// compute.
+template <int SAMPLE, int W1T, int TIMED, int STAT>
 __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const WalkParams p) {
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
+    // the staging buffers and row scales are padded for the past-the-end tile slots (below)
+    __shared__ __align__(16) float stage_a[STAT ? 16 * MFMA_STATIC_STRIDE + STAT_PAD : 4];
+    __shared__ __align__(16) float stage_b[STAT ? 16 * MFMA_STATIC_STRIDE + STAT_PAD : 4];
+    __shared__ __align__(16) unsigned char tiles_s[STAT ? MFMA_STATIC_LDS_SLOTS * WALK_WAVES *
+                                                              TILE_LDS_BYTES : 16];
+    __shared__ __align__(16) uint32_t w1q_s[STAT ? W1Q_BYTES / 4 : 4];
+    __shared__ __align__(16) float s1_s[STAT ? MAX_BS : 4];
+    __shared__ __align__(16) float scl_s[STAT ? STAT_SLOT_ROWS : 4];
+    __shared__ __align__(16) uint64_t lkeys_s[STAT ? WALK_WAVES * MAX_RT * WAVE : 2];
+    __shared__ __align__(16) int32_t tok_s[STAT ? MAX_BS : 4];
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
-    const int wave = tid / WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);   // uniform: scalar branches
     const int c = lane & 15;   // A: row within the tile; B/D: request within the request tile
     const int g = lane >> 4;   // k-chunk group; D: rows g*4 .. g*4+3
     const int row0 = blockIdx.x * p.rows_per_wg;
@@ -61,15 +85,24 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     const int ntw = p.total_units;                             // tile slots per wave
     const int lds_tw = p.lds_units;
 
-    unsigned char* lds_tiles = smem;
-    float* stage = reinterpret_cast<float*>(smem + (size_t)lds_tw * WALK_WAVES * TILE_LDS_BYTES);
+    // dynamic layout (without STAT): LDS tiles, staging buffers, W1 codes, their scales, row
+    // scales, lane keys, tokens
+    unsigned char* const d_tiles = smem;
+    float* const d_stage = reinterpret_cast<float*>(smem + (size_t)lds_tw * WALK_WAVES * TILE_LDS_BYTES);
     const int ss = p.stage_stride;
     const int nbuf = p.stage_bufs;   // 1 or 2 (the host guarantees at least one)
-    uint32_t* w1q = reinterpret_cast<uint32_t*>(stage + (size_t)p.stage_bufs * 16 * ss);
-    float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
-    float* scl = s1 + MAX_BS;
-    uint64_t* lkeys = reinterpret_cast<uint64_t*>(scl + ((p.rows_per_wg * 4 + 15) / 16) * 4);
-    int32_t* tok = reinterpret_cast<int32_t*>(lkeys + WALK_WAVES * MAX_RT * WAVE);
+    uint32_t* const d_w1q = reinterpret_cast<uint32_t*>(d_stage + (size_t)p.stage_bufs * 16 * ss);
+    float* const d_s1 = reinterpret_cast<float*>(d_w1q + W1Q_BYTES / 4);
+    float* const d_scl = d_s1 + MAX_BS;
+    uint64_t* const d_lkeys = reinterpret_cast<uint64_t*>(d_scl + ((p.rows_per_wg * 4 + 15) / 16) * 4);
+    unsigned char* lds_tiles = STAT ? tiles_s : d_tiles;
+    float* const buf0 = STAT ? stage_a : d_stage;
+    float* const buf1 = STAT ? stage_b : d_stage + (size_t)16 * ss;
+    uint32_t* w1q = STAT ? w1q_s : d_w1q;
+    float* s1 = STAT ? s1_s : d_s1;
+    float* scl = STAT ? scl_s : d_scl;
+    uint64_t* lkeys = STAT ? lkeys_s : d_lkeys;
+    int32_t* tok = STAT ? tok_s : reinterpret_cast<int32_t*>(d_lkeys + WALK_WAVES * MAX_RT * WAVE);
 
     // ---- fill: W2 tiles as A operands (VGPRs, then LDS), row scales into LDS ---------------
     auto load_a = [&](int tl, int kb) -> v4i {
@@ -84,16 +117,20 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qa[tw][kb] = tl < ntiles ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
     }
-    for (int tw = NT_REG; tw < NT_REG + lds_tw; ++tw) {
+    // with STAT every LDS slot is written (zero codes past the slice's tiles): the tile loop
+    // multiplies all of them
+    for (int tw = NT_REG; tw < NT_REG + (STAT ? MFMA_STATIC_LDS_SLOTS : lds_tw); ++tw) {
         const int tl = tw * WALK_WAVES + wave;
-        if (tl < ntiles) {
+        const bool have = tl < ntiles && tw < NT_REG + lds_tw;
+        if (have || STAT) {
             v4i* dst = reinterpret_cast<v4i*>(
                 lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) * TILE_LDS_BYTES);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) dst[kb * WAVE + lane] = load_a(tl, kb);
+            for (int kb = 0; kb < 4; ++kb)
+                dst[kb * WAVE + lane] = have ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
         }
     }
-    for (int i = tid; i < ntiles * TILE_ROWS; i += WALK_THREADS)
+    for (int i = tid; i < (STAT ? STAT_SLOT_ROWS : ntiles * TILE_ROWS); i += WALK_THREADS)
         scl[i] = i < nrows ? p.scale[row0 + i] : 0.0f;
     load_start_tokens(p, tok);
     __syncthreads();
@@ -105,12 +142,12 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     // instruction moves 64 lanes x 16 bytes to consecutive LDS; row segments are whole 16-byte
     // units (V and row0 are multiples of 4) and lanes past a segment's end stay idle.
     const int units = nrows / 4;
-    auto stage_base = [&](int rt, int t, int buf) {
+    auto stage_base = [&](int rt, int t, float* dst_buf) {
         for (int r = 0; r < 16; ++r) {
             const int b = rt * 16 + r;
             if (b >= p.bs) break;
             const float* src = p.base + ((int64_t)b * p.T + t) * p.V + row0;
-            float* dst = stage + (size_t)(buf * 16 + r) * ss;
+            float* dst = dst_buf + (size_t)r * ss;
             for (int u0 = wave * WAVE; u0 < units; u0 += WALK_THREADS) {
                 if (u0 + lane < units)
                     __builtin_amdgcn_global_load_lds((global_void_ptr)(src + 4 * (u0 + lane)),
@@ -118,23 +155,23 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             }
         }
     };
-    stage_base(0, 0, 0);
+    stage_base(0, 0, buf0);
 
     for (int t = 0; t < p.T; ++t) {
         gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane);
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
-        for (int rt = 0; rt < nrt; ++rt) {
-            const int buf = nbuf == 2 ? (rt & 1) : 0;
+        // one request tile: its base logits are in `cur`; the next tile's copy goes to `nxt`
+        auto request_tile = [&](int rt, float* cur, float* nxt) __attribute__((always_inline)) {
             if (nbuf == 1 && rt > 0) {
                 __syncthreads();   // every wave is done with the previous request tile
-                stage_base(rt, t, 0);
+                stage_base(rt, t, cur);
             }
             __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed ...
             __syncthreads();                  // ... and every other wave's
-            if (nbuf == 2 && rt + 1 < nrt) stage_base(rt + 1, t, buf ^ 1);
-            const float* sbase = stage + (size_t)(buf * 16 + c) * ss;
+            if (nbuf == 2 && rt + 1 < nrt) stage_base(rt + 1, t, nxt);
+            const float* sbase = cur + (size_t)c * ss;
             const int b = rt * 16 + c;
             const bool vb = b < p.bs;
             v4i bop[4];
@@ -154,11 +191,13 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 }
             }
             // Rows vt .. vt+3 of request b from the accumulator of one tile: their logits (and
-            // bf16 rows and noise when sampling) and the quantity the argmax compares. The group
-            // is wholly inside the slice or wholly past its end (partial last tile); past-the-end
-            // groups and requests past bs read in-bounds LDS, are computed, and are dropped.
-            auto scores4 = [&](const v4i acc, int vt, bool store, float (&sc)[4]) {
-                const int off = vt - row0;                       // < ntiles * 16 <= rows_per_wg
+            // bf16 rows and noise when sampling), the quantity the argmax compares, and in `out`
+            // the bits store4 writes (fp32 logits, or two words of bf16 pairs). The group is
+            // wholly inside the slice or wholly past its end (partial last tile); past-the-end
+            // groups (and, with STAT, slots past the slice's tiles: the arrays are padded for
+            // them) and requests past bs read in-bounds LDS, are computed, and are dropped.
+            auto scores4 = [&](const v4i acc, int vt, float (&sc)[4], uint32_t (&out)[4]) {
+                const int off = vt - row0;
                 const float4 sv = *reinterpret_cast<const float4*>(scl + off);
                 const float4 bv = *reinterpret_cast<const float4*>(sbase + off);
                 const bool ok = vb && vt < vend;
@@ -168,18 +207,18 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 l[2] = walk_logit(bv.z, sv.z, sb, acc[2]);
                 l[3] = walk_logit(bv.w, sv.w, sb, acc[3]);
                 if constexpr (!SAMPLE) {
-                    if (store && p.out_logits != nullptr && ok)
-                        *reinterpret_cast<float4*>(p.out_logits + orow + vt) =
-                            make_float4(l[0], l[1], l[2], l[3]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sc[i] = l[i];
+                    for (int i = 0; i < 4; ++i) {
+                        sc[i] = l[i];
+                        out[i] = __float_as_uint(l[i]);
+                    }
                 } else {
                     uint32_t h[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) h[i] = bf16_bits(l[i]);
-                    if (store && ok)
-                        *reinterpret_cast<uint2*>(p.draft_logits + orow + vt) =
-                            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                    out[0] = h[0] | (h[1] << 16);
+                    out[1] = h[2] | (h[3] << 16);
+                    out[2] = out[3] = 0;
                     // vt is a multiple of 4: one Philox call yields the words of all 4 rows
                     const uint4 w = philox4x32_10((uint32_t)vt >> 2, (uint32_t)P, (uint32_t)(P >> 32),
                                                   0u, (uint32_t)seed, (uint32_t)(seed >> 32));
@@ -193,11 +232,50 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 }
                 return ok;
             };
+            // writes what scores4 left in `out` (greedy: only when the caller asked for logits)
+            auto store4 = [&](int vt, bool ok, const uint32_t (&out)[4]) {
+                if constexpr (!SAMPLE) {
+                    if (p.out_logits != nullptr && ok)
+                        *reinterpret_cast<uint4*>(p.out_logits + orow + vt) =
+                            make_uint4(out[0], out[1], out[2], out[3]);
+                } else {
+                    if (ok)
+                        *reinterpret_cast<uint2*>(p.draft_logits + orow + vt) =
+                            make_uint2(out[0], out[1]);
+                }
+            };
 
             // Every tile of this wave in increasing row order: register tiles (all their MFMAs
             // first, each into its own accumulator, so the matrix core runs ahead while the VALU
             // finishes tile after tile), then LDS tiles, then streamed ones.
             auto for_tiles = [&](auto&& fin) {
+                if constexpr (STAT) {
+                    // At most NT_STAT tile slots per wave, all on chip: every slot's MFMAs are
+                    // issued first and every slot is finished, with no branch on the tile, so
+                    // the compiler can overlap one tile's LDS reads with another's arithmetic.
+                    // Slots past the slice's tiles hold zero codes and their rows are past vend.
+                    v4i accs[NT_STAT];
+#pragma unroll
+                    for (int tw = 0; tw < NT_STAT; ++tw) {
+                        accs[tw] = (v4i){0, 0, 0, 0};
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
+                            v4i a;
+                            if (tw < NT_REG)
+                                a = qa[tw][kb];
+                            else
+                                a = reinterpret_cast<const v4i*>(
+                                    lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) *
+                                                    TILE_LDS_BYTES)[kb * WAVE + lane];
+                            accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop[kb], accs[tw],
+                                                                             0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int tw = 0; tw < NT_STAT; ++tw)
+                        fin(accs[tw], row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4, tw);
+                    return;
+                }
                 v4i accs[NT_REG];
 #pragma unroll
                 for (int tw = 0; tw < NT_REG; ++tw) {
@@ -212,7 +290,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 #pragma unroll
                 for (int tw = 0; tw < NT_REG; ++tw) {
                     const int tl = tw * WALK_WAVES + wave;
-                    if (tl < ntiles) fin(accs[tw], row0 + tl * TILE_ROWS + g * 4);
+                    if (tl < ntiles) fin(accs[tw], row0 + tl * TILE_ROWS + g * 4, tw);
                 }
                 for (int tw = NT_REG; tw < ntw; ++tw) {
                     const int tl = tw * WALK_WAVES + wave;
@@ -231,7 +309,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(load_a(tl, kb), bop[kb],
                                                                             acc, 0, 0, 0);
                         }
-                        fin(acc, row0 + tl * TILE_ROWS + g * 4);
+                        fin(acc, row0 + tl * TILE_ROWS + g * 4, tw);
                     }
                 }
             };
@@ -242,26 +320,58 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             // NaN is the one case a float compare cannot order; a lane that meets one (or a
             // false alarm such as inf - inf in its check sum) sends its wave through the exact
             // pass below, which builds the order-preserving key of every value.
-            float run_v = -INFINITY;
-            uint32_t run_i = 0xFFFFFFFFu;
-            bool nan_seen = false;
-            for_tiles([&](const v4i acc, int vt) {
+            // Four running maxima, one per row of the group, so that the compare-and-select
+            // chains are independent; merged afterwards by value, then lowest row. The check sum
+            // of all scores is NaN if any score is (or on an inf - inf false alarm). With STAT
+            // the stores wait until every slot is scored (stores in between would split the
+            // code into blocks the compiler schedules one at a time).
+            float run_v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            uint32_t run_i[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+            float chk = 0.0f;
+            uint32_t held[STAT ? NT_STAT : 1][4];
+            for_tiles([&](const v4i acc, int vt, int tw) {
                 float sc[4];
-                const bool ok = scores4(acc, vt, true, sc);
-                const float chk = ok ? (sc[0] + sc[1]) + (sc[2] + sc[3]) : 0.0f;
-                nan_seen = nan_seen || chk != chk;
+                uint32_t out[4];
+                const bool ok = scores4(acc, vt, sc, out);
+                if constexpr (STAT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) held[tw][i] = out[i];
+                } else {
+                    store4(vt, ok, out);
+                }
+                chk += ok ? (sc[0] + sc[1]) + (sc[2] + sc[3]) : 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float x = ok ? sc[i] : -INFINITY;
-                    if (x > run_v) {
-                        run_v = x;
-                        run_i = (uint32_t)(vt + i);
+                    if (x > run_v[i]) {
+                        run_v[i] = x;
+                        run_i[i] = (uint32_t)(vt + i);
                     }
                 }
             });
+            if constexpr (STAT) {
+                if (SAMPLE || p.out_logits != nullptr) {
+#pragma unroll
+                    for (int tw = 0; tw < NT_STAT; ++tw) {
+                        const int vt = row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4;
+                        store4(vt, vb && vt < vend, held[tw]);
+                    }
+                }
+            }
+            const bool nan_seen = chk != chk;
+            float bv = run_v[0];
+            uint32_t bi = run_i[0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) {
+                // an empty chain has index 0xFFFFFFFF and value -inf: it never wins
+                if (run_v[i] > bv || (run_v[i] == bv && run_i[i] < bi)) {
+                    bv = run_v[i];
+                    bi = run_i[i];
+                }
+            }
             uint64_t best;
-            if (run_i != 0xFFFFFFFFu) {
-                best = argmax_key(run_v, run_i);
+            if (bi != 0xFFFFFFFFu) {
+                best = argmax_key(bv, bi);
             } else {
                 // every row of this lane was -inf (or it had none): its first row wins
                 const int vt0 = row0 + wave * TILE_ROWS + g * 4;
@@ -269,9 +379,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             }
             if (__any(nan_seen)) {
                 best = 0;
-                for_tiles([&](const v4i acc, int vt) {
+                for_tiles([&](const v4i acc, int vt, int) {
                     float sc[4];
-                    const bool ok = scores4(acc, vt, false, sc);
+                    uint32_t out[4];
+                    const bool ok = scores4(acc, vt, sc, out);
                     const uint64_t keep = ok ? ~0ull : 0ull;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -281,11 +392,19 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 });
             }
             lkeys[(wave * MAX_RT + rt) * WAVE + lane] = best;
+        };
+        for (int rt = 0; rt < nrt; ++rt) {
+            // the buffer each tile reads is named in the code (not picked by an index), so that
+            // with STAT the compiler can tell it apart from the one the DMA writes
+            if (nbuf == 1 || (rt & 1) == 0)
+                request_tile(rt, buf0, buf1);
+            else
+                request_tile(rt, buf1, buf0);
         }
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
         // the first request tile of step t+1 streams in while the combine of step t waits
-        if (nbuf && t + 1 < p.T) stage_base(0, t + 1, 0);
+        if (nbuf && t + 1 < p.T) stage_base(0, t + 1, buf0);
 
         if (wave == 0) {
             uint64_t k = 0;
@@ -305,8 +424,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     }
 }
 
-const void* mfma_walk_kernel(int sample, int w1t, bool timed) {
-#define DSPARK_MFMA(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI>)
+template <int STAT>
+static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
+#define DSPARK_MFMA(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT>)
     if (timed) return sample ? DSPARK_MFMA(1, DT_BF16, 1) : DSPARK_MFMA(0, DT_BF16, 1);
     if (sample) {
         switch (w1t) {
@@ -321,6 +441,11 @@ const void* mfma_walk_kernel(int sample, int w1t, bool timed) {
         default: return DSPARK_MFMA(0, DT_F16, 0);
     }
 #undef DSPARK_MFMA
+}
+
+const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage) {
+    return static_stage ? mfma_kernel_for<1>(sample, w1t, timed)
+                        : mfma_kernel_for<0>(sample, w1t, timed);
 }
 
 int mfma_fixed_lds_bytes(int rows_per_wg) { return mfma_fixed_lds(rows_per_wg); }
