@@ -603,11 +603,11 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         prev = 0;
     }
     uint64_t seed = 0, P0 = 0;
-    float temp = 1.0f;
+    float rtemp = 1.0f;
     if constexpr (SAMPLE) {
         seed = p.seeds[b];
         P0 = p.positions ? (uint64_t)p.positions[b] : 0;
-        temp = p.temps[b];
+        rtemp = inv_temperature(p.temps[b]);
     }
     const int32_t* req_cand = p.cand + (int64_t)b * p.T * p.k;
     const int own = (lane & 15) * 4 + (lane >> 4);  // this lane's candidate within the wave's 64
@@ -668,8 +668,7 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
             } else {
                 const uint32_t h = bf16_bits(l);
                 if (has) p.out_bf16[row * p.V + blk.v] = (uint16_t)h;
-                float xs = bf16_value(h);
-                if (temp != 1.0f) xs = xs / temp;
+                const float xs = bf16_value(h) * rtemp;
                 const float g = gumbel_from_word(noise_word(seed, P0 + (uint64_t)t, blk.v));
                 key = argmax_key(xs + g, blk.v);
             }

@@ -113,11 +113,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                     const float sb = s1[b];
                     const int64_t orow = ((int64_t)b * p.T + t) * p.V;
                     uint64_t seed = 0, P = 0;
-                    float temp = 1.0f;
+                    float rtemp = 1.0f;
                     if constexpr (SAMPLE) {
                         seed = p.seeds[b];
                         P = (uint64_t)(p.positions ? p.positions[b] : 0) + (uint64_t)t;
-                        temp = p.temps[b];
+                        rtemp = inv_temperature(p.temps[b]);
                     }
                     // logit of row v -> output store, offered to this lane's running argmax (its
                     // rows come in increasing index order)
@@ -130,8 +130,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                         } else {
                             const uint32_t h = bf16_bits(l);
                             p.draft_logits[orow + v] = (uint16_t)h;
-                            float x = bf16_value(h);
-                            if (temp != 1.0f) x = x / temp;
+                            const float x = bf16_value(h) * rtemp;
                             const float g = gumbel_from_word(noise_word(seed, P, (uint32_t)v));
                             run.offer(x + g, (uint32_t)v, true);
                         }

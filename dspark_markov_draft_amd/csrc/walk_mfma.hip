@@ -182,12 +182,12 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             const float sb = vb ? s1[b] : 0.0f;
             const int64_t orow = ((int64_t)(vb ? b : 0) * p.T + t) * p.V;
             uint64_t seed = 0, P = 0;
-            float temp = 1.0f;
+            float rtemp = 1.0f;
             if constexpr (SAMPLE) {
                 if (vb) {
                     seed = p.seeds[b];
                     P = (uint64_t)(p.positions ? p.positions[b] : 0) + (uint64_t)t;
-                    temp = p.temps[b];
+                    rtemp = inv_temperature(p.temps[b]);
                 }
             }
             // Rows vt .. vt+3 of request b from the accumulator of one tile: their logits (and
@@ -225,9 +225,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float x = bf16_value(h[i]);
-                        if (temp != 1.0f) x = x / temp;
-                        sc[i] = x + gumbel_from_word(words[i]);
+                        sc[i] = bf16_value(h[i]) * rtemp + gumbel_from_word(words[i]);
                     }
                 }
                 return ok;

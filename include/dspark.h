@@ -145,7 +145,8 @@ int dspark_walk_greedy(const int8_t* w2_q, const float* w2_scale, const void* w1
  *       row the sample is drawn from
  * Sample: x = Philox4x32-10(counter (v >> 2, lo32 P, hi32 P, 0), key seed)[v & 3],
  * u = (2 (x >> 9) + 1) 2^-24, g = -log(-log u), token = argmax_v (lb[v] / temperature + g)
- * with torch.argmax order; the divide is skipped at temperature 1.0.
+ * with torch.argmax order. The quotient is taken as lb[v] * (1 / temperature) with the
+ * reciprocal rounded once (within one fp32 ulp of lb[v] / temperature; exact at 1.0).
  */
 int dspark_walk_sample(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
                        const float* base_logits, const int32_t* start_tokens, int64_t bs,
