@@ -14,15 +14,26 @@ constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workg
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;
 constexpr int DOT4_REG_SETS = 3;  // lane-per-row kernel: row sets of 256 rows held in registers
 // MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
-// two staging buffers of 16 rows of MFMA_STATIC_STRIDE floats (157 odd 16-byte units), up to
-// MFMA_STATIC_LDS_SLOTS LDS tiles per wave, W1 codes and scales, row scales, lane keys, tokens
+// two staging buffers for 16 rows of at most MFMA_STATIC_STRIDE floats (157 odd 16-byte units),
+// up to MFMA_STATIC_LDS_SLOTS LDS tiles per wave, W1 codes and scales, row scales, lane keys,
+// tokens. Every wave has MFMA_STATIC_TILE_SLOTS tile slots (8 in registers, then LDS), covering
+// MFMA_STATIC_SLOT_ROWS rows; the row-scale array and the staging buffers are sized for reads of
+// all of them. A staging buffer also holds whole 64-lane copy instructions (64 units each).
 constexpr int MFMA_STATIC_ROWS = 624;
 constexpr int MFMA_STATIC_STRIDE = 628;
 constexpr int MFMA_STATIC_LDS_SLOTS = 2;
+constexpr int MFMA_STATIC_TILE_SLOTS = 8 + MFMA_STATIC_LDS_SLOTS;
+constexpr int MFMA_STATIC_SLOT_ROWS = MFMA_STATIC_TILE_SLOTS * WALK_WAVES * 16;
+constexpr int MFMA_STATIC_COPY_UNITS = (16 * MFMA_STATIC_STRIDE / 4 + WAVE - 1) / WAVE * WAVE;
+constexpr int MFMA_STATIC_STAGE_FLOATS =
+    MFMA_STATIC_COPY_UNITS * 4 > 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS
+        ? MFMA_STATIC_COPY_UNITS * 4
+        : 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS;
 constexpr int MFMA_STATIC_LDS_BYTES =
-    2 * 16 * MFMA_STATIC_STRIDE * 4 + MFMA_STATIC_LDS_SLOTS * WALK_WAVES * 4 * WAVE * 16 +
-    W1Q_BYTES + MAX_BS * 4 + MFMA_STATIC_ROWS * 4 + WALK_WAVES * (MAX_BS / 16) * WAVE * 8 +
+    2 * MFMA_STATIC_STAGE_FLOATS * 4 + MFMA_STATIC_LDS_SLOTS * WALK_WAVES * 4 * WAVE * 16 +
+    W1Q_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 + WALK_WAVES * (MAX_BS / 16) * WAVE * 8 +
     MAX_BS * 4;
+static_assert(MFMA_STATIC_SLOT_ROWS >= MFMA_STATIC_ROWS, "static slices fit in the tile slots");
 
 struct WalkParams {
     const int8_t* q;

@@ -38,13 +38,13 @@ constexpr int TILE_ROWS = 16;
 constexpr int NT_REG = 8;                       // W2 tiles per wave held in VGPRs
 constexpr int TILE_LDS_BYTES = 4 * WAVE * 16;   // one tile: 4 K-blocks x 64 lanes x 16 bytes
 constexpr int MAX_RT = MAX_BS / 16;             // 16-request tiles
-constexpr int NT_STAT = NT_REG + MFMA_STATIC_LDS_SLOTS;   // tile slots per wave with STAT
-constexpr int STAT_SLOT_ROWS = NT_STAT * WALK_WAVES * TILE_ROWS;   // rows the slots cover
-static_assert(STAT_SLOT_ROWS >= MFMA_STATIC_ROWS, "STAT slices fit on chip");
-// Row c of a staging buffer is read at c * stride + [0, STAT_SLOT_ROWS): the last row runs past
-// the buffer's 16 rows by at most this many floats (the slots past the slice's end)
-constexpr int STAT_PAD = STAT_SLOT_ROWS - MFMA_STATIC_STRIDE;
-static_assert(STAT_PAD >= 0 && STAT_PAD % 4 == 0, "STAT staging pad");
+constexpr int NT_STAT = MFMA_STATIC_TILE_SLOTS;   // tile slots per wave with STAT
+static_assert(NT_STAT == NT_REG + MFMA_STATIC_LDS_SLOTS, "STAT tile slots");
+static_assert(NT_STAT * WALK_WAVES * TILE_ROWS == MFMA_STATIC_SLOT_ROWS, "STAT slot rows");
+// copy instructions per wave for one request tile with STAT: at most one after each tile slot
+constexpr int STAT_COPY_SLOTS = MFMA_STATIC_COPY_UNITS / WAVE / WALK_WAVES;
+static_assert(MFMA_STATIC_COPY_UNITS % (WAVE * WALK_WAVES) == 0 && STAT_COPY_SLOTS <= NT_STAT,
+              "STAT copy slots");
 constexpr int LKEY_BYTES = WALK_WAVES * MAX_RT * WAVE * 8;
 
 // dynamic LDS besides the W2 tiles: W1 codes, their scales, row scales, lane keys, tokens
@@ -64,13 +64,13 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
     // the staging buffers and row scales are padded for the past-the-end tile slots (below)
-    __shared__ __align__(16) float stage_a[STAT ? 16 * MFMA_STATIC_STRIDE + STAT_PAD : 4];
-    __shared__ __align__(16) float stage_b[STAT ? 16 * MFMA_STATIC_STRIDE + STAT_PAD : 4];
+    __shared__ __align__(16) float stage_a[STAT ? MFMA_STATIC_STAGE_FLOATS : 4];
+    __shared__ __align__(16) float stage_b[STAT ? MFMA_STATIC_STAGE_FLOATS : 4];
     __shared__ __align__(16) unsigned char tiles_s[STAT ? MFMA_STATIC_LDS_SLOTS * WALK_WAVES *
                                                               TILE_LDS_BYTES : 16];
     __shared__ __align__(16) uint32_t w1q_s[STAT ? W1Q_BYTES / 4 : 4];
     __shared__ __align__(16) float s1_s[STAT ? MAX_BS : 4];
-    __shared__ __align__(16) float scl_s[STAT ? STAT_SLOT_ROWS : 4];
+    __shared__ __align__(16) float scl_s[STAT ? MFMA_STATIC_SLOT_ROWS : 4];
     __shared__ __align__(16) uint64_t lkeys_s[STAT ? WALK_WAVES * MAX_RT * WAVE : 2];
     __shared__ __align__(16) int32_t tok_s[STAT ? MAX_BS : 4];
     const int tid = threadIdx.x;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 dst[kb * WAVE + lane] = have ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
         }
     }
-    for (int i = tid; i < (STAT ? STAT_SLOT_ROWS : ntiles * TILE_ROWS); i += WALK_THREADS)
+    for (int i = tid; i < (STAT ? MFMA_STATIC_SLOT_ROWS : ntiles * TILE_ROWS); i += WALK_THREADS)
         scl[i] = i < nrows ? p.scale[row0 + i] : 0.0f;
     load_start_tokens(p, tok);
     __syncthreads();
@@ -142,7 +142,35 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     // instruction moves 64 lanes x 16 bytes to consecutive LDS; row segments are whole 16-byte
     // units (V and row0 are multiples of 4) and lanes past a segment's end stay idle.
     const int units = nrows / 4;
+    // STAT: the copy of a request tile is one flat list of full instructions over the buffer's
+    // 16-byte units. Unit L is unit L % upr of row L / upr (upr: units per padded row), and
+    // instruction j (units 64j .. 64j+63) belongs to wave j % 4, so each wave has at most
+    // STAT_COPY_SLOTS of them and can issue them one at a time between its tile slots: a wave
+    // that issues many copies back to back while HBM is busy stalls in the issue itself. Pad
+    // units, and units past the tile's last valid request (last instruction only), copy an
+    // in-bounds unit of the slice; no valid row ever reads them. The division is a multiply and
+    // shift, exact for L < 2^12 and upr <= 157 (the error stays below 2^-8 < 1/upr).
+    const int upr = ss / 4;
+    const uint32_t upr_inv = (1u << 20) / (uint32_t)upr + 1u;
+    auto copy_job = [&](int rt, int t, float* dst_buf, int j) {
+        const int nv = min(16, p.bs - rt * 16);              // valid requests of the tile (>= 1)
+        if (j * WAVE >= nv * upr) return;                     // past the tile's instructions
+        int L = j * WAVE + lane;                              // < MFMA_STATIC_COPY_UNITS
+        // computed where issued: hoisted out of the step loop, the addresses of every slot's
+        // copy would hold registers the tile loop needs
+        asm volatile("" : "+v"(L));
+        const int r = (int)(((uint32_t)L * upr_inv) >> 20);
+        const int u = L - r * upr;
+        const int rc = min(r, nv - 1), uc = min(u, units - 1);
+        const float* src = p.base + ((int64_t)(rt * 16 + rc) * p.T + t) * p.V + row0 + 4 * uc;
+        __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(dst_buf + j * WAVE * 4),
+                                         16, 0, 0);
+    };
     auto stage_base = [&](int rt, int t, float* dst_buf) {
+        if constexpr (STAT) {
+            for (int s = 0; s < STAT_COPY_SLOTS; ++s) copy_job(rt, t, dst_buf, s * WALK_WAVES + wave);
+            return;
+        }
         for (int r = 0; r < 16; ++r) {
             const int b = rt * 16 + r;
             if (b >= p.bs) break;
@@ -170,7 +198,8 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             }
             __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed ...
             __syncthreads();                  // ... and every other wave's
-            if (nbuf == 2 && rt + 1 < nrt) stage_base(rt + 1, t, nxt);
+            const bool prefetch = nbuf == 2 && rt + 1 < nrt;
+            if (!STAT && prefetch) stage_base(rt + 1, t, nxt);
             const float* sbase = cur + (size_t)c * ss;
             const int b = rt * 16 + c;
             const bool vb = b < p.bs;
@@ -246,7 +275,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             // Every tile of this wave in increasing row order: register tiles (all their MFMAs
             // first, each into its own accumulator, so the matrix core runs ahead while the VALU
             // finishes tile after tile), then LDS tiles, then streamed ones.
-            auto for_tiles = [&](auto&& fin) {
+            auto for_tiles = [&](auto&& fin, auto&& after) {
                 if constexpr (STAT) {
                     // At most NT_STAT tile slots per wave, all on chip: every slot's MFMAs are
                     // issued first and every slot is finished, with no branch on the tile, so
@@ -270,8 +299,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                         }
                     }
 #pragma unroll
-                    for (int tw = 0; tw < NT_STAT; ++tw)
+                    for (int tw = 0; tw < NT_STAT; ++tw) {
                         fin(accs[tw], row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4, tw);
+                        after(tw);
+                    }
                     return;
                 }
                 v4i accs[NT_REG];
@@ -346,6 +377,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                         run_i[i] = (uint32_t)(vt + i);
                     }
                 }
+            }, [&](int tw) {
+                // this wave's share of the next request tile's copy, spread over the slots
+                if constexpr (STAT) {
+                    if (prefetch && tw < STAT_COPY_SLOTS) copy_job(rt + 1, t, nxt, tw * WALK_WAVES + wave);
+                }
             });
             if constexpr (STAT) {
                 if (SAMPLE || p.out_logits != nullptr) {
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                         const uint64_t k = argmax_key(sc[i], (uint32_t)(vt + i)) & keep;
                         best = k > best ? k : best;
                     }
-                });
+                }, [](int) {});
             }
             lkeys[(wave * MAX_RT + rt) * WAVE + lane] = best;
         };
