@@ -62,16 +62,26 @@ __device__ __forceinline__ float walk_logit(float base, float s_row, float s1, i
 }
 
 // ---------------------------------------------------------------------------------------------
-// bf16, round to nearest even; NaN stays a quiet NaN (vLLM PR #62958, Details: draft_logits
-// are the bf16 logits the sample was drawn from).
+// bf16, round to nearest even; a NaN keeps its sign and top payload bits and becomes quiet:
+// (bits >> 16) | 0x40 (vLLM PR #62958, Details: draft_logits are the bf16 logits the sample was
+// drawn from). gfx950's packed conversion v_cvt_pk_bf16_f32 gives exactly these bits (checked
+// on the device against the integer rule over 67.5M patterns: every high half with the tie and
+// boundary low halves, NaN payloads and denormals included), two values per instruction and
+// without the NaN branch the integer rule needs.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    if (x != x) return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef float float2_vt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_vt __attribute__((ext_vector_type(2)));
+// bf16(lo) in bits 0..15, bf16(hi) in bits 16..31
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+    const float2_vt v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_vt));
 }
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return bf16x2_bits(x, 0.0f) & 0xFFFFu; }
 
 __device__ __forceinline__ float bf16_value(uint32_t h) { return __uint_as_float(h << 16); }
+// the two values of a bf16x2_bits pair
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; a round takes the 64-bit
@@ -96,6 +106,43 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
         c2 = n2;
     }
     return make_uint4(c0, c1, c2, c3);
+}
+
+// The same generator for a run of counters (c0, lo32 P, hi32 P, 0) that differ only in c0 (one
+// request at one draft position, every vocabulary group): round 0's product of M1 and hi32 P
+// does not depend on c0 and is taken once per run.
+struct PhiloxRun {
+    uint32_t n0;   // round 0's new c0: hi(M1 * hi32 P) ^ lo32 P ^ k0
+    uint32_t c1;   // round 0's new c1: lo(M1 * hi32 P)
+    uint32_t k0, k1;
+};
+__device__ __forceinline__ PhiloxRun philox_run(uint64_t seed, uint64_t P) {
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint32_t)(P >> 32);
+    PhiloxRun r;
+    r.k0 = (uint32_t)seed;
+    r.k1 = (uint32_t)(seed >> 32);
+    r.n0 = (uint32_t)(p1 >> 32) ^ (uint32_t)P ^ r.k0;
+    r.c1 = (uint32_t)p1;
+    return r;
+}
+__device__ __forceinline__ uint4 philox_run_words(const PhiloxRun& run, uint32_t c0) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint32_t x0 = run.n0, x1 = run.c1, x2 = (uint32_t)(p0 >> 32) ^ run.k1, x3 = (uint32_t)p0;
+    uint32_t k0 = run.k0, k1 = run.k1;
+#pragma unroll
+    for (int r = 1; r < 10; ++r) {
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+        const uint64_t q0 = (uint64_t)0xD2511F53u * x0;
+        const uint64_t q1 = (uint64_t)0xCD9E8D57u * x2;
+        const uint32_t n0 = (uint32_t)(q1 >> 32) ^ x1 ^ k0;
+        const uint32_t n2 = (uint32_t)(q0 >> 32) ^ x3 ^ k1;
+        x1 = (uint32_t)q1;
+        x3 = (uint32_t)q0;
+        x0 = n0;
+        x2 = n2;
+    }
+    return make_uint4(x0, x1, x2, x3);
 }
 
 // Noise word of vocabulary entry v at draft position P for a request keyed by `seed`

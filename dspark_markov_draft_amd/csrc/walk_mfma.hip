@@ -219,6 +219,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     rtemp = inv_temperature(p.temps[b]);
                 }
             }
+            const PhiloxRun prun = philox_run(seed, P);
             // Rows vt .. vt+3 of request b from the accumulator of one tile: their logits (and
             // bf16 rows and noise when sampling), the quantity the argmax compares, and in `out`
             // the bits store4 writes (fp32 logits, or two words of bf16 pairs). The group is
@@ -242,20 +243,16 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                         out[i] = __float_as_uint(l[i]);
                     }
                 } else {
-                    uint32_t h[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) h[i] = bf16_bits(l[i]);
-                    out[0] = h[0] | (h[1] << 16);
-                    out[1] = h[2] | (h[3] << 16);
+                    out[0] = bf16x2_bits(l[0], l[1]);
+                    out[1] = bf16x2_bits(l[2], l[3]);
                     out[2] = out[3] = 0;
+                    const float x[4] = {bf16_lo(out[0]), bf16_hi(out[0]), bf16_lo(out[1]),
+                                        bf16_hi(out[1])};
                     // vt is a multiple of 4: one Philox call yields the words of all 4 rows
-                    const uint4 w = philox4x32_10((uint32_t)vt >> 2, (uint32_t)P, (uint32_t)(P >> 32),
-                                                  0u, (uint32_t)seed, (uint32_t)(seed >> 32));
+                    const uint4 w = philox_run_words(prun, (uint32_t)vt >> 2);
                     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sc[i] = bf16_value(h[i]) * rtemp + gumbel_from_word(words[i]);
-                    }
+                    for (int i = 0; i < 4; ++i) sc[i] = x[i] * rtemp + gumbel_from_word(words[i]);
                 }
                 return ok;
             };
