@@ -134,9 +134,7 @@ __device__ __forceinline__ int hsum(const int4 a) { return (a.x + a.y) + (a.z + 
 
 // One W1 row quantised by one wave (lane l holds elements 4l .. 4l+3): returns lane l's four
 // codes and sets s1 = absmax / 127 (codes = rint(w * 127 / absmax), zero for a zero row).
-template <int W1T>
-__device__ __forceinline__ uint32_t w1_row_codes(const void* w1, int32_t row, int lane, float& s1) {
-    const float4 w = load4_as_f32<W1T>(w1, (int64_t)row * RANK + lane * 4);
+__device__ __forceinline__ uint32_t w1_row_quantise(const float4 w, float& s1) {
     float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
     a = wave_max_nonneg_f32(a);
     const float inv = w1_code_scale(a);
@@ -149,17 +147,24 @@ __device__ __forceinline__ uint32_t w1_row_codes(const void* w1, int32_t row, in
 // lanes on the row. More: sixteen lanes share a row: lane
 // (quarter q, ql) holds elements 16 ql .. 16 ql + 15 of request 4 (iteration * 4 + wave) + q,
 // so one wave instruction serves 4 requests; all of a wave's rows are loaded before any is used.
+// after_issue() runs once the wave's loads are issued and before their values are used: loads
+// it issues complete after the W1 rows (vector memory returns in issue order) without delaying
+// them.
 constexpr int GATHER_ITERS = MAX_BS / (WALK_WAVES * 4);   // 4 request groups per wave at bs 64
 
-template <int W1T>
+template <int W1T, typename AfterIssue>
 __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32_t* tok,
-                                                uint32_t* w1q, float* s1, int wave, int lane) {
+                                                uint32_t* w1q, float* s1, int wave, int lane,
+                                                AfterIssue&& after_issue) {
     if (p.bs <= WALK_WAVES) {
         // at most one request per wave: all 64 lanes on one row (elements 4l .. 4l+3)
         const int b = wave;
+        float4 w = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (b < p.bs) w = load4_as_f32<W1T>(p.w1, (int64_t)tok[b] * RANK + lane * 4);
+        after_issue();
         if (b < p.bs) {
             float sb;
-            w1q[w1q_chunk_dword(b, lane >> 2) + (lane & 3)] = w1_row_codes<W1T>(p.w1, tok[b], lane, sb);
+            w1q[w1q_chunk_dword(b, lane >> 2) + (lane & 3)] = w1_row_quantise(w, sb);
             if (lane == 0) s1[b] = sb;
         }
         return;
@@ -175,6 +180,7 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
             for (int k = 0; k < 4; ++k) wv[it][k] = load4_as_f32<W1T>(p.w1, e + 4 * k);
         }
     }
+    after_issue();
 #pragma unroll
     for (int it = 0; it < GATHER_ITERS; ++it) {
         if ((it * WALK_WAVES + wave) * 4 < p.bs) {    // wave-uniform: some request of it exists

@@ -96,7 +96,16 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
     stamp<TIMED>(p, 1);
 
     for (int t = 0; t < p.T; ++t) {
-        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane);
+        // wave 0 runs the combine, whose polls would wait behind any load it has in flight
+        // (vector memory returns in issue order): its share of this step's first base logits is
+        // issued here, behind the W1 row loads, instead of before the previous combine
+        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {
+            if (wave == 0 && t > 0) {
+#pragma unroll
+                for (int u = 0; u < PF_DEPTH; ++u)
+                    if (u < p.bs) load_base(pf[u], u, t);
+            }
+        });
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
@@ -202,8 +211,8 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
 
-        // the next step's first base logits load while the combine waits
-        if (t + 1 < p.T) {
+        // the next step's first base logits load while the combine waits (wave 0: see above)
+        if (t + 1 < p.T && wave != 0) {
 #pragma unroll
             for (int u = 0; u < PF_DEPTH; ++u)
                 if (u < p.bs) load_base(pf[u], u, t + 1);

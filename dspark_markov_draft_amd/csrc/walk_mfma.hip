@@ -186,7 +186,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     stage_base(0, 0, buf0);
 
     for (int t = 0; t < p.T; ++t) {
-        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane);
+        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [] {});
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
