@@ -54,12 +54,13 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         const int64_t fixed = mfma_fixed_lds_bytes((int)rpw);
         const int64_t want = bs > 16 ? 2 : 1;
         const bool stat = rpw <= MFMA_STATIC_ROWS && stage_stride <= MFMA_STATIC_STRIDE;
+        const int64_t dyn_max = (int64_t)dev.max_lds - MFMA_DYN_STATIC_RESERVE;   // without STAT
         if (stat) {
             // all LDS is static and of fixed size (both staging buffers exist for any batch)
             stage_bufs = want;
             if (MFMA_STATIC_LDS_BYTES > (int64_t)dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
         } else {
-            stage_bufs = ((int64_t)dev.max_lds - fixed) / buf_bytes;
+            stage_bufs = (dyn_max - fixed) / buf_bytes;
             if (stage_bufs > want) stage_bufs = want;
             if (stage_bufs < 1) return DSPARK_ERR_UNSUPPORTED;    // the caller falls back
         }
@@ -68,7 +69,7 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         units = (tiles + WALK_WAVES - 1) / WALK_WAVES;              // tile slots per wave
         reg_units = units < MFMA_REG_TILES ? units : MFMA_REG_TILES;
         int64_t room = stat ? MFMA_STATIC_LDS_SLOTS
-                            : ((int64_t)dev.max_lds - fixed - stage_lds) / (WALK_WAVES * MFMA_TILE_LDS);
+                            : (dyn_max - fixed - stage_lds) / (WALK_WAVES * MFMA_TILE_LDS);
         if (room < 0) room = 0;
         lds_units = units - reg_units;
         if (lds_units > room) lds_units = room;
@@ -77,6 +78,7 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         if (lds_rows > lds_units * WALK_WAVES * 16) lds_rows = lds_units * WALK_WAVES * 16;
         lds_bytes = stat ? MFMA_STATIC_LDS_BYTES
                          : lds_units * WALK_WAVES * MFMA_TILE_LDS + fixed + stage_lds;
+        if (!stat && lds_bytes > dyn_max) return DSPARK_ERR_UNSUPPORTED;
     }
     if (lds_bytes < LDS_MIN_BYTES) lds_bytes = LDS_MIN_BYTES;
     if ((size_t)lds_bytes > dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
@@ -186,7 +188,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
                               plan.stage_stride <= MFMA_STATIC_STRIDE;
     const int dyn_lds = static_stage ? 0 : plan.lds_bytes;
     const void* fn = plan.path == DSPARK_PATH_MFMA
-                         ? mfma_walk_kernel(a.sample, w1t, timed, static_stage)
+                         ? mfma_walk_kernel(a.sample, w1t, timed, static_stage,
+                                            a.out_logits != nullptr)
                          : dot4_walk_kernel(a.sample, w1t, timed);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_lds) !=
         hipSuccess) {

@@ -2,6 +2,8 @@
 // several): launch parameters, clock stamps, the per-step W1 gather, and the grid-wide combine.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -29,10 +31,15 @@ constexpr int MFMA_STATIC_STAGE_FLOATS =
     MFMA_STATIC_COPY_UNITS * 4 > 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS
         ? MFMA_STATIC_COPY_UNITS * 4
         : 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS;
+// per-request sampling constants, loaded once per call: seed, position offset, 1 / temperature
+constexpr int MFMA_REQ_CONST_BYTES = MAX_BS * (8 + 8 + 4);
 constexpr int MFMA_STATIC_LDS_BYTES =
     2 * MFMA_STATIC_STAGE_FLOATS * 4 + MFMA_STATIC_LDS_SLOTS * WALK_WAVES * 4 * WAVE * 16 +
     W1Q_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 + WALK_WAVES * (MAX_BS / 16) * WAVE * 8 +
-    MAX_BS * 4;
+    MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
+// The kernel with dynamic LDS has small static arrays too (the request constants and the
+// unused forms of the static buffers): its dynamic LDS leaves this much of the CU's LDS free.
+constexpr int MFMA_DYN_STATIC_RESERVE = 2048;
 static_assert(MFMA_STATIC_SLOT_ROWS >= MFMA_STATIC_ROWS, "static slices fit in the tile slots");
 
 struct WalkParams {
@@ -152,7 +159,7 @@ __device__ __forceinline__ uint32_t w1_row_quantise(const float4 w, float& s1) {
 // them.
 constexpr int GATHER_ITERS = MAX_BS / (WALK_WAVES * 4);   // 4 request groups per wave at bs 64
 
-template <int W1T, typename AfterIssue>
+template <int W1T, int MAX_NIT = 2, typename AfterIssue>
 __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32_t* tok,
                                                 uint32_t* w1q, float* s1, int wave, int lane,
                                                 AfterIssue&& after_issue) {
@@ -169,40 +176,60 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
         }
         return;
     }
-    const int q = lane >> 4, ql = lane & 15;
-    float4 wv[GATHER_ITERS][4];
+    // Iterations it0 .. it0 + NIT - 1, NIT a template argument so that the code is
+    // straight-line: all their loads are issued before any is used. (With a branch per iteration
+    // the compiler moved each iteration's loads next to their use, one memory round trip per
+    // iteration.) At most two iterations' rows are held at once, which the register budget of
+    // the MFMA kernel allows. Lanes of requests past bs load request 0's row and drop the result.
+    auto gather = [&](auto nit_c, int it0, bool issue_hook) {
+        constexpr int NIT = decltype(nit_c)::value;
+        const int q = lane >> 4, ql = lane & 15;
+        float4 wv[NIT][4];
 #pragma unroll
-    for (int it = 0; it < GATHER_ITERS; ++it) {
-        const int b = (it * WALK_WAVES + wave) * 4 + q;
-        if ((it * WALK_WAVES + wave) * 4 < p.bs && b < p.bs) {
-            const int64_t e = (int64_t)tok[b] * RANK + ql * 16;
+        for (int i = 0; i < NIT; ++i) {
+            const int it = it0 + i;
+            const int b = (it * WALK_WAVES + wave) * 4 + q;
+            const int64_t e = (int64_t)tok[b < p.bs ? b : 0] * RANK + ql * 16;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) wv[it][k] = load4_as_f32<W1T>(p.w1, e + 4 * k);
+            for (int k = 0; k < 4; ++k) wv[i][k] = load4_as_f32<W1T>(p.w1, e + 4 * k);
         }
-    }
-    after_issue();
+        if (issue_hook) after_issue();
 #pragma unroll
-    for (int it = 0; it < GATHER_ITERS; ++it) {
-        if ((it * WALK_WAVES + wave) * 4 < p.bs) {    // wave-uniform: some request of it exists
+        for (int i = 0; i < NIT; ++i) {
+            const int it = it0 + i;
             const int b = (it * WALK_WAVES + wave) * 4 + q;
             float a = 0.0f;
-            if (b < p.bs) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    a = fmaxf(a, fmaxf(fmaxf(fabsf(wv[it][k].x), fabsf(wv[it][k].y)),
-                                       fmaxf(fabsf(wv[it][k].z), fabsf(wv[it][k].w))));
-            }
+            for (int k = 0; k < 4; ++k)
+                a = fmaxf(a, fmaxf(fmaxf(fabsf(wv[i][k].x), fabsf(wv[i][k].y)),
+                                   fmaxf(fabsf(wv[i][k].z), fabsf(wv[i][k].w))));
             a = row16_max_nonneg_f32(a);
+            const float inv = w1_code_scale(a);
+            uint4 codes;
+            codes.x = pack_codes(wv[i][0], inv);
+            codes.y = pack_codes(wv[i][1], inv);
+            codes.z = pack_codes(wv[i][2], inv);
+            codes.w = pack_codes(wv[i][3], inv);
             if (b < p.bs) {
-                const float inv = w1_code_scale(a);
-                uint4 codes;
-                codes.x = pack_codes(wv[it][0], inv);
-                codes.y = pack_codes(wv[it][1], inv);
-                codes.z = pack_codes(wv[it][2], inv);
-                codes.w = pack_codes(wv[it][3], inv);
                 *reinterpret_cast<uint4*>(w1q + w1q_chunk_dword(b, ql)) = codes;
                 if (ql == 0) s1[b] = a * (1.0f / 127.0f);
             }
+        }
+    };
+    // iterations with a request for some wave: 16 requests per iteration
+    static_assert(GATHER_ITERS == 4 && (MAX_NIT == 1 || MAX_NIT == 2), "gather passes");
+    if (p.bs <= 16) {
+        gather(std::integral_constant<int, 1>{}, 0, true);
+    } else if constexpr (MAX_NIT == 2) {
+        gather(std::integral_constant<int, 2>{}, 0, true);
+        if (p.bs > 32) gather(std::integral_constant<int, 2>{}, 2, false);
+    } else {
+        // one iteration per pass (kernels with no registers to spare)
+        gather(std::integral_constant<int, 1>{}, 0, true);
+        gather(std::integral_constant<int, 1>{}, 1, false);
+        if (p.bs > 32) {
+            gather(std::integral_constant<int, 1>{}, 2, false);
+            gather(std::integral_constant<int, 1>{}, 3, false);
         }
     }
 }
@@ -341,7 +368,7 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
 
 // Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0/1; w1t: DT_*).
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
-const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage);
+const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits);
 int mfma_fixed_lds_bytes(int rows_per_wg);
 
 }  // namespace dspark

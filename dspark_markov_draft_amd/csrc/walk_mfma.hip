@@ -59,7 +59,7 @@ __host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
 // to assume that any LDS read may alias the DMA's target, and waits for every DMA in flight
 // before each LDS read, which serialises the next request tile's copy with the current tile's
 // compute.
-template <int SAMPLE, int W1T, int TIMED, int STAT>
+template <int SAMPLE, int W1T, int TIMED, int STAT, int OUTL>
 __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const WalkParams p) {
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
@@ -73,6 +73,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     __shared__ __align__(16) float scl_s[STAT ? MFMA_STATIC_SLOT_ROWS : 4];
     __shared__ __align__(16) uint64_t lkeys_s[STAT ? WALK_WAVES * MAX_RT * WAVE : 2];
     __shared__ __align__(16) int32_t tok_s[STAT ? MAX_BS : 4];
+    __shared__ __align__(16) uint64_t rq_seed[SAMPLE ? MAX_BS : 2];
+    __shared__ __align__(16) uint64_t rq_pos[SAMPLE ? MAX_BS : 2];
+    __shared__ __align__(16) float rq_rtemp[SAMPLE ? MAX_BS : 4];
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);   // uniform: scalar branches
@@ -133,6 +136,14 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     for (int i = tid; i < (STAT ? MFMA_STATIC_SLOT_ROWS : ntiles * TILE_ROWS); i += WALK_THREADS)
         scl[i] = i < nrows ? p.scale[row0 + i] : 0.0f;
     load_start_tokens(p, tok);
+    if constexpr (SAMPLE) {
+        // read once here rather than at every request tile, where each read was a round trip
+        if (tid < p.bs) {
+            rq_seed[tid] = p.seeds[tid];
+            rq_pos[tid] = (uint64_t)(p.positions ? p.positions[tid] : 0);
+            rq_rtemp[tid] = inv_temperature(p.temps[tid]);
+        }
+    }
     __syncthreads();
     stamp<TIMED>(p, 1);
 
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     stage_base(0, 0, buf0);
 
     for (int t = 0; t < p.T; ++t) {
-        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [] {});
+        gather_w1_codes<W1T, SAMPLE ? 1 : 2>(p, tok, w1q, s1, wave, lane, [] {});
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
@@ -214,9 +225,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             float rtemp = 1.0f;
             if constexpr (SAMPLE) {
                 if (vb) {
-                    seed = p.seeds[b];
-                    P = (uint64_t)(p.positions ? p.positions[b] : 0) + (uint64_t)t;
-                    rtemp = inv_temperature(p.temps[b]);
+                    // volatile: read here, not hoisted out of the step loop, where every request
+                    // tile's values would hold registers through the whole walk
+                    seed = *reinterpret_cast<volatile uint64_t*>(&rq_seed[b]);
+                    P = *reinterpret_cast<volatile uint64_t*>(&rq_pos[b]) + (uint64_t)t;
+                    rtemp = *reinterpret_cast<volatile float*>(&rq_rtemp[b]);
                 }
             }
             const PhiloxRun prun = philox_run(seed, P);
@@ -354,15 +367,16 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             float run_v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             uint32_t run_i[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
             float chk = 0.0f;
-            uint32_t held[STAT ? NT_STAT : 1][4];
+            constexpr bool HOLD = STAT && (SAMPLE || OUTL);   // outputs held until all slots
+            uint32_t held[HOLD ? NT_STAT : 1][4];
             for_tiles([&](const v4i acc, int vt, int tw) {
                 float sc[4];
                 uint32_t out[4];
                 const bool ok = scores4(acc, vt, sc, out);
-                if constexpr (STAT) {
+                if constexpr (HOLD) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) held[tw][i] = out[i];
-                } else {
+                } else if constexpr (!STAT) {
                     store4(vt, ok, out);
                 }
                 chk += ok ? (sc[0] + sc[1]) + (sc[2] + sc[3]) : 0.0f;
@@ -380,7 +394,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     if (prefetch && tw < STAT_COPY_SLOTS) copy_job(rt + 1, t, nxt, tw * WALK_WAVES + wave);
                 }
             });
-            if constexpr (STAT) {
+            if constexpr (HOLD) {
                 if (SAMPLE || p.out_logits != nullptr) {
 #pragma unroll
                     for (int tw = 0; tw < NT_STAT; ++tw) {
@@ -455,9 +469,12 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     }
 }
 
-template <int STAT>
+// OUTL: a greedy kernel with STAT holds its logits for the optional fp32 output (every other
+// kernel writes its outputs as before); one without (OUTL = 0) is used when none is asked for
+template <int STAT, int OUTL>
 static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
-#define DSPARK_MFMA(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT>)
+#define DSPARK_MFMA(S, W, TI) \
+    reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT, (S ? 1 : OUTL)>)
     if (timed) return sample ? DSPARK_MFMA(1, DT_BF16, 1) : DSPARK_MFMA(0, DT_BF16, 1);
     if (sample) {
         switch (w1t) {
@@ -474,9 +491,10 @@ static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
 #undef DSPARK_MFMA
 }
 
-const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage) {
-    return static_stage ? mfma_kernel_for<1>(sample, w1t, timed)
-                        : mfma_kernel_for<0>(sample, w1t, timed);
+const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits) {
+    if (!static_stage) return mfma_kernel_for<0, 1>(sample, w1t, timed);
+    return out_logits ? mfma_kernel_for<1, 1>(sample, w1t, timed)
+                      : mfma_kernel_for<1, 0>(sample, w1t, timed);
 }
 
 int mfma_fixed_lds_bytes(int rows_per_wg) { return mfma_fixed_lds(rows_per_wg); }
