@@ -88,6 +88,11 @@ __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p 
 // products of M0 * c0 and M1 * c2 and yields (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key
 // advances by the Weyl constants between rounds.
 // ---------------------------------------------------------------------------------------------
+// a ^ b ^ c in one v_bitop3_b32 (truth table 0x96), where the compiler emits two XORs
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -98,8 +103,8 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
         }
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
@@ -135,8 +140,8 @@ __device__ __forceinline__ uint4 philox_run_words(const PhiloxRun& run, uint32_t
         k1 += 0xBB67AE85u;
         const uint64_t q0 = (uint64_t)0xD2511F53u * x0;
         const uint64_t q1 = (uint64_t)0xCD9E8D57u * x2;
-        const uint32_t n0 = (uint32_t)(q1 >> 32) ^ x1 ^ k0;
-        const uint32_t n2 = (uint32_t)(q0 >> 32) ^ x3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(q1 >> 32), x1, k0);
+        const uint32_t n2 = xor3((uint32_t)(q0 >> 32), x3, k1);
         x1 = (uint32_t)q1;
         x3 = (uint32_t)q0;
         x0 = n0;
