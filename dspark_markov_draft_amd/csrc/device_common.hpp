@@ -240,6 +240,43 @@ __device__ __forceinline__ float wave_max_nonneg_f32(float x) {
 // ---------------------------------------------------------------------------------------------
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
+// The same four elements in two steps: the raw words (f32: four; bf16 / f16: two, in x and y),
+// then their values. fence_raw4 between them makes every load before it issue first and every
+// use of the words come after it (the words are in-out operands of an empty asm, so the compiler
+// waits for their loads there, once, and cannot move a conversion above it).
+template <int DT>
+__device__ __forceinline__ uint4 load4_raw(const void* base, int64_t elem) {
+    if constexpr (DT == DT_F32) {
+        return *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + elem);
+    } else {
+        const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + elem);
+        return make_uint4(r.x, r.y, 0u, 0u);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void fence_raw4(uint4& r) {
+    if constexpr (DT == DT_F32)
+        asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w)::"memory");
+    else
+        asm volatile("" : "+v"(r.x), "+v"(r.y)::"memory");
+}
+template <int DT>
+__device__ __forceinline__ float4 raw4_to_f32(const uint4 r) {
+    if constexpr (DT == DT_F32) {
+        return make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                           __uint_as_float(r.w));
+    } else if constexpr (DT == DT_BF16) {
+        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+    } else {
+        const _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(r.x & 0xFFFFu));
+        const _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(r.x >> 16));
+        const _Float16 h2 = __builtin_bit_cast(_Float16, (uint16_t)(r.y & 0xFFFFu));
+        const _Float16 h3 = __builtin_bit_cast(_Float16, (uint16_t)(r.y >> 16));
+        return make_float4((float)h0, (float)h1, (float)h2, (float)h3);
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ float4 load4_as_f32(const void* base, int64_t elem) {
     if constexpr (DT == DT_F32) {

@@ -25,7 +25,7 @@ constexpr int MFMA_MIN_BS_SAMPLE = 4;
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int path,
+static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int path, int sample,
                      dspark_walk_plan* plan) {
     const int64_t quantum = path == DSPARK_PATH_MFMA ? 16 : 4;
     int64_t rpw = (V + cap - 1) / cap;
@@ -58,7 +58,7 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         if (stat) {
             // all LDS is static and of fixed size (both staging buffers exist for any batch)
             stage_bufs = want;
-            if (MFMA_STATIC_LDS_BYTES > (int64_t)dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
+            if (mfma_static_lds_bytes(sample) > (int64_t)dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
         } else {
             stage_bufs = (dyn_max - fixed) / buf_bytes;
             if (stage_bufs > want) stage_bufs = want;
@@ -67,8 +67,10 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         const int64_t stage_lds = stage_bufs * buf_bytes;
         const int64_t tiles = rpw / 16;
         units = (tiles + WALK_WAVES - 1) / WALK_WAVES;              // tile slots per wave
-        reg_units = units < MFMA_REG_TILES ? units : MFMA_REG_TILES;
-        int64_t room = stat ? MFMA_STATIC_LDS_SLOTS
+        const int64_t reg_tiles =
+            stat ? MFMA_STATIC_TILE_SLOTS - mfma_static_lds_slots(sample) : MFMA_REG_TILES;
+        reg_units = units < reg_tiles ? units : reg_tiles;
+        int64_t room = stat ? mfma_static_lds_slots(sample)
                             : (dyn_max - fixed - stage_lds) / (WALK_WAVES * MFMA_TILE_LDS);
         if (room < 0) room = 0;
         lds_units = units - reg_units;
@@ -76,7 +78,7 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         reg_rows = rpw < reg_units * WALK_WAVES * 16 ? rpw : reg_units * WALK_WAVES * 16;
         lds_rows = rpw - reg_rows;
         if (lds_rows > lds_units * WALK_WAVES * 16) lds_rows = lds_units * WALK_WAVES * 16;
-        lds_bytes = stat ? MFMA_STATIC_LDS_BYTES
+        lds_bytes = stat ? mfma_static_lds_bytes(sample)
                          : lds_units * WALK_WAVES * MFMA_TILE_LDS + fixed + stage_lds;
         if (!stat && lds_bytes > dyn_max) return DSPARK_ERR_UNSUPPORTED;
     }
@@ -123,9 +125,9 @@ int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, int sampl
     int path = (bs >= min_bs && V % 4 == 0) ? DSPARK_PATH_MFMA : DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_DOT4) path = DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_MFMA && V % 4 == 0) path = DSPARK_PATH_MFMA;
-    if (path == DSPARK_PATH_MFMA && plan_path(dev, cap, bs, V, path, plan) == DSPARK_OK)
+    if (path == DSPARK_PATH_MFMA && plan_path(dev, cap, bs, V, path, sample, plan) == DSPARK_OK)
         return DSPARK_OK;
-    return plan_path(dev, cap, bs, V, DSPARK_PATH_DOT4, plan);
+    return plan_path(dev, cap, bs, V, DSPARK_PATH_DOT4, sample, plan);
 }
 
 // The kernels' waits need all their workgroups resident at once. The grid never exceeds the
@@ -144,7 +146,7 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
         int cap = dev.cus < MAX_WORKGROUPS ? dev.cus : MAX_WORKGROUPS;
         const int dbg_cap = debug_knobs().max_workgroups;
         if (dbg_cap > 0 && dbg_cap < cap) cap = dbg_cap;
-        const int st = plan_path(dev, cap, a.bs, a.V, DSPARK_PATH_DOT4, &plan);
+        const int st = plan_path(dev, cap, a.bs, a.V, DSPARK_PATH_DOT4, a.sample, &plan);
         if (st != DSPARK_OK) return st;
     }
     WalkParams p;

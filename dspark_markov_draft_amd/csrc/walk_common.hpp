@@ -17,14 +17,16 @@ constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;
 constexpr int DOT4_REG_SETS = 3;  // lane-per-row kernel: row sets of 256 rows held in registers
 // MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
 // two staging buffers for 16 rows of at most MFMA_STATIC_STRIDE floats (157 odd 16-byte units),
-// up to MFMA_STATIC_LDS_SLOTS LDS tiles per wave, W1 codes and scales, row scales, lane keys,
+// up to mfma_static_lds_slots() LDS tiles per wave, W1 codes and scales, row scales, lane keys,
 // tokens. Every wave has MFMA_STATIC_TILE_SLOTS tile slots (8 in registers, then LDS), covering
 // MFMA_STATIC_SLOT_ROWS rows; the row-scale array and the staging buffers are sized for reads of
 // all of them. A staging buffer also holds whole 64-lane copy instructions (64 units each).
 constexpr int MFMA_STATIC_ROWS = 624;
 constexpr int MFMA_STATIC_STRIDE = 628;
-constexpr int MFMA_STATIC_LDS_SLOTS = 2;
-constexpr int MFMA_STATIC_TILE_SLOTS = 8 + MFMA_STATIC_LDS_SLOTS;
+constexpr int MFMA_STATIC_TILE_SLOTS = 10;
+// tile slots per wave held in LDS (the rest in registers): the sampling kernel holds one more in
+// LDS, which leaves its Philox sampler the registers it would otherwise take from spills
+__host__ __device__ constexpr int mfma_static_lds_slots(int sample) { return sample ? 3 : 2; }
 constexpr int MFMA_STATIC_SLOT_ROWS = MFMA_STATIC_TILE_SLOTS * WALK_WAVES * 16;
 constexpr int MFMA_STATIC_COPY_UNITS = (16 * MFMA_STATIC_STRIDE / 4 + WAVE - 1) / WAVE * WAVE;
 constexpr int MFMA_STATIC_STAGE_FLOATS =
@@ -33,10 +35,12 @@ constexpr int MFMA_STATIC_STAGE_FLOATS =
         : 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS;
 // per-request sampling constants, loaded once per call: seed, position offset, 1 / temperature
 constexpr int MFMA_REQ_CONST_BYTES = MAX_BS * (8 + 8 + 4);
-constexpr int MFMA_STATIC_LDS_BYTES =
-    2 * MFMA_STATIC_STAGE_FLOATS * 4 + MFMA_STATIC_LDS_SLOTS * WALK_WAVES * 4 * WAVE * 16 +
-    W1Q_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 + WALK_WAVES * (MAX_BS / 16) * WAVE * 8 +
-    MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
+__host__ __device__ constexpr int mfma_static_lds_bytes(int sample) {
+    return 2 * MFMA_STATIC_STAGE_FLOATS * 4 + mfma_static_lds_slots(sample) * WALK_WAVES * 4 * WAVE * 16 +
+           W1Q_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 + WALK_WAVES * (MAX_BS / 16) * WAVE * 8 +
+           MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
+}
+static_assert(mfma_static_lds_bytes(1) <= 160 * 1024, "static LDS fits a CU");
 // The kernel with dynamic LDS has small static arrays too (the request constants and the
 // unused forms of the static buffers): its dynamic LDS leaves this much of the CU's LDS free.
 constexpr int MFMA_DYN_STATIC_RESERVE = 2048;
@@ -179,21 +183,34 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
     // Iterations it0 .. it0 + NIT - 1, NIT a template argument so that the code is
     // straight-line: all their loads are issued before any is used. (With a branch per iteration
     // the compiler moved each iteration's loads next to their use, one memory round trip per
-    // iteration.) At most two iterations' rows are held at once, which the register budget of
-    // the MFMA kernel allows. Lanes of requests past bs load request 0's row and drop the result.
+    // iteration.) At most MAX_NIT iterations' rows are held at once, as the caller's register
+    // budget allows. Lanes of requests past bs load request 0's row and drop the result.
     auto gather = [&](auto nit_c, int it0, bool issue_hook) {
         constexpr int NIT = decltype(nit_c)::value;
         const int q = lane >> 4, ql = lane & 15;
-        float4 wv[NIT][4];
+        uint4 raw[NIT][4];
+        // (issued last group first: a pass that shares no leading loads with the one-group
+        // pass is not merged with it by the compiler, which put a wait inside the merged code)
 #pragma unroll
-        for (int i = 0; i < NIT; ++i) {
+        for (int ii = 0; ii < NIT; ++ii) {
+            const int i = NIT - 1 - ii;
             const int it = it0 + i;
             const int b = (it * WALK_WAVES + wave) * 4 + q;
             const int64_t e = (int64_t)tok[b < p.bs ? b : 0] * RANK + ql * 16;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) wv[i][k] = load4_as_f32<W1T>(p.w1, e + 4 * k);
+            for (int k = 0; k < 4; ++k) raw[i][k] = load4_raw<W1T>(p.w1, e + 4 * k);
         }
         if (issue_hook) after_issue();
+        // without the fence the compiler starts converting the first rows (to free their
+        // registers) before the later loads are issued: one round trip per iteration again
+        float4 wv[NIT][4];
+#pragma unroll
+        for (int i = 0; i < NIT; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                fence_raw4<W1T>(raw[i][k]);
+                wv[i][k] = raw4_to_f32<W1T>(raw[i][k]);
+            }
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
             const int it = it0 + i;
@@ -217,9 +234,12 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
         }
     };
     // iterations with a request for some wave: 16 requests per iteration
-    static_assert(GATHER_ITERS == 4 && (MAX_NIT == 1 || MAX_NIT == 2), "gather passes");
+    static_assert(GATHER_ITERS == 4 && (MAX_NIT == 1 || MAX_NIT == 2 || MAX_NIT == 4),
+                  "gather passes");
     if (p.bs <= 16) {
         gather(std::integral_constant<int, 1>{}, 0, true);
+    } else if constexpr (MAX_NIT == 4) {
+        gather(std::integral_constant<int, 4>{}, 0, true);   // groups past bs load request 0
     } else if constexpr (MAX_NIT == 2) {
         gather(std::integral_constant<int, 2>{}, 0, true);
         if (p.bs > 32) gather(std::integral_constant<int, 2>{}, 2, false);

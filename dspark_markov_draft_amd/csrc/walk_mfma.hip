@@ -39,7 +39,7 @@ constexpr int NT_REG = 8;                       // W2 tiles per wave held in VGP
 constexpr int TILE_LDS_BYTES = 4 * WAVE * 16;   // one tile: 4 K-blocks x 64 lanes x 16 bytes
 constexpr int MAX_RT = MAX_BS / 16;             // 16-request tiles
 constexpr int NT_STAT = MFMA_STATIC_TILE_SLOTS;   // tile slots per wave with STAT
-static_assert(NT_STAT == NT_REG + MFMA_STATIC_LDS_SLOTS, "STAT tile slots");
+static_assert(NT_STAT == NT_REG + mfma_static_lds_slots(0), "STAT tile slots");
 static_assert(NT_STAT * WALK_WAVES * TILE_ROWS == MFMA_STATIC_SLOT_ROWS, "STAT slot rows");
 // copy instructions per wave for one request tile with STAT: at most one after each tile slot
 constexpr int STAT_COPY_SLOTS = MFMA_STATIC_COPY_UNITS / WAVE / WALK_WAVES;
@@ -66,7 +66,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     // the staging buffers and row scales are padded for the past-the-end tile slots (below)
     __shared__ __align__(16) float stage_a[STAT ? MFMA_STATIC_STAGE_FLOATS : 4];
     __shared__ __align__(16) float stage_b[STAT ? MFMA_STATIC_STAGE_FLOATS : 4];
-    __shared__ __align__(16) unsigned char tiles_s[STAT ? MFMA_STATIC_LDS_SLOTS * WALK_WAVES *
+    // W2 tile slots per wave in registers (the rest of the NT_STAT slots with STAT are in LDS)
+    constexpr int NTR = STAT ? NT_STAT - mfma_static_lds_slots(SAMPLE) : NT_REG;
+    __shared__ __align__(16) unsigned char tiles_s[STAT ? mfma_static_lds_slots(SAMPLE) * WALK_WAVES *
                                                               TILE_LDS_BYTES : 16];
     __shared__ __align__(16) uint32_t w1q_s[STAT ? W1Q_BYTES / 4 : 4];
     __shared__ __align__(16) float s1_s[STAT ? MAX_BS : 4];
@@ -113,21 +115,21 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
         if (row >= vend) return (v4i){0, 0, 0, 0};
         return *reinterpret_cast<const v4i*>(p.q + (int64_t)row * RANK + g * 64 + kb * 16);
     };
-    v4i qa[NT_REG][4];
+    v4i qa[NTR][4];
 #pragma unroll
-    for (int tw = 0; tw < NT_REG; ++tw) {
+    for (int tw = 0; tw < NTR; ++tw) {
         const int tl = tw * WALK_WAVES + wave;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qa[tw][kb] = tl < ntiles ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
     }
     // with STAT every LDS slot is written (zero codes past the slice's tiles): the tile loop
     // multiplies all of them
-    for (int tw = NT_REG; tw < NT_REG + (STAT ? MFMA_STATIC_LDS_SLOTS : lds_tw); ++tw) {
+    for (int tw = NTR; tw < NTR + (STAT ? mfma_static_lds_slots(SAMPLE) : lds_tw); ++tw) {
         const int tl = tw * WALK_WAVES + wave;
-        const bool have = tl < ntiles && tw < NT_REG + lds_tw;
+        const bool have = tl < ntiles && tw < NTR + lds_tw;
         if (have || STAT) {
             v4i* dst = reinterpret_cast<v4i*>(
-                lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) * TILE_LDS_BYTES);
+                lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) * TILE_LDS_BYTES);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 dst[kb * WAVE + lane] = have ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     stage_base(0, 0, buf0);
 
     for (int t = 0; t < p.T; ++t) {
-        gather_w1_codes<W1T, SAMPLE ? 1 : 2>(p, tok, w1q, s1, wave, lane, [] {});
+        gather_w1_codes<W1T, STAT ? 4 : 2>(p, tok, w1q, s1, wave, lane, [] {});
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
@@ -298,11 +300,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) {
                             v4i a;
-                            if (tw < NT_REG)
+                            if (tw < NTR)
                                 a = qa[tw][kb];
                             else
                                 a = reinterpret_cast<const v4i*>(
-                                    lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) *
+                                    lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) *
                                                     TILE_LDS_BYTES)[kb * WAVE + lane];
                             accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop[kb], accs[tw],
                                                                              0, 0, 0);
@@ -315,9 +317,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     }
                     return;
                 }
-                v4i accs[NT_REG];
+                v4i accs[NTR];
 #pragma unroll
-                for (int tw = 0; tw < NT_REG; ++tw) {
+                for (int tw = 0; tw < NTR; ++tw) {
                     accs[tw] = (v4i){0, 0, 0, 0};
                     if (tw * WALK_WAVES + wave < ntiles) {
 #pragma unroll
@@ -327,17 +329,17 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     }
                 }
 #pragma unroll
-                for (int tw = 0; tw < NT_REG; ++tw) {
+                for (int tw = 0; tw < NTR; ++tw) {
                     const int tl = tw * WALK_WAVES + wave;
                     if (tl < ntiles) fin(accs[tw], row0 + tl * TILE_ROWS + g * 4, tw);
                 }
-                for (int tw = NT_REG; tw < ntw; ++tw) {
+                for (int tw = NTR; tw < ntw; ++tw) {
                     const int tl = tw * WALK_WAVES + wave;
                     if (tl < ntiles) {
                         v4i acc = {0, 0, 0, 0};
-                        if (tw < NT_REG + lds_tw) {
+                        if (tw < NTR + lds_tw) {
                             const v4i* src = reinterpret_cast<const v4i*>(
-                                lds_tiles + (size_t)((tw - NT_REG) * WALK_WAVES + wave) * TILE_LDS_BYTES);
+                                lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) * TILE_LDS_BYTES);
 #pragma unroll
                             for (int kb = 0; kb < 4; ++kb)
                                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane],
