@@ -107,8 +107,13 @@ SMALL = [  # V, T, bs, dtype, grid cap (0 = one workgroup per CU)
     (3000, 5, 64, torch.bfloat16, 0),       # full batch
     (257, 16, 2, torch.float32, 0),         # one workgroup, 16 steps
     (1, 2, 1, torch.bfloat16, 0),           # a single-entry vocabulary
-    (40001, 2, 17, torch.bfloat16, 8),      # MFMA: LDS and streamed tiles, ragged request tile
+    (40000, 2, 17, torch.bfloat16, 8),      # MFMA, dynamic LDS: LDS and streamed tiles, ragged
+                                            # request tile
     (4099, 3, 33, torch.float16, 0),        # V % 4 != 0: scalar base / draft-logit accesses
+    (12288, 3, 21, torch.bfloat16, 0),      # MFMA, static LDS: two request tiles (5 in the
+                                            # second), W1 gather of four groups with idle ones
+    (8192, 2, 40, torch.float16, 0),        # MFMA, static LDS: three request tiles
+    (12480, 2, 24, torch.float32, 20),      # MFMA, static LDS: 624-row slices (the largest)
 ]
 
 
