@@ -282,9 +282,135 @@ __device__ __forceinline__ uint64_t* result_word(const WalkParams& p, int rep, i
     return p.result + ((size_t)rep * MAX_STEPS + t) * MAX_BS + b;
 }
 
+// Grid-wide combine for one or two requests (NB = bs). Every step but the last has no reducer:
+// every workgroup stores its key and reads all the keys of the step itself, which saves the
+// second cross-chip hop of the reducer scheme (reducer -> result word -> every workgroup). The
+// keys of a step sit in REPL = 16 / NB replicas, each holding request b's keys of all workgroups
+// side by side ([t][replica][b][workgroup] in the step's slot region): a workgroup writes its key
+// into every replica and reads replica wg % REPL, so one wave load reads 64 keys from four cache
+// lines, and each line is read by at most nwg / REPL workgroups per round instead of all.
+// Having seen all keys of step t, a workgroup knows every workgroup has read all keys of step
+// t-1 (each read them before storing its key of step t), so it clears its own keys of step t-1.
+// The last step stores its keys into replica 0 only, for one reducer per request (workgroup
+// b % nwg), which writes the token and clears the request's keys of steps T-1 and T-2; nothing
+// is published. The workspace is all zero when the walk ends. Waits keep two rounds of loads in
+// flight and are bounded by the spin limit.
+__device__ __forceinline__ uint64_t* replica_slot(const WalkParams& p, int t, int rep, int nb,
+                                                  int b, int w) {
+    return p.slots + (size_t)t * gridDim.x * p.stride + (size_t)(rep * nb + b) * gridDim.x + w;
+}
+
+template <int TIMED, int NB>
+__device__ __forceinline__ void combine_step_small(const WalkParams& p, int t, uint64_t key,
+                                                   int32_t* tok, int lane) {
+    constexpr int REPL = 16 / NB;
+    static_assert(REPL * NB <= 16, "replicas fit the slot region of a step");
+    const int nwg = gridDim.x;
+    const int wg = blockIdx.x;
+    const bool last = t + 1 == p.T;
+    // lane l < REPL * NB stores request l % NB's key into replica l / NB
+    auto key_of_lane = [&](int src) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)key, src);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((uint32_t)(key >> 32), src);
+        return ((uint64_t)hi << 32) | lo;
+    };
+    uint64_t kb = key_of_lane(0);
+    if constexpr (NB == 2) kb = (lane & 1) ? key_of_lane(1) : kb;
+    const int my_rep = lane / NB, my_b = lane % NB;
+    if (lane < (last ? NB : REPL * NB)) st_dev(replica_slot(p, t, my_rep, NB, my_b, wg), kb);
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 2);
+
+    constexpr int NL = MAX_WORKGROUPS / WAVE;  // key loads per lane and request per round
+    bool mine[NB];
+    bool any = false;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        mine[b] = !last || b % nwg == wg;
+        any = any || mine[b];
+    }
+    const int rd_rep = last ? 0 : wg % REPL;
+    uint64_t best[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) best[b] = 0;
+    if (any) {
+        // unconditional loads (lanes past the grid re-read the last key)
+        auto issue = [&](uint64_t (&v)[NB][NL]) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int k = 0; k < NL; ++k)
+                    v[b][k] = ld_dev(replica_slot(p, t, rd_rep, NB, b, min(lane + k * WAVE, nwg - 1)));
+        };
+        auto complete = [&](const uint64_t (&v)[NB][NL]) {
+            bool all = true;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                uint64_t m = 0;
+#pragma unroll
+                for (int k = 0; k < NL; ++k) {
+                    all = all && (!mine[b] || v[b][k] != 0);
+                    m = v[b][k] > m ? v[b][k] : m;
+                }
+                best[b] = m;
+            }
+            if (p.wait_unset)
+                all = all && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) != 0;
+            return __all(all);
+        };
+        uint64_t va[NB][NL], vb[NB][NL];
+        uint32_t spins = 0;
+        issue(va);
+        while (true) {
+            issue(vb);
+            if (complete(va)) break;
+            issue(va);
+            if (complete(vb)) break;
+            if (++spins > p.spin_limit) {
+                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                break;
+            }
+        }
+    }
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 3);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        if (!mine[b]) continue;
+        uint64_t k = wave_max_u64(best[b]);
+        if (k == 0) k = 1;  // only after a timeout
+        uint32_t token = key_index(k);
+        if (token >= (uint32_t)p.V) token = 0;
+        if (b % nwg == wg && lane == 0) p.tokens[b * p.T + t] = (int32_t)token;
+        if (lane == b) tok[b] = (int32_t)token;
+        if (last) {
+            // the reducer clears the request's keys: replica 0 of this step, every replica of the
+            // step before
+#pragma unroll
+            for (int k = 0; k < NL; ++k) {
+                const int w = lane + k * WAVE;
+                if (w < nwg) {
+                    st_dev(replica_slot(p, t, 0, NB, b, w), 0);
+                    if (t > 0)
+                        for (int r = 0; r < REPL; ++r) st_dev(replica_slot(p, t - 1, r, NB, b, w), 0);
+                }
+            }
+        }
+    }
+    if (!last && t > 0 && lane < REPL * NB) st_dev(replica_slot(p, t - 1, my_rep, NB, my_b, wg), 0);
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 4);
+}
+
 template <int TIMED>
 __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_t key,
                                              int32_t* tok, int lane) {
+    if (p.bs == 1) {
+        combine_step_small<TIMED, 1>(p, t, key, tok, lane);
+        return;
+    }
+    if (p.bs == 2) {
+        combine_step_small<TIMED, 2>(p, t, key, tok, lane);
+        return;
+    }
     const int nwg = gridDim.x;
     const int wg = blockIdx.x;
     uint64_t* step_slots = p.slots + (size_t)t * nwg * p.stride;
