@@ -197,6 +197,28 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
         }
     };
     stage_base(0, 0, buf0);
+    // The same copy issued by waves 1-3 only: wave 0 runs the combine right after, and a copy it
+    // issued would delay its slot store (a wave issuing copies while HBM is busy stalls in the
+    // issue) and its polls (they would complete behind the copy, in issue order).
+    auto stage_base_w123 = [&](int rt, int t, float* dst_buf) {
+        if (wave == 0) return;
+        if constexpr (STAT) {
+            for (int j = wave - 1; j < STAT_COPY_SLOTS * WALK_WAVES; j += WALK_WAVES - 1)
+                copy_job(rt, t, dst_buf, j);
+            return;
+        }
+        for (int r = 0; r < 16; ++r) {
+            const int b = rt * 16 + r;
+            if (b >= p.bs) break;
+            const float* src = p.base + ((int64_t)b * p.T + t) * p.V + row0;
+            float* dst = dst_buf + (size_t)r * ss;
+            for (int u0 = (wave - 1) * WAVE; u0 < units; u0 += WALK_THREADS - WAVE) {
+                if (u0 + lane < units)
+                    __builtin_amdgcn_global_load_lds((global_void_ptr)(src + 4 * (u0 + lane)),
+                                                     (lds_void_ptr)(dst + 4 * u0), 16, 0, 0);
+            }
+        }
+    };
 
     for (int t = 0; t < p.T; ++t) {
         gather_w1_codes<W1T, STAT ? 4 : 2>(p, tok, w1q, s1, wave, lane, [] {});
@@ -451,7 +473,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
         // the first request tile of step t+1 streams in while the combine of step t waits
-        if (nbuf && t + 1 < p.T) stage_base(0, t + 1, buf0);
+        if (nbuf && t + 1 < p.T) stage_base_w123(0, t + 1, buf0);
 
         if (wave == 0) {
             uint64_t k = 0;
