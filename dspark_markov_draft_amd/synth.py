@@ -50,6 +50,12 @@ CASES: Dict[str, Case] = {c.name: c for c in [
     Case("v129280_t5_bs64", 4, 3, 129280, 5, 64, "bf16", 0.02, 3.0, modes=("sample", "greedy")),
     Case("topk512_v151936_t7_bs64", 5, 0, 151936, 7, 64, "bf16", 0.02, 3.0, k=512,
          modes=("greedy", "sample")),
+    # the library's largest supported shape (V = 270336, 16 draft steps, 64 requests), same
+    # distributions as the V = 151936 workloads: a parity case, not a measured workload
+    Case("vmax270336_t16_bs64", 6, 0, 270336, 16, 64, "bf16", 0.02, 3.0,
+         modes=("greedy", "sample")),
+    Case("vmax270336_t16_bs1", 6, 1, 270336, 16, 1, "bf16", 0.02, 3.0,
+         modes=("greedy", "sample")),
 ]}
 
 

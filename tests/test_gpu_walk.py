@@ -157,6 +157,12 @@ FULL = [
     ("v248320_t16_bs1", "sample", None),
     ("v248320_t16_bs1", "greedy", None),
     ("v129280_t5_bs64", "sample", [5, 40]),
+    # the largest supported shape: 1056-row slices, so the 64-request walk runs the MFMA kernel
+    # with dynamic LDS, one staging buffer and streamed tiles, and the one-request walk holds two
+    # LDS row sets
+    ("vmax270336_t16_bs64", "greedy", [0, 63]),
+    ("vmax270336_t16_bs64", "sample", [31, 62]),
+    ("vmax270336_t16_bs1", "sample", None),
 ]
 
 
