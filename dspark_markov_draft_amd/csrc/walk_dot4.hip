@@ -220,12 +220,14 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
         if (wave == 0) {
             uint64_t k = 0;
             if (lane < p.bs) {
-                k = wkeys[lane];
+                // the four waves' keys: all read before any compare (one LDS round trip)
+                uint64_t o[WALK_WAVES];
 #pragma unroll
-                for (int w = 1; w < WALK_WAVES; ++w) {
-                    const uint64_t o = wkeys[w * MAX_BS + lane];
-                    k = o > k ? o : k;
-                }
+                for (int w = 0; w < WALK_WAVES; ++w) o[w] = wkeys[w * MAX_BS + lane];
+                asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+                const uint64_t k01 = o[1] > o[0] ? o[1] : o[0];
+                const uint64_t k23 = o[3] > o[2] ? o[3] : o[2];
+                k = k23 > k01 ? k23 : k01;
             }
             combine_step<TIMED>(p, t, k, tok, lane);
         }

@@ -478,14 +478,25 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
         if (wave == 0) {
             uint64_t k = 0;
             if (lane < p.bs) {
+                // the 16 lane keys of request `lane` (4 waves x 4 row groups): all reads are
+                // issued before any compare (read one at a time, each was a separate LDS round
+                // trip on the combine's critical path), then reduced as a tree
                 const int rt = lane >> 4, cc = lane & 15;
+                uint64_t o[16];
 #pragma unroll
                 for (int w = 0; w < WALK_WAVES; ++w)
 #pragma unroll
-                    for (int gg = 0; gg < 4; ++gg) {
-                        const uint64_t o = lkeys[(w * MAX_RT + rt) * WAVE + gg * 16 + cc];
-                        k = o > k ? o : k;
-                    }
+                    for (int gg = 0; gg < 4; ++gg)
+                        o[w * 4 + gg] = lkeys[(w * MAX_RT + rt) * WAVE + gg * 16 + cc];
+                asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]),
+                             "+v"(o[5]), "+v"(o[6]), "+v"(o[7]), "+v"(o[8]), "+v"(o[9]),
+                             "+v"(o[10]), "+v"(o[11]), "+v"(o[12]), "+v"(o[13]), "+v"(o[14]),
+                             "+v"(o[15]));
+#pragma unroll
+                for (int n = 8; n >= 1; n /= 2)
+#pragma unroll
+                    for (int i = 0; i < n; ++i) o[i] = o[i + n] > o[i] ? o[i + n] : o[i];
+                k = o[0];
             }
             combine_step<TIMED>(p, t, k, tok, lane);
         }
