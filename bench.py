@@ -14,6 +14,11 @@ dispatch records (hipExtLaunchKernel), so launch queueing is not charged to the 
 reported: the same after a 512 MiB *write* (caches full of dirty lines, whose write-back the
 walk then pays), a warm back-to-back rate, and a sweep over the other shapes of that table.
 
+`w2_roofline` is the bound on W2 traffic alone: R_W2 = max((B_W2 + (T-1) B_str) / HBM peak,
+T B_res / LDS peak), with B_res and B_str the W2 bytes the walk keeps on chip and re-reads from
+memory every step (the library's plan), B_W2 = V x 256 read once; `frac` = R_W2 / kernel time.
+For the top-k walk the W2 traffic is the gathered candidate rows, bs T k 256 bytes, at HBM peak.
+
 `roofline.traffic` is the HBM traffic per launch measured by the FETCH_SIZE / WRITE_SIZE
 counters (profiles/traffic.json, calibrated against a plain copy of known size); it is reported
 only while the library sources hash to what they were when the counters were taken.
@@ -39,6 +44,22 @@ HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
 KERNEL_NAMES = {1: "dense_walk_dot4_kernel", 2: "dense_walk_mfma_kernel"}
 TOPK_KERNELS = "topk_select_kernel+topk_walk_kernel"
+# LDS read peak: 128 bytes per clock per compute unit x 256 units x 2.4 GHz
+LDS_PEAK_GBS = 128 * 256 * 2.4
+
+
+def w2_roofline(w, plan, kernel_us):
+    """The W2-traffic roofline of one walk call (microseconds) and the fraction of it reached."""
+    if w.k:
+        r_hbm = w.bs * w.T * w.k * 256 / (HBM_PEAK_GBS * 1e3)
+        r_lds = 0.0
+    else:
+        r_hbm = (w.V * 256 + (w.T - 1) * plan["streamed_bytes"]) / (HBM_PEAK_GBS * 1e3)
+        r_lds = w.T * plan["resident_bytes"] / (LDS_PEAK_GBS * 1e3)
+    r = max(r_hbm, r_lds)
+    return {"r_w2_us": round(r, 3), "hbm_term_us": round(r_hbm, 3), "lds_term_us": round(r_lds, 3),
+            "eager_w2_us": round(w.T * w.V * 256 / (HBM_PEAK_GBS * 1e3), 3),
+            "kernel_us": round(kernel_us, 3), "frac": round(r / kernel_us, 4)}
 
 
 def log(*a):
@@ -259,6 +280,7 @@ def main():
     med = float(np.median(us))
     nbytes = w.algorithmic_bytes()
     kmean = float(np.mean(kus))
+    w2 = w2_roofline(w, plan, kmean)
     achieved = nbytes / (kmean * 1e-6) / 1e9
     log(f"[bench] median {med:.2f} us  p10 {np.percentile(us, 10):.2f}  p90 "
         f"{np.percentile(us, 90):.2f}  warm {warm_us:.2f} us  kernel mean {kmean:.2f} us "
@@ -285,6 +307,7 @@ def main():
                 log(f"[bench] {name} {mode}: {e}")
                 continue
             nb = w.algorithmic_bytes()
+            s_plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
             entry = {"workload": name, "mode": mode, "us_median": round(float(np.median(s_us)), 2),
                      "us_p10": round(float(np.percentile(s_us, 10)), 2),
                      "us_p90": round(float(np.percentile(s_us, 90)), 2),
@@ -292,7 +315,8 @@ def main():
                      "kernel_us_mean": round(float(np.mean(s_kus)), 2),
                      "kernel_parts_us": w.kernel_parts_us,
                      "hbm_frac": round(nb / (float(np.mean(s_kus)) * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                       4)}
+                                       4),
+                     "w2_frac": w2_roofline(w, s_plan, float(np.mean(s_kus)))["frac"]}
             sweep.append(entry)
             log(f"[bench] {name} {mode}: {entry}")
 
@@ -332,6 +356,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
                      "kernel": kernel},
+        "w2_roofline": w2,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
