@@ -397,3 +397,52 @@ def test_graph_capture_replay():
         assert torch.equal(logits, ref_l), i
         assert float(scratch.abs().sum()) > 0
     assert int(ws.count_nonzero()) == 0
+
+
+# ----------------------------------------------------------------------------------------------
+# the one- and two-request combine (every workgroup reads all keys from one of 16 / bs
+# replicas; one reducer per request at the last step)
+# ----------------------------------------------------------------------------------------------
+SMALL_COMBINE = [  # V, T, bs, grid cap (0 = one workgroup per CU)
+    (9000, 1, 1, 0),      # the last step is the only step: reducer only
+    (9000, 1, 2, 0),
+    (9000, 2, 1, 0),      # one all-poll step, then the reducer clears both steps
+    (9000, 5, 1, 3),      # three workgroups: replicas read by fewer workgroups than exist
+    (9000, 5, 2, 2),
+    (20000, 16, 1, 0),    # the deepest walk
+    (20000, 16, 2, 0),
+]
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+@pytest.mark.parametrize("V,T,bs,cap", SMALL_COMBINE)
+def test_small_batch_combine(V, T, bs, cap, mode):
+    """Two calls on one workspace: both match the oracle and leave the workspace all zero (a key
+    left behind would let the next call's wait finish early)."""
+    dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+    p = random_problem(V, T, bs, seed=V + 31 * T + bs + cap)
+    qs = p.quantize()
+    ws = dm.new_workspace(bs, T, V)
+    for _ in range(2):
+        if mode == "greedy":
+            tok, out = p.greedy(qs=qs, ws=ws)
+            rep = p.check_greedy(tok, out)
+        else:
+            tok, out = p.sample(qs=qs, ws=ws)
+            rep = p.check_sample(tok, out)
+        assert rep.ok, rep.summary()
+        assert dm.dspark_workspace_status(ws) == 0
+        assert int(ws.count_nonzero()) == 0
+
+
+def test_workspace_shared_across_batch_sizes():
+    """One workspace (sized for the largest call) serves walks of 3, 1, 2 and 3 requests in turn:
+    the two key layouts (per-workgroup slots, per-request replicas) both leave it zero."""
+    V, T = 7000, 4
+    ws = dm.new_workspace(3, T, V)
+    for bs in (3, 1, 2, 3):
+        p = random_problem(V, T, bs, seed=500 + bs)
+        tok, logits = p.greedy(ws=ws)
+        rep = p.check_greedy(tok, logits)
+        assert rep.ok, rep.summary()
+        assert int(ws.count_nonzero()) == 0
