@@ -193,7 +193,8 @@ __device__ __forceinline__ bool buf_slot(const uint32_t* cnt, uint32_t e) {
 
 // Radix levels over the keys in LDS (all threads): from bit `lo` down, among keys whose bits
 // above `lo` equal `prefix`, the need-th largest. The first level below bit 51 takes 12 bits,
-// later ones 10 (NBINS = 1024 takes only 10-bit levels). Returns the full 51-bit key. The keys
+// later ones 10 (NBINS = 1024 takes only 10-bit levels). Returns the full 51-bit key, or the
+// lowest key of a bin all of whose keys are needed (the same threshold for `>=`). The keys
 // are buf[e] for e < n_linear, or, with n_linear < 0, the wave regions of counts cnt.
 template <int NBINS = L1_BINS>
 __device__ __forceinline__ uint64_t lds_select(const uint64_t* buf, const uint32_t* cnt,
@@ -218,11 +219,16 @@ __device__ __forceinline__ uint64_t lds_select(const uint64_t* buf, const uint32
             if (lane == 0) {
                 sh[0] = d;
                 sh[1] = above;
+                sh[5] = hist[d];
             }
         }
         __syncthreads();
         prefix = (prefix << w) | sh[0];
         need -= sh[1];
+        // Every key of the chosen bin is needed: the keys >= the bin's lowest possible key are
+        // exactly the `need` wanted ones (those of higher bins at every level, and this bin's),
+        // so that key serves as the threshold without resolving the lower bits.
+        if (sh[5] == need) return prefix << lo;
     }
     return prefix;
 }
