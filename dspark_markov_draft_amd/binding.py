@@ -23,7 +23,7 @@ MAX_STEPS, MAX_BS, MAX_V, MAX_TOPK = 16, 64, 270336, 2048
 DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG, DEBUG_STAMPS = 1, 2, 3, 4
 DEBUG_FORCE_PATH = 5
 DEBUG_KERNEL_TIMING = 6
-PATH_DOT4, PATH_MFMA = 1, 2
+PATH_DOT4, PATH_MFMA, PATH_MFMA1 = 1, 2, 3
 STAMPS_PER_WG = 82
 
 OK = 0

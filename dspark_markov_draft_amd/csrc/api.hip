@@ -297,7 +297,8 @@ int dspark_debug_set(int key, int64_t value) {
         case DSPARK_DEBUG_SPIN_LIMIT: k.spin_limit = (uint32_t)value; return DSPARK_OK;
         case DSPARK_DEBUG_WAIT_UNSET_FLAG: k.wait_unset = (uint32_t)value; return DSPARK_OK;
         case DSPARK_DEBUG_FORCE_PATH:
-            if (value != 0 && value != DSPARK_PATH_DOT4 && value != DSPARK_PATH_MFMA)
+            if (value != 0 && value != DSPARK_PATH_DOT4 && value != DSPARK_PATH_MFMA &&
+                value != DSPARK_PATH_MFMA1)
                 return DSPARK_ERR_INVALID_ARG;
             k.force_path = (int)value;
             return DSPARK_OK;

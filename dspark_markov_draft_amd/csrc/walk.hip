@@ -27,7 +27,7 @@ static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int path, int sample,
                      dspark_walk_plan* plan) {
-    const int64_t quantum = path == DSPARK_PATH_MFMA ? 16 : 4;
+    const int64_t quantum = path == DSPARK_PATH_MFMA ? 16 : 4;   // (MFMA1 handles partial tiles)
     int64_t rpw = (V + cap - 1) / cap;
     if (rpw < WALK_THREADS) rpw = V < WALK_THREADS ? V : WALK_THREADS;
     rpw = round_up(rpw, quantum);
@@ -35,7 +35,16 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
 
     int64_t reg_rows, lds_rows, units, reg_units, lds_units, lds_bytes;
     int64_t stage_bufs = 0, stage_stride = 0;
-    if (path == DSPARK_PATH_DOT4) {
+    if (path == DSPARK_PATH_MFMA1) {
+        // one request: every row in registers as 16-row tiles, at most MFMA1_TILES per wave
+        if (rpw > MFMA1_MAX_ROWS) return DSPARK_ERR_UNSUPPORTED;   // the caller falls back
+        units = ((rpw + 15) / 16 + WALK_WAVES - 1) / WALK_WAVES;   // tiles per wave
+        reg_units = units;
+        lds_units = 0;
+        reg_rows = rpw;
+        lds_rows = 0;
+        lds_bytes = DOT4_FIXED_LDS;
+    } else if (path == DSPARK_PATH_DOT4) {
         units = (rpw + WALK_THREADS - 1) / WALK_THREADS;            // row sets
         reg_units = units < DOT4_REG_SETS ? units : DOT4_REG_SETS;
         lds_units = units - reg_units;
@@ -122,10 +131,13 @@ int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, int sampl
     if (dbg.max_workgroups > 0 && dbg.max_workgroups < cap) cap = dbg.max_workgroups;
     if (cap < 1) return DSPARK_ERR_NO_DEVICE;
     const int min_bs = sample ? MFMA_MIN_BS_SAMPLE : MFMA_MIN_BS_GREEDY;
-    int path = (bs >= min_bs && V % 4 == 0) ? DSPARK_PATH_MFMA : DSPARK_PATH_DOT4;
+    int path = (bs >= min_bs && V % 4 == 0) ? DSPARK_PATH_MFMA
+               : bs == 1                      ? DSPARK_PATH_MFMA1
+                                              : DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_DOT4) path = DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_MFMA && V % 4 == 0) path = DSPARK_PATH_MFMA;
-    if (path == DSPARK_PATH_MFMA && plan_path(dev, cap, bs, V, path, sample, plan) == DSPARK_OK)
+    if (dbg.force_path == DSPARK_PATH_MFMA1 && bs == 1) path = DSPARK_PATH_MFMA1;
+    if (path != DSPARK_PATH_DOT4 && plan_path(dev, cap, bs, V, path, sample, plan) == DSPARK_OK)
         return DSPARK_OK;
     return plan_path(dev, cap, bs, V, DSPARK_PATH_DOT4, sample, plan);
 }
@@ -192,7 +204,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     const void* fn = plan.path == DSPARK_PATH_MFMA
                          ? mfma_walk_kernel(a.sample, w1t, timed, static_stage,
                                             a.out_logits != nullptr)
-                         : dot4_walk_kernel(a.sample, w1t, timed);
+                     : plan.path == DSPARK_PATH_MFMA1 ? mfma1_walk_kernel(a.sample, w1t, timed)
+                                                       : dot4_walk_kernel(a.sample, w1t, timed);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_lds) !=
         hipSuccess) {
         (void)hipGetLastError();

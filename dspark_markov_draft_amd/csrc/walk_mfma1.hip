@@ -1,0 +1,200 @@
+// Dense walk for one request on the matrix cores.
+//
+// What it computes: as the other dense-walk kernels (vLLM PR #62958, int8 DSpark Markov walk,
+// Overview and Details; vLLM PR #64476, Claims): l[v] = base[0,t,v] + s[v] * s1 * sum_k q[v,k]
+// q1[k], then the first-maximum argmax (greedy) or the Gumbel-max of bf16(l) / temp + noise.
+//
+// One request makes each step a GEMV, and the lane-per-row v_dot4 kernel spends most of its
+// step issuing VALU work: 64 v_dot4 per row plus a move per W2 word held in AGPRs. Here the
+// workgroup's W2 rows sit in registers as the A operands of v_mfma_i32_16x16x64_i8 (which reads
+// them from AGPRs directly), and the request's W1 codes are the B operand of all 16 columns:
+// every column of the 16 x 16 result holds the same 16 dot products. Lane l receives rows
+// 4 (l / 16) .. 4 (l / 16) + 3 of the tile, so among four tiles it finishes one row of its own
+// choosing (tile (l / 4) % 4, row 4 (l / 16) + l % 4), and the 64 lanes finish 64 distinct rows
+// with no data movement between lanes. The matrix core does four times the MACs the method
+// needs (the 16 columns hold 16 copies of one), which at 16 cycles per MFMA is 40 MFMAs, ~0.3 us
+// per step for a 640-row slice; the VALU only finishes three rows per lane.
+//
+// The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves (tile tw * 4 + wave),
+// at most MFMA1_TILES per wave. A lane holds, for tile slot tw and K-block kb, bytes
+// g * 64 + kb * 16 .. +15 of its row (g = lane / 16), the K order of the multi-request MFMA
+// kernel, and the W1 codes are read from LDS in the same order. Everything else (the per-step
+// W1 gather, base-logit prefetch, the running argmax and the grid-wide combine) is the v_dot4
+// kernel's, so both give the same exact int32 sums, logits and tokens.
+#include "walk_common.hpp"
+
+namespace dspark {
+
+typedef int v4i1 __attribute__((ext_vector_type(4)));
+
+constexpr int M1_GROUPS = (MFMA1_TILES + 3) / 4;   // rows each lane finishes per step
+
+template <int SAMPLE, int W1T, int TIMED>
+__global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const WalkParams p) {
+    stamp<TIMED>(p, 0);
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int c = lane & 15;   // A: row within the tile
+    const int g = lane >> 4;   // K group; result rows 4g .. 4g+3
+    const int ts = (lane >> 2) & 3;   // which of four tiles this lane finishes a row of
+    const int ri = lane & 3;          // and which of its four result rows
+    const int row0 = blockIdx.x * p.rows_per_wg;
+    const int nrows = min(p.rows_per_wg, p.V - row0);
+    const int vend = row0 + nrows;
+    const int ntiles = (nrows + 15) / 16;
+
+    uint32_t* w1q = reinterpret_cast<uint32_t*>(smem);
+    float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
+    uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
+    int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
+
+    // ---- fill: this wave's tiles as A operands; zero past the slice -----------------------
+    v4i1 qa[MFMA1_TILES][4];
+#pragma unroll
+    for (int tw = 0; tw < MFMA1_TILES; ++tw) {
+        const int tl = tw * WALK_WAVES + wave;
+        const int row = row0 + tl * 16 + c;
+        const bool have = tl < ntiles && row < vend;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            qa[tw][kb] = have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + g * 64 + kb * 16)
+                              : (v4i1){0, 0, 0, 0};
+    }
+    // the rows this lane finishes: group gi takes tile slot 4 gi + ts, row 4 g + ri of it
+    int vrow[M1_GROUPS];
+    bool vok[M1_GROUPS];
+    float sc[M1_GROUPS];
+#pragma unroll
+    for (int gi = 0; gi < M1_GROUPS; ++gi) {
+        const int tw = 4 * gi + ts;
+        vrow[gi] = row0 + (tw * WALK_WAVES + wave) * 16 + 4 * g + ri;
+        vok[gi] = tw < MFMA1_TILES && vrow[gi] < vend;
+        sc[gi] = vok[gi] ? p.scale[vrow[gi]] : 0.0f;
+    }
+    load_start_tokens(p, tok);
+
+    float pf[M1_GROUPS];   // base logits of the next step to be scored
+    auto load_base = [&](int t) {
+        const float* br = p.base + (int64_t)t * p.V;
+#pragma unroll
+        for (int gi = 0; gi < M1_GROUPS; ++gi) pf[gi] = vok[gi] ? br[vrow[gi]] : 0.0f;
+    };
+    load_base(0);
+    __syncthreads();
+    stamp<TIMED>(p, 1);
+
+    uint64_t seed = 0;
+    uint64_t pos0 = 0;
+    float rtemp = 1.0f;
+    if constexpr (SAMPLE) {
+        seed = p.seeds[0];
+        pos0 = (uint64_t)(p.positions ? p.positions[0] : 0);
+        rtemp = inv_temperature(p.temps[0]);
+    }
+
+    for (int t = 0; t < p.T; ++t) {
+        // wave 0 runs the combine, whose polls would wait behind any load it has in flight
+        // (vector memory returns in issue order): its base logits of this step are issued here,
+        // behind the W1 row loads, instead of before the previous combine
+        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {
+            if (wave == 0 && t > 0) load_base(t);
+        });
+        __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
+
+        float cur[M1_GROUPS];
+#pragma unroll
+        for (int gi = 0; gi < M1_GROUPS; ++gi) cur[gi] = pf[gi];
+        v4i1 bop[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            bop[kb] = *reinterpret_cast<const v4i1*>(w1q + w1q_chunk_dword(0, g * 4 + kb));
+        const float sb = s1[0];
+
+        // every tile slot's MFMAs first (slots past the slice hold zero codes), then the finish
+        v4i1 acc[MFMA1_TILES];
+#pragma unroll
+        for (int tw = 0; tw < MFMA1_TILES; ++tw) {
+            acc[tw] = (v4i1){0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb], acc[tw], 0, 0, 0);
+        }
+        const int64_t orow = (int64_t)t * p.V;
+        const uint64_t P = pos0 + (uint64_t)t;
+        RunningArgmax run;
+#pragma unroll
+        for (int gi = 0; gi < M1_GROUPS; ++gi) {
+            // this lane's row of tile slot 4 gi + ts: component ri of that slot's result
+            int a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tw = 4 * gi + j;
+                const v4i1 x = tw < MFMA1_TILES ? acc[tw] : (v4i1){0, 0, 0, 0};
+                int s = x[0];
+                s = ri == 1 ? x[1] : s;
+                s = ri == 2 ? x[2] : s;
+                s = ri == 3 ? x[3] : s;
+                a[j] = s;
+            }
+            int dot = a[0];
+            dot = ts == 1 ? a[1] : dot;
+            dot = ts == 2 ? a[2] : dot;
+            dot = ts == 3 ? a[3] : dot;
+            const int v = vrow[gi];
+            const float l = walk_logit(cur[gi], sc[gi], sb, dot);
+            if constexpr (!SAMPLE) {
+                if (p.out_logits && vok[gi]) p.out_logits[orow + v] = l;
+                run.offer(l, (uint32_t)v, vok[gi]);
+            } else {
+                const uint32_t h = bf16_bits(l);
+                if (vok[gi]) p.draft_logits[orow + v] = (uint16_t)h;
+                const float x = bf16_value(h) * rtemp;
+                const float gn = gumbel_from_word(noise_word(seed, P, (uint32_t)v));
+                run.offer(x + gn, (uint32_t)v, vok[gi]);
+            }
+        }
+        const uint64_t best = wave_max_u64(run.key());
+        if (lane == 0) wkeys[wave * MAX_BS] = best;
+        __syncthreads();
+        stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
+
+        // the next step's base logits load while the combine waits (wave 0: see above)
+        if (t + 1 < p.T && wave != 0) load_base(t + 1);
+        if (wave == 0) {
+            uint64_t k = 0;
+            if (lane == 0) {
+                uint64_t o[WALK_WAVES];
+#pragma unroll
+                for (int w = 0; w < WALK_WAVES; ++w) o[w] = wkeys[w * MAX_BS];
+                const uint64_t k01 = o[1] > o[0] ? o[1] : o[0];
+                const uint64_t k23 = o[3] > o[2] ? o[3] : o[2];
+                k = k23 > k01 ? k23 : k01;
+            }
+            combine_step<TIMED>(p, t, k, tok, lane);
+        }
+        __syncthreads();
+    }
+}
+
+const void* mfma1_walk_kernel(int sample, int w1t, bool timed) {
+#define DSPARK_MFMA1(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma1_kernel<S, W, TI>)
+    if (timed) return sample ? DSPARK_MFMA1(1, DT_BF16, 1) : DSPARK_MFMA1(0, DT_BF16, 1);
+    if (sample) {
+        switch (w1t) {
+            case DT_F32: return DSPARK_MFMA1(1, DT_F32, 0);
+            case DT_BF16: return DSPARK_MFMA1(1, DT_BF16, 0);
+            default: return DSPARK_MFMA1(1, DT_F16, 0);
+        }
+    }
+    switch (w1t) {
+        case DT_F32: return DSPARK_MFMA1(0, DT_F32, 0);
+        case DT_BF16: return DSPARK_MFMA1(0, DT_BF16, 0);
+        default: return DSPARK_MFMA1(0, DT_F16, 0);
+    }
+#undef DSPARK_MFMA1
+}
+
+}  // namespace dspark

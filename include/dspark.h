@@ -98,18 +98,21 @@ typedef struct dspark_walk_plan {
     int64_t resident_bytes;      /* int8 W2 bytes held on chip (whole grid) */
     int64_t streamed_bytes;      /* int8 W2 bytes re-read per step (whole grid) */
     int32_t lds_bytes;           /* dynamic LDS per workgroup */
-    int32_t path;                /* DSPARK_PATH_DOT4 (few requests) or DSPARK_PATH_MFMA */
-    int32_t reg_units;           /* register row sets (dot4) or 16-row tiles per wave (MFMA) */
+    int32_t path;                /* DSPARK_PATH_DOT4, DSPARK_PATH_MFMA or DSPARK_PATH_MFMA1 */
+    int32_t reg_units;           /* register row sets (dot4) or 16-row tiles per wave (MFMA kernels) */
     int32_t lds_units;           /* LDS row sets (dot4) or tiles per wave (MFMA) */
     int32_t total_units;         /* all row sets / tiles per wave (the rest are streamed) */
     int32_t stage_bufs;          /* MFMA: LDS buffers staging a 16-request tile's base logits */
     int32_t stage_stride;        /* MFMA: floats per request row in such a buffer */
 } dspark_walk_plan;
 
-/* Which kernel runs a dense walk: a few requests are GEMVs (lane-per-row v_dot4 kernel, up to 2
- * requests greedy, 3 sampling), more make every step a GEMM (int8 matrix cores, 16 requests per
- * tile). The plan queries below report the greedy walk's plan. */
-enum dspark_path { DSPARK_PATH_DOT4 = 1, DSPARK_PATH_MFMA = 2 };
+/* Which kernel runs a dense walk: a few requests are GEMVs, more make every step a GEMM (int8
+ * matrix cores, 16 requests per tile: DSPARK_PATH_MFMA, from 3 requests greedy and 4 sampling).
+ * One request runs on the matrix cores too when each workgroup's slice is at most 640 rows (V up
+ * to about 163K), with its W1 codes in all 16 columns (DSPARK_PATH_MFMA1); otherwise, and for 2
+ * (greedy) or 2-3 (sampling) requests, the lane-per-row v_dot4 kernel runs (DSPARK_PATH_DOT4).
+ * The plan queries below report the greedy walk's plan. */
+enum dspark_path { DSPARK_PATH_DOT4 = 1, DSPARK_PATH_MFMA = 2, DSPARK_PATH_MFMA1 = 3 };
 
 int dspark_walk_plan_query(int64_t bs, int64_t T, int64_t V, dspark_walk_plan* plan);
 
@@ -196,7 +199,8 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *   DSPARK_DEBUG_WAIT_UNSET_FLAG: non-zero makes the grid-wide waits also wait for a workspace
  *       flag that nothing sets, so each runs into its spin limit (for the timeout test);
  *   DSPARK_DEBUG_FORCE_PATH: 0 chooses by batch size; DSPARK_PATH_DOT4 / DSPARK_PATH_MFMA force
- *       that kernel for every batch size (both compute the same results);
+ *       that kernel for every batch size, DSPARK_PATH_MFMA1 for one request whose slices fit it
+ *       (all compute the same results);
  *   DSPARK_DEBUG_STAMPS: a device address (8-byte aligned) of 256 x 82 uint64 words, or 0.
  *       When set, dense walks with bf16 W1 run an instrumented build of the same kernel that
  *       stores the 100 MHz device clock per workgroup: [0] start, [1] W2 resident, then per step

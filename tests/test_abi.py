@@ -62,7 +62,11 @@ def test_plan_partition(bs, cus, V):
         assert e.status == B.ERR_UNSUPPORTED
         return
     mfma_ok = bs >= 3 and V % 4 == 0                 # the greedy plan
-    if not mfma_ok:
+    rpw4 = -(-max(-(-V // min(cus, 256)), min(V, 256)) // 4) * 4
+    if bs == 1:
+        # one request: the matrix-core kernel when a slice fits its 640 register rows
+        assert p["path"] == (B.PATH_MFMA1 if rpw4 <= 640 else B.PATH_DOT4)
+    elif not mfma_ok:
         assert p["path"] == B.PATH_DOT4
     elif p["path"] == B.PATH_DOT4:
         # the MFMA kernel was refused only because one staging buffer (16 request rows of the
@@ -80,7 +84,10 @@ def test_plan_partition(bs, cus, V):
     assert rpw % quantum == 0
     assert p["rows_in_registers"] + p["rows_in_lds"] + p["rows_streamed"] == rpw
     assert p["resident_bytes"] + p["streamed_bytes"] == V * 256
-    if not mfma:
+    if p["path"] == B.PATH_MFMA1:
+        assert p["rows_in_registers"] == rpw <= 640 and p["rows_in_lds"] == 0
+        assert p["total_units"] == -(-(-(-rpw // 16)) // 4) <= 10
+    elif not mfma:
         assert p["rows_in_registers"] <= 3 * 256 and p["rows_in_lds"] <= 512
         assert p["total_units"] == -(-rpw // 256)
     else:
@@ -211,7 +218,7 @@ def test_misc_validation():
     assert L.dspark_workspace_status(None, None) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(99, 1) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_SPIN_LIMIT, -1) == B.ERR_INVALID_ARG
-    assert L.dspark_debug_set(B.DEBUG_FORCE_PATH, 3) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(B.DEBUG_FORCE_PATH, 4) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_STAMPS, 12) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_KERNEL_TIMING, 4097) == B.ERR_INVALID_ARG
     n = ctypes.c_int32(-1)

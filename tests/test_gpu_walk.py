@@ -26,7 +26,7 @@ def _reset_knobs():
         dm.dspark_debug_set(key, 0)
 
 
-PATHS = [0, B.PATH_DOT4, B.PATH_MFMA]   # 0: chosen by batch size
+PATHS = [0, B.PATH_DOT4, B.PATH_MFMA, B.PATH_MFMA1]   # 0: chosen by batch size (MFMA1: 1 request)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -182,24 +182,28 @@ def test_parity_full_size(name, mode, reqs):
 
 
 @pytest.mark.parametrize("name,mode,reqs", [("v151936_t7_bs1", "greedy", None),
+                                            ("v151936_t7_bs1", "sample", None),
                                             ("v151936_t7_bs16", "sample", [3, 12])])
 def test_paths_agree_bitwise(name, mode, reqs):
-    """Both kernels form each logit with the same exact int32 sum and the same fp32 operations,
-    so they must agree bit for bit; each is also checked against the oracle."""
+    """All kernels form each logit with the same exact int32 sum and the same fp32 operations,
+    so they must agree bit for bit; each is also checked against the oracle. (The one-request
+    MFMA kernel only takes one request: at bs 16 forcing it leaves the batched kernel.)"""
     inp = make_inputs(CASES[name])
     p = Problem(inp.w1, inp.w2, inp.base, inp.start, seeds=inp.seeds,
                 temps=inp.temperature.numpy())
     qs = p.quantize()
     outs = []
-    for path in (B.PATH_DOT4, B.PATH_MFMA):
+    for path in (B.PATH_DOT4, B.PATH_MFMA, B.PATH_MFMA1):
         dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
         outs.append(p.greedy(qs=qs) if mode == "greedy" else p.sample(qs=qs))
-    assert np.array_equal(outs[0][0], outs[1][0])
-    assert np.array_equal(outs[0][1].view(np.uint32 if mode == "greedy" else np.uint16),
-                          outs[1][1].view(np.uint32 if mode == "greedy" else np.uint16))
-    rep = (p.check_greedy(*outs[1], requests=reqs) if mode == "greedy"
-           else p.check_sample(*outs[1], requests=reqs))
-    assert rep.ok, rep.summary()
+    for o in outs[1:]:
+        assert np.array_equal(outs[0][0], o[0])
+        assert np.array_equal(outs[0][1].view(np.uint32 if mode == "greedy" else np.uint16),
+                              o[1].view(np.uint32 if mode == "greedy" else np.uint16))
+    for o in outs[1:]:
+        rep = (p.check_greedy(*o, requests=reqs) if mode == "greedy"
+               else p.check_sample(*o, requests=reqs))
+        assert rep.ok, rep.summary()
 
 
 @pytest.mark.parametrize("path", [B.PATH_DOT4, B.PATH_MFMA])
