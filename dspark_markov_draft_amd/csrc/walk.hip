@@ -36,14 +36,15 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
     int64_t reg_rows, lds_rows, units, reg_units, lds_units, lds_bytes;
     int64_t stage_bufs = 0, stage_stride = 0;
     if (path == DSPARK_PATH_MFMA1) {
-        // one request: every row in registers as 16-row tiles, at most MFMA1_TILES per wave
+        // one request: every row on chip as 16-row tiles, MFMA1_TILES per wave in registers,
+        // up to MFMA1_LDS_TILES more in LDS
         if (rpw > MFMA1_MAX_ROWS) return DSPARK_ERR_UNSUPPORTED;   // the caller falls back
         units = ((rpw + 15) / 16 + WALK_WAVES - 1) / WALK_WAVES;   // tiles per wave
-        reg_units = units;
-        lds_units = 0;
-        reg_rows = rpw;
-        lds_rows = 0;
-        lds_bytes = DOT4_FIXED_LDS;
+        reg_units = units < MFMA1_TILES ? units : MFMA1_TILES;
+        lds_units = units - reg_units;
+        reg_rows = rpw < reg_units * WALK_WAVES * 16 ? rpw : reg_units * WALK_WAVES * 16;
+        lds_rows = rpw - reg_rows;
+        lds_bytes = lds_units * WALK_WAVES * MFMA_TILE_LDS + DOT4_FIXED_LDS;
     } else if (path == DSPARK_PATH_DOT4) {
         units = (rpw + WALK_THREADS - 1) / WALK_THREADS;            // row sets
         reg_units = units < DOT4_REG_SETS ? units : DOT4_REG_SETS;
@@ -204,7 +205,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     const void* fn = plan.path == DSPARK_PATH_MFMA
                          ? mfma_walk_kernel(a.sample, w1t, timed, static_stage,
                                             a.out_logits != nullptr)
-                     : plan.path == DSPARK_PATH_MFMA1 ? mfma1_walk_kernel(a.sample, w1t, timed)
+                     : plan.path == DSPARK_PATH_MFMA1
+                         ? mfma1_walk_kernel(a.sample, w1t, timed, plan.lds_units > 0)
                                                        : dot4_walk_kernel(a.sample, w1t, timed);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_lds) !=
         hipSuccess) {

@@ -15,8 +15,9 @@ constexpr int W1Q_BYTES = MAX_BS * RANK;         // int8 codes of the gathered W
 constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workgroup per CU
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;
 constexpr int DOT4_REG_SETS = 3;  // lane-per-row kernel: row sets of 256 rows held in registers
-constexpr int MFMA1_TILES = 10;   // one-request MFMA kernel: 16-row tiles per wave in registers
-constexpr int MFMA1_MAX_ROWS = MFMA1_TILES * WALK_WAVES * 16;   // 640 rows per workgroup
+constexpr int MFMA1_TILES = 10;      // one-request MFMA kernel: 16-row tiles per wave in registers
+constexpr int MFMA1_LDS_TILES = 8;   // and at most this many more in LDS (4 KB each)
+constexpr int MFMA1_MAX_ROWS = (MFMA1_TILES + MFMA1_LDS_TILES) * WALK_WAVES * 16;   // 1152
 // MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
 // two staging buffers for 16 rows of at most MFMA_STATIC_STRIDE floats (157 odd 16-byte units),
 // up to mfma_static_lds_slots() LDS tiles per wave, W1 codes and scales, row scales, lane keys,
@@ -516,7 +517,7 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
 
 // Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0/1; w1t: DT_*).
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
-const void* mfma1_walk_kernel(int sample, int w1t, bool timed);
+const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles);
 const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits);
 int mfma_fixed_lds_bytes(int rows_per_wg);
 

@@ -11,26 +11,32 @@
 // every column of the 16 x 16 result holds the same 16 dot products. Lane l receives rows
 // 4 (l / 16) .. 4 (l / 16) + 3 of the tile, so among four tiles it finishes one row of its own
 // choosing (tile (l / 4) % 4, row 4 (l / 16) + l % 4), and the 64 lanes finish 64 distinct rows
-// with no data movement between lanes. The matrix core does four times the MACs the method
-// needs (the 16 columns hold 16 copies of one), which at 16 cycles per MFMA is 40 MFMAs, ~0.3 us
-// per step for a 640-row slice; the VALU only finishes three rows per lane.
+// with no data movement between lanes. The matrix core does 16 times the MACs the method needs
+// (the 16 columns hold 16 copies of one), which at 16 cycles per MFMA is 40 MFMAs, ~0.3 us per
+// step for a 640-row slice; the VALU only finishes three rows per lane.
 //
-// The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves (tile tw * 4 + wave),
-// at most MFMA1_TILES per wave. A lane holds, for tile slot tw and K-block kb, bytes
-// g * 64 + kb * 16 .. +15 of its row (g = lane / 16), the K order of the multi-request MFMA
-// kernel, and the W1 codes are read from LDS in the same order. Everything else (the per-step
-// W1 gather, base-logit prefetch, the running argmax and the grid-wide combine) is the v_dot4
-// kernel's, so both give the same exact int32 sums, logits and tokens.
+// The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves (tile tw * 4 + wave):
+// the first MFMA1_TILES slots of each wave in registers, up to MFMA1_LDS_TILES more in LDS (a
+// K-block of a tile is 64 consecutive 16-byte lane slots there, read without bank conflicts).
+// A lane holds, for tile slot tw and K-block kb, bytes g * 64 + kb * 16 .. +15 of its row
+// (g = lane / 16), the K order of the multi-request MFMA kernel, and the W1 codes are read from
+// LDS in the same order. Everything else (the per-step W1 gather, base-logit prefetch, the
+// running argmax and the grid-wide combine) is the v_dot4 kernel's, so both give the same exact
+// int32 sums, logits and tokens.
 #include "walk_common.hpp"
 
 namespace dspark {
 
 typedef int v4i1 __attribute__((ext_vector_type(4)));
 
-constexpr int M1_GROUPS = (MFMA1_TILES + 3) / 4;   // rows each lane finishes per step
+constexpr int M1_TILE_LDS_BYTES = 4 * WAVE * 16;
 
-template <int SAMPLE, int W1T, int TIMED>
+// LDS: slices of more than MFMA1_TILES tiles per wave (the LDS tile slots exist); without it the
+// kernel has only the register slots, and no code or registers for the others.
+template <int SAMPLE, int W1T, int TIMED, int LDS>
 __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const WalkParams p) {
+    constexpr int M1_SLOTS = MFMA1_TILES + (LDS ? MFMA1_LDS_TILES : 0);   // tile slots per wave
+    constexpr int M1_GROUPS = (M1_SLOTS + 3) / 4;   // rows each lane finishes per step, at most
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -44,8 +50,12 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     const int nrows = min(p.rows_per_wg, p.V - row0);
     const int vend = row0 + nrows;
     const int ntiles = (nrows + 15) / 16;
+    const int ntl = LDS ? p.lds_units : 0;        // LDS tile slots per wave
+    const int nslots = MFMA1_TILES + ntl;         // tile slots per wave
+    const int ngroups = (nslots + 3) / 4;         // uniform
 
-    uint32_t* w1q = reinterpret_cast<uint32_t*>(smem);
+    unsigned char* lds_tiles = smem;
+    uint32_t* w1q = reinterpret_cast<uint32_t*>(smem + (size_t)ntl * WALK_WAVES * M1_TILE_LDS_BYTES);
     float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
     int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
@@ -62,6 +72,19 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
             qa[tw][kb] = have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + g * 64 + kb * 16)
                               : (v4i1){0, 0, 0, 0};
     }
+    // LDS slots (zero codes past the slice: their MFMAs give zeros)
+    for (int tw = MFMA1_TILES; tw < nslots; ++tw) {
+        const int tl = tw * WALK_WAVES + wave;
+        const int row = row0 + tl * 16 + c;
+        const bool have = tl < ntiles && row < vend;
+        v4i1* dst = reinterpret_cast<v4i1*>(
+            lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            dst[kb * WAVE + lane] =
+                have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + g * 64 + kb * 16)
+                     : (v4i1){0, 0, 0, 0};
+    }
     // the rows this lane finishes: group gi takes tile slot 4 gi + ts, row 4 g + ri of it
     int vrow[M1_GROUPS];
     bool vok[M1_GROUPS];
@@ -70,7 +93,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     for (int gi = 0; gi < M1_GROUPS; ++gi) {
         const int tw = 4 * gi + ts;
         vrow[gi] = row0 + (tw * WALK_WAVES + wave) * 16 + 4 * g + ri;
-        vok[gi] = tw < MFMA1_TILES && vrow[gi] < vend;
+        vok[gi] = tw < nslots && vrow[gi] < vend;
         sc[gi] = vok[gi] ? p.scale[vrow[gi]] : 0.0f;
     }
     load_start_tokens(p, tok);
@@ -113,8 +136,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
             bop[kb] = *reinterpret_cast<const v4i1*>(w1q + w1q_chunk_dword(0, g * 4 + kb));
         const float sb = s1[0];
 
-        // every tile slot's MFMAs first (slots past the slice hold zero codes), then the finish
-        v4i1 acc[MFMA1_TILES];
+        // every register slot's MFMAs first (slots past the slice hold zero codes), then the LDS
+        // slots', then the finish
+        v4i1 acc[M1_SLOTS];
 #pragma unroll
         for (int tw = 0; tw < MFMA1_TILES; ++tw) {
             acc[tw] = (v4i1){0, 0, 0, 0};
@@ -122,17 +146,30 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
             for (int kb = 0; kb < 4; ++kb)
                 acc[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb], acc[tw], 0, 0, 0);
         }
+#pragma unroll
+        for (int tw = MFMA1_TILES; tw < M1_SLOTS; ++tw) {
+            acc[tw] = (v4i1){0, 0, 0, 0};
+            if (tw < nslots) {
+                const v4i1* src = reinterpret_cast<const v4i1*>(
+                    lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    acc[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane], bop[kb],
+                                                                    acc[tw], 0, 0, 0);
+            }
+        }
         const int64_t orow = (int64_t)t * p.V;
         const uint64_t P = pos0 + (uint64_t)t;
         RunningArgmax run;
 #pragma unroll
         for (int gi = 0; gi < M1_GROUPS; ++gi) {
+            if (LDS && gi >= ngroups) break;
             // this lane's row of tile slot 4 gi + ts: component ri of that slot's result
             int a[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int tw = 4 * gi + j;
-                const v4i1 x = tw < MFMA1_TILES ? acc[tw] : (v4i1){0, 0, 0, 0};
+                const v4i1 x = tw < M1_SLOTS ? acc[tw] : (v4i1){0, 0, 0, 0};
                 int s = x[0];
                 s = ri == 1 ? x[1] : s;
                 s = ri == 2 ? x[2] : s;
@@ -179,8 +216,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     }
 }
 
-const void* mfma1_walk_kernel(int sample, int w1t, bool timed) {
-#define DSPARK_MFMA1(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma1_kernel<S, W, TI>)
+template <int LDS>
+static const void* mfma1_kernel_for(int sample, int w1t, bool timed) {
+#define DSPARK_MFMA1(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma1_kernel<S, W, TI, LDS>)
     if (timed) return sample ? DSPARK_MFMA1(1, DT_BF16, 1) : DSPARK_MFMA1(0, DT_BF16, 1);
     if (sample) {
         switch (w1t) {
@@ -195,6 +233,10 @@ const void* mfma1_walk_kernel(int sample, int w1t, bool timed) {
         default: return DSPARK_MFMA1(0, DT_F16, 0);
     }
 #undef DSPARK_MFMA1
+}
+
+const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles) {
+    return lds_tiles ? mfma1_kernel_for<1>(sample, w1t, timed) : mfma1_kernel_for<0>(sample, w1t, timed);
 }
 
 }  // namespace dspark

@@ -64,8 +64,9 @@ def test_plan_partition(bs, cus, V):
     mfma_ok = bs >= 3 and V % 4 == 0                 # the greedy plan
     rpw4 = -(-max(-(-V // min(cus, 256)), min(V, 256)) // 4) * 4
     if bs == 1:
-        # one request: the matrix-core kernel when a slice fits its 640 register rows
-        assert p["path"] == (B.PATH_MFMA1 if rpw4 <= 640 else B.PATH_DOT4)
+        # one request: the matrix-core kernel when a slice fits its 640 register rows and 512
+        # LDS rows
+        assert p["path"] == (B.PATH_MFMA1 if rpw4 <= 1152 else B.PATH_DOT4)
     elif not mfma_ok:
         assert p["path"] == B.PATH_DOT4
     elif p["path"] == B.PATH_DOT4:
@@ -85,8 +86,10 @@ def test_plan_partition(bs, cus, V):
     assert p["rows_in_registers"] + p["rows_in_lds"] + p["rows_streamed"] == rpw
     assert p["resident_bytes"] + p["streamed_bytes"] == V * 256
     if p["path"] == B.PATH_MFMA1:
-        assert p["rows_in_registers"] == rpw <= 640 and p["rows_in_lds"] == 0
-        assert p["total_units"] == -(-(-(-rpw // 16)) // 4) <= 10
+        assert p["rows_in_registers"] == min(rpw, 640) and p["rows_streamed"] == 0
+        assert p["rows_in_lds"] == rpw - min(rpw, 640) <= 512
+        assert p["total_units"] == -(-(-(-rpw // 16)) // 4) <= 18
+        assert p["reg_units"] == min(p["total_units"], 10)
     elif not mfma:
         assert p["rows_in_registers"] <= 3 * 256 and p["rows_in_lds"] <= 512
         assert p["total_units"] == -(-rpw // 256)

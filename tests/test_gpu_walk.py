@@ -114,6 +114,8 @@ SMALL = [  # V, T, bs, dtype, grid cap (0 = one workgroup per CU)
                                             # second), W1 gather of four groups with idle ones
     (8192, 2, 40, torch.float16, 0),        # MFMA, static LDS: three request tiles
     (12480, 2, 24, torch.float32, 20),      # MFMA, static LDS: 624-row slices (the largest)
+    (20000, 3, 1, torch.bfloat16, 20),      # one request, 1000-row slices: LDS tiles (MFMA1)
+    (9000, 2, 1, torch.float16, 8),         # one request, 1128-row slices: 8 LDS tiles, ragged
 ]
 
 
@@ -183,6 +185,7 @@ def test_parity_full_size(name, mode, reqs):
 
 @pytest.mark.parametrize("name,mode,reqs", [("v151936_t7_bs1", "greedy", None),
                                             ("v151936_t7_bs1", "sample", None),
+                                            ("v248320_t16_bs1", "greedy", None),
                                             ("v151936_t7_bs16", "sample", [3, 12])])
 def test_paths_agree_bitwise(name, mode, reqs):
     """All kernels form each logit with the same exact int32 sum and the same fp32 operations,
