@@ -108,9 +108,10 @@ typedef struct dspark_walk_plan {
 
 /* Which kernel runs a dense walk: a few requests are GEMVs, more make every step a GEMM (int8
  * matrix cores, 16 requests per tile: DSPARK_PATH_MFMA, from 3 requests greedy and 4 sampling).
- * One request runs on the matrix cores too when each workgroup's slice is at most 640 rows (V up
- * to about 163K), with its W1 codes in all 16 columns (DSPARK_PATH_MFMA1); otherwise, and for 2
- * (greedy) or 2-3 (sampling) requests, the lane-per-row v_dot4 kernel runs (DSPARK_PATH_DOT4).
+ * One request runs on the matrix cores too when each workgroup's slice is at most 1152 rows
+ * (every supported V on a 256-CU device), with its W1 codes in all 16 columns
+ * (DSPARK_PATH_MFMA1); otherwise, and for 2 (greedy) or 2-3 (sampling) requests, the
+ * lane-per-row v_dot4 kernel runs (DSPARK_PATH_DOT4).
  * The plan queries below report the greedy walk's plan. */
 enum dspark_path { DSPARK_PATH_DOT4 = 1, DSPARK_PATH_MFMA = 2, DSPARK_PATH_MFMA1 = 3 };
 
