@@ -453,3 +453,29 @@ def test_workspace_shared_across_batch_sizes():
         rep = p.check_greedy(tok, logits)
         assert rep.ok, rep.summary()
         assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("V,T,bs", [(12288, 3, 20), (12288, 3, 40), (12288, 4, 64), (8192, 2, 48)])
+def test_batched_greedy_without_logits_same_tokens(V, T, bs):
+    """The timed greedy configuration (no fp32 logits output) is its own kernel build for batched
+    walks (it holds no logits between its tile slots). Its tokens equal those of the run with
+    logits, which is checked against the oracle: two, three and four 16-request tiles."""
+    p = random_problem(V, T, bs, seed=V + bs)
+    qs = p.quantize()
+    tok, logits = p.greedy(want_logits=True, qs=qs)
+    rep = p.check_greedy(tok, logits)
+    assert rep.ok, rep.summary()
+    for _ in range(2):
+        tok2, _ = p.greedy(want_logits=False, qs=qs)
+        assert np.array_equal(tok, tok2)
+
+
+def test_full_size_batched_greedy_without_logits_same_tokens():
+    inp = make_inputs(CASES["v151936_t7_bs64"])
+    p = Problem(inp.w1, inp.w2, inp.base, inp.start)
+    qs = p.quantize()
+    a, logits = p.greedy(want_logits=True, qs=qs)
+    rep = p.check_greedy(a, logits, requests=[0, 40, 63])
+    assert rep.ok, rep.summary()
+    b, _ = p.greedy(want_logits=False, qs=qs)
+    assert np.array_equal(a, b)
