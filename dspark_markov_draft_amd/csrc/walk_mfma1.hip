@@ -18,9 +18,10 @@
 // The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves (tile tw * 4 + wave):
 // the first MFMA1_TILES slots of each wave in registers, up to MFMA1_LDS_TILES more in LDS (a
 // K-block of a tile is 64 consecutive 16-byte lane slots there, read without bank conflicts).
-// A lane holds, for tile slot tw and K-block kb, bytes g * 64 + kb * 16 .. +15 of its row
-// (g = lane / 16), the K order of the multi-request MFMA kernel, and the W1 codes are read from
-// LDS in the same order. Everything else (the per-step W1 gather, base-logit prefetch, the
+// A lane holds, for tile slot tw and K-block kb, bytes kb * 64 + g * 16 .. +15 of its row
+// (g = lane / 16), and the W1 codes are read from LDS in the same order: any order of K serves
+// if A and B share it, and this one makes each fill instruction read 64 contiguous bytes of each
+// of 16 rows (16 cache lines per 1 KB, where the multi-request kernel's order touches 32). Everything else (the per-step W1 gather, base-logit prefetch, the
 // running argmax and the grid-wide combine) is the v_dot4 kernel's, so both give the same exact
 // int32 sums, logits and tokens.
 #include "walk_common.hpp"
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         const bool have = tl < ntiles && row < vend;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            qa[tw][kb] = have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + g * 64 + kb * 16)
+            qa[tw][kb] = have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + kb * 64 + g * 16)
                               : (v4i1){0, 0, 0, 0};
     }
     // LDS slots (zero codes past the slice: their MFMAs give zeros)
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
             dst[kb * WAVE + lane] =
-                have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + g * 64 + kb * 16)
+                have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + kb * 64 + g * 16)
                      : (v4i1){0, 0, 0, 0};
     }
     // the rows this lane finishes: group gi takes tile slot 4 gi + ts, row 4 g + ri of it
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         v4i1 bop[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            bop[kb] = *reinterpret_cast<const v4i1*>(w1q + w1q_chunk_dword(0, g * 4 + kb));
+            bop[kb] = *reinterpret_cast<const v4i1*>(w1q + w1q_chunk_dword(0, kb * 4 + g));
         const float sb = s1[0];
 
         // every register slot's MFMAs first (slots past the slice hold zero codes), then the LDS
