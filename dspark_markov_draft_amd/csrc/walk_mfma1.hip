@@ -73,18 +73,19 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
             qa[tw][kb] = have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + kb * 64 + g * 16)
                               : (v4i1){0, 0, 0, 0};
     }
-    // LDS slots (zero codes past the slice: their MFMAs give zeros)
+    // LDS slots, copied by DMA straight from memory (a K-block is the 64 consecutive 16-byte lane
+    // slots one global_load_lds writes). Rows past the slice copy the slice's first row: their
+    // products are never finished.
     for (int tw = MFMA1_TILES; tw < nslots; ++tw) {
         const int tl = tw * WALK_WAVES + wave;
-        const int row = row0 + tl * 16 + c;
-        const bool have = tl < ntiles && row < vend;
-        v4i1* dst = reinterpret_cast<v4i1*>(
-            lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES);
+        int row = row0 + tl * 16 + c;
+        if (!(tl < ntiles && row < vend)) row = row0;
+        unsigned char* dst = lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            dst[kb * WAVE + lane] =
-                have ? *reinterpret_cast<const v4i1*>(p.q + (int64_t)row * RANK + kb * 64 + g * 16)
-                     : (v4i1){0, 0, 0, 0};
+            __builtin_amdgcn_global_load_lds(
+                (__attribute__((address_space(1))) void*)(p.q + (int64_t)row * RANK + kb * 64 + g * 16),
+                (__attribute__((address_space(3))) void*)(dst + kb * WAVE * 16), 16, 0, 0);
     }
     // the rows this lane finishes: group gi takes tile slot 4 gi + ts, row 4 g + ri of it
     int vrow[M1_GROUPS];
@@ -106,7 +107,8 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         for (int gi = 0; gi < M1_GROUPS; ++gi) pf[gi] = vok[gi] ? br[vrow[gi]] : 0.0f;
     };
     load_base(0);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's tile copies have landed, and every wave's
+    __syncthreads();                  // after the barrier
     stamp<TIMED>(p, 1);
 
     uint64_t seed = 0;
