@@ -44,7 +44,8 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         lds_units = units - reg_units;
         reg_rows = rpw < reg_units * WALK_WAVES * 16 ? rpw : reg_units * WALK_WAVES * 16;
         lds_rows = rpw - reg_rows;
-        lds_bytes = lds_units * WALK_WAVES * MFMA_TILE_LDS + DOT4_FIXED_LDS;
+        // (the variant with LDS slots always has MFMA1_LDS_TILES of them)
+        lds_bytes = (lds_units ? MFMA1_LDS_TILES : 0) * WALK_WAVES * MFMA_TILE_LDS + DOT4_FIXED_LDS;
     } else if (path == DSPARK_PATH_DOT4) {
         units = (rpw + WALK_THREADS - 1) / WALK_THREADS;            // row sets
         reg_units = units < DOT4_REG_SETS ? units : DOT4_REG_SETS;

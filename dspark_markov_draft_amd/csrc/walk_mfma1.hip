@@ -51,12 +51,14 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     const int nrows = min(p.rows_per_wg, p.V - row0);
     const int vend = row0 + nrows;
     const int ntiles = (nrows + 15) / 16;
-    const int ntl = LDS ? p.lds_units : 0;        // LDS tile slots per wave
-    const int nslots = MFMA1_TILES + ntl;         // tile slots per wave
-    const int ngroups = (nslots + 3) / 4;         // uniform
+    // tile slots per wave holding rows; the LDS variant multiplies all its MFMA1_LDS_TILES LDS
+    // slots (branch-free), those past nslots hold copies of the slice's first row, not finished
+    const int ntl = LDS ? p.lds_units : 0;
+    const int nslots = MFMA1_TILES + ntl;
 
     unsigned char* lds_tiles = smem;
-    uint32_t* w1q = reinterpret_cast<uint32_t*>(smem + (size_t)ntl * WALK_WAVES * M1_TILE_LDS_BYTES);
+    uint32_t* w1q = reinterpret_cast<uint32_t*>(
+        smem + (size_t)(LDS ? MFMA1_LDS_TILES : 0) * WALK_WAVES * M1_TILE_LDS_BYTES);
     float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
     int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
@@ -76,10 +78,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     // LDS slots, copied by DMA straight from memory (a K-block is the 64 consecutive 16-byte lane
     // slots one global_load_lds writes). Rows past the slice copy the slice's first row: their
     // products are never finished.
-    for (int tw = MFMA1_TILES; tw < nslots; ++tw) {
+    for (int tw = MFMA1_TILES; tw < M1_SLOTS; ++tw) {
         const int tl = tw * WALK_WAVES + wave;
         int row = row0 + tl * 16 + c;
-        if (!(tl < ntiles && row < vend)) row = row0;
+        if (!(tw < nslots && tl < ntiles && row < vend)) row = row0;
         unsigned char* dst = lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -152,21 +154,18 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
 #pragma unroll
         for (int tw = MFMA1_TILES; tw < M1_SLOTS; ++tw) {
             acc[tw] = (v4i1){0, 0, 0, 0};
-            if (tw < nslots) {
-                const v4i1* src = reinterpret_cast<const v4i1*>(
-                    lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES);
+            const v4i1* src = reinterpret_cast<const v4i1*>(
+                lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES);
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    acc[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane], bop[kb],
-                                                                    acc[tw], 0, 0, 0);
-            }
+            for (int kb = 0; kb < 4; ++kb)
+                acc[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane], bop[kb],
+                                                                acc[tw], 0, 0, 0);
         }
         const int64_t orow = (int64_t)t * p.V;
         const uint64_t P = pos0 + (uint64_t)t;
         RunningArgmax run;
 #pragma unroll
         for (int gi = 0; gi < M1_GROUPS; ++gi) {
-            if (LDS && gi >= ngroups) break;
             // this lane's row of tile slot 4 gi + ts: component ri of that slot's result
             int a[4];
 #pragma unroll
