@@ -123,12 +123,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     }
 
     for (int t = 0; t < p.T; ++t) {
-        // wave 0 runs the combine, whose polls would wait behind any load it has in flight
-        // (vector memory returns in issue order): its base logits of this step are issued here,
-        // behind the W1 row loads, instead of before the previous combine
-        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {
-            if (wave == 0 && t > 0) load_base(t);
-        });
+        // every wave's base logits of this step were issued before the previous combine: the
+        // first poll round waits behind them (vector memory returns in issue order), which costs
+        // little, as the combine waits for the last workgroup anyway, while the W1 row of wave 0's
+        // gather has nothing queued ahead of it
+        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {});
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
@@ -200,8 +199,8 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
 
-        // the next step's base logits load while the combine waits (wave 0: see above)
-        if (t + 1 < p.T && wave != 0) load_base(t + 1);
+        // the next step's base logits load while the combine waits
+        if (t + 1 < p.T) load_base(t + 1);
         if (wave == 0) {
             uint64_t k = 0;
             if (lane == 0) {
