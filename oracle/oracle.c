@@ -53,7 +53,7 @@
 /* Quantisation (PR #62958, Overview: int8 W2 with one fp32 scale per row).                  */
 /* Reading: symmetric absmax, s = absmax/127 in IEEE fp32, q = rint(w/s) (half to even) in    */
 /* [-127, 127]. Zero row: s = 0, q = 0. Any non-finite element: error (PR #62958, Details:    */
-/* unsupported input fails with a clear error).                                              */
+/* inputs the kernel does not handle are rejected with an explicit error, not computed).     */
 /* ---------------------------------------------------------------------------------------- */
 int oracle_quantize_w2(const float* w2, int64_t V, int64_t R, int8_t* q, float* s) {
     if (!w2 || !q || !s || V < 0 || R <= 0) return ORACLE_ERR_ARG;
