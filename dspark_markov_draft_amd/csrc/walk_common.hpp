@@ -118,13 +118,25 @@ __device__ __forceinline__ float w1_code_scale(float absmax) {
 
 // Four int8 codes rint(w * inv) (round half to even) in one dword. With inv = 127 / absmax of
 // the row, |w * inv| <= 127 * (1 + 2^-23)^2 < 127.5, so every code lies in [-127, 127] without
-// a clamp.
+// a clamp. The rounding: for |x| < 2^22, the fp32 sum x + 1.5 * 2^23 is rounded to an integer
+// (its unit in the last place is 1) half to even, and as 1.5 * 2^23 is even that integer is
+// 1.5 * 2^23 + rint(x); its bit pattern is 0x4B400000 + rint(x), whose low byte is the code in
+// two's complement. Three byte permutes pack the four low bytes. The product is rounded before
+// the sum: the empty asm makes it a value of its own, so the compiler cannot contract the two
+// into one fused multiply-add, which would round w * inv + 1.5 * 2^23 once and could differ
+// from rint of the rounded product.
+__device__ __forceinline__ uint32_t rne_code_bits(float w, float inv) {
+    float x = w * inv;
+    asm volatile("" : "+v"(x));
+    return __float_as_uint(x + 12582912.0f);   // + 1.5 * 2^23
+}
 __device__ __forceinline__ uint32_t pack_codes(const float4 w, float inv) {
-    const uint32_t c0 = (uint32_t)(int32_t)rintf(w.x * inv) & 0xFFu;
-    const uint32_t c1 = (uint32_t)(int32_t)rintf(w.y * inv) & 0xFFu;
-    const uint32_t c2 = (uint32_t)(int32_t)rintf(w.z * inv) & 0xFFu;
-    const uint32_t c3 = (uint32_t)(int32_t)rintf(w.w * inv);
-    return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    const uint32_t b0 = rne_code_bits(w.x, inv), b1 = rne_code_bits(w.y, inv);
+    const uint32_t b2 = rne_code_bits(w.z, inv), b3 = rne_code_bits(w.w, inv);
+    // v_perm_b32(hi, lo, sel): byte i of the result is byte sel_i of {hi, lo} (lo = 0..3)
+    const uint32_t p01 = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);   // b0.byte0, b1.byte0
+    const uint32_t p23 = __builtin_amdgcn_perm(b3, b2, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
 // maximum of non-negative floats over each 16-lane row of the wave (all 16 lanes get it)
