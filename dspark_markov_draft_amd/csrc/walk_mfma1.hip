@@ -63,6 +63,19 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
     int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
 
+    // ---- step 0's W1 codes, by the last wave before its share of the fill ----------------
+    // The start token is known at launch, so its row is gathered while the other waves' fill
+    // streams in (an out-of-range token reads row 0, as load_start_tokens() makes it); this
+    // wave's fill then queues behind two short memory round trips instead of the step waiting
+    // for a gather after the whole fill.
+    if (wave == WALK_WAVES - 1) {
+        int s0 = p.start[0];
+        if (s0 < 0 || s0 >= p.V) s0 = 0;
+        float sb;
+        const uint32_t codes = w1_row_quantise(load4_as_f32<W1T>(p.w1, (int64_t)s0 * RANK + lane * 4), sb);
+        w1q[w1q_chunk_dword(0, lane >> 2) + (lane & 3)] = codes;
+        if (lane == 0) s1[0] = sb;
+    }
     // ---- fill: this wave's tiles as A operands; zero past the slice -----------------------
     v4i1 qa[MFMA1_TILES][4];
 #pragma unroll
@@ -127,8 +140,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         // first poll round waits behind them (vector memory returns in issue order), which costs
         // little, as the combine waits for the last workgroup anyway, while the W1 row of wave 0's
         // gather has nothing queued ahead of it
-        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {});
-        __syncthreads();
+        if (t > 0) {
+            gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {});
+            __syncthreads();
+        }
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
         float cur[M1_GROUPS];
