@@ -15,12 +15,13 @@ constexpr size_t WS_ERR = 0;          // u32 error word (DSPARK_ERR_TIMEOUT / IN
 constexpr int RESULT_REPLICAS = 8;    // copies of the result words, read by disjoint workgroups
 constexpr size_t WS_RESULT = 4096;    // u64 [8 copies][16 steps][64 requests]: each step's winner
 constexpr size_t WS_SLOTS = WS_RESULT + (size_t)RESULT_REPLICAS * 16 * 64 * 8;  // then
-                                      // u64 [T][256 workgroups][slot stride]: per-workgroup keys
+                                      // u64 [T][256 workgroups x slot stride]: workgroup keys
 constexpr size_t WS_TOPK = WS_SLOTS;  // top-k calls use the same region for candidate lists
 constexpr size_t WS_ALIGN = 256;
 constexpr int MAX_WORKGROUPS = 256;
 
-// keys per workgroup slot: whole 128-byte lines, so no two workgroups write the same line
+// the key region of one step holds 256 x slot_stride(bs) keys, laid out request-major
+// ([request][workgroup]; for one or two requests as replicas of that)
 inline int slot_stride(int64_t bs) { return (int)((bs + 15) / 16 * 16); }
 inline size_t dense_slot_bytes(int64_t bs, int64_t T) {
     return (size_t)T * MAX_WORKGROUPS * (size_t)slot_stride(bs) * 8;

@@ -284,7 +284,8 @@ __device__ __forceinline__ void load_start_tokens(const WalkParams& p, int32_t* 
 }
 
 // Grid-wide combine of step t, run by wave 0 (all 64 lanes). `key` (lanes < bs) is this
-// workgroup's best key for request `lane`. Each workgroup stores its keys into its own slot;
+// workgroup's best key for request `lane`. Each workgroup stores its key of request b into slot
+// [b][workgroup] of the step (request-major: a reducer's poll round reads whole cache lines);
 // the workgroup owning request b (b % num workgroups) waits for all slots of b, takes their
 // maximum, writes the token and publishes the winning key in result[t][b] (not for the last
 // step) in RESULT_REPLICAS copies on separate cache lines, clears the slots it read and its
@@ -429,19 +430,21 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
     const int nwg = gridDim.x;
     const int wg = blockIdx.x;
     uint64_t* step_slots = p.slots + (size_t)t * nwg * p.stride;
-    if (lane < p.bs) st_dev(step_slots + (size_t)wg * p.stride + lane, key);
+    // request-major: the keys of request b of all workgroups side by side, so its reducer's poll
+    // round reads nwg / 16 whole cache lines
+    if (lane < p.bs) st_dev(step_slots + (size_t)lane * nwg + wg, key);
     stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 2);
 
     constexpr int NL = MAX_WORKGROUPS / WAVE;  // slot loads per lane per round
     for (int b = wg; b < p.bs; b += nwg) {
-        const uint64_t* col = step_slots + b;
+        const uint64_t* col = step_slots + (size_t)b * nwg;
         // unconditional loads (lanes past the grid re-read the last slot), so that the compiler
         // can count the loads in flight
         auto issue = [&](uint64_t (&v)[NL]) {
 #pragma unroll
             for (int k = 0; k < NL; ++k) {
                 const int w = min(lane + k * WAVE, nwg - 1);
-                v[k] = ld_dev(col + (size_t)w * p.stride);
+                v[k] = ld_dev(col + w);
             }
         };
         auto complete = [&](const uint64_t (&v)[NL], uint64_t& best) {
@@ -483,7 +486,7 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
             const int w = lane + k * WAVE;
-            if (w < nwg) st_dev(step_slots + (size_t)w * p.stride + b, 0);
+            if (w < nwg) st_dev(step_slots + (size_t)b * nwg + w, 0);
         }
     }
     stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 3);
