@@ -12,7 +12,7 @@ namespace dspark {
 // Workspace layout of a walk call (bytes from the start of the caller's workspace). A walk
 // leaves every word it uses at zero when it exits, so the caller zeroes the workspace once.
 constexpr size_t WS_ERR = 0;          // u32 error word (DSPARK_ERR_TIMEOUT / INVALID_ARG)
-constexpr int RESULT_REPLICAS = 8;    // copies of the result words, read by disjoint workgroups
+constexpr int RESULT_REPLICAS = 16;   // copies of the result words, read by disjoint workgroups
 constexpr size_t WS_RESULT = 4096;    // u64 [8 copies][16 steps][64 requests]: each step's winner
 constexpr size_t WS_SLOTS = WS_RESULT + (size_t)RESULT_REPLICAS * 16 * 64 * 8;  // then
                                       // u64 [T][256 workgroups x slot stride]: workgroup keys

@@ -39,10 +39,9 @@ def test_status_strings():
 
 
 def test_workspace_bytes():
-    # 8 copies of the result words + per-workgroup slots of whole 128-byte lines (up to 256
-    # workgroups)
+    # 16 copies of the result words + a key region of 256 workgroups x 16 keys per step
     one = B.dspark_walk_workspace_bytes(1, 1, 10, 0)
-    assert one >= 4096 + 8 * 16 * 64 * 8 + 256 * 128 and one % 256 == 0
+    assert one >= 4096 + 16 * 16 * 64 * 8 + 256 * 128 and one % 256 == 0
     big = B.dspark_walk_workspace_bytes(64, 16, 270336, 0)
     assert big >= 16 * 256 * 64 * 8 and big % 256 == 0
     assert B.dspark_walk_workspace_bytes(64, 16, 4096, 0) == big      # independent of V
