@@ -242,6 +242,77 @@ def test_special_values_both_paths(mode, path):
     assert rep.ok, rep.summary()
 
 
+def _zero_w2_problem(base_rows, start=0):
+    V = base_rows.shape[-1]
+    w = torch.zeros(V, 256, dtype=torch.bfloat16)
+    base = np.asarray(base_rows, np.float32)[None]
+    return Problem(w, w.clone(), base, np.array([start], np.int32))
+
+
+@pytest.mark.parametrize("path", [B.PATH_DOT4, B.PATH_MFMA1])
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_special_values_one_request(mode, path):
+    """One request (the MFMA1 kernel's shape): W2 = 0, so each step's logits are its base row
+    exactly and planted values reach the grid-wide argmax as they are. V = 39990 gives 157
+    workgroups of 256 rows, the last holding 54 (three full 16-row tiles and a partial one); the
+    specials sit in the first, middle and last workgroups."""
+    V = 39990
+    rng = np.random.default_rng(78)
+    rows, want = [], []
+    r = rng.normal(0.0, 3.0, V).astype(np.float32); r[[100, 20000, V - 1]] = np.nan
+    rows.append(r); want.append(100)
+    rows.append(np.full(V, -np.inf, np.float32)); want.append(0)
+    r = rng.normal(0.0, 3.0, V).astype(np.float32); r[25050], r[25051] = np.inf, -np.inf
+    rows.append(r); want.append(25050)
+    rows.append(np.where(rng.random(V) < 0.5, 0.0, -0.0).astype(np.float32)); want.append(0)
+    r = rng.normal(0.0, 3.0, V).astype(np.float32); r[30007], r[30008], r[30003] = np.nan, np.inf, np.inf
+    rows.append(r); want.append(30007)          # a NaN outranks the +inf before it
+    r = np.full(V, -np.inf, np.float32); r[V - 1] = np.nan
+    rows.append(r); want.append(V - 1)
+    r = rng.normal(0.0, 3.0, V).astype(np.float32); r[V - 10:] = np.inf
+    rows.append(r); want.append(V - 10)
+    base = np.stack(rows)
+    for t, row in enumerate(rows):
+        assert want[t] == int(torch.argmax(torch.from_numpy(row)))
+    p = _zero_w2_problem(base, start=5)
+    assert B.dspark_walk_plan_query(1, len(rows), V)["path"] == B.PATH_MFMA1
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
+    if mode == "greedy":
+        tok, logits = p.greedy()
+        assert np.array_equal(logits[0], base, equal_nan=True)
+        assert list(tok[0]) == want
+    else:
+        tok, lb = p.sample()
+        rep = p.check_sample(tok, lb)
+        assert rep.ok, rep.summary()
+        assert tok[0, 0] == 100 and tok[0, 1] == 0 and tok[0, 5] == V - 1
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_one_request_grid_invariant(mode):
+    """One request on MFMA1 at several grid sizes: 27 workgroups of 1112 rows (640 in register
+    tiles, 472 in LDS tiles), a cap of 117 (116 workgroups of 260 rows, a partial tile each)
+    and the device's own grid. Every grid gives the same bits, and the workspace ends zeroed."""
+    V = 30000
+    p = random_problem(V, 5, 1, seed=12)
+    qs = p.quantize()
+    ws = dm.new_workspace(1, 5, V)
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, B.PATH_MFMA1)
+    ref = None
+    for cap in (27, 117, 0):
+        dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+        assert B.dspark_walk_plan_query(1, 5, V)["path"] == B.PATH_MFMA1, cap
+        out = p.greedy(qs=qs, ws=ws) if mode == "greedy" else p.sample(qs=qs, ws=ws)
+        bits = (out[0], out[1].view(np.uint32 if mode == "greedy" else np.uint16))
+        if ref is None:
+            ref = bits
+            rep = p.check_greedy(*out) if mode == "greedy" else p.check_sample(*out)
+            assert rep.ok, rep.summary()
+        else:
+            assert np.array_equal(bits[0], ref[0]) and np.array_equal(bits[1], ref[1]), cap
+        assert int(ws.count_nonzero()) == 0
+
+
 def test_full_size_without_out_logits_same_tokens():
     """The timed configuration (greedy, no logits output) emits the same tokens."""
     inp = make_inputs(CASES["v151936_t7_bs1"])
@@ -255,13 +326,6 @@ def test_full_size_without_out_logits_same_tokens():
 # ----------------------------------------------------------------------------------------------
 # torch.argmax order through the grid-wide combine (ties and NaN in different workgroups)
 # ----------------------------------------------------------------------------------------------
-def _zero_w2_problem(base_rows, start=0):
-    V = base_rows.shape[-1]
-    w = torch.zeros(V, 256, dtype=torch.bfloat16)
-    base = np.asarray(base_rows, np.float32)[None]
-    return Problem(w, w.clone(), base, np.array([start], np.int32))
-
-
 @pytest.mark.parametrize("mode", ["greedy", "sample"])
 def test_argmax_order_across_workgroups(mode):
     V = 151936      # 255 workgroups of 596 rows
