@@ -388,6 +388,16 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         const int g = s * SEL_THREADS + tid;
         stash[s] = load_group_clamped<VEC>(p, x, g, ngroups);
     }
+    // and the first batch of the main pass, so that it is in flight while the chunk's histogram
+    // and bound are computed (every workgroup starts at once, so HBM would idle meanwhile)
+    constexpr int BATCH = MAIN_UNROLL * SEL_THREADS;
+    int g0 = STASH_GROUPS * SEL_THREADS;
+    float4 cur[MAIN_UNROLL];
+#pragma unroll
+    for (int u = 0; u < MAIN_UNROLL; ++u) {
+        const int g = g0 + u * SEL_THREADS + tid;
+        cur[u] = load_group_clamped<VEC>(p, x, g, ngroups);
+    }
     __syncthreads();
     // its top-12-bit histogram; -inf over the output
 #pragma unroll
@@ -441,14 +451,6 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         offer(stash[s], g, g < ngroups);
     }
     // the rest of the row, one batch in flight while the previous one is examined
-    constexpr int BATCH = MAIN_UNROLL * SEL_THREADS;
-    int g0 = STASH_GROUPS * SEL_THREADS;
-    float4 cur[MAIN_UNROLL];
-#pragma unroll
-    for (int u = 0; u < MAIN_UNROLL; ++u) {
-        const int g = g0 + u * SEL_THREADS + tid;
-        cur[u] = load_group_clamped<VEC>(p, x, g, ngroups);
-    }
     for (; g0 < ngroups; g0 += BATCH) {
         float4 nxt[MAIN_UNROLL];
 #pragma unroll
@@ -497,13 +499,22 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     constexpr uint32_t SMALL_CAP = 1024;
     uint64_t* small = reinterpret_cast<uint64_t*>(hist);
     uint32_t* hist2 = hist + 2 * SMALL_CAP;          // 1024 bins after the small list
+    // This wave's region (n_mine <= REGION_CAP here: no overflow) is read into registers once,
+    // all reads issued together, for both passes below.
+    constexpr int MINE_REGS = (REGION_CAP + WAVE - 1) / WAVE;
     const uint64_t* mine = buf + wave * REGION_CAP;
     const uint32_t n_mine = cnt[wave];
+    uint64_t mk[MINE_REGS];
+#pragma unroll
+    for (int i = 0; i < MINE_REGS; ++i) {
+        const uint32_t e = (uint32_t)(i * WAVE + lane);
+        mk[i] = e < n_mine ? mine[e] : 0ull;
+    }
     uint32_t n_hi = 0, n_eq = 0;
-    for (uint32_t e0 = 0; e0 < n_mine; e0 += WAVE) {
-        const uint32_t e = e0 + lane;
-        const uint64_t ck = e < n_mine ? mine[e] : 0ull;
-        const uint32_t bin = (uint32_t)(ck >> L1_SHIFT);
+#pragma unroll
+    for (int i = 0; i < MINE_REGS; ++i) {
+        const uint32_t e = (uint32_t)(i * WAVE + lane);
+        const uint32_t bin = (uint32_t)(mk[i] >> L1_SHIFT);
         n_hi += (uint32_t)__popcll(__ballot(e < n_mine && bin > d1));
         n_eq += (uint32_t)__popcll(__ballot(e < n_mine && bin == d1));
     }
@@ -521,9 +532,10 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         off_eq += w < wave ? wc[SEL_WAVES + w] : 0u;
         m += wc[SEL_WAVES + w];
     }
-    for (uint32_t e0 = 0; e0 < n_mine; e0 += WAVE) {
-        const uint32_t e = e0 + lane;
-        const uint64_t ck = e < n_mine ? mine[e] : 0ull;
+#pragma unroll
+    for (int i = 0; i < MINE_REGS; ++i) {
+        const uint32_t e = (uint32_t)(i * WAVE + lane);
+        const uint64_t ck = mk[i];
         const uint32_t bin = (uint32_t)(ck >> L1_SHIFT);
         const bool hi = e < n_mine && bin > d1, eq = e < n_mine && bin == d1;
         const uint64_t mh = __ballot(hi), me = __ballot(eq);
@@ -642,10 +654,16 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         const int64_t row = (int64_t)b * p.T + t;
         const float4 w = load4_as_f32<W1T>(p.w1, (int64_t)prev * RANK + lane * 4);
         if constexpr (!MULTI) {
+            // Vector loads complete in issue order, so the order of issue is chosen: the W1 row
+            // first (its wait then covers nothing else), the index two steps ahead next (the
+            // next step waits for it before its rows, and then waits for nothing issued after
+            // it), the next step's rows last. The scheduling barrier keeps the rows there; left to
+            // itself the scheduler sank the rows below the wait for the W1 row.
+            next_idx = cand_index(min(t + 2, p.T - 1), wave * WAVE + own);
             // unconditional (past the last step they re-read the last step's rows), so that
             // no branch keeps the compiler from counting the loads in flight
             load_block(min(t + 1, p.T - 1), fill_idx, fill);
-            next_idx = cand_index(min(t + 2, p.T - 1), wave * WAVE + own);
+            __builtin_amdgcn_sched_barrier(0);
         }
         float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
         a = wave_max_nonneg_f32(a);
