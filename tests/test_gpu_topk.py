@@ -35,6 +35,7 @@ SMALL = [  # V, T, bs, dtype, k
     (1, 2, 1, torch.bfloat16, 1),
     (9000, 2, 64, torch.bfloat16, 1),
     (12345, 3, 7, torch.bfloat16, 777),
+    (6000, 1, 4, torch.bfloat16, 300),      # a single step
 ]
 
 

@@ -116,6 +116,8 @@ SMALL = [  # V, T, bs, dtype, grid cap (0 = one workgroup per CU)
     (12480, 2, 24, torch.float32, 20),      # MFMA, static LDS: 624-row slices (the largest)
     (20000, 3, 1, torch.bfloat16, 20),      # one request, 1000-row slices: LDS tiles (MFMA1)
     (9000, 2, 1, torch.float16, 8),         # one request, 1128-row slices: 8 LDS tiles, ragged
+    (30000, 1, 1, torch.bfloat16, 0),       # a single step: the first step is also the last
+    (6000, 1, 20, torch.float32, 0),        # a single step, batched
 ]
 
 
@@ -504,6 +506,26 @@ def test_small_batch_combine(V, T, bs, cap, mode):
         assert rep.ok, rep.summary()
         assert dm.dspark_workspace_status(ws) == 0
         assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_single_step_leaves_workspace_zeroed(path):
+    """T = 1: the first step is also the last one, whose combine clears what it used. Greedy
+    and sample in turn on one workspace, at one request and at 20; the workspace ends zeroed
+    after every call, and the tokens match the oracle's."""
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
+    ws = dm.new_workspace(20, 1, 30000)
+    for bs, seed in ((1, 31), (20, 32)):
+        p = random_problem(30000, 1, bs, seed=seed)
+        qs = p.quantize()
+        tok, logits = p.greedy(qs=qs, ws=ws)
+        assert int(ws.count_nonzero()) == 0
+        rep = p.check_greedy(tok, logits)
+        assert rep.ok, rep.summary()
+        stok, lb = p.sample(qs=qs, ws=ws)
+        assert int(ws.count_nonzero()) == 0
+        rep = p.check_sample(stok, lb)
+        assert rep.ok, rep.summary()
 
 
 def test_workspace_shared_across_batch_sizes():
