@@ -423,27 +423,44 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     for (int i = tid; i < L1_BINS; i += SEL_THREADS) hist[i] = 0;  // now: the offered keys
     __syncthreads();
 
-    // every key in a bin >= bin_lo into this wave's LDS region (wave-uniform count, no atomics
-    // for the position) and into the histogram
+    // Every key in a bin >= bin_lo goes into this wave's LDS region (wave-uniform count, no
+    // atomics for the position) and into the histogram. Membership is one float compare per
+    // element: the keys order values as IEEE comparison does (-0 with +0), with NaN above +inf,
+    // so "key >= the bin's lowest key B" is "not (x < t)" for t the value whose key is B (NaN
+    // passes, as it should). The bins below -inf's key hold no value (t = -inf admits all).
+    // Those above +inf's hold only NaN: t = +inf then also admits +inf, a key below the bound.
+    // Extra keys below the bound are harmless: at least k keys reach it, so the k-th largest
+    // offered key, and every key the select emits, is one of those.
+    const uint32_t kB = bin_lo << (32 - L1_BITS);
+    const float t_lo = kB <= ORDER_KEY_NEG_INF ? -INFINITY
+                       : kB > 0xFF800000u      ? INFINITY
+                       : kB >= 0x80000000u     ? __uint_as_float(kB & 0x7FFFFFFFu)
+                                               : __uint_as_float(~kB);
     uint64_t* region = buf + wave * REGION_CAP;
     uint32_t n_region = 0;
+    // A group's members are appended in one pass: each lane counts its members c (0..4), its
+    // position is the members of the lanes below it, read from three ballots of c's bits.
     auto offer = [&](const float4 a, int g, bool present) {
         const float e[4] = {a.x, a.y, a.z, a.w};
+        bool in[4];
+        uint32_t c = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int i = 4 * g + u;
-            const uint32_t bin = top_bin(e[u]);
-            const bool in = present && (VEC || i < p.V) && bin >= bin_lo;
-            const uint64_t m = __ballot(in);
-            if (m) {
-                const uint32_t pos = n_region + lanes_below(m);
-                if (in) {
-                    atomicAdd(&hist[bin], 1u);
-                    if (pos < (uint32_t)REGION_CAP) region[pos] = composite_key(e[u], (uint32_t)i);
-                }
-                n_region += (uint32_t)__popcll(m);
+            in[u] = present && (VEC || 4 * g + u < p.V) && !(e[u] < t_lo);
+            c += in[u] ? 1u : 0u;
+        }
+        if (__ballot(c != 0) == 0) return;
+        const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+        uint32_t pos = n_region + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (in[u]) {
+                atomicAdd(&hist[top_bin(e[u])], 1u);
+                if (pos < (uint32_t)REGION_CAP) region[pos] = composite_key(e[u], (uint32_t)(4 * g + u));
+                ++pos;
             }
         }
+        n_region += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
     };
 #pragma unroll
     for (int s = 0; s < STASH_GROUPS; ++s) {
