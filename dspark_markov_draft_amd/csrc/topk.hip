@@ -412,9 +412,19 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         }
     }
     __syncthreads();
+    // The bound: the bin of the chunk's kb-th largest key. When the chunk is the whole row, kb
+    // = k. Otherwise kb = ceil(2 k chunk / V), twice the chunk's expected share of the row's top
+    // k (at most k): on a row without order about 2k keys then reach the bound, not k V / chunk,
+    // and fewer of the scan's groups hold a key that does. A row where fewer than k keys reach
+    // it (the chunk holding more than its share of the top) takes the exact fallback.
+    uint32_t kb = (uint32_t)p.k;
+    if (p.V > STASH_ELEMS) {
+        const int64_t e = (2 * (int64_t)p.k * STASH_ELEMS + p.V - 1) / p.V;
+        kb = (uint32_t)(e < 1 ? 1 : e < p.k ? e : p.k);
+    }
     if (tid < WAVE) {
         uint32_t d, above;
-        select_digit<L1_BINS>(hist, (uint32_t)p.k, lane, d, above);
+        select_digit<L1_BINS>(hist, kb, lane, d, above);
         if (lane == 0) sh[0] = d;
     }
     __syncthreads();
@@ -488,9 +498,14 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     __syncthreads();
     tk_stamp<TIMED>(p.stamps, row * 8 + 2);
     bool overflow = false;
+    uint32_t offered = 0;
 #pragma unroll
-    for (int r = 0; r < SEL_WAVES; ++r) overflow = overflow || cnt[r] > (uint32_t)REGION_CAP;
-    if (overflow) {
+    for (int r = 0; r < SEL_WAVES; ++r) {
+        overflow = overflow || cnt[r] > (uint32_t)REGION_CAP;
+        offered += cnt[r];
+    }
+    // too many keys for the buffer, or too few reached the bound to hold the row's top k
+    if (overflow || offered < (uint32_t)p.k) {
         select_fallback<VEC>(p, x, out, buf, hist, sh, cnt, tid, lane);
         tk_stamp<TIMED>(p.stamps, row * 8 + 4);
         return;

@@ -144,6 +144,32 @@ def test_topk_select_kth_bin_sizes(n_bin, k):
         assert np.array_equal(np.flatnonzero(np.isfinite(dense[0, t])), want), t
 
 
+@pytest.mark.parametrize("k", [100, 512])
+def test_topk_bound_from_ordered_rows(k):
+    """The select bounds each row by a key of its first 18432-element chunk chosen to let about
+    2k keys through on an unordered row. Rows in descending order put the whole top of the row in
+    that chunk, so fewer than k keys reach the bound; rows in ascending order let nearly all
+    through. Both take the exact fallback; a random row takes the main path. The candidate set
+    is the k largest (lower index first among equals) in every case."""
+    V, T = 60000, 3
+    rng = np.random.default_rng(k)
+    base = np.zeros((1, T, V), np.float32)
+    base[0, 0] = -np.arange(V, dtype=np.float32) * 1e-3        # descending
+    base[0, 1] = np.arange(V, dtype=np.float32) * 1e-3         # ascending
+    base[0, 2] = rng.normal(0.0, 3.0, V).astype(np.float32)
+    p = _zero_w_problem(base)
+    for mode in ("greedy", "sample"):
+        tok, dense = p.topk(k, sample=mode == "sample")
+        rep = p.check_topk(k, tok, dense, sample=mode == "sample")
+        assert rep.ok, rep.summary()
+        # greedy: fp32 logits; sample: bf16 bits, -inf being 0xFF80
+        kept = np.isfinite(dense[0]) if mode == "greedy" else dense[0] != 0xFF80
+        for t in range(T):
+            row = base[0, t]
+            want = np.sort(np.lexsort((np.arange(V), -row))[:k])
+            assert np.array_equal(np.flatnonzero(kept[t]), want), (mode, t)
+
+
 @pytest.mark.parametrize("mode", ["greedy", "sample"])
 def test_topk_all_candidates_neg_inf_gives_token_zero(mode):
     """A step whose candidates are all -inf: the dense row is -inf everywhere, and torch.argmax
