@@ -146,7 +146,7 @@ def test_topk_select_kth_bin_sizes(n_bin, k):
 
 @pytest.mark.parametrize("k", [100, 512])
 def test_topk_bound_from_ordered_rows(k):
-    """The select bounds each row by a key of its first 18432-element chunk chosen to let about
+    """The select bounds each row by a key of its first 18432-element chunk, chosen to let about
     2k keys through on an unordered row. Rows in descending order put the whole top of the row in
     that chunk, so fewer than k keys reach the bound; rows in ascending order let nearly all
     through. Both take the exact fallback; a random row takes the main path. The candidate set
