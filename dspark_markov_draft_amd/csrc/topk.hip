@@ -682,6 +682,20 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
     // for it), the candidates' logits and keys, then one barrier for the step's argmax. The
     // next step's rows load into `fill` (from `fill_idx`, loaded a step earlier) while the W1
     // row is in flight, and the index two steps ahead into `next_idx`.
+    // When sampling, the candidates' bf16 logits go to the dense output one step late. Stores
+    // share the in-order count of vector memory operations with loads, so a store issued at the
+    // end of a step would hold the next step's wait for its W1 row until the store completed.
+    // Issued after that W1 load instead, it has the whole next step to complete. (One candidate
+    // per lane; a lane with none holds pend_off < 0.) The greedy walk stores only when its fp32
+    // logits are asked for, and stores at once: the pending state cost its timed configuration,
+    // which stores nothing, more than it saved.
+    constexpr bool DEFER = SAMPLE && !MULTI;
+    int64_t pend_off = -1;
+    uint32_t pend_val = 0;
+    auto flush_pending = [&]() {
+        if constexpr (DEFER)
+            if (pend_off >= 0) p.out_bf16[pend_off] = (uint16_t)pend_val;
+    };
     auto step = [&](int t, CandBlock& use, CandBlock& fill, uint32_t fill_idx, uint32_t& next_idx) {
         const int64_t row = (int64_t)b * p.T + t;
         const float4 w = load4_as_f32<W1T>(p.w1, (int64_t)prev * RANK + lane * 4);
@@ -696,6 +710,7 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
             // no branch keeps the compiler from counting the loads in flight
             load_block(min(t + 1, p.T - 1), fill_idx, fill);
             __builtin_amdgcn_sched_barrier(0);
+            flush_pending();   // the previous step's logit, behind this step's loads
         }
         float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
         a = wave_max_nonneg_f32(a);
@@ -718,12 +733,18 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
             }
             const float l = walk_logit(blk.base, blk.s, sb, acc);
             uint64_t key;
+            const int64_t off = row * p.V + blk.v;
             if constexpr (!SAMPLE) {
-                if (has && p.out_f32) p.out_f32[row * p.V + blk.v] = l;
+                if (has && p.out_f32) p.out_f32[off] = l;
                 key = argmax_key(l, blk.v);
             } else {
                 const uint32_t h = bf16_bits(l);
-                if (has) p.out_bf16[row * p.V + blk.v] = (uint16_t)h;
+                if constexpr (DEFER) {
+                    pend_off = has ? off : -1;
+                    pend_val = h;
+                } else {
+                    if (has) p.out_bf16[off] = (uint16_t)h;
+                }
                 const float xs = bf16_value(h) * rtemp;
                 const float g = gumbel_from_word(noise_word(seed, P0 + (uint64_t)t, blk.v));
                 key = argmax_key(xs + g, blk.v);
@@ -763,6 +784,7 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         step(t, ra, rb, ib, ia);
         if (t + 1 < p.T) step(t + 1, rb, ra, ia, ib);
     }
+    flush_pending();   // the last step's logit (sampling)
     // every candidate list of this request has been read before the last barrier: clear them,
     // so that the workspace is all zero again for the dense walk
     __syncthreads();
