@@ -250,8 +250,8 @@ def main():
         print(sources_digest(args.print_digest))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
-              "walk's sharding across GPUs is a design, not an implementation.", file=sys.stderr)
+        print(f"bench.py: the walk runs on one GPU only (asked for --gpus {args.gpus}); its "
+              "sharding across GPUs is designed but not implemented.", file=sys.stderr)
         sys.exit(2)
 
     dev = torch.device("cuda:0")
