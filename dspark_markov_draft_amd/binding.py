@@ -109,6 +109,65 @@ def _p(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# The C ABI sees pointers only, so the wrappers check what it cannot: every tensor's dtype and
+# shape against the sizes the call is made with, and that all of them sit on one CUDA device.
+# A mismatch raises ValueError before anything reaches the library (a short or mistyped buffer
+# would otherwise be read or written past its end by the kernels).
+_W_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
+
+
+def _expect(t, name: str, dtypes, shape, optional: bool = False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not torch.is_tensor(t):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be {want}, got {str(t.dtype).replace('torch.', '')}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(**tensors):
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a CUDA device, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+
+
+def _check_walk_args(q, s, w1, base, start, workspace, draft_tokens):
+    _expect(base, "base", torch.float32, None)
+    if base.dim() != 3:
+        raise ValueError(f"base must be [bs, T, V], got shape {tuple(base.shape)}")
+    bs, T, V = base.shape
+    _expect(q, "q", torch.int8, (V, RANK))
+    _expect(s, "s", torch.float32, (V,))
+    _expect(w1, "w1", _W_DTYPES, (V, RANK))
+    _expect(start, "start", torch.int32, (bs,))
+    if not torch.is_tensor(workspace) or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D tensor")
+    _expect(draft_tokens, "draft_tokens", torch.int32, (bs, T))
+    return bs, T, V
+
+
+def _check_sample_args(bs, seeds, temperature, positions):
+    _expect(seeds, "seeds", torch.int64, (bs,))
+    _expect(temperature, "temperature", torch.float32, (bs,))
+    _expect(positions, "positions", torch.int64, (bs,), optional=True)
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -123,11 +182,17 @@ def _dtype_code(t: torch.Tensor) -> int:
 def dspark_quantize_w2(w2: torch.Tensor, q: Optional[torch.Tensor] = None,
                        s: Optional[torch.Tensor] = None, stream=None):
     """W2 [V, 256] (fp32 / bf16 / fp16, device) -> (q int8 [V, 256], s fp32 [V])."""
+    _expect(w2, "w2", _W_DTYPES, None)
+    if w2.dim() != 2:
+        raise ValueError(f"w2 must be [V, {RANK}], got shape {tuple(w2.shape)}")
     V, R = w2.shape
     if q is None:
         q = torch.empty((V, R), dtype=torch.int8, device=w2.device)
     if s is None:
         s = torch.empty((V,), dtype=torch.float32, device=w2.device)
+    _expect(q, "q", torch.int8, (V, R))
+    _expect(s, "s", torch.float32, (V,))
+    _same_device(w2=w2, q=q, s=s)
     _check(lib().dspark_quantize_w2(_p(w2), _dtype_code(w2), V, R, _p(q), _p(s), _stream(stream)))
     return q, s
 
@@ -157,9 +222,14 @@ def dspark_walk_plan_for(cus: int, max_lds: int, bs: int, T: int, V: int) -> dic
 def dspark_walk_greedy(q, s, w1, base, start, workspace, draft_tokens=None, out_logits=None,
                        stream=None):
     """Greedy walk. base [bs, T, V] fp32; start [bs] int32. Returns draft_tokens [bs, T] int32."""
-    bs, T, V = base.shape
-    if draft_tokens is None:
+    _expect(base, "base", torch.float32, None)
+    bs, T, V = base.shape if base.dim() == 3 else (0, 0, 0)
+    if draft_tokens is None and base.dim() == 3:
         draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
+    bs, T, V = _check_walk_args(q, s, w1, base, start, workspace, draft_tokens)
+    _expect(out_logits, "out_logits", torch.float32, (bs, T, V), optional=True)
+    _same_device(q=q, s=s, w1=w1, base=base, start=start, workspace=workspace,
+                 draft_tokens=draft_tokens, out_logits=out_logits)
     _check(lib().dspark_walk_greedy(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base), _p(start),
                                     bs, T, V, q.shape[1], _p(draft_tokens), _p(out_logits),
                                     _p(workspace), workspace.numel() * workspace.element_size(),
@@ -172,11 +242,19 @@ def dspark_walk_sample(q, s, w1, base, start, seeds, temperature, workspace, pos
     """Probabilistic walk. seeds [bs] int64 holding the uint64 bits; temperature [bs] fp32;
     positions [bs] int64 or None. Returns (draft_tokens [bs, T] int32, draft_logits [bs, T, V]
     bf16)."""
-    bs, T, V = base.shape
-    if draft_tokens is None:
-        draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
-    if draft_logits is None:
-        draft_logits = torch.empty((bs, T, V), dtype=torch.bfloat16, device=base.device)
+    _expect(base, "base", torch.float32, None)
+    if base.dim() == 3:
+        bs, T, V = base.shape
+        if draft_tokens is None:
+            draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
+        if draft_logits is None:
+            draft_logits = torch.empty((bs, T, V), dtype=torch.bfloat16, device=base.device)
+    bs, T, V = _check_walk_args(q, s, w1, base, start, workspace, draft_tokens)
+    _check_sample_args(bs, seeds, temperature, positions)
+    _expect(draft_logits, "draft_logits", torch.bfloat16, (bs, T, V))
+    _same_device(q=q, s=s, w1=w1, base=base, start=start, workspace=workspace,
+                 draft_tokens=draft_tokens, draft_logits=draft_logits, seeds=seeds,
+                 temperature=temperature, positions=positions)
     _check(lib().dspark_walk_sample(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base), _p(start),
                                     bs, T, V, q.shape[1], _p(seeds), _p(positions),
                                     _p(temperature), _p(draft_tokens), _p(draft_logits),
@@ -190,11 +268,23 @@ def dspark_walk_topk(q, s, w1, base, start, k, workspace, sample=False, seeds=No
                      stream=None):
     """Top-k walk. Returns (draft_tokens, draft_logits): draft_logits is bf16 [bs, T, V] when
     sampling, else the fp32 [bs, T, V] tensor passed in (or None)."""
-    bs, T, V = base.shape
-    if draft_tokens is None:
-        draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
-    if sample and draft_logits is None:
-        draft_logits = torch.empty((bs, T, V), dtype=torch.bfloat16, device=base.device)
+    _expect(base, "base", torch.float32, None)
+    if base.dim() == 3:
+        bs, T, V = base.shape
+        if draft_tokens is None:
+            draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
+        if sample and draft_logits is None:
+            draft_logits = torch.empty((bs, T, V), dtype=torch.bfloat16, device=base.device)
+    bs, T, V = _check_walk_args(q, s, w1, base, start, workspace, draft_tokens)
+    if sample:
+        _check_sample_args(bs, seeds, temperature, positions)
+        _expect(draft_logits, "draft_logits", torch.bfloat16, (bs, T, V))
+    else:
+        _expect(draft_logits, "draft_logits", torch.float32, (bs, T, V), optional=True)
+    _same_device(q=q, s=s, w1=w1, base=base, start=start, workspace=workspace,
+                 draft_tokens=draft_tokens, draft_logits=draft_logits,
+                 seeds=seeds if sample else None, temperature=temperature if sample else None,
+                 positions=positions if sample else None)
     _check(lib().dspark_walk_topk(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base), _p(start), bs,
                                   T, V, q.shape[1], int(k), int(bool(sample)), _p(seeds),
                                   _p(positions), _p(temperature), _p(draft_tokens),
@@ -205,6 +295,17 @@ def dspark_walk_topk(q, s, w1, base, start, k, workspace, sample=False, seeds=No
 
 def dspark_workspace_status(workspace, stream=None) -> int:
     return int(lib().dspark_workspace_status(_p(workspace), _stream(stream)))
+
+
+def check_workspace(workspace, stream=None) -> None:
+    """Synchronising check of the error a walk recorded in its workspace (for callers that share
+    the GPU with other work). On DSPARK_ERR_TIMEOUT the tokens of that walk are invalid and the
+    workspace may hold stale keys: it is zeroed again before the error is raised, so the next
+    walk can use it. Any recorded error raises DsparkError."""
+    st = dspark_workspace_status(workspace, stream)
+    if st == ERR_TIMEOUT:
+        workspace.zero_()
+    _check(st)
 
 
 def dspark_philox_words(seed: int, position: int, v0: int, n: int, device="cuda",

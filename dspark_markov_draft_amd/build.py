@@ -1,14 +1,20 @@
-"""Build libdspark.so in-tree with hipcc for gfx950 (no JIT, no torch extension machinery)."""
+"""Build libdspark.so in-tree with hipcc for gfx950 (no JIT, no torch extension machinery).
+
+Each .hip source is compiled to its own object in parallel (the kernels are template-heavy and
+one file takes tens of seconds), then the objects are linked into the shared library.
+"""
 import glob
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdspark.so")
+OBJ_DIR = os.path.join(HERE, "_build")
 
 HIPCC_FLAGS = [
-    "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -19,15 +25,37 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
+def _jobs() -> int:
+    n = os.cpu_count() or 4
+    for var in ("MAX_JOBS", "CMAKE_BUILD_PARALLEL_LEVEL"):
+        v = os.environ.get(var)
+        if v and v.isdigit():
+            n = min(n, int(v))
+    return max(1, min(n, 16))
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+
+    def compile_one(src):
+        obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
+        cmd = [hipcc, *HIPCC_FLAGS, *inc, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+        objs = list(ex.map(compile_one, sources()))
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed:\n{r.stderr}")
+        raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
     return LIB
 

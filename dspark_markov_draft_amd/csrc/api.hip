@@ -78,7 +78,7 @@ const char* dspark_status_string(int status) {
         case DSPARK_ERR_NO_DEVICE: return "no gfx950 HIP device";
         case DSPARK_ERR_LAUNCH: return "HIP launch or copy failed";
         case DSPARK_ERR_NONFINITE: return "W2 holds a NaN or infinity";
-        case DSPARK_ERR_TIMEOUT: return "grid-wide wait hit its spin limit";
+        case DSPARK_ERR_TIMEOUT: return "grid-wide wait hit its time bound";
         default: return "unknown status";
     }
 }
@@ -294,7 +294,10 @@ int dspark_debug_set(int key, int64_t value) {
     DebugKnobs& k = debug_knobs();
     switch (key) {
         case DSPARK_DEBUG_MAX_WORKGROUPS: k.max_workgroups = (int)value; return DSPARK_OK;
-        case DSPARK_DEBUG_SPIN_LIMIT: k.spin_limit = (uint32_t)value; return DSPARK_OK;
+        case DSPARK_DEBUG_SPIN_LIMIT:
+            if (value > 0xFFFFFFFFll) return DSPARK_ERR_INVALID_ARG;
+            k.spin_ticks = (uint32_t)value;
+            return DSPARK_OK;
         case DSPARK_DEBUG_WAIT_UNSET_FLAG: k.wait_unset = (uint32_t)value; return DSPARK_OK;
         case DSPARK_DEBUG_FORCE_PATH:
             if (value != 0 && value != DSPARK_PATH_DOT4 && value != DSPARK_PATH_MFMA &&

@@ -151,7 +151,7 @@ __device__ __forceinline__ uint4 philox_run_words(const PhiloxRun& run, uint32_t
 }
 
 // Noise word of vocabulary entry v at draft position P for a request keyed by `seed`
-// (vLLM PR #62958, Details: Philox keyed by request seed and draft position):
+// (vLLM PR #62958, Details: the noise comes from Philox, with the request's seed and the draft position as inputs):
 // counter (v >> 2, lo32 P, hi32 P, 0), key (lo32 seed, hi32 seed), word v & 3.
 __device__ __forceinline__ uint32_t noise_word(uint64_t seed, uint64_t P, uint32_t v) {
     const uint4 r = philox4x32_10(v >> 2, (uint32_t)P, (uint32_t)(P >> 32), 0u, (uint32_t)seed,

@@ -33,7 +33,7 @@ inline size_t topk_bytes(int64_t bs, int64_t T, int64_t k) {
 // Process-wide test hooks (dspark_debug_set).
 struct DebugKnobs {
     int max_workgroups = 0;
-    uint32_t spin_limit = 0;
+    uint32_t spin_ticks = 0;
     uint32_t wait_unset = 0;
     uintptr_t stamps = 0;
     int force_path = 0;

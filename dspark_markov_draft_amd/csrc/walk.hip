@@ -147,7 +147,7 @@ int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, int sampl
 // The kernels' waits need all their workgroups resident at once. The grid never exceeds the
 // compute units, and each workgroup asks for more than half of a CU's LDS, so each CU holds at
 // most one; with the device otherwise idle they are all resident. If they are not (other work
-// holds CUs), the waits run into their spin limit and the call reports DSPARK_ERR_TIMEOUT
+// holds CUs), the waits run into their time bound and the call reports DSPARK_ERR_TIMEOUT
 // instead of hanging. A cooperative launch would guarantee residency but costs ~20 us per
 // launch on this stack, an order of magnitude above a plain launch.
 int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipStream_t stream) {
@@ -192,7 +192,7 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     p.stage_stride = plan.stage_stride;
     p.vec_ok = vec_ok ? 1 : 0;
     const DebugKnobs& dbg = debug_knobs();
-    p.spin_limit = dbg.spin_limit ? dbg.spin_limit : DEFAULT_SPIN_LIMIT;
+    p.spin_ticks = dbg.spin_ticks ? dbg.spin_ticks : DEFAULT_SPIN_TICKS;
     p.wait_unset = dbg.wait_unset ? 1 : 0;
     p.stamps = reinterpret_cast<uint64_t*>(dbg.stamps);
     const bool timed = p.stamps != nullptr && a.w1_dtype == DSPARK_BF16;

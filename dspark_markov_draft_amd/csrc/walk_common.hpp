@@ -13,7 +13,11 @@ constexpr int WALK_THREADS = 256;
 constexpr int WALK_WAVES = WALK_THREADS / WAVE;  // 4: one wave per SIMD
 constexpr int W1Q_BYTES = MAX_BS * RANK;         // int8 codes of the gathered W1 rows (LDS)
 constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workgroup per CU
-constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 22;
+// Bound of every grid-wide wait, in ticks of the 100 MHz constant clock: 10 ms, some thousand
+// times the longest healthy wait (the first step's, behind the W2 fill). A walk whose
+// workgroups are not all resident at once (other work holds compute units) thus gives up within
+// milliseconds per wait and reports DSPARK_ERR_TIMEOUT.
+constexpr uint32_t DEFAULT_SPIN_TICKS = 1000000u;
 constexpr int DOT4_REG_SETS = 3;  // lane-per-row kernel: row sets of 256 rows held in registers
 constexpr int MFMA1_TILES = 10;      // one-request MFMA kernel: 16-row tiles per wave in registers
 constexpr int MFMA1_LDS_TILES = 8;   // and at most this many more in LDS (4 KB each)
@@ -75,8 +79,22 @@ struct WalkParams {
     int vec_ok;             // base / draft_logits rows allow float4 and 4 x bf16 accesses
     int stage_bufs;         // MFMA: LDS buffers for the base logits of a 16-request tile (0-2)
     int stage_stride;       // MFMA: floats per request row in a staging buffer
-    uint32_t spin_limit;
+    uint32_t spin_ticks;    // bound of each grid-wide wait (100 MHz clock ticks)
     int wait_unset;
+};
+
+// Elapsed-time bound of one grid-wide wait on the constant 100 MHz clock (s_memrealtime). Each
+// pass of a wait loop reads the clock first (now()) and compares it last (expired()): the scalar
+// read returns while the pass's polls are in flight, and the loop keeps the shape of a plain
+// counted loop. (A check only every n-th pass made the compiler copy the poll registers across
+// the back edge, waiting for every load in flight on each pass.)
+struct WaitBound {
+    uint64_t t0;
+    __device__ __forceinline__ WaitBound() : t0(__builtin_amdgcn_s_memrealtime()) {}
+    __device__ __forceinline__ static uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
+    __device__ __forceinline__ bool expired(uint64_t t, uint32_t ticks) const {
+        return t - t0 > (uint64_t)ticks;
+    }
 };
 
 // Instrumented builds record the constant-rate device clock (s_memrealtime, 100 MHz) per
@@ -293,7 +311,7 @@ __device__ __forceinline__ void load_start_tokens(const WalkParams& p, int32_t* 
 // every workgroup waits for its copy (workgroup w reads copy w % RESULT_REPLICAS) of the result
 // words of step t and writes the new tokens into `tok`. Both waits keep two rounds of loads in
 // flight: a store that becomes visible is seen about one load latency later, not one and a half.
-// All waits are bounded by the spin limit.
+// All waits are bounded in time (WaitBound).
 __device__ __forceinline__ uint64_t* result_word(const WalkParams& p, int rep, int t, int b) {
     return p.result + ((size_t)rep * MAX_STEPS + t) * MAX_BS + b;
 }
@@ -310,7 +328,7 @@ __device__ __forceinline__ uint64_t* result_word(const WalkParams& p, int rep, i
 // The last step stores its keys into replica 0 only, for one reducer per request (workgroup
 // b % nwg), which writes the token and clears the request's keys of steps T-1 and T-2; nothing
 // is published. The workspace is all zero when the walk ends. Waits keep two rounds of loads in
-// flight and are bounded by the spin limit.
+// flight and are bounded in time (WaitBound).
 __device__ __forceinline__ uint64_t* replica_slot(const WalkParams& p, int t, int rep, int nb,
                                                   int b, int w) {
     return p.slots + (size_t)t * gridDim.x * p.stride + (size_t)(rep * nb + b) * gridDim.x + w;
@@ -375,14 +393,15 @@ __device__ __forceinline__ void combine_step_small(const WalkParams& p, int t, u
             return __all(all);
         };
         uint64_t va[NB][NL], vb[NB][NL];
-        uint32_t spins = 0;
+        const WaitBound wait;
         issue(va);
         while (true) {
+            const uint64_t now = WaitBound::now();
             issue(vb);
             if (complete(va)) break;
             issue(va);
             if (complete(vb)) break;
-            if (++spins > p.spin_limit) {
+            if (wait.expired(now, p.spin_ticks)) {
                 if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
                 break;
             }
@@ -462,14 +481,15 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
         };
         uint64_t va[NL], vb[NL];
         uint64_t best = 0;
-        uint32_t spins = 0;
+        const WaitBound wait;
         issue(va);
         while (true) {
+            const uint64_t now = WaitBound::now();
             issue(vb);
             if (complete(va, best)) break;
             issue(va);
             if (complete(vb, best)) break;
-            if (++spins > p.spin_limit) {
+            if (wait.expired(now, p.spin_ticks)) {
                 if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
                 break;
             }
@@ -494,7 +514,7 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
     if (t + 1 < p.T) {
         const uint64_t* mine = result_word(p, wg % RESULT_REPLICAS, t, lane < p.bs ? lane : 0);
         uint64_t ka, kb;
-        uint32_t spins = 0;
+        const WaitBound wait;
         auto seen = [&](uint64_t k) {
             bool ok = lane >= p.bs || k != 0;
             if (p.wait_unset)
@@ -505,6 +525,7 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
         uint64_t k = 0;
         ka = ld_dev(mine);
         while (true) {
+            const uint64_t now = WaitBound::now();
             kb = ld_dev(mine);
             if (seen(ka)) {
                 k = ka;
@@ -515,7 +536,7 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
                 k = kb;
                 break;
             }
-            if (++spins > p.spin_limit) {
+            if (wait.expired(now, p.spin_ticks)) {
                 if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
                 k = kb;
                 break;

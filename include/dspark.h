@@ -9,8 +9,8 @@
  * then the step takes the first-maximum argmax (greedy) or a Gumbel-max sample, and the
  * chosen token is prev for step t + 1 (prev at t = 0 is the request's start token). W2 is
  * held as int8 with one fp32 scale per row (same page, Overview). Probabilistic drafting
- * stores the bf16 logits it sampled from, and its noise is Philox keyed by the request seed
- * and the draft position (same page, Details). Argmax follows torch.argmax: the first NaN
+ * stores the bf16 logits it sampled from, and its Gumbel noise comes from Philox4x32-10 with the
+ * request's seed as key and its draft position in the counter (same page, Details). Argmax follows torch.argmax: the first NaN
  * wins, else the first maximum (vLLM PR #64476, Claims and Validation). The top-k variant
  * takes the k best base logits once per draft position, biases only those, and scatters them
  * into a row that is -inf elsewhere before the unchanged sampler runs (vLLM PR #49969
@@ -49,7 +49,7 @@ enum dspark_status {
     DSPARK_ERR_NO_DEVICE = -4,    /* no HIP device, or not a device this library was built for */
     DSPARK_ERR_LAUNCH = -5,       /* a HIP launch or copy failed */
     DSPARK_ERR_NONFINITE = -6,    /* dspark_quantize_w2 met a NaN or infinity in W2 */
-    DSPARK_ERR_TIMEOUT = -7       /* a walk's grid-wide wait hit its spin limit (see dspark_workspace_status) */
+    DSPARK_ERR_TIMEOUT = -7       /* a walk's grid-wide wait hit its time bound (see dspark_workspace_status) */
 };
 
 enum dspark_dtype { DSPARK_F32 = 0, DSPARK_BF16 = 1, DSPARK_F16 = 2 };
@@ -178,9 +178,11 @@ int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, 
 /*
  * Error word of a walk workspace: synchronises `stream`, returns DSPARK_OK or the error the
  * last walk recorded, and clears it. Diagnostic call, not for hot loops.
- *   DSPARK_ERR_TIMEOUT: a grid-wide wait hit its spin limit (the walk's workgroups were not all
- *       resident at once, e.g. other work held compute units). The tokens of that call are
- *       invalid, and the workspace must be zeroed again before the next call.
+ *   DSPARK_ERR_TIMEOUT: a grid-wide wait ran past its time bound (10 ms by default): the walk's
+ *       workgroups were not all resident at once, e.g. other work held compute units. The tokens
+ *       of that call are invalid, and the workspace must be zeroed again before the next call
+ *       (a workgroup that arrived late may have left keys in it). Callers that share the GPU
+ *       with other work should check this after their walks.
  *   DSPARK_ERR_INVALID_ARG: a start token was outside [0, V) (it was replaced by 0).
  */
 int dspark_workspace_status(void* workspace, void* stream);
@@ -195,10 +197,10 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
 /*
  * Test hooks (process-wide, not thread-safe):
  *   DSPARK_DEBUG_MAX_WORKGROUPS: cap the dense walk's grid (0 = one per compute unit);
- *   DSPARK_DEBUG_SPIN_LIMIT: iterations of the grid-wide wait before DSPARK_ERR_TIMEOUT is
- *       recorded (0 = default);
+ *   DSPARK_DEBUG_SPIN_LIMIT: bound of each grid-wide wait, in ticks of the 100 MHz device clock,
+ *       before DSPARK_ERR_TIMEOUT is recorded (0 = the default, 10 ms; at most 2^32 - 1);
  *   DSPARK_DEBUG_WAIT_UNSET_FLAG: non-zero makes the grid-wide waits also wait for a workspace
- *       flag that nothing sets, so each runs into its spin limit (for the timeout test);
+ *       flag that nothing sets, so each runs into its time bound (for the timeout test);
  *   DSPARK_DEBUG_FORCE_PATH: 0 chooses by batch size; DSPARK_PATH_DOT4 / DSPARK_PATH_MFMA force
  *       that kernel for every batch size, DSPARK_PATH_MFMA1 for one request whose slices fit it
  *       (all compute the same results);

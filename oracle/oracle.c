@@ -11,7 +11,8 @@
  *    the argmax or a sample, and the chosen token is the next step's prev. W2 is stored as int8
  *    with one fp32 scale per row.
  *  - PR #62958, Details: probabilistic drafting stores the bf16 logits it sampled from in
- *    draft_logits; the sampling noise is Philox keyed by the request seed and the draft position.
+ *    draft_logits; its Gumbel noise words are Philox outputs whose key is the request's seed and
+ *    whose counter holds the draft position.
  *    The rank is 256.
  *  - vLLM PR #64476 (Markov bias in the Gumbel kernel), Claims: the combine follows
  *    torch.argmax (the first NaN wins, otherwise the first maximum); the temperature divide is
@@ -115,8 +116,8 @@ void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
 }
 
 /* The noise word for vocabulary entry v of draft position P of a request with this seed    */
-/* (PR #62958, Details: Philox keyed by request seed and draft position). Reading: counter  */
-/* (v >> 2, lo32(P), hi32(P), 0), key (lo32(seed), hi32(seed)), word v & 3.                  */
+/* (PR #62958, Details: Philox with the request seed and draft position as inputs).         */
+/* Reading: counter (v >> 2, lo32(P), hi32(P), 0), key (lo32(seed), hi32(seed)), word v & 3. */
 uint32_t oracle_noise_word(uint64_t seed, uint64_t P, int64_t v) {
     uint32_t ctr[4] = {(uint32_t)((uint64_t)v >> 2), (uint32_t)P, (uint32_t)(P >> 32), 0u};
     uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
