@@ -72,6 +72,8 @@ def lib():
         L.dspark_walk_plan_query.argtypes = [i64, i64, i64, ctypes.POINTER(WalkPlan)]
         L.dspark_walk_greedy.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, vp, vp, vp,
                                          ctypes.c_size_t, vp]
+        L.dspark_walk_greedy_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, vp,
+                                                 vp, vp, vp]
         L.dspark_walk_sample.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, vp, vp, vp,
                                          vp, vp, vp, ctypes.c_size_t, vp]
         L.dspark_walk_topk.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i64, i32, vp,
@@ -84,7 +86,7 @@ def lib():
         L.dspark_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
                                           ctypes.POINTER(i32)]
         for name in ["dspark_quantize_w2", "dspark_walk_plan_query", "dspark_walk_plan_for",
-                     "dspark_walk_greedy",
+                     "dspark_walk_greedy", "dspark_walk_greedy_noalloc",
                      "dspark_walk_sample", "dspark_walk_topk", "dspark_workspace_status",
                      "dspark_philox_words", "dspark_debug_set", "dspark_kernel_times"]:
             getattr(L, name).restype = i32
@@ -234,6 +236,32 @@ def dspark_walk_greedy(q, s, w1, base, start, workspace, draft_tokens=None, out_
                                     bs, T, V, q.shape[1], _p(draft_tokens), _p(out_logits),
                                     _p(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
+    return draft_tokens
+
+
+def dspark_walk_greedy_noalloc(q, s, w1, base, start, draft_tokens=None, out_logits=None,
+                               error_word=None, stream=None):
+    """Greedy walk on the library-held scratch (no workspace argument; allocates nothing when
+    draft_tokens is given). error_word: optional int32 [1] device tensor, zeroed by the caller,
+    where the walk records -status on an error. Returns draft_tokens [bs, T] int32."""
+    _expect(base, "base", torch.float32, None)
+    if base.dim() == 3 and draft_tokens is None:
+        draft_tokens = torch.empty(base.shape[:2], dtype=torch.int32, device=base.device)
+    if base.dim() != 3:
+        raise ValueError(f"base must be [bs, T, V], got shape {tuple(base.shape)}")
+    bs, T, V = base.shape
+    _expect(q, "q", torch.int8, (V, RANK))
+    _expect(s, "s", torch.float32, (V,))
+    _expect(w1, "w1", _W_DTYPES, (V, RANK))
+    _expect(start, "start", torch.int32, (bs,))
+    _expect(draft_tokens, "draft_tokens", torch.int32, (bs, T))
+    _expect(out_logits, "out_logits", torch.float32, (bs, T, V), optional=True)
+    _expect(error_word, "error_word", torch.int32, (1,), optional=True)
+    _same_device(q=q, s=s, w1=w1, base=base, start=start, draft_tokens=draft_tokens,
+                 out_logits=out_logits, error_word=error_word)
+    _check(lib().dspark_walk_greedy_noalloc(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base),
+                                            _p(start), bs, T, V, q.shape[1], _p(draft_tokens),
+                                            _p(out_logits), _p(error_word), _stream(stream)))
     return draft_tokens
 
 

@@ -3,6 +3,8 @@
 // checks, and dispatch to the kernels' launchers.
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace dspark {
@@ -61,6 +63,45 @@ static int check_walk_common(const int8_t* q, const float* s, const void* w1, co
         return DSPARK_ERR_INVALID_ARG;
     if (ws_bytes < dspark_walk_workspace_bytes(bs, T, V, k)) return DSPARK_ERR_WORKSPACE;
     return DSPARK_OK;
+}
+
+// ---- library-held scratch of the no-allocation greedy walk ---------------------------------
+// For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+// loops, harnesses that forbid allocation): dspark_walk_greedy_noalloc keeps the walk's
+// workspace in this file-scope device array instead of a caller workspace. It is sized for the
+// largest dense walk (64 requests, 16 steps); every GPU the library runs on holds its own copy
+// until the process ends. In host code `scratch` names a host-side stand-in, so its device
+// address is looked up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is ever handed to kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES =
+    (WS_SLOTS + (size_t)DSPARK_MAX_STEPS * MAX_WORKGROUPS * DSPARK_MAX_BS * 8 + WS_ALIGN - 1) /
+    WS_ALIGN * WS_ALIGN;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+static void* g_scratch_ptr[64];
+static std::mutex g_scratch_mutex;
+
+// The device address of this device's copy of `scratch` (looked up on the first call per
+// device); NULL if the lookup failed.
+static void* scratch_address(int dev) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Zeroes n16 16-byte words from p (the part of the scratch a call uses; a kernel rather than a
+// memset node, so that the call stays safe to capture into a graph).
+__global__ void clear_scratch_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 }  // namespace dspark
@@ -177,6 +218,60 @@ int dspark_walk_greedy(const int8_t* w2_q, const float* w2_scale, const void* w1
     a.T = (int)T;
     a.V = (int)V;
     return dense_walk(a, rank, workspace_bytes, stream);
+}
+
+int dspark_walk_greedy_noalloc(const int8_t* w2_q, const float* w2_scale, const void* w1,
+                               int w1_dtype, const float* base_logits,
+                               const int32_t* start_tokens, int64_t bs, int64_t T, int64_t V,
+                               int64_t rank, int32_t* draft_tokens, float* out_logits,
+                               uint32_t* error_word, void* stream) {
+    if (bs < 1 || T < 1 || V < 1) return DSPARK_ERR_INVALID_ARG;
+    if (bs > DSPARK_MAX_BS || T > DSPARK_MAX_STEPS || V > DSPARK_MAX_V) return DSPARK_ERR_UNSUPPORTED;
+    const size_t need = dspark_walk_workspace_bytes(bs, T, V, 0);
+    if (need > NOALLOC_SCRATCH_BYTES) return DSPARK_ERR_UNSUPPORTED;
+    WalkLaunch a = {};
+    a.q = w2_q;
+    a.scale = w2_scale;
+    a.w1 = w1;
+    a.w1_dtype = w1_dtype;
+    a.base = base_logits;
+    a.start = start_tokens;
+    a.tokens = draft_tokens;
+    a.out_logits = out_logits;
+    a.error_word = error_word;
+    a.sample = 0;
+    a.bs = (int)bs;
+    a.T = (int)T;
+    a.V = (int)V;
+    // every check of the greedy walk, before any device work
+    int st = check_walk_shape(bs, T, V, rank, w1_dtype);
+    if (st != DSPARK_OK) return st;
+    if (!w2_q || !w2_scale || !w1 || !base_logits || !start_tokens || !draft_tokens)
+        return DSPARK_ERR_INVALID_ARG;
+    if (!aligned16(w2_q) || !aligned16(w1) || !aligned4(w2_scale) || !aligned4(base_logits) ||
+        !aligned4(start_tokens) || !aligned4(draft_tokens))
+        return DSPARK_ERR_INVALID_ARG;
+    if (error_word && !aligned4(error_word)) return DSPARK_ERR_INVALID_ARG;
+    if (out_logits && !aligned4(out_logits)) return DSPARK_ERR_INVALID_ARG;
+    DeviceInfo dev;
+    st = current_device_info(&dev);
+    if (st != DSPARK_OK) return st;
+    void* ws = scratch_address(dev.device);
+    if (ws == nullptr) return DSPARK_ERR_LAUNCH;
+    a.workspace = ws;
+    st = check_walk_common(a.q, a.scale, a.w1, a.base, a.start, a.tokens, ws,
+                           NOALLOC_SCRATCH_BYTES, bs, T, V, 0);
+    if (st != DSPARK_OK) return st;
+    dspark_walk_plan plan;
+    st = plan_walk(dev, bs, T, V, 0, &plan);
+    if (st != DSPARK_OK) return st;
+    // the walk needs the words it uses zeroed; one that timed out may have left keys behind
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t n16 = need / 16;
+    const size_t blocks = (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024;
+    clear_scratch_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint4*>(ws), n16);
+    if (hipGetLastError() != hipSuccess) return DSPARK_ERR_LAUNCH;
+    return launch_dense_walk(a, plan, s);
 }
 
 int dspark_walk_sample(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,

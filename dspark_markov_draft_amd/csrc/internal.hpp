@@ -66,6 +66,7 @@ struct WalkLaunch {
     const int64_t* positions;
     const float* temps;
     void* workspace;
+    uint32_t* error_word;     // where errors are recorded; NULL: the workspace's error word
     int bs, T, V;
     int sample;
 };

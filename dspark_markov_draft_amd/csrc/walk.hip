@@ -178,7 +178,7 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     char* ws = static_cast<char*>(a.workspace);
     p.result = reinterpret_cast<uint64_t*>(ws + WS_RESULT);
     p.slots = reinterpret_cast<uint64_t*>(ws + WS_SLOTS);
-    p.err = reinterpret_cast<uint32_t*>(ws + WS_ERR);
+    p.err = a.error_word ? a.error_word : reinterpret_cast<uint32_t*>(ws + WS_ERR);
     p.never = reinterpret_cast<const uint32_t*>(ws + WS_ERR + 4);
     p.bs = a.bs;
     p.T = a.T;

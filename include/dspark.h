@@ -140,6 +140,27 @@ int dspark_walk_greedy(const int8_t* w2_q, const float* w2_scale, const void* w1
                        float* out_logits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The greedy walk without a caller workspace, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation. It
+ * computes exactly what dspark_walk_greedy computes (same kernels, same bits) and allocates
+ * nothing: its workspace is a library-held device array of 2,232,320 bytes, sized for the
+ * largest walk (bs 64, T 16), one copy per GPU, held until the process ends. Arguments as
+ * dspark_walk_greedy, without workspace and workspace_bytes, plus
+ *   error_word: a device uint32 the caller zeroes, where a walk records an error as
+ *       -dspark_status (DSPARK_ERR_TIMEOUT, or DSPARK_ERR_INVALID_ARG for a start token outside
+ *       [0, V)); or NULL, where such errors are not reported.
+ * Each call first clears the part of the array it uses (a fill kernel on `stream`), then walks.
+ * All calls on one GPU share its array: calls that overlap on one GPU (other streams, other
+ * threads) race and must not be made. Shapes beyond the array's size cannot occur within the
+ * supported envelope; they would return DSPARK_ERR_UNSUPPORTED.
+ */
+int dspark_walk_greedy_noalloc(const int8_t* w2_q, const float* w2_scale, const void* w1,
+                               int w1_dtype, const float* base_logits,
+                               const int32_t* start_tokens, int64_t bs, int64_t T, int64_t V,
+                               int64_t rank, int32_t* draft_tokens, float* out_logits,
+                               uint32_t* error_word, void* stream);
+
+/*
  * Probabilistic walk (PR #62958, Details; PR #64476, Claims).
  * Arguments as dspark_walk_greedy, plus
  *   seeds [bs] uint64: per-request Philox key (lo32, hi32)

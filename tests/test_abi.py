@@ -148,6 +148,35 @@ def test_greedy_validation(kw, code):
     assert _greedy(**kw) == code
 
 
+def _noalloc(**kw):
+    a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=1, T=7, V=151936,
+             rank=256, tokens=FAKE, logits=None, err=None, stream=None)
+    a.update(kw)
+    return B.lib().dspark_walk_greedy_noalloc(a["q"], a["s"], a["w1"], a["dt"], a["base"],
+                                              a["start"], a["bs"], a["T"], a["V"], a["rank"],
+                                              a["tokens"], a["logits"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), B.ERR_INVALID_ARG),
+    (dict(s=None), B.ERR_INVALID_ARG),
+    (dict(tokens=None), B.ERR_INVALID_ARG),
+    (dict(q=FAKE + 4), B.ERR_INVALID_ARG),
+    (dict(err=FAKE + 2), B.ERR_INVALID_ARG),
+    (dict(logits=FAKE + 2), B.ERR_INVALID_ARG),
+    (dict(bs=0), B.ERR_INVALID_ARG),
+    (dict(rank=128), B.ERR_UNSUPPORTED),
+    (dict(T=17), B.ERR_UNSUPPORTED),
+    (dict(bs=65), B.ERR_UNSUPPORTED),
+    (dict(V=270337), B.ERR_UNSUPPORTED),
+    (dict(dt=7), B.ERR_UNSUPPORTED),
+])
+def test_noalloc_validation(kw, code):
+    """The no-allocation walk checks its arguments on the host like the greedy walk (its
+    largest shape, bs 64 x 16 steps, fits its scratch by construction)."""
+    assert _noalloc(**kw) == code
+
+
 def _sample(**kw):
     a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=1, T=7, V=151936,
              rank=256, seeds=FAKE, pos=None, temp=FAKE, tokens=FAKE, lb=FAKE, ws=FAKE,
@@ -239,5 +268,7 @@ def test_no_device_without_gpu():
     """Valid arguments on a machine with no GPU: the device check refuses the call."""
     assert _greedy() == B.ERR_NO_DEVICE
     assert _sample() == B.ERR_NO_DEVICE
+    assert _noalloc() == B.ERR_NO_DEVICE
+    assert _noalloc(bs=64, T=16, V=270336) == B.ERR_NO_DEVICE
     p = B.WalkPlan()
     assert B.lib().dspark_walk_plan_query(1, 7, 151936, ctypes.byref(p)) == B.ERR_NO_DEVICE
