@@ -74,6 +74,8 @@ def lib():
         L.oracle_walk.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, vp,
                                   vp, vp, vp, vp, vp]
         L.oracle_walk.restype = ctypes.c_int
+        L.oracle_verify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp]
+        L.oracle_verify.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -191,3 +193,32 @@ def walk(q, s, w1, base, start, k=0, sample=False, seeds=None, positions=None, t
     if st != OK:
         raise OracleError(f"oracle_walk failed ({st})")
     return tokens, logits, lb
+
+
+VERIFY_TOKEN, VERIFY_BLOCK = 0, 1
+
+
+def verify(draft_lb, draft_tokens, target_logits, temps, uniforms, mode=VERIFY_TOKEN):
+    """Verification of drafted blocks (see oracle_verify in oracle.c).
+
+    draft_lb uint16 [bs, T, V] (bf16 bits), draft_tokens int32 [bs, T], target_logits fp32
+    [bs, T + 1, V], temps fp32 [bs], uniforms fp32 [bs, T + 1]. Returns (accepted int32 [bs],
+    out_tokens int32 [bs, T + 1] (kept prefix, the next token, then -1), accept_prob fp64 [bs, T]
+    (min(1, p/q) per step in token mode, h_i in block mode))."""
+    lb = _c(draft_lb, np.uint16)
+    X = _c(draft_tokens, np.int32)
+    tg = _c(target_logits, np.float32)
+    tp = _c(temps, np.float32)
+    un = _c(uniforms, np.float32)
+    bs, T, V = lb.shape
+    if X.shape != (bs, T) or tg.shape != (bs, T + 1, V) or tp.shape != (bs,) or \
+            un.shape != (bs, T + 1):
+        raise OracleError("verify: inconsistent shapes")
+    acc = np.empty(bs, np.int32)
+    out = np.empty((bs, T + 1), np.int32)
+    prob = np.empty((bs, T), np.float64)
+    st = lib().oracle_verify(_ptr(lb), _ptr(X), _ptr(tg), _ptr(tp), _ptr(un), bs, T, V, int(mode),
+                             _ptr(acc), _ptr(out), _ptr(prob))
+    if st != OK:
+        raise OracleError(f"oracle_verify failed ({st})")
+    return acc, out, prob

@@ -320,3 +320,186 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* ======================================================================================== */
+/* Verification of a drafted block against the target model's logits.                      */
+/*                                                                                          */
+/* The pages: probabilistic drafting stores the bf16 logits it sampled from in draft_logits  */
+/* so that rejection sampling works on exactly that distribution (vLLM PR #62958, Details),  */
+/* and block verification keeps the target distribution across draft steps (vLLM PR #64476, */
+/* Validation). They give neither algorithm; these are the published ones:                   */
+/*  - mode 0, token verification: speculative sampling, Leviathan, Kalman, Matias, "Fast      */
+/*    Inference from Transformers via Speculative Decoding", ICML 2023, Algorithm 1 (and      */
+/*    Chen et al., "Accelerating Large Language Model Decoding with Speculative Sampling",    */
+/*    2023, Algorithm 2): draft token i is kept with probability min(1, p_i(x_i) / q_i(x_i)) */
+/*    until the first rejection, which is replaced by a draw from the normalised             */
+/*    max(p_i - q_i, 0); if every draft token is kept, one more token is drawn from p_T.     */
+/*  - mode 1, block verification: Sun, Mendlovic, Leviathan, Aharoni, Beirami, Ro, Suresh,   */
+/*    "Block Verification Accelerates Speculative Decoding", ICLR 2025, Algorithm 2: with    */
+/*    weights w_0 = 1, w_i = min(w_{i-1} p_{i-1}(x_{i-1}) / q_{i-1}(x_{i-1}), 1), and        */
+/*    h_i = R_i / (R_i + 1 - w_i), R_i = sum_x max(w_i p_i(x) - q_i(x), 0) for i < T,         */
+/*    h_T = w_T, the kept length is the largest i with eta_i <= h_i (0 if none); the next     */
+/*    token is drawn from p_T if all T are kept, else from the normalised                    */
+/*    max(w_tau p_tau - q_tau, 0).                                                           */
+/* Rows (0-based): q_t = softmax(bf16 draft_logits[b,t] / temp) is the distribution draft    */
+/* token t was drawn from (the walk's Gumbel-max over the stored bf16 row samples exactly    */
+/* this), p_t = softmax(target_logits[b,t] / temp), t = 0..T (row T scores the position      */
+/* after the block).                                                                         */
+/* Readings where the pages are silent:                                                      */
+/*  - one temperature per request divides both the draft and the target logits;            */
+/*  - the random draws are inputs: uniforms[b, i] (i < T) is the acceptance draw of step i   */
+/*    (eta_{i+1} in the block paper's 1-based notation), uniforms[b, T] draws the final      */
+/*    token by inverting the CDF of its (unnormalised) distribution r in vocabulary order:   */
+/*    the first y with r(0) + ... + r(y) > u * sum(r); a draw is kept when u <= its          */
+/*    acceptance probability;                                                                */
+/*  - ratios with q = 0: p / q is +inf (min gives 1) when p > 0, and 0 when p = 0; a weight  */
+/*    of 0 stays 0; h_i = 1 where R_i + 1 - w_i = 0 (then R_i = 0 and w_i = 1, and the       */
+/*    algorithm's outputs do not depend on h_i);                                             */
+/*  - a final distribution of total mass 0 (a rejection where p_tau <= w q_tau everywhere, */
+/*    reachable only through rounding) is replaced by p_tau.                                 */
+/* Everything is fp64: z = logit / temp, probabilities exp(z - max z) / sum exp(z - max z).  */
+/* ======================================================================================== */
+static void oracle_probs_row(const double* z, int64_t V, double* prob) {
+    double m = -INFINITY;
+    for (int64_t x = 0; x < V; ++x)
+        if (z[x] > m) m = z[x];
+    double sum = 0.0;
+    for (int64_t x = 0; x < V; ++x) {
+        prob[x] = (m == -INFINITY) ? 0.0 : exp(z[x] - m);
+        sum += prob[x];
+    }
+    for (int64_t x = 0; x < V; ++x) prob[x] = sum > 0.0 ? prob[x] / sum : 0.0;
+}
+
+/* p / q for the ratio of a drafted token (q = 0: +inf when p > 0, else 0) */
+static double oracle_ratio(double p, double q) {
+    if (q > 0.0) return p / q;
+    return p > 0.0 ? INFINITY : 0.0;
+}
+
+/* Index drawn from the unnormalised distribution r by inverse CDF with uniform u. */
+static int64_t oracle_inverse_cdf(const double* r, int64_t V, double u) {
+    double mass = 0.0;
+    for (int64_t x = 0; x < V; ++x) mass += r[x];
+    const double target = u * mass;
+    double c = 0.0;
+    int64_t last = -1;
+    for (int64_t x = 0; x < V; ++x) {
+        c += r[x];
+        if (r[x] > 0.0) last = x;
+        if (c > target) return x;
+    }
+    return last;
+}
+
+int oracle_verify(const uint16_t* draft_logits, const int32_t* draft_tokens,
+                  const float* target_logits, const float* temps, const float* uniforms,
+                  int64_t bs, int64_t T, int64_t V, int mode, int32_t* accepted,
+                  int32_t* out_tokens, double* accept_prob) {
+    if (!draft_logits || !draft_tokens || !target_logits || !temps || !uniforms || !accepted ||
+        !out_tokens || bs < 1 || T < 1 || V < 1 || (mode != 0 && mode != 1))
+        return ORACLE_ERR_ARG;
+    double* z = (double*)malloc((size_t)V * sizeof(double));
+    double* P = (double*)malloc((size_t)(T + 1) * (size_t)V * sizeof(double));
+    double* Q = (double*)malloc((size_t)T * (size_t)V * sizeof(double));
+    double* r = (double*)malloc((size_t)V * sizeof(double));
+    double* w = (double*)malloc((size_t)(T + 1) * sizeof(double));
+    double* h = (double*)malloc((size_t)(T + 1) * sizeof(double));
+    int status = ORACLE_OK;
+    if (!z || !P || !Q || !r || !w || !h) status = ORACLE_ERR_ARG;
+
+    for (int64_t b = 0; b < bs && status == ORACLE_OK; ++b) {
+        const double temp = (double)temps[b];
+        const int32_t* X = draft_tokens + b * T;
+        const float* u = uniforms + b * (T + 1);
+        if (!(temp > 0.0) || !isfinite(temp)) { status = ORACLE_ERR_ARG; break; }
+        for (int64_t t = 0; t < T; ++t)
+            if (X[t] < 0 || X[t] >= V) status = ORACLE_ERR_ARG;
+        if (status != ORACLE_OK) break;
+        /* the rows' probabilities */
+        for (int64_t t = 0; t <= T && status == ORACLE_OK; ++t) {
+            const float* row = target_logits + (b * (T + 1) + t) * V;
+            for (int64_t x = 0; x < V; ++x) {
+                if (isnan(row[x])) status = ORACLE_ERR_ARG;
+                z[x] = (double)row[x] / temp;
+            }
+            oracle_probs_row(z, V, P + t * V);
+        }
+        for (int64_t t = 0; t < T && status == ORACLE_OK; ++t) {
+            const uint16_t* row = draft_logits + (b * T + t) * V;
+            for (int64_t x = 0; x < V; ++x) {
+                const float f = oracle_bf16_to_f32(row[x]);
+                if (isnan(f)) status = ORACLE_ERR_ARG;
+                z[x] = (double)f / temp;
+            }
+            oracle_probs_row(z, V, Q + t * V);
+        }
+        if (status != ORACLE_OK) break;
+
+        int64_t tau;
+        double weight;
+        if (mode == 0) {
+            /* token verification: keep while u_i <= min(1, p_i(x_i) / q_i(x_i)) */
+            tau = T;
+            for (int64_t i = 0; i < T; ++i) {
+                double a = oracle_ratio(P[i * V + X[i]], Q[i * V + X[i]]);
+                if (a > 1.0) a = 1.0;
+                h[i + 1] = a;
+                if (tau == T && !((double)u[i] <= a)) tau = i;
+            }
+            weight = 1.0;
+        } else {
+            /* block verification */
+            w[0] = 1.0;
+            for (int64_t i = 1; i <= T; ++i) {
+                double wi = 0.0;
+                if (w[i - 1] > 0.0) {
+                    wi = w[i - 1] * oracle_ratio(P[(i - 1) * V + X[i - 1]], Q[(i - 1) * V + X[i - 1]]);
+                    if (wi > 1.0) wi = 1.0;
+                }
+                w[i] = wi;
+            }
+            for (int64_t i = 1; i <= T; ++i) {
+                if (i < T) {
+                    double R = 0.0;
+                    for (int64_t x = 0; x < V; ++x) {
+                        const double d = w[i] * P[i * V + x] - Q[i * V + x];
+                        if (d > 0.0) R += d;
+                    }
+                    const double den = R + 1.0 - w[i];
+                    h[i] = den > 0.0 ? R / den : 1.0;
+                } else {
+                    h[i] = w[T];
+                }
+            }
+            tau = 0;
+            for (int64_t i = 1; i <= T; ++i)
+                if ((double)u[i - 1] <= h[i]) tau = i;
+            weight = w[tau];
+        }
+        /* the token after the kept prefix */
+        const double* Pt = P + tau * V;
+        double mass = 0.0;
+        for (int64_t x = 0; x < V; ++x) {
+            r[x] = (tau == T) ? Pt[x] : weight * Pt[x] - Q[tau * V + x];
+            if (r[x] < 0.0) r[x] = 0.0;
+            mass += r[x];
+        }
+        if (!(mass > 0.0))
+            for (int64_t x = 0; x < V; ++x) r[x] = Pt[x];
+        const int64_t y = oracle_inverse_cdf(r, V, (double)u[T]);
+
+        accepted[b] = (int32_t)tau;
+        for (int64_t i = 0; i <= T; ++i)
+            out_tokens[b * (T + 1) + i] = i < tau ? X[i] : (i == tau ? (int32_t)y : -1);
+        if (accept_prob)
+            for (int64_t i = 0; i < T; ++i) accept_prob[b * T + i] = h[i + 1];
+    }
+    free(z);
+    free(P);
+    free(Q);
+    free(r);
+    free(w);
+    free(h);
+    return status;
+}
