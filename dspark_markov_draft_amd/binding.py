@@ -80,6 +80,10 @@ def lib():
                                        vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dspark_walk_plan_for.argtypes = [ctypes.c_int32, i64, i64, i64, i64,
                                            ctypes.POINTER(WalkPlan)]
+        L.dspark_verify_workspace_bytes.argtypes = [i64, i64, i64]
+        L.dspark_verify_workspace_bytes.restype = ctypes.c_size_t
+        L.dspark_verify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp,
+                                    ctypes.c_size_t, vp]
         L.dspark_workspace_status.argtypes = [vp, vp]
         L.dspark_philox_words.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i64, i64, vp, vp]
         L.dspark_debug_set.argtypes = [i32, i64]
@@ -88,7 +92,8 @@ def lib():
         for name in ["dspark_quantize_w2", "dspark_walk_plan_query", "dspark_walk_plan_for",
                      "dspark_walk_greedy", "dspark_walk_greedy_noalloc",
                      "dspark_walk_sample", "dspark_walk_topk", "dspark_workspace_status",
-                     "dspark_philox_words", "dspark_debug_set", "dspark_kernel_times"]:
+                     "dspark_philox_words", "dspark_debug_set", "dspark_kernel_times",
+                     "dspark_verify"]:
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -319,6 +324,51 @@ def dspark_walk_topk(q, s, w1, base, start, k, workspace, sample=False, seeds=No
                                   _p(draft_logits), _p(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return draft_tokens, draft_logits
+
+
+VERIFY_TOKEN, VERIFY_BLOCK = 0, 1
+
+
+def dspark_verify_workspace_bytes(bs: int, T: int, V: int) -> int:
+    return int(lib().dspark_verify_workspace_bytes(bs, T, V))
+
+
+def dspark_verify(draft_logits, draft_tokens, target_logits, temperature, uniforms, workspace,
+                  mode=VERIFY_TOKEN, accepted=None, out_tokens=None, accept_prob=None,
+                  stream=None):
+    """Verification of drafted blocks (token or block verification). draft_logits bf16
+    [bs, T, V]; draft_tokens int32 [bs, T]; target_logits fp32 [bs, T + 1, V]; temperature fp32
+    [bs]; uniforms fp32 [bs, T + 1]. Returns (accepted int32 [bs], out_tokens int32 [bs, T + 1],
+    accept_prob fp32 [bs, T] or None)."""
+    _expect(draft_logits, "draft_logits", torch.bfloat16, None)
+    if draft_logits.dim() != 3:
+        raise ValueError(f"draft_logits must be [bs, T, V], got {tuple(draft_logits.shape)}")
+    bs, T, V = draft_logits.shape
+    dev = draft_logits.device
+    if accepted is None:
+        accepted = torch.empty(bs, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((bs, T + 1), dtype=torch.int32, device=dev)
+    _expect(draft_tokens, "draft_tokens", torch.int32, (bs, T))
+    _expect(target_logits, "target_logits", torch.float32, (bs, T + 1, V))
+    _expect(temperature, "temperature", torch.float32, (bs,))
+    _expect(uniforms, "uniforms", torch.float32, (bs, T + 1))
+    _expect(accepted, "accepted", torch.int32, (bs,))
+    _expect(out_tokens, "out_tokens", torch.int32, (bs, T + 1))
+    _expect(accept_prob, "accept_prob", torch.float32, (bs, T), optional=True)
+    if not torch.is_tensor(workspace) or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D tensor")
+    if mode not in (VERIFY_TOKEN, VERIFY_BLOCK):
+        raise ValueError("mode must be VERIFY_TOKEN or VERIFY_BLOCK")
+    _same_device(draft_logits=draft_logits, draft_tokens=draft_tokens,
+                 target_logits=target_logits, temperature=temperature, uniforms=uniforms,
+                 accepted=accepted, out_tokens=out_tokens, accept_prob=accept_prob,
+                 workspace=workspace)
+    _check(lib().dspark_verify(_p(draft_logits), _p(draft_tokens), _p(target_logits),
+                               _p(temperature), _p(uniforms), bs, T, V, int(mode), _p(accepted),
+                               _p(out_tokens), _p(accept_prob), _p(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return accepted, out_tokens, accept_prob
 
 
 def dspark_workspace_status(workspace, stream=None) -> int:

@@ -352,6 +352,50 @@ int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, 
     return launch_topk_walk(a, static_cast<hipStream_t>(stream));
 }
 
+size_t dspark_verify_workspace_bytes(int64_t bs, int64_t T, int64_t V) {
+    if (bs < 1 || T < 1 || V < 1) return WS_ALIGN;
+    if (bs > DSPARK_MAX_BS) bs = DSPARK_MAX_BS;
+    if (T > DSPARK_MAX_STEPS) T = DSPARK_MAX_STEPS;
+    if (V > DSPARK_MAX_V) V = DSPARK_MAX_V;
+    return verify_workspace_bytes(bs, T, V);
+}
+
+int dspark_verify(const uint16_t* draft_logits, const int32_t* draft_tokens,
+                  const float* target_logits, const float* temperature, const float* uniforms,
+                  int64_t bs, int64_t T, int64_t V, int mode, int32_t* accepted,
+                  int32_t* out_tokens, float* accept_prob, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    if (bs < 1 || T < 1 || V < 1) return DSPARK_ERR_INVALID_ARG;
+    if (bs > DSPARK_MAX_BS || T > DSPARK_MAX_STEPS || V > DSPARK_MAX_V) return DSPARK_ERR_UNSUPPORTED;
+    if (mode != DSPARK_VERIFY_TOKEN && mode != DSPARK_VERIFY_BLOCK) return DSPARK_ERR_INVALID_ARG;
+    if (!draft_logits || !draft_tokens || !target_logits || !temperature || !uniforms ||
+        !accepted || !out_tokens || !workspace)
+        return DSPARK_ERR_INVALID_ARG;
+    if (((uintptr_t)draft_logits & 1u) || !aligned4(draft_tokens) || !aligned4(target_logits) ||
+        !aligned4(temperature) || !aligned4(uniforms) || !aligned4(accepted) ||
+        !aligned4(out_tokens) || (accept_prob && !aligned4(accept_prob)) || !aligned16(workspace))
+        return DSPARK_ERR_INVALID_ARG;
+    if (workspace_bytes < dspark_verify_workspace_bytes(bs, T, V)) return DSPARK_ERR_WORKSPACE;
+    DeviceInfo dev;
+    const int st = current_device_info(&dev);
+    if (st != DSPARK_OK) return st;
+    VerifyLaunch a;
+    a.draft_logits = draft_logits;
+    a.draft_tokens = draft_tokens;
+    a.target_logits = target_logits;
+    a.temperature = temperature;
+    a.uniforms = uniforms;
+    a.accepted = accepted;
+    a.out_tokens = out_tokens;
+    a.accept_prob = accept_prob;
+    a.workspace = workspace;
+    a.bs = (int)bs;
+    a.T = (int)T;
+    a.V = (int)V;
+    a.mode = mode;
+    return launch_verify(a, static_cast<hipStream_t>(stream));
+}
+
 int dspark_workspace_status(void* workspace, void* stream) {
     if (!workspace || !aligned16(workspace)) return DSPARK_ERR_INVALID_ARG;
     DeviceInfo dev;

@@ -83,6 +83,25 @@ struct TopkLaunch {
 };
 int launch_topk_walk(const TopkLaunch& a, hipStream_t stream);
 
+// Verification of drafted blocks (csrc/verify.hip). Workspace: the error word at WS_ERR, then
+// one state slot per request from VERIFY_WS_STATE, then per-chunk partial results.
+constexpr size_t VERIFY_WS_STATE = 256;
+constexpr size_t VERIFY_STATE_BYTES = 512;
+struct VerifyLaunch {
+    const uint16_t* draft_logits;
+    const int32_t* draft_tokens;
+    const float* target_logits;
+    const float* temperature;
+    const float* uniforms;
+    int32_t* accepted;
+    int32_t* out_tokens;
+    float* accept_prob;
+    void* workspace;
+    int bs, T, V, mode;
+};
+size_t verify_workspace_bytes(int64_t bs, int64_t T, int64_t V);
+int launch_verify(const VerifyLaunch& a, hipStream_t stream);
+
 // Walk kernel launch: plain, or with dispatch-recorded events while kernel timing is on.
 hipError_t launch_walk_kernel(const void* fn, dim3 grid, dim3 block, void** args, size_t lds,
                               hipStream_t stream);

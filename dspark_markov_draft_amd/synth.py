@@ -103,3 +103,37 @@ def make_inputs(case: Case, bs: Optional[int] = None, V: Optional[int] = None,
 def seeds_as_int64(seeds: np.ndarray) -> torch.Tensor:
     """uint64 request seeds as a same-bits int64 tensor (torch has no uint64 arithmetic)."""
     return torch.from_numpy(np.ascontiguousarray(seeds, dtype=np.uint64).view(np.int64))
+
+
+@dataclass
+class VerifyInputs:
+    draft_lb: torch.Tensor       # [bs, T, V] bf16 (CPU)
+    draft_tokens: torch.Tensor   # [bs, T] int32
+    target: torch.Tensor         # [bs, T + 1, V] fp32
+    temperature: torch.Tensor    # [bs] fp32
+    uniforms: torch.Tensor       # [bs, T + 1] fp32 in (0, 1)
+
+
+def make_verify_inputs(bs: int, T: int, V: int, seed: int, draft_std: float = 3.0,
+                       target_noise: float = 1.0, temperature: Optional[float] = 1.0
+                       ) -> VerifyInputs:
+    """Seeded inputs of a block verification, shaped like a probabilistic walk's output: draft
+    logits ~ N(0, draft_std^2) rounded to bf16 (the stored rows); target logits for rows
+    0..T-1 = those draft logits + N(0, target_noise^2) (a target model close to the draft),
+    row T ~ N(0, draft_std^2); draft tokens uniform on [0, V) (so that steps are both kept and
+    rejected); uniforms uniform on [2^-24, 1); temperature fixed, or (None) uniform on
+    [0.5, 1.5] per request. Each tensor has its own generator seeded seed * 10 + tensor id."""
+    def gen(i):
+        return torch.Generator().manual_seed(seed * 10 + i)
+    draft = torch.randn(bs, T, V, generator=gen(0)) * draft_std
+    lb = draft.to(torch.bfloat16)
+    target = torch.empty(bs, T + 1, V)
+    target[:, :T] = lb.float() + torch.randn(bs, T, V, generator=gen(1)) * target_noise
+    target[:, T] = torch.randn(bs, V, generator=gen(2)) * draft_std
+    tokens = torch.randint(0, V, (bs, T), generator=gen(3), dtype=torch.int64).to(torch.int32)
+    u = torch.rand(bs, T + 1, generator=gen(4)).clamp_min(2.0 ** -24)
+    if temperature is None:
+        temps = 0.5 + torch.rand(bs, generator=gen(5))
+    else:
+        temps = torch.full((bs,), float(temperature))
+    return VerifyInputs(lb, tokens, target, temps.float(), u.float())

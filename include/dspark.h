@@ -197,6 +197,49 @@ int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, 
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Verification of drafted blocks against the target model, on the stored bf16 draft rows
+ * (vLLM PR #62958, Details: rejection sampling works on exactly the distribution the draft
+ * sampled from; vLLM PR #64476, Validation: block verification keeps the target distribution).
+ * The pages give no algorithm; the two modes are published ones:
+ *   DSPARK_VERIFY_TOKEN: speculative sampling (Leviathan, Kalman, Matias, ICML 2023,
+ *     Algorithm 1): draft token t is kept while uniforms[b, t] <= min(1, p_t(x_t) / q_t(x_t));
+ *     the first rejected step is replaced by a draw from the normalised max(p_t - q_t, 0).
+ *   DSPARK_VERIFY_BLOCK: block verification (Sun et al., "Block Verification Accelerates
+ *     Speculative Decoding", ICLR 2025, Algorithm 2): weights w_0 = 1,
+ *     w_t = min(w_{t-1} p_{t-1}(x_{t-1}) / q_{t-1}(x_{t-1}), 1); h_t = R_t / (R_t + 1 - w_t)
+ *     with R_t = sum_x max(w_t p_t(x) - q_t(x), 0) for t < T, h_T = w_T; the kept length is
+ *     the largest t with uniforms[b, t - 1] <= h_t (0 if none), and the next token is drawn
+ *     from max(w_tau p_tau - q_tau, 0).
+ * With every draft token kept, the next token is drawn from p_T. q_t = softmax(draft row t /
+ * temperature[b]) and p_t = softmax(target row t / temperature[b]). The next token is the
+ * inverse-CDF draw with u = uniforms[b, T]: the first vocabulary index whose running mass
+ * exceeds u times the distribution's total (a total of 0, reachable only through rounding,
+ * falls back to p_tau).
+ *   draft_logits  [bs, T, V] bf16 bits (dspark_walk_sample / dspark_walk_topk output)
+ *   draft_tokens  [bs, T] int32
+ *   target_logits [bs, T + 1, V] fp32: row t scores position t of the block, row T the one after
+ *   temperature   [bs] fp32, finite and > 0 (the draft's and the target's)
+ *   uniforms      [bs, T + 1] fp32 in (0, 1): the caller's random draws
+ *   accepted      [bs] int32 out: kept length tau in 0..T
+ *   out_tokens    [bs, T + 1] int32 out: the kept draft tokens, the next token, then -1
+ *   accept_prob   [bs, T] fp32 out or NULL: min(1, p_t/q_t) (token) or h_{t+1} (block)
+ *   workspace of dspark_verify_workspace_bytes(bs, T, V) bytes, zeroed once (left zeroed; it may
+ *     be the walk's workspace if large enough for both)
+ * Preconditions (not checked): every row holds a finite entry and no NaN or +inf; tokens lie in
+ * [0, V) (others are read as 0 and recorded as DSPARK_ERR_INVALID_ARG in the workspace's error
+ * word). Same envelope as the walks: bs <= 64, T <= 16, V <= 270336.
+ */
+enum dspark_verify_mode { DSPARK_VERIFY_TOKEN = 0, DSPARK_VERIFY_BLOCK = 1 };
+
+size_t dspark_verify_workspace_bytes(int64_t bs, int64_t T, int64_t V);
+
+int dspark_verify(const uint16_t* draft_logits, const int32_t* draft_tokens,
+                  const float* target_logits, const float* temperature, const float* uniforms,
+                  int64_t bs, int64_t T, int64_t V, int mode, int32_t* accepted,
+                  int32_t* out_tokens, float* accept_prob, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
  * Error word of a walk workspace: synchronises `stream`, returns DSPARK_OK or the error the
  * last walk recorded, and clears it. Diagnostic call, not for hot loops.
  *   DSPARK_ERR_TIMEOUT: a grid-wide wait ran past its time bound (10 ms by default): the walk's

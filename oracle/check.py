@@ -146,3 +146,105 @@ def check_walk(q, s, w1, base, start, tokens, *, sample=False, seeds=None, temps
                     rep.near_ties.append((b, t, tok, got, gap))
             prev = got
     return rep
+
+
+# ----------------------------------------------------------------------------------------------
+# verification of drafted blocks
+# ----------------------------------------------------------------------------------------------
+TOL_PROB = 1e-4     # acceptance probabilities (fp32 softmax and sums against fp64)
+TOL_U = 1e-5        # inverse-CDF draws: the next token may be any the oracle draws for u +- this
+
+
+@dataclass
+class VerifyReport:
+    requests: int = 0
+    max_prob_err: float = 0.0
+    kept_total: int = 0
+    near_ties: List[tuple] = field(default_factory=list)     # (b, what)
+    failures: List[str] = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> str:
+        return (f"requests={self.requests} kept={self.kept_total} "
+                f"max|dprob|={self.max_prob_err:.3g} near-ties={len(self.near_ties)} "
+                f"failures={len(self.failures)}" +
+                ("" if self.ok else "\n  " + "\n  ".join(self.failures[:10])))
+
+
+def _implied_decisions(mode, tau, T):
+    """Per step i (0-based), the accept/reject decision a verifier must have taken to end with
+    kept length tau (None where the outcome does not depend on it)."""
+    d = [None] * T
+    if mode == 0:
+        for i in range(T):
+            if i < tau:
+                d[i] = True
+            elif i == tau:
+                d[i] = False
+    else:       # block: tau = largest i with u_{i-1} <= h_i
+        for i in range(1, T + 1):
+            if i == tau:
+                d[i - 1] = True
+            elif i > tau:
+                d[i - 1] = False
+    return d
+
+
+def check_verify(lb, X, tg, temps, u, mode, acc, out, prob=None, tol_prob=TOL_PROB,
+                 tol_u=TOL_U) -> VerifyReport:
+    """Compare a verification's outputs (acc [bs], out [bs, T + 1], prob [bs, T] or None) with
+    the oracle on the same inputs. The kept length must equal the oracle's unless every step
+    whose decision differs has its uniform within tol_prob of the oracle's acceptance
+    probability (a near tie; then the next token is not compared). The next token must lie
+    among the oracle's draws for uniforms in [u - tol_u, u + tol_u] (the draw is monotone in
+    u, so between the draws at the two ends)."""
+    from . import verify as oracle_verify
+    lb = np.asarray(lb, np.uint16)
+    u = np.asarray(u, np.float32)
+    bs, T, V = lb.shape
+    acc_o, out_o, prob_o = oracle_verify(lb, X, tg, temps, u, mode)
+    lo_u, hi_u = u.copy(), u.copy()
+    lo_u[:, T] = np.maximum(u[:, T] - np.float32(tol_u), np.float32(2.0 ** -24))
+    hi_u[:, T] = np.minimum(u[:, T] + np.float32(tol_u), np.float32(1.0 - 2.0 ** -24))
+    _, out_lo, _ = oracle_verify(lb, X, tg, temps, lo_u, mode)
+    _, out_hi, _ = oracle_verify(lb, X, tg, temps, hi_u, mode)
+    rep = VerifyReport(requests=bs)
+    if prob is not None:
+        err = np.abs(np.asarray(prob, np.float64) - prob_o)
+        rep.max_prob_err = float(err.max())
+        if not rep.max_prob_err <= tol_prob:
+            b, t = np.unravel_index(int(err.argmax()), err.shape)
+            rep.failures.append(f"b={b} t={t}: accept prob {prob[b, t]} vs oracle {prob_o[b, t]}")
+    for b in range(bs):
+        tau = int(acc[b])
+        rep.kept_total += max(tau, 0)
+        if not 0 <= tau <= T:
+            rep.failures.append(f"b={b}: kept length {tau} out of range")
+            continue
+        if not np.array_equal(out[b, :tau], X[b, :tau]) or (out[b, tau + 1:] != -1).any():
+            rep.failures.append(f"b={b}: output {out[b].tolist()} is not the kept prefix, a token, -1s")
+            continue
+        if not 0 <= int(out[b, tau]) < V:
+            rep.failures.append(f"b={b}: next token {int(out[b, tau])} out of range")
+            continue
+        if tau != int(acc_o[b]):
+            want = _implied_decisions(mode, tau, T)
+            orc = [bool(u[b, i] <= prob_o[b, i]) for i in range(T)]
+            bad = [i for i in range(T) if want[i] is not None and want[i] != orc[i] and
+                   not abs(float(u[b, i]) - float(prob_o[b, i])) <= tol_prob]
+            if bad:
+                rep.failures.append(f"b={b}: kept {tau} vs oracle {int(acc_o[b])} (steps {bad})")
+            else:
+                rep.near_ties.append((b, f"kept {tau} vs {int(acc_o[b])}"))
+            continue
+        y, y_lo, y_hi = int(out[b, tau]), int(out_lo[b, tau]), int(out_hi[b, tau])
+        if y != int(out_o[b, tau]):
+            if min(y_lo, y_hi) <= y <= max(y_lo, y_hi):
+                rep.near_ties.append((b, f"next token {y} vs {int(out_o[b, tau])}"))
+            else:
+                rep.failures.append(f"b={b}: next token {y} vs oracle {int(out_o[b, tau])} "
+                                    f"(draws for u +- {tol_u}: {y_lo}..{y_hi})")
+    return rep

@@ -177,6 +177,44 @@ def test_noalloc_validation(kw, code):
     assert _noalloc(**kw) == code
 
 
+def _verify(**kw):
+    a = dict(lb=FAKE, X=FAKE, tg=FAKE, temp=FAKE, u=FAKE, bs=4, T=7, V=151936, mode=0,
+             acc=FAKE, out=FAKE, prob=None, ws=FAKE, wsb=1 << 24, stream=None)
+    a.update(kw)
+    return B.lib().dspark_verify(a["lb"], a["X"], a["tg"], a["temp"], a["u"], a["bs"], a["T"],
+                                 a["V"], a["mode"], a["acc"], a["out"], a["prob"], a["ws"],
+                                 a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lb=None), B.ERR_INVALID_ARG),
+    (dict(tg=None), B.ERR_INVALID_ARG),
+    (dict(u=None), B.ERR_INVALID_ARG),
+    (dict(out=None), B.ERR_INVALID_ARG),
+    (dict(ws=None), B.ERR_INVALID_ARG),
+    (dict(lb=FAKE + 1), B.ERR_INVALID_ARG),
+    (dict(tg=FAKE + 2), B.ERR_INVALID_ARG),
+    (dict(prob=FAKE + 2), B.ERR_INVALID_ARG),
+    (dict(ws=FAKE + 8), B.ERR_INVALID_ARG),
+    (dict(mode=2), B.ERR_INVALID_ARG),
+    (dict(bs=0), B.ERR_INVALID_ARG),
+    (dict(T=17), B.ERR_UNSUPPORTED),
+    (dict(bs=65), B.ERR_UNSUPPORTED),
+    (dict(V=270337), B.ERR_UNSUPPORTED),
+    (dict(wsb=1000), B.ERR_WORKSPACE),
+])
+def test_verify_validation(kw, code):
+    assert _verify(**kw) == code
+
+
+def test_verify_workspace_bytes():
+    n = B.lib().dspark_verify_workspace_bytes
+    assert n(64, 7, 151936) % 256 == 0
+    assert n(64, 7, 151936) >= 64 * 8 * 75 * 16          # chunk statistics at the smallest chunk
+    assert n(1, 1, 1) <= n(64, 16, 270336) < 8 << 20
+    assert n(64, 16, 270336) == n(65, 17, 300000)       # clamped to the envelope
+
+
 def _sample(**kw):
     a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=1, T=7, V=151936,
              rank=256, seeds=FAKE, pos=None, temp=FAKE, tokens=FAKE, lb=FAKE, ws=FAKE,
@@ -269,6 +307,7 @@ def test_no_device_without_gpu():
     assert _greedy() == B.ERR_NO_DEVICE
     assert _sample() == B.ERR_NO_DEVICE
     assert _noalloc() == B.ERR_NO_DEVICE
+    assert _verify() == B.ERR_NO_DEVICE
     assert _noalloc(bs=64, T=16, V=270336) == B.ERR_NO_DEVICE
     p = B.WalkPlan()
     assert B.lib().dspark_walk_plan_query(1, 7, 151936, ctypes.byref(p)) == B.ERR_NO_DEVICE

@@ -3,6 +3,7 @@ torch's bf16 rounding, and a planted token error is caught."""
 import numpy as np
 import torch
 
+import oracle
 from oracle.check import _bf16_interval, _bf16_within_tol, bf16_bits_to_f32, check_walk
 
 
@@ -49,3 +50,38 @@ def test_checker_catches_wrong_token(orc):
     off = logits.copy()
     off[0, 2, 17] += 3e-3
     assert not check_walk(q, s, w1, base, start, tokens, logits=off).ok
+
+
+def test_verify_checker_catches_planted_mistakes():
+    """The verification checker accepts the oracle's own outputs and rejects a wrong next token,
+    a wrong kept length away from any near tie, a kept prefix that is not the draft, and an
+    acceptance probability off by more than its tolerance."""
+    import torch
+    from oracle.check import check_verify
+    from dspark_markov_draft_amd.synth import make_verify_inputs
+    v = make_verify_inputs(16, 4, 700, 5, temperature=None)
+    lb = v.draft_lb.view(torch.int16).numpy().view(np.uint16)
+    args = (lb, v.draft_tokens.numpy(), v.target.numpy(), v.temperature.numpy(),
+            v.uniforms.numpy())
+    for mode in (0, 1):
+        acc, out, prob = oracle.verify(*args, mode)
+        prob = prob.astype(np.float32)
+        assert check_verify(*args, mode, acc, out, prob).ok
+        b = int(np.argmax(acc < 4))                      # a request with a drawn next token
+        bad = out.copy(); bad[b, acc[b]] = (bad[b, acc[b]] + 7) % 700
+        assert not check_verify(*args, mode, acc, bad, prob).ok
+        u = v.uniforms.numpy()
+        far = [i for i in range(16) if acc[i] < 4 and
+               (np.abs(u[i, :4] - oracle.verify(*args, mode)[2][i]) > 1e-2).all()]
+        i = far[0]
+        acc2, out2 = acc.copy(), out.copy()
+        acc2[i] += 1
+        out2[i, :acc2[i]] = args[1][i, :acc2[i]]
+        out2[i, acc2[i]] = 0
+        out2[i, acc2[i] + 1:] = -1
+        assert not check_verify(*args, mode, acc2, out2, prob).ok
+        bad = out.copy(); bad[b, 0] = (bad[b, 0] + 1) % 700 if acc[b] > 0 else bad[b, 0]
+        if acc[b] > 0:
+            assert not check_verify(*args, mode, acc, bad, prob).ok
+        p2 = prob.copy(); p2[3, 1] += 5e-4
+        assert not check_verify(*args, mode, acc, out, p2).ok
