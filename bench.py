@@ -12,12 +12,26 @@ call; `value` is the median. The roofline figures divide the algorithmic bytes b
 duration of the kernel alone, taken in a second cold pass from events that the kernel's own
 dispatch records (hipExtLaunchKernel), so launch queueing is not charged to the kernel. Also
 reported: the same after a 512 MiB *write* (caches full of dirty lines, whose write-back the
-walk then pays), a warm back-to-back rate, and a sweep over the other shapes of that table.
+walk then pays), a warm back-to-back rate, and a sweep over the other shapes of that table and
+over the verification of a drafted block (token and block verification) at the batched shape.
 
-`w2_roofline` is the bound on W2 traffic alone: R_W2 = max((B_W2 + (T-1) B_str) / HBM peak,
-T B_res / LDS peak), with B_res and B_str the W2 bytes the walk keeps on chip and re-reads from
-memory every step (the library's plan), B_W2 = V x 256 read once; `frac` = R_W2 / kernel time.
-For the top-k walk the W2 traffic is the gathered candidate rows, bs T k 256 bytes, at HBM peak.
+Bounds reported beside the measured time (`bounds`):
+  * `w2_roofline`: R_W2 = max((B_W2 + (T-1) B_str) / HBM peak, T B_res / LDS peak), with B_res
+    and B_str the W2 bytes the walk keeps on chip and re-reads every step (the library's plan),
+    B_W2 = V x 256 read once; `frac` = R_W2 / kernel time. For the top-k walk the W2 traffic is
+    the gathered candidate rows, bs T k 256 bytes, at HBM peak;
+  * R_full: every algorithmic byte of the call at HBM peak;
+  * F_ALU: bs T V 256 int8 multiply-adds at the full v_dot4 rate (157.3 T/s), F_MFMA at the
+    dense int8 matrix-core rate (2.5 P/s);
+  * `stamps`: an instrumented build of the same kernel records the device's 100 MHz clock per
+    workgroup at each phase of each step (cold calls): the median W2 fill, per step the W1
+    gather, the slice dot products + argmax, the key store, and the wait from a workgroup's own
+    key store until it holds the step's token; along the critical path, the time from the last
+    workgroup's key store until every workgroup holds the token; the barrier stall share is a
+    workgroup's summed waits over its whole span (median over workgroups);
+  * `exchange_floor`: per-step time of the same greedy kernel at V = 65536 (256 workgroups of
+    256 rows: a quarter of the headline's slice), from 16- and 7-step walks, beside the
+    headline's own per-step time.
 
 `roofline.traffic` is the HBM traffic per launch measured by the FETCH_SIZE / WRITE_SIZE
 counters (profiles/traffic.json, calibrated against a plain copy of known size); it is reported
@@ -38,14 +52,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import dspark_markov_draft_amd as dm  # noqa: E402
-from dspark_markov_draft_amd.synth import CASES, make_inputs, seeds_as_int64  # noqa: E402
+from dspark_markov_draft_amd.synth import (CASES, Case, make_inputs, make_verify_inputs,  # noqa: E402
+                                           seeds_as_int64)
 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
 KERNEL_NAMES = {1: "dense_walk_dot4_kernel", 2: "dense_walk_mfma_kernel", 3: "dense_walk_mfma1_kernel"}
 TOPK_KERNELS = "topk_select_kernel+topk_walk_kernel"
+VERIFY_KERNELS = "verify_*_kernel"
 # LDS read peak: 128 bytes per clock per compute unit x 256 units x 2.4 GHz
 LDS_PEAK_GBS = 128 * 256 * 2.4
+DOT4_MACS = 157.3e12          # int8 v_dot4 multiply-adds per second (256 CUs, 2.4 GHz)
+MFMA_I8_MACS = 2.5e15         # dense int8 matrix-core multiply-adds per second (5.0 POP/s)
+STAMPS_PER_WG = 82
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
 def w2_roofline(w, plan, kernel_us):
@@ -62,8 +85,16 @@ def w2_roofline(w, plan, kernel_us):
             "kernel_us": round(kernel_us, 3), "frac": round(r / kernel_us, 4)}
 
 
-def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+def bounds(w, kernel_us):
+    """R_full (all algorithmic bytes at HBM peak) and the ALU floors of a walk call, with the
+    fraction of each reached."""
+    r_full = w.algorithmic_bytes() / (HBM_PEAK_GBS * 1e3)
+    out = {"r_full_us": round(r_full, 3), "r_full_frac": round(r_full / kernel_us, 4)}
+    if isinstance(w, Walk):
+        macs = w.bs * w.T * (w.k if w.k else w.V) * 256
+        out["f_alu_us"] = round(macs / DOT4_MACS * 1e6, 3)
+        out["f_mfma_us"] = round(macs / MFMA_I8_MACS * 1e6, 3)
+    return out
 
 
 class Walk:
@@ -71,6 +102,7 @@ class Walk:
 
     def __init__(self, case, mode, dev):
         self.case, self.mode, self.dev = case, mode, dev
+        self.name = case.name
         inp = make_inputs(case)
         self.inp = inp
         self.w1 = inp.w1.to(dev)
@@ -118,6 +150,38 @@ class Walk:
         return n
 
 
+class Verify:
+    """Verification of drafted blocks (dspark_verify) on seeded inputs shaped like the
+    probabilistic walk's output at bs requests, T draft tokens, vocabulary V."""
+
+    def __init__(self, bs, T, V, mode, dev):
+        self.bs, self.T, self.V, self.k = bs, T, V, 0
+        self.mode = mode
+        self.name = f"verify_{mode}_v{V}_t{T}_bs{bs}"
+        v = make_verify_inputs(bs, T, V, seed=V + bs + T)
+        self.lb = v.draft_lb.to(dev)
+        self.tokens = v.draft_tokens.to(dev)
+        self.target = v.target.to(dev)
+        self.temps = v.temperature.to(dev)
+        self.u = v.uniforms.to(dev)
+        self.ws = torch.zeros(dm.dspark_verify_workspace_bytes(bs, T, V), dtype=torch.uint8,
+                              device=dev)
+        self.acc = torch.empty(bs, dtype=torch.int32, device=dev)
+        self.out = torch.empty((bs, T + 1), dtype=torch.int32, device=dev)
+        self.code = dm.VERIFY_TOKEN if mode == "token" else dm.VERIFY_BLOCK
+
+    def launch(self):
+        dm.dspark_verify(self.lb, self.tokens, self.target, self.temps, self.u, self.ws,
+                         mode=self.code, accepted=self.acc, out_tokens=self.out)
+
+    def algorithmic_bytes(self):
+        """One read of every target row (T + 1 per request, fp32) and draft row (bf16), the
+        tokens and uniforms; the outputs."""
+        bs, T, V = self.bs, self.T, self.V
+        return bs * (T + 1) * V * 4 + bs * T * V * 2 + bs * T * 4 + bs * (T + 1) * 4 + \
+            bs * (T + 2) * 4
+
+
 def _timed_calls(w, steps, flush_fn, stream):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -133,17 +197,18 @@ def _timed_calls(w, steps, flush_fn, stream):
 
 
 def kernel_times(w, steps, flush_fn):
-    """Dispatch-recorded durations of the walk's kernels alone (events written by each kernel's
+    """Dispatch-recorded durations of the call's kernels alone (events written by each kernel's
     own dispatch packet), same cold protocol as the call timing; summed per call (the top-k
-    walk runs two kernels)."""
+    walk runs two kernels, a verification four or six)."""
     from dspark_markov_draft_amd.binding import DEBUG_KERNEL_TIMING
-    dm.dspark_debug_set(DEBUG_KERNEL_TIMING, 4 * steps)
+    ring = min(4096, 8 * steps)
+    dm.dspark_debug_set(DEBUG_KERNEL_TIMING, ring)
     try:
         for i in range(steps):
             flush_fn(i)
             w.launch()
         torch.cuda.synchronize()
-        t = np.array(dm.dspark_kernel_times(4 * steps))
+        t = np.array(dm.dspark_kernel_times(ring))
         per_call = len(t) // steps
         t = t[:per_call * steps].reshape(steps, per_call)
         w.kernel_parts_us = [round(float(m), 2) for m in t.mean(axis=0)]
@@ -178,12 +243,101 @@ def time_walk(w, steps, warmup, flush, stream, dirty=False):
     return us, wall, warm_us, dirty_us, kus
 
 
+def stamp_split(w, flush, calls=5):
+    """Per-phase times of a dense walk from its instrumented build (bf16 W1 only): medians over
+    `calls` cold calls of the per-workgroup medians, in microseconds."""
+    from dspark_markov_draft_amd.binding import DEBUG_STAMPS
+    plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
+    nwg, T = plan["num_workgroups"], w.T
+    buf = torch.zeros(256 * STAMPS_PER_WG, dtype=torch.int64, device=w.dev)
+    sink = torch.empty(1, dtype=torch.float32, device=flush.device)
+    runs = []
+    dm.dspark_debug_set(DEBUG_STAMPS, buf.data_ptr())
+    try:
+        w.launch()
+        for _ in range(calls):
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
+            buf.zero_()
+            w.launch()
+            torch.cuda.synchronize()
+            runs.append(buf.view(256, STAMPS_PER_WG)[:nwg].cpu().numpy().astype(np.int64))
+    finally:
+        dm.dspark_debug_set(DEBUG_STAMPS, 0)
+    tick = 0.01   # us per tick of the 100 MHz clock
+
+    def one(s):
+        start, res = s[:, 0], s[:, 1]
+        end = s[:, 2 + 5 * (T - 1) + 4]
+        r = {"fill_median_us": np.median(res - start) * tick,
+             "fill_last_us": (res.max() - start.min()) * tick,
+             "span_us": (end.max() - start.min()) * tick}
+        g, d, st, wt, cc, ce = [], [], [], [], [], []
+        waits = np.zeros(len(s))
+        for t in range(T):
+            b = 2 + 5 * t
+            prev = res if t == 0 else s[:, b - 1]
+            g.append(np.median(s[:, b] - prev))
+            d.append(np.median(s[:, b + 1] - s[:, b]))
+            st.append(np.median(s[:, b + 2] - s[:, b + 1]))
+            wait = s[:, b + 4] - s[:, b + 2]
+            waits += wait
+            wt.append(np.median(wait))
+            last_store = s[:, b + 2].max()
+            ce.append(s[:, b + 4].max() - last_store)
+            cc.append(last_store - (res.max() if t == 0 else s[:, b - 1].max()))
+        r["per_step_median_us"] = {"w1_gather": np.mean(g[1:] if T > 1 else g) * tick,
+                                   "dot_argmax": np.mean(d) * tick, "key_store": np.mean(st) * tick,
+                                   "wait_for_token": np.mean(wt) * tick}
+        r["critical_path_per_step_us"] = {
+            "compute_to_last_store": np.mean(cc[1:] if T > 1 else cc) * tick,
+            "last_store_to_all_hold_token": np.mean(ce) * tick}
+        r["barrier_stall_share"] = float(np.median(waits / (end - start)))
+        return r
+
+    rs = [one(s) for s in runs]
+
+    def med(path):
+        vals = []
+        for r in rs:
+            v = r
+            for k in path:
+                v = v[k]
+            vals.append(v)
+        return round(float(np.median(vals)), 3)
+
+    out = {"workload": f"{w.name}:{w.mode}", "calls": calls, "workgroups": nwg,
+           "fill_median_us": med(["fill_median_us"]), "fill_last_us": med(["fill_last_us"]),
+           "span_us": med(["span_us"]), "barrier_stall_share": med(["barrier_stall_share"]),
+           "per_step_median_us": {k: med(["per_step_median_us", k]) for k in rs[0]["per_step_median_us"]},
+           "critical_path_per_step_us": {k: med(["critical_path_per_step_us", k])
+                                         for k in rs[0]["critical_path_per_step_us"]}}
+    return out
+
+
+def exchange_floor(dev, flush, stream, steps):
+    """Per-step time of the greedy one-request kernel with small slices (V = 65536: 256
+    workgroups of 256 rows), from kernel times of 16- and 7-step walks."""
+    res = {}
+    for V in (65536,):
+        k = {}
+        for T in (7, 16):
+            case = Case(f"floor_v{V}_t{T}_bs1", 7, T, V, T, 1, "bf16", 0.02, 3.0)
+            w = Walk(case, "greedy", dev)
+            _, _, _, _, kus = time_walk(w, steps, 3, flush, stream)
+            k[T] = float(np.mean(kus))
+            del w
+        res[f"v{V}"] = {"kernel_us_t7": round(k[7], 3), "kernel_us_t16": round(k[16], 3),
+                        "per_step_us": round((k[16] - k[7]) / 9.0, 3)}
+    return res
+
+
 COMMON_SOURCES = ["device_common.hpp", "internal.hpp", "walk_common.hpp", "walk.hip", "api.hip"]
 KERNEL_SOURCES = {
     "dense_walk_dot4_kernel": COMMON_SOURCES + ["walk_dot4.hip"],
     "dense_walk_mfma_kernel": COMMON_SOURCES + ["walk_mfma.hip"],
     "dense_walk_mfma1_kernel": COMMON_SOURCES + ["walk_mfma1.hip"],
     "topk_select_kernel+topk_walk_kernel": COMMON_SOURCES + ["topk.hip"],
+    VERIFY_KERNELS: ["device_common.hpp", "internal.hpp", "api.hip", "verify.hip"],
 }
 
 
@@ -232,6 +386,25 @@ def cpu_baseline(case, budget_s=20.0):
                       f"all {case.bs} request(s)), wall clock per call, median"}
 
 
+SWEEP = [("v151936_t7_bs1", "sample"), ("v151936_t7_bs16", "greedy"),
+         ("v151936_t7_bs16", "sample"), ("v151936_t7_bs64", "greedy"),
+         ("v151936_t7_bs64", "sample"), ("v151936_t16_bs1", "greedy"),
+         ("v151936_t16_bs1", "sample"), ("v129280_t5_bs1", "greedy"),
+         ("v129280_t5_bs1", "sample"), ("v129280_t5_bs64", "greedy"),
+         ("v129280_t5_bs64", "sample"), ("v248320_t16_bs1", "greedy"),
+         ("v248320_t16_bs1", "sample"),
+         ("topk512_v151936_t7_bs64", "greedy"), ("topk512_v151936_t7_bs64", "sample"),
+         ("verify:64:7:151936", "token"), ("verify:64:7:151936", "block"),
+         ("verify:16:7:151936", "token"), ("verify:16:7:151936", "block")]
+
+
+def make_workload(name, mode, dev):
+    if name.startswith("verify:"):
+        _, bs, T, V = name.split(":")
+        return Verify(int(bs), int(T), int(V), mode, dev)
+    return Walk(CASES[name], mode, dev)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,7 +412,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default=None, help="time one case:mode only (profiling)")
+    ap.add_argument("--no-evidence", action="store_true",
+                    help="skip the stamped runs and the exchange floor")
+    ap.add_argument("--only", default=None,
+                    help="time one case:mode only (profiling); verification as "
+                         "verify:bs:T:V:token|block")
     ap.add_argument("--print-digest", default=None, metavar="KERNEL",
                     help="print the source digest of a kernel (for the traffic record) and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -268,39 +445,40 @@ def main():
             "written")
         del src, dst
 
-    head_case, head_mode = CASES["v151936_t7_bs1"], "greedy"
+    head_name, head_mode = "v151936_t7_bs1", "greedy"
     if args.only:
-        name, mode = args.only.split(":")
-        head_case, head_mode = CASES[name], mode
+        head_name, head_mode = args.only.rsplit(":", 1)
 
-    log(f"[bench] headline {head_case.name} {head_mode}: steps={args.steps} warmup={args.warmup}")
-    w = Walk(head_case, head_mode, dev)
-    plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
+    log(f"[bench] headline {head_name} {head_mode}: steps={args.steps} warmup={args.warmup}")
+    w = make_workload(head_name, head_mode, dev)
+    plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V) if isinstance(w, Walk) else None
     us, wall, warm_us, dirty_us, kus = time_walk(w, args.steps, args.warmup, flush, stream,
                                                  dirty=True)
     med = float(np.median(us))
     nbytes = w.algorithmic_bytes()
     kmean = float(np.mean(kus))
-    w2 = w2_roofline(w, plan, kmean)
+    w2 = w2_roofline(w, plan, kmean) if plan else None
+    head_bounds = bounds(w, kmean)
     achieved = nbytes / (kmean * 1e-6) / 1e9
     log(f"[bench] median {med:.2f} us  p10 {np.percentile(us, 10):.2f}  p90 "
         f"{np.percentile(us, 90):.2f}  warm {warm_us:.2f} us  kernel mean {kmean:.2f} us "
         f"(per kernel {w.kernel_parts_us})")
+    head_parts = w.kernel_parts_us
+
+    evidence = {}
+    if not args.no_evidence and not args.only:
+        try:
+            evidence["stamps"] = [stamp_split(w, flush)]
+            log(f"[bench] stamps {evidence['stamps'][0]}")
+        except dm.DsparkError as e:
+            log(f"[bench] stamps: {e}")
 
     sweep = []
     if not args.no_sweep and not args.only:
-        for name, mode in [("v151936_t7_bs1", "sample"), ("v151936_t7_bs16", "greedy"),
-                           ("v151936_t7_bs16", "sample"), ("v151936_t7_bs64", "greedy"),
-                           ("v151936_t7_bs64", "sample"), ("v151936_t16_bs1", "greedy"),
-                           ("v151936_t16_bs1", "sample"), ("v129280_t5_bs1", "greedy"),
-                           ("v129280_t5_bs1", "sample"), ("v129280_t5_bs64", "greedy"),
-                           ("v129280_t5_bs64", "sample"), ("v248320_t16_bs1", "greedy"),
-                           ("v248320_t16_bs1", "sample"),
-                           ("topk512_v151936_t7_bs64", "greedy"),
-                           ("topk512_v151936_t7_bs64", "sample")]:
+        for name, mode in SWEEP:
             del w
             torch.cuda.empty_cache()
-            w = Walk(CASES[name], mode, dev)
+            w = make_workload(name, mode, dev)
             try:
                 s_us, _, s_warm, _, s_kus = time_walk(w, max(10, args.steps // 2), 3, flush,
                                                       stream)
@@ -308,27 +486,49 @@ def main():
                 log(f"[bench] {name} {mode}: {e}")
                 continue
             nb = w.algorithmic_bytes()
-            s_plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
-            entry = {"workload": name, "mode": mode, "us_median": round(float(np.median(s_us)), 2),
+            km = float(np.mean(s_kus))
+            entry = {"workload": w.name, "mode": mode, "us_median": round(float(np.median(s_us)), 2),
                      "us_p10": round(float(np.percentile(s_us, 10)), 2),
                      "us_p90": round(float(np.percentile(s_us, 90)), 2),
                      "us_warm": round(s_warm, 2),
-                     "kernel_us_mean": round(float(np.mean(s_kus)), 2),
+                     "kernel_us_mean": round(km, 2),
                      "kernel_parts_us": w.kernel_parts_us,
-                     "hbm_frac": round(nb / (float(np.mean(s_kus)) * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                       4),
-                     "w2_frac": w2_roofline(w, s_plan, float(np.mean(s_kus)))["frac"]}
+                     "hbm_frac": round(nb / (km * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            if isinstance(w, Walk):
+                s_plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
+                entry["w2_frac"] = w2_roofline(w, s_plan, km)["frac"]
+            entry.update(bounds(w, km))
             sweep.append(entry)
             log(f"[bench] {name} {mode}: {entry}")
+            if not args.no_evidence and name == "v151936_t7_bs64" and mode == "greedy":
+                try:
+                    evidence.setdefault("stamps", []).append(stamp_split(w, flush))
+                    log(f"[bench] stamps {evidence['stamps'][-1]}")
+                except dm.DsparkError as e:
+                    log(f"[bench] stamps: {e}")
+        del w
+        torch.cuda.empty_cache()
+    if not args.no_evidence and not args.only:
+        floor = exchange_floor(dev, flush, stream, max(10, args.steps // 2))
+        heads = {(e["workload"], e["mode"]): e["kernel_us_mean"] for e in sweep}
+        t16 = heads.get(("v151936_t16_bs1", "greedy"))
+        if t16 is not None:
+            floor["v151936"] = {"kernel_us_t7": round(kmean, 3), "kernel_us_t16": t16,
+                                "per_step_us": round((t16 - kmean) / 9.0, 3)}
+        evidence["exchange_floor"] = floor
+        log(f"[bench] exchange floor {floor}")
 
     cpu = None
     if not args.no_cpu and not args.only:
         log("[bench] CPU oracle baseline ...")
-        cpu = cpu_baseline(head_case)
+        cpu = cpu_baseline(CASES[head_name])
         log(f"[bench] oracle {cpu['value']:.0f} us/walk on {cpu['cores']} threads")
 
-    kernel = TOPK_KERNELS if head_case.k else KERNEL_NAMES.get(plan["path"], "?")
-    tr = measured_traffic(f"{head_case.name}:{head_mode}", kernel)
+    if plan is not None:
+        kernel = TOPK_KERNELS if CASES[head_name].k else KERNEL_NAMES.get(plan["path"], "?")
+    else:
+        kernel = VERIFY_KERNELS
+    tr = measured_traffic(f"{head_name}:{head_mode}", kernel)
     traffic = None if tr is None else tr["fetch_bytes"] + tr["write_bytes"]
 
     out = {
@@ -344,24 +544,49 @@ def main():
         "vs_baseline": None,
         "dtype": "int8 x int8 -> int32 dot products, fp32 logits",
         "data": "synthetic (seeded N(0, 0.02^2) bf16 W1/W2, N(0, 3^2) fp32 base logits)",
-        "config": {"workload": f"{head_case.name}:{head_mode}", "V": head_case.V, "draft_steps": head_case.T, "bs": head_case.bs, "rank": 256,
-                   "w_dtype": head_case.wdtype, "cache": "L2 and MALL evicted by a 512 MiB read before each call",
+        "config": {"workload": f"{head_name}:{head_mode}", "V": w_v(head_name),
+                   "draft_steps": w_t(head_name), "bs": w_bs(head_name), "rank": 256,
+                   "w_dtype": "bf16",
+                   "cache": "L2 and MALL evicted by a 512 MiB read before each call",
                    "plan": plan},
         "latency_us": {"median": round(med, 3), "p10": round(float(np.percentile(us, 10)), 3),
                        "p90": round(float(np.percentile(us, 90)), 3), "warm": round(warm_us, 3),
                        "after_dirty_flush_median": round(float(np.median(dirty_us)), 3),
                        "kernel_only_mean": round(kmean, 3),
                        "kernel_only_median": round(float(np.median(kus)), 3),
+                       "kernel_parts_us": head_parts,
                        "wall_per_call_incl_flush": round(wall / args.steps * 1e6, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
                      "kernel": kernel},
         "w2_roofline": w2,
+        "bounds": head_bounds,
+        "evidence": evidence,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
     print(json.dumps(out), flush=True)
+
+
+def _case_dims(name):
+    if name.startswith("verify:"):
+        _, bs, T, V = name.split(":")
+        return int(V), int(T), int(bs)
+    c = CASES[name]
+    return c.V, c.T, c.bs
+
+
+def w_v(name):
+    return _case_dims(name)[0]
+
+
+def w_t(name):
+    return _case_dims(name)[1]
+
+
+def w_bs(name):
+    return _case_dims(name)[2]
 
 
 if __name__ == "__main__":

@@ -102,7 +102,8 @@ struct VerifyLaunch {
 size_t verify_workspace_bytes(int64_t bs, int64_t T, int64_t V);
 int launch_verify(const VerifyLaunch& a, hipStream_t stream);
 
-// Walk kernel launch: plain, or with dispatch-recorded events while kernel timing is on.
+// Kernel launch (walks and verification): plain, or with dispatch-recorded events while kernel
+// timing is on.
 hipError_t launch_walk_kernel(const void* fn, dim3 grid, dim3 block, void** args, size_t lds,
                               hipStream_t stream);
 int set_kernel_timing(int64_t ring_size);

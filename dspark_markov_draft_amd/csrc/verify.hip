@@ -525,16 +525,26 @@ int verify_groups(int bs, int T, int V) {
 }
 
 template <int J, int VEC>
-int launch_verify_j(const VerifyParams& p, hipStream_t s) {
+int launch_verify_j(const VerifyParams& p_in, hipStream_t s) {
+    VerifyParams p = p_in;
+    void* args[] = {&p};
     const dim3 blk(VT);
-    hipLaunchKernelGGL((verify_stats_kernel<J, VEC>), dim3(p.C, p.bs * (p.T + 1)), blk, 0, s, p);
-    hipLaunchKernelGGL(verify_decide_kernel, dim3(p.bs), blk, 0, s, p);
+    auto go = [&](const void* fn, dim3 grid) {
+        return launch_walk_kernel(fn, grid, blk, args, 0, s) == hipSuccess;
+    };
+    bool ok = go(reinterpret_cast<const void*>(&verify_stats_kernel<J, VEC>),
+                 dim3(p.C, p.bs * (p.T + 1)));
+    ok = ok && go(reinterpret_cast<const void*>(&verify_decide_kernel), dim3(p.bs));
     if (p.mode == 1 && p.T > 1)
-        hipLaunchKernelGGL((verify_residual_kernel<J, VEC>), dim3(p.C, p.bs * (p.T - 1)), blk, 0, s, p);
-    if (p.mode == 1) hipLaunchKernelGGL(verify_choose_kernel, dim3(p.bs), blk, 0, s, p);
-    hipLaunchKernelGGL((verify_mass_kernel<J, VEC>), dim3(p.C, p.bs), blk, 0, s, p);
-    hipLaunchKernelGGL((verify_draw_kernel<J, VEC>), dim3(p.bs), blk, 0, s, p);
-    if (hipGetLastError() != hipSuccess) return DSPARK_ERR_LAUNCH;
+        ok = ok && go(reinterpret_cast<const void*>(&verify_residual_kernel<J, VEC>),
+                      dim3(p.C, p.bs * (p.T - 1)));
+    if (p.mode == 1) ok = ok && go(reinterpret_cast<const void*>(&verify_choose_kernel), dim3(p.bs));
+    ok = ok && go(reinterpret_cast<const void*>(&verify_mass_kernel<J, VEC>), dim3(p.C, p.bs));
+    ok = ok && go(reinterpret_cast<const void*>(&verify_draw_kernel<J, VEC>), dim3(p.bs));
+    if (!ok) {
+        (void)hipGetLastError();
+        return DSPARK_ERR_LAUNCH;
+    }
     return DSPARK_OK;
 }
 

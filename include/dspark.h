@@ -276,10 +276,10 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *       row * 8 + (0 start, 1 first bound, 2 row scanned, 3 k-th key, 4 done) for each
  *       (request, step) row of the candidate select, and 8192 + request * 40 + (0 start, then
  *       per step t: 1 + 2t W1 codes ready, 2 + 2t token known) for the walk. For profiling only;
- *   DSPARK_DEBUG_KERNEL_TIMING: n in 1..4096 launches every later walk kernel on the current
- *       device with hipExtLaunchKernel and one of a ring of n HIP event pairs, which the dispatch
- *       records at the kernel's start and end (read them with dspark_kernel_times); 0 frees the
- *       ring. For benchmarks; do not enable it around graph capture.
+ *   DSPARK_DEBUG_KERNEL_TIMING: n in 1..4096 launches every later walk and verification kernel
+ *       on the current device with hipExtLaunchKernel and one of a ring of n HIP event pairs,
+ *       which the dispatch records at the kernel's start and end (read them with
+ *       dspark_kernel_times); 0 frees the ring. For benchmarks; not around graph capture.
  */
 enum dspark_debug_key {
     DSPARK_DEBUG_MAX_WORKGROUPS = 1,
@@ -291,7 +291,7 @@ enum dspark_debug_key {
 };
 int dspark_debug_set(int key, int64_t value);
 
-/* Durations in microseconds of the walk kernels launched while DSPARK_DEBUG_KERNEL_TIMING was on,
+/* Durations in microseconds of the kernels launched while DSPARK_DEBUG_KERNEL_TIMING was on,
  * since it was switched on or last read: at most the ring size and `max` of the most recent,
  * oldest first, into `us`; their number into *count. Blocks until those kernels have finished.
  * Returns DSPARK_ERR_INVALID_ARG for null pointers or max < 0, DSPARK_ERR_LAUNCH if an event
