@@ -150,6 +150,25 @@ class Walk:
         return n
 
 
+class Pruned(Walk):
+    """The lossless top-k pruned greedy walk (dspark_walk_greedy_pruned) on a workload's inputs:
+    the dense greedy walk's tokens, computing only the W2 rows of the k best base logits on the
+    steps the load-time bound certifies."""
+
+    def __init__(self, case, k, dev):
+        super().__init__(case, "greedy", dev)
+        self.k = k
+        self.name = f"pruned{k}_{case.name}"
+        self.ws = dm.new_workspace(self.bs, self.T, self.V, k)
+        self.bound = dm.dspark_w2_prune_bound(self.q, self.s)
+        self.dense_steps = torch.zeros(self.bs, dtype=torch.int32, device=dev)
+
+    def launch(self):
+        dm.dspark_walk_greedy_pruned(self.q, self.s, self.w1, self.base, self.start, self.k,
+                                     self.bound, self.ws, draft_tokens=self.tokens,
+                                     dense_steps=self.dense_steps)
+
+
 class Verify:
     """Verification of drafted blocks (dspark_verify) on seeded inputs shaped like the
     probabilistic walk's output at bs requests, T draft tokens, vocabulary V."""
@@ -394,11 +413,16 @@ SWEEP = [("v151936_t7_bs1", "sample"), ("v151936_t7_bs16", "greedy"),
          ("v129280_t5_bs64", "sample"), ("v248320_t16_bs1", "greedy"),
          ("v248320_t16_bs1", "sample"),
          ("topk512_v151936_t7_bs64", "greedy"), ("topk512_v151936_t7_bs64", "sample"),
+         ("pruned:512:v151936_t7_bs1", "greedy"), ("pruned:512:v151936_t7_bs16", "greedy"),
+         ("pruned:512:v151936_t7_bs64", "greedy"),
          ("verify:64:7:151936", "token"), ("verify:64:7:151936", "block"),
          ("verify:16:7:151936", "token"), ("verify:16:7:151936", "block")]
 
 
 def make_workload(name, mode, dev):
+    if name.startswith("pruned:"):
+        _, k, case = name.split(":")
+        return Pruned(CASES[case], int(k), dev)
     if name.startswith("verify:"):
         _, bs, T, V = name.split(":")
         return Verify(int(bs), int(T), int(V), mode, dev)
@@ -464,6 +488,12 @@ def main():
         f"{np.percentile(us, 90):.2f}  warm {warm_us:.2f} us  kernel mean {kmean:.2f} us "
         f"(per kernel {w.kernel_parts_us})")
     head_parts = w.kernel_parts_us
+    if isinstance(w, Verify):
+        kernel = VERIFY_KERNELS
+    elif w.k:
+        kernel = TOPK_KERNELS
+    else:
+        kernel = KERNEL_NAMES.get(plan["path"], "?")
 
     evidence = {}
     if not args.no_evidence and not args.only:
@@ -497,6 +527,8 @@ def main():
             if isinstance(w, Walk):
                 s_plan = dm.dspark_walk_plan_query(w.bs, w.T, w.V)
                 entry["w2_frac"] = w2_roofline(w, s_plan, km)["frac"]
+            if isinstance(w, Pruned):
+                entry["dense_steps"] = int(w.dense_steps.sum().item())
             entry.update(bounds(w, km))
             sweep.append(entry)
             log(f"[bench] {name} {mode}: {entry}")
@@ -524,10 +556,6 @@ def main():
         cpu = cpu_baseline(CASES[head_name])
         log(f"[bench] oracle {cpu['value']:.0f} us/walk on {cpu['cores']} threads")
 
-    if plan is not None:
-        kernel = TOPK_KERNELS if CASES[head_name].k else KERNEL_NAMES.get(plan["path"], "?")
-    else:
-        kernel = VERIFY_KERNELS
     tr = measured_traffic(f"{head_name}:{head_mode}", kernel)
     traffic = None if tr is None else tr["fetch_bytes"] + tr["write_bytes"]
 
@@ -570,6 +598,8 @@ def main():
 
 
 def _case_dims(name):
+    if name.startswith("pruned:"):
+        name = name.split(":")[2]
     if name.startswith("verify:"):
         _, bs, T, V = name.split(":")
         return int(V), int(T), int(bs)

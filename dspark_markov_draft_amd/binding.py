@@ -80,6 +80,9 @@ def lib():
                                        vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dspark_walk_plan_for.argtypes = [ctypes.c_int32, i64, i64, i64, i64,
                                            ctypes.POINTER(WalkPlan)]
+        L.dspark_w2_prune_bound.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.dspark_walk_greedy_pruned.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i64,
+                                                vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dspark_verify_workspace_bytes.argtypes = [i64, i64, i64]
         L.dspark_verify_workspace_bytes.restype = ctypes.c_size_t
         L.dspark_verify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp,
@@ -93,7 +96,7 @@ def lib():
                      "dspark_walk_greedy", "dspark_walk_greedy_noalloc",
                      "dspark_walk_sample", "dspark_walk_topk", "dspark_workspace_status",
                      "dspark_philox_words", "dspark_debug_set", "dspark_kernel_times",
-                     "dspark_verify"]:
+                     "dspark_verify", "dspark_w2_prune_bound", "dspark_walk_greedy_pruned"]:
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -324,6 +327,45 @@ def dspark_walk_topk(q, s, w1, base, start, k, workspace, sample=False, seeds=No
                                   _p(draft_logits), _p(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return draft_tokens, draft_logits
+
+
+def dspark_w2_prune_bound(q, s, bound=None, stream=None):
+    """Load-time bound B = max_v s[v] * sum_k |q[v,k]| of the lossless pruned walk, as a device
+    fp32 tensor of one element."""
+    _expect(q, "q", torch.int8, None)
+    if q.dim() != 2:
+        raise ValueError(f"q must be [V, {RANK}], got shape {tuple(q.shape)}")
+    V = q.shape[0]
+    _expect(s, "s", torch.float32, (V,))
+    if bound is None:
+        bound = torch.empty(1, dtype=torch.float32, device=q.device)
+    _expect(bound, "bound", torch.float32, (1,))
+    _same_device(q=q, s=s, bound=bound)
+    _check(lib().dspark_w2_prune_bound(_p(q), _p(s), V, q.shape[1], _p(bound), _stream(stream)))
+    return bound
+
+
+def dspark_walk_greedy_pruned(q, s, w1, base, start, k, w2_bound, workspace, draft_tokens=None,
+                              out_logits=None, dense_steps=None, stream=None):
+    """Lossless top-k pruned greedy walk: the tokens of dspark_walk_greedy, computing only the
+    W2 rows of the k best base logits on every step the bound certifies. Returns draft_tokens."""
+    _expect(base, "base", torch.float32, None)
+    if base.dim() == 3 and draft_tokens is None:
+        draft_tokens = torch.empty(base.shape[:2], dtype=torch.int32, device=base.device)
+    bs, T, V = _check_walk_args(q, s, w1, base, start, workspace, draft_tokens)
+    _expect(w2_bound, "w2_bound", torch.float32, (1,))
+    _expect(out_logits, "out_logits", torch.float32, (bs, T, V), optional=True)
+    _expect(dense_steps, "dense_steps", torch.int32, (bs,), optional=True)
+    _same_device(q=q, s=s, w1=w1, base=base, start=start, workspace=workspace,
+                 draft_tokens=draft_tokens, w2_bound=w2_bound, out_logits=out_logits,
+                 dense_steps=dense_steps)
+    _check(lib().dspark_walk_greedy_pruned(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base),
+                                           _p(start), bs, T, V, q.shape[1], int(k), _p(w2_bound),
+                                           _p(draft_tokens), _p(out_logits), _p(dense_steps),
+                                           _p(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(stream)))
+    return draft_tokens
 
 
 VERIFY_TOKEN, VERIFY_BLOCK = 0, 1

@@ -352,6 +352,56 @@ int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, 
     return launch_topk_walk(a, static_cast<hipStream_t>(stream));
 }
 
+int dspark_w2_prune_bound(const int8_t* w2_q, const float* w2_scale, int64_t V, int64_t rank,
+                          float* bound, void* stream) {
+    if (!w2_q || !w2_scale || !bound || V < 1 || rank < 1) return DSPARK_ERR_INVALID_ARG;
+    if (!aligned16(w2_q) || !aligned4(w2_scale) || !aligned4(bound)) return DSPARK_ERR_INVALID_ARG;
+    if (rank != DSPARK_RANK || V > DSPARK_MAX_V) return DSPARK_ERR_UNSUPPORTED;
+    DeviceInfo dev;
+    const int st = current_device_info(&dev);
+    if (st != DSPARK_OK) return st;
+    return launch_w2_bound(w2_q, w2_scale, V, bound, static_cast<hipStream_t>(stream));
+}
+
+int dspark_walk_greedy_pruned(const int8_t* w2_q, const float* w2_scale, const void* w1,
+                              int w1_dtype, const float* base_logits,
+                              const int32_t* start_tokens, int64_t bs, int64_t T, int64_t V,
+                              int64_t rank, int64_t k, const float* w2_bound,
+                              int32_t* draft_tokens, float* out_logits, int32_t* dense_steps,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_walk_shape(bs, T, V, rank, w1_dtype);
+    if (st != DSPARK_OK) return st;
+    if (k < 1 || k > V) return DSPARK_ERR_INVALID_ARG;
+    if (k > DSPARK_MAX_TOPK) return DSPARK_ERR_UNSUPPORTED;
+    if (!w2_bound || !aligned4(w2_bound)) return DSPARK_ERR_INVALID_ARG;
+    st = check_walk_common(w2_q, w2_scale, w1, base_logits, start_tokens, draft_tokens, workspace,
+                           workspace_bytes, bs, T, V, k);
+    if (st != DSPARK_OK) return st;
+    if ((out_logits && !aligned16(out_logits)) || (dense_steps && !aligned4(dense_steps)))
+        return DSPARK_ERR_INVALID_ARG;
+    DeviceInfo dev;
+    st = current_device_info(&dev);
+    if (st != DSPARK_OK) return st;
+    TopkLaunch a = {};
+    a.w.q = w2_q;
+    a.w.scale = w2_scale;
+    a.w.w1 = w1;
+    a.w.w1_dtype = w1_dtype;
+    a.w.base = base_logits;
+    a.w.start = start_tokens;
+    a.w.tokens = draft_tokens;
+    a.w.out_logits = out_logits;
+    a.w.workspace = workspace;
+    a.w.bs = (int)bs;
+    a.w.T = (int)T;
+    a.w.V = (int)V;
+    a.w.sample = 0;
+    a.k = (int)k;
+    a.w2_bound = w2_bound;
+    a.dense_steps = dense_steps;
+    return launch_topk_walk(a, static_cast<hipStream_t>(stream));
+}
+
 size_t dspark_verify_workspace_bytes(int64_t bs, int64_t T, int64_t V) {
     if (bs < 1 || T < 1 || V < 1) return WS_ALIGN;
     if (bs > DSPARK_MAX_BS) bs = DSPARK_MAX_BS;

@@ -80,7 +80,10 @@ int launch_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
 struct TopkLaunch {
     WalkLaunch w;
     int k;
+    const float* w2_bound;    // non-null: the lossless pruned greedy walk
+    int32_t* dense_steps;     // pruned walk: per request, steps computed over the whole row
 };
+int launch_w2_bound(const int8_t* q, const float* s, int64_t V, float* bound, hipStream_t stream);
 int launch_topk_walk(const TopkLaunch& a, hipStream_t stream);
 
 // Verification of drafted blocks (csrc/verify.hip). Workspace: the error word at WS_ERR, then

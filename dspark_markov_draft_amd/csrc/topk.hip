@@ -614,8 +614,17 @@ struct TopkWalkParams {
     int32_t* cand;         // [bs][T][k] from topk_select_kernel; cleared at the end
     uint32_t* err;
     uint64_t* stamps;      // instrumented builds
+    const float* w2_bound; // pruned greedy walk: the load-time bound B (see dspark_w2_prune_bound)
+    int32_t* dense_steps;  // pruned greedy walk: per request, steps computed over the whole row
     int bs, T, V, k;
 };
+
+// Value of the float whose order key is the high word of `key` (order_key32 inverted; every
+// NaN maps back to a NaN, the canonical zero to +0).
+__device__ __forceinline__ float key_value(uint64_t key) {
+    const uint32_t k32 = (uint32_t)(key >> 32);
+    return __uint_as_float((k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32);
+}
 
 // The 64 candidates of one wave for one step. Rows are read cooperatively so that every load
 // instruction fetches whole cache lines: in load i (0..15) the 16 lanes of lane group r (lanes
@@ -638,10 +647,19 @@ __device__ __forceinline__ int row16_sum_i32(int x) {
 
 // MULTI: k > TKW_THREADS, candidates in several chunks per step, loaded as they are scored;
 // otherwise one candidate per thread, the next step's loaded while this step is scored.
-template <int SAMPLE, int W1T, bool MULTI, bool TIMED>
+// PRUNE (greedy only): the lossless top-k pruned walk. Its result is the dense greedy walk's:
+// a step keeps its candidates' argmax only when no other row can reach it. Every non-candidate
+// v has base[v] <= kth (the smallest candidate base logit) and |bias(v)| <= B * a, with B the
+// load-time bound max_v s[v] * sum_k |q[v,k]| and a = max_k |W1[prev,k]| (the codes times their
+// scale never exceed a), so its logit is at most kth + B * a up to rounding. The step is
+// certified when the best candidate logit exceeds that by a relative margin of 2^-16 (far above
+// the few ulps of rounding in either logit); otherwise, and whenever a value is not finite, the
+// step is computed over every row, as the dense walk does, with the same rounding.
+template <int SAMPLE, int W1T, bool MULTI, bool TIMED, bool PRUNE = false>
 __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkParams p) {
     __shared__ __align__(16) uint32_t w1q[TKW_WAVES][RANK / 4];  // one copy per wave
     __shared__ uint64_t wkeys[2][TKW_WAVES];                      // by step parity
+    __shared__ float wmin[2][TKW_WAVES];                          // PRUNE: smallest candidate base
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
     const int b = blockIdx.x;
     const int64_t st0 = TK_WALK_STAMPS0 + (int64_t)b * 40;
@@ -660,6 +678,8 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         rtemp = inv_temperature(p.temps[b]);
     }
     const int32_t* req_cand = p.cand + (int64_t)b * p.T * p.k;
+    const float w2_bound = PRUNE ? p.w2_bound[0] : 0.0f;
+    int dense_count = 0;
     const int own = (lane & 15) * 4 + (lane >> 4);  // this lane's candidate within the wave's 64
     // raw index of candidate j of step t (j clamped into the list; load_block bounds the value)
     auto cand_index = [&](int t, int j) -> uint32_t {
@@ -720,6 +740,7 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         tk_stamp<TIMED>(p.stamps, st0 + 1 + 2 * t);
         const int4 wc = reinterpret_cast<const int4*>(w1q[wave])[lane & 15];
         uint64_t best = 0;
+        float min_base = INFINITY;
         auto score = [&](const CandBlock& blk, bool has) {
             int acc = 0;
 #pragma unroll
@@ -750,6 +771,8 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
                 key = argmax_key(xs + g, blk.v);
             }
             if (has) best = key > best ? key : best;
+            if constexpr (PRUNE)
+                if (has) min_base = fminf(min_base, blk.base);
         };
         if constexpr (MULTI) {
             for (int c0 = 0; c0 < p.k; c0 += TKW_THREADS) {
@@ -761,11 +784,44 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
             score(use, wave * WAVE + own < p.k);
         }
         best = wave_max_u64(best);
+        if constexpr (PRUNE) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) min_base = fminf(min_base, __shfl_xor(min_base, o, WAVE));
+            if (lane == 0) wmin[t & 1][wave] = min_base;
+        }
         if (lane == 0) wkeys[t & 1][wave] = best;
         __syncthreads();
         uint64_t m = wkeys[t & 1][0];
 #pragma unroll
         for (int w2 = 1; w2 < TKW_WAVES; ++w2) m = wkeys[t & 1][w2] > m ? wkeys[t & 1][w2] : m;
+        if constexpr (PRUNE) {
+            float kth = wmin[t & 1][0];
+#pragma unroll
+            for (int w2 = 1; w2 < TKW_WAVES; ++w2) kth = fminf(kth, wmin[t & 1][w2]);
+            const float lstar = key_value(m);
+            const float reach = w2_bound * a;        // bound on any row's |bias| this step
+            const float margin = (fabsf(lstar) + fabsf(kth) + reach) * 0x1p-16f;
+            // false for any NaN or infinity (then the difference or the margin is not finite)
+            const bool certified = lstar - kth > reach + margin;
+            if (!certified) {
+                // the whole row, every row scored as the dense walk scores it
+                best = 0;
+                for (int r0 = 0; r0 < p.V; r0 += TKW_THREADS) {
+                    const int j = r0 + wave * WAVE + own;
+                    load_block(t, (uint32_t)min(j, p.V - 1), use);
+                    score(use, j < p.V);
+                }
+                best = wave_max_u64(best);
+                __syncthreads();                     // every wave has read this step's keys
+                if (lane == 0) wkeys[t & 1][wave] = best;
+                __syncthreads();
+                m = wkeys[t & 1][0];
+#pragma unroll
+                for (int w2 = 1; w2 < TKW_WAVES; ++w2)
+                    m = wkeys[t & 1][w2] > m ? wkeys[t & 1][w2] : m;
+                ++dense_count;
+            }
+        }
         // every candidate at -inf: the dense row is -inf throughout, whose first max is 0
         uint32_t token = (uint32_t)(m >> 32) <= ORDER_KEY_NEG_INF ? 0u : key_index(m);
         if (token >= (uint32_t)p.V) token = 0;
@@ -785,11 +841,20 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         if (t + 1 < p.T) step(t + 1, rb, ra, ia, ib);
     }
     flush_pending();   // the last step's logit (sampling)
+    if constexpr (PRUNE)
+        if (tid == 0 && p.dense_steps) p.dense_steps[b] = dense_count;
     // every candidate list of this request has been read before the last barrier: clear them,
     // so that the workspace is all zero again for the dense walk
     __syncthreads();
     int32_t* clr = p.cand + (int64_t)b * p.T * p.k;
     for (int i = tid; i < p.T * p.k; i += TKW_THREADS) clr[i] = 0;
+}
+
+template <bool MULTI>
+static const void* pruned_walk_fn(int w1t) {
+    if (w1t == DT_F32) return reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_F32, MULTI, false, true>);
+    if (w1t == DT_BF16) return reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_BF16, MULTI, false, true>);
+    return reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_F16, MULTI, false, true>);
 }
 
 template <bool MULTI>
@@ -852,13 +917,17 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
     kp.cand = cand;
     kp.err = reinterpret_cast<uint32_t*>(ws + WS_ERR);
     kp.stamps = sp.stamps;
+    kp.w2_bound = a.w2_bound;
+    kp.dense_steps = a.dense_steps;
     kp.bs = w.bs;
     kp.T = w.T;
     kp.V = w.V;
     kp.k = a.k;
     const int w1t = w.w1_dtype == DSPARK_F32 ? DT_F32 : w.w1_dtype == DSPARK_BF16 ? DT_BF16 : DT_F16;
     void* kargs[] = {&kp};
-    const void* fn = a.k > TKW_THREADS ? topk_walk_fn<true>(w.sample, w1t, timed)
+    const void* fn = a.w2_bound ? (a.k > TKW_THREADS ? pruned_walk_fn<true>(w1t)
+                                                     : pruned_walk_fn<false>(w1t))
+                   : a.k > TKW_THREADS ? topk_walk_fn<true>(w.sample, w1t, timed)
                                        : topk_walk_fn<false>(w.sample, w1t, timed);
     e = launch_walk_kernel(fn, dim3((unsigned)w.bs), dim3(TKW_THREADS),
                            kargs, 0, stream);
@@ -866,6 +935,43 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
         (void)hipGetLastError();
         return DSPARK_ERR_LAUNCH;
     }
+    return DSPARK_OK;
+}
+
+// ---- load-time bound of the lossless pruned walk -----------------------------------------------
+// B = max_v fl(s[v] * sum_k |q[v,k]|): one wave per row at a time (lane l sums the magnitudes of
+// codes 4l .. 4l+3), the largest product folded into *bound with an unsigned atomic max of its
+// bits (every product is >= 0, where IEEE order is unsigned order). *bound starts at zero.
+__global__ __launch_bounds__(256) void w2_bound_zero_kernel(float* bound) { *bound = 0.0f; }
+
+__global__ __launch_bounds__(256) void w2_bound_kernel(const int8_t* q, const float* s, int V,
+                                                       float* bound) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = (int)(blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE);
+    const int nwaves = (int)(gridDim.x * (blockDim.x / WAVE));
+    float best = 0.0f;
+    for (int v = wave; v < V; v += nwaves) {
+        const uint32_t w = reinterpret_cast<const uint32_t*>(q + (int64_t)v * RANK)[lane];
+        int l1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = (int)(int8_t)(w >> (8 * i));
+            l1 += c < 0 ? -c : c;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) l1 += __shfl_xor(l1, o, WAVE);
+        best = fmaxf(best, s[v] * (float)l1);
+    }
+    if (lane == 0 && best > 0.0f)
+        __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(bound), __float_as_uint(best),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int launch_w2_bound(const int8_t* q, const float* s, int64_t V, float* bound, hipStream_t stream) {
+    w2_bound_zero_kernel<<<1, 1, 0, stream>>>(bound);
+    const int64_t blocks = (V + 3) / 4 < 2048 ? (V + 3) / 4 : 2048;
+    w2_bound_kernel<<<(unsigned)blocks, 256, 0, stream>>>(q, s, (int)V, bound);
+    if (hipGetLastError() != hipSuccess) return DSPARK_ERR_LAUNCH;
     return DSPARK_OK;
 }
 

@@ -197,6 +197,38 @@ int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, 
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Lossless top-k pruning of W2 for the greedy walk (vLLM PR #62958, Details, names a PR that
+ * prunes W2 with top-k without loss; the pages give no algorithm). Reading: at each step only the
+ * W2 rows of the k largest base logits are multiplied (the candidates of dspark_walk_topk), and
+ * the step keeps their argmax only if no other row can reach it: every other row v has
+ * base[v] <= kth, the smallest candidate base logit, and |bias(v)| <= B * max_k |W1[prev,k]|,
+ * so the step is certified when the best candidate logit exceeds kth + B * max|W1[prev]| (with a
+ * relative margin of 2^-16 for rounding). A step that is not certified is computed over the whole
+ * vocabulary. The tokens are therefore those of dspark_walk_greedy on the same inputs.
+ *
+ * dspark_w2_prune_bound (load time, after dspark_quantize_w2): *bound = B =
+ *   max_v fl32(w2_scale[v] * sum_k |w2_q[v,k]|), into a device fp32 word. Enqueues two kernels.
+ *
+ * dspark_walk_greedy_pruned: arguments as dspark_walk_greedy, plus
+ *   k           candidates per step, 1 <= k <= min(V, DSPARK_MAX_TOPK)
+ *   w2_bound    device fp32 word holding B for these w2_q / w2_scale
+ *   out_logits  [bs, T, V] fp32 or NULL: the logits of the rows each step evaluated (the
+ *               candidates, or every row of a step that was not certified), -inf elsewhere
+ *   dense_steps [bs] int32 or NULL: per request, the number of steps computed over every row
+ *   workspace of dspark_walk_workspace_bytes(bs, T, V, k) bytes (as dspark_walk_topk)
+ * Base logits must not hold NaN (as dspark_walk_topk).
+ */
+int dspark_w2_prune_bound(const int8_t* w2_q, const float* w2_scale, int64_t V, int64_t rank,
+                          float* bound, void* stream);
+
+int dspark_walk_greedy_pruned(const int8_t* w2_q, const float* w2_scale, const void* w1,
+                              int w1_dtype, const float* base_logits,
+                              const int32_t* start_tokens, int64_t bs, int64_t T, int64_t V,
+                              int64_t rank, int64_t k, const float* w2_bound,
+                              int32_t* draft_tokens, float* out_logits, int32_t* dense_steps,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Verification of drafted blocks against the target model, on the stored bf16 draft rows
  * (vLLM PR #62958, Details: rejection sampling works on exactly the distribution the draft
  * sampled from; vLLM PR #64476, Validation: block verification keeps the target distribution).

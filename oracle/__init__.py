@@ -76,6 +76,8 @@ def lib():
         L.oracle_walk.restype = ctypes.c_int
         L.oracle_verify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp]
         L.oracle_verify.restype = ctypes.c_int
+        L.oracle_w2_l1_bound.argtypes = [vp, vp, i64, i64]
+        L.oracle_w2_l1_bound.restype = f32
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -222,3 +224,12 @@ def verify(draft_lb, draft_tokens, target_logits, temps, uniforms, mode=VERIFY_T
     if st != OK:
         raise OracleError(f"oracle_verify failed ({st})")
     return acc, out, prob
+
+
+def w2_l1_bound(q, s) -> float:
+    """max_v fl32(s[v] * sum_k |q[v,k]|): per unit of max |W1[prev]|, a bound on every row's
+    bias (the lossless top-k pruning certificate; see oracle_w2_l1_bound in oracle.c)."""
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    V, R = q.shape
+    return float(lib().oracle_w2_l1_bound(_ptr(q), _ptr(s), V, R))

@@ -503,3 +503,26 @@ int oracle_verify(const uint16_t* draft_logits, const int32_t* draft_tokens,
     free(h);
     return status;
 }
+
+/* ======================================================================================== */
+/* Lossless top-k pruning of W2 for the greedy walk (vLLM PR #62958, Details, names a PR      */
+/* that prunes W2 with top-k, losslessly; the pages give no algorithm). Reading: at each step  */
+/* only the W2 rows of the k largest base logits are multiplied, and the step is accepted only */
+/* if no other row can reach the best candidate's logit; otherwise the step is computed over  */
+/* the whole vocabulary. The walk's result is then by definition the dense greedy walk's       */
+/* (oracle_walk), which is what its outputs are checked against. The one quantity the pruned  */
+/* walk adds is this load-time bound on every row's bias per unit of W1 magnitude:            */
+/*     B = max_v fl32( s[v] * fl32(sum_k |q[v,k]|) ),                                         */
+/* so that |deq(W2)[v] . w| <= sum_k |s[v] q[v,k]| |w_k| <= B * max_k |w_k| for every row v.   */
+/* The integer sum is exact in fp32 (at most 256 * 127); one product is rounded.               */
+/* ======================================================================================== */
+float oracle_w2_l1_bound(const int8_t* q, const float* s, int64_t V, int64_t R) {
+    float best = 0.0f;
+    for (int64_t v = 0; v < V; ++v) {
+        int32_t l1 = 0;
+        for (int64_t k = 0; k < R; ++k) l1 += q[v * R + k] < 0 ? -q[v * R + k] : q[v * R + k];
+        const float c = s[v] * (float)l1;
+        if (c > best) best = c;
+    }
+    return best;
+}

@@ -215,6 +215,41 @@ def test_verify_workspace_bytes():
     assert n(64, 16, 270336) == n(65, 17, 300000)       # clamped to the envelope
 
 
+def _pruned(**kw):
+    a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=1, T=7, V=151936,
+             rank=256, k=512, bound=FAKE, tokens=FAKE, logits=None, dense=None, ws=FAKE,
+             wsb=1 << 24, stream=None)
+    a.update(kw)
+    return B.lib().dspark_walk_greedy_pruned(a["q"], a["s"], a["w1"], a["dt"], a["base"],
+                                             a["start"], a["bs"], a["T"], a["V"], a["rank"],
+                                             a["k"], a["bound"], a["tokens"], a["logits"],
+                                             a["dense"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bound=None), B.ERR_INVALID_ARG),
+    (dict(bound=FAKE + 2), B.ERR_INVALID_ARG),
+    (dict(q=None), B.ERR_INVALID_ARG),
+    (dict(logits=FAKE + 4), B.ERR_INVALID_ARG),
+    (dict(dense=FAKE + 2), B.ERR_INVALID_ARG),
+    (dict(k=0), B.ERR_INVALID_ARG),
+    (dict(k=151937), B.ERR_INVALID_ARG),
+    (dict(k=2049), B.ERR_UNSUPPORTED),
+    (dict(T=17), B.ERR_UNSUPPORTED),
+    (dict(wsb=100), B.ERR_WORKSPACE),
+])
+def test_pruned_validation(kw, code):
+    assert _pruned(**kw) == code
+
+
+def test_prune_bound_validation():
+    L = B.lib()
+    assert L.dspark_w2_prune_bound(None, FAKE, 10, 256, FAKE, None) == B.ERR_INVALID_ARG
+    assert L.dspark_w2_prune_bound(FAKE, FAKE, 0, 256, FAKE, None) == B.ERR_INVALID_ARG
+    assert L.dspark_w2_prune_bound(FAKE + 4, FAKE, 10, 256, FAKE, None) == B.ERR_INVALID_ARG
+    assert L.dspark_w2_prune_bound(FAKE, FAKE, 10, 128, FAKE, None) == B.ERR_UNSUPPORTED
+
+
 def _sample(**kw):
     a = dict(q=FAKE, s=FAKE, w1=FAKE, dt=B.BF16, base=FAKE, start=FAKE, bs=1, T=7, V=151936,
              rank=256, seeds=FAKE, pos=None, temp=FAKE, tokens=FAKE, lb=FAKE, ws=FAKE,
@@ -308,6 +343,7 @@ def test_no_device_without_gpu():
     assert _sample() == B.ERR_NO_DEVICE
     assert _noalloc() == B.ERR_NO_DEVICE
     assert _verify() == B.ERR_NO_DEVICE
+    assert _pruned() == B.ERR_NO_DEVICE
     assert _noalloc(bs=64, T=16, V=270336) == B.ERR_NO_DEVICE
     p = B.WalkPlan()
     assert B.lib().dspark_walk_plan_query(1, 7, 151936, ctypes.byref(p)) == B.ERR_NO_DEVICE
