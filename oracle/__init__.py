@@ -78,6 +78,10 @@ def lib():
         L.oracle_verify.restype = ctypes.c_int
         L.oracle_w2_l1_bound.argtypes = [vp, vp, i64, i64]
         L.oracle_w2_l1_bound.restype = f32
+        L.oracle_icdf_uniform.argtypes = [u64, u64]
+        L.oracle_icdf_uniform.restype = ctypes.c_double
+        L.oracle_icdf_draw.argtypes = [vp, i64, f32, ctypes.c_double]
+        L.oracle_icdf_draw.restype = i64
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -153,8 +157,8 @@ def topk(row: np.ndarray, k: int) -> np.ndarray:
 
 
 def step(q, s, w1, base_row, prev, cand=None, sample=False, seed=0, P=0, temp=1.0):
-    """One step of one request. Returns (token, logits fp32 [V], lb uint16 [V] | None,
-    score fp32 [V] | None)."""
+    """One step of one request. sample: False (greedy), True or 1 (Gumbel), 2 (inverse CDF).
+    Returns (token, logits fp32 [V], lb uint16 [V] | None, score fp32 [V] | None)."""
     q = _c(q, np.int8)
     s = _c(s, np.float32)
     w1 = _c(w1, np.float32)
@@ -165,7 +169,7 @@ def step(q, s, w1, base_row, prev, cand=None, sample=False, seed=0, P=0, temp=1.
     score = np.empty(V, np.float32) if sample else None
     c = None if cand is None else _c(cand, np.int32)
     tok = lib().oracle_step(_ptr(q), _ptr(s), _ptr(w1), V, R, _ptr(base_row), int(prev), _ptr(c),
-                            0 if c is None else c.size, int(bool(sample)), int(seed), int(P),
+                            0 if c is None else c.size, int(sample), int(seed), int(P),
                             float(temp), _ptr(logits), _ptr(lb), _ptr(score))
     if tok < 0:
         raise OracleError(f"oracle_step failed ({tok})")
@@ -190,7 +194,7 @@ def walk(q, s, w1, base, start, k=0, sample=False, seeds=None, positions=None, t
     ps = None if positions is None else _c(positions, np.int64)
     tp = None if temps is None else _c(temps, np.float32)
     st = lib().oracle_walk(_ptr(q), _ptr(s), _ptr(w1), _ptr(base), _ptr(start), bs, T, V, R, k,
-                           int(bool(sample)), _ptr(sd), _ptr(ps), _ptr(tp), _ptr(tokens),
+                           int(sample), _ptr(sd), _ptr(ps), _ptr(tp), _ptr(tokens),
                            _ptr(logits), _ptr(lb))
     if st != OK:
         raise OracleError(f"oracle_walk failed ({st})")
@@ -233,3 +237,14 @@ def w2_l1_bound(q, s) -> float:
     s = _c(s, np.float32)
     V, R = q.shape
     return float(lib().oracle_w2_l1_bound(_ptr(q), _ptr(s), V, R))
+
+
+def icdf_uniform(seed: int, P: int) -> float:
+    """The inverse-CDF sampler's uniform for a request seed and draft position."""
+    return float(lib().oracle_icdf_uniform(seed, P))
+
+
+def icdf_draw(lb_row, temp: float, u: float) -> int:
+    """Inverse-CDF draw from a stored bf16 row (uint16 bits) with uniform u (-1: invalid row)."""
+    r = _c(lb_row, np.uint16)
+    return int(lib().oracle_icdf_draw(_ptr(r), r.size, float(temp), float(u)))

@@ -25,10 +25,13 @@ from typing import List, Optional
 
 import numpy as np
 
+from . import icdf_draw as oracle_icdf_draw
+from . import icdf_uniform as oracle_icdf_uniform
 from . import step as oracle_step
 from . import topk as oracle_topk
 
 TOL = 2e-3
+TOL_ICDF_U = 1e-5   # inverse-CDF sampling: any draw of the stored row for u +- this
 
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
@@ -92,6 +95,10 @@ def check_walk(q, s, w1, base, start, tokens, *, sample=False, seeds=None, temps
     q, s: the ORACLE's own quantisation of W2; w1 fp32 [V, R]; base [bs, T, V] fp32; start [bs];
     tokens [bs, T] from the walk under test; logits fp32 [bs, T, V] (greedy, optional);
     lb uint16 [bs, T, V] (sample, optional); requests: subset of request indices to check.
+    sample: False (greedy), True or 1 (Gumbel), 2 (inverse CDF). For the inverse-CDF sampler a
+    token that differs from the oracle's is accepted if it is a draw of the row the walk stored
+    (already checked against the oracle's logits) for some uniform within TOL_ICDF_U of the
+    step's: the draw is monotone in u, so between the draws at the two ends.
     """
     bs, T, V = base.shape
     rep = Report()
@@ -132,7 +139,17 @@ def check_walk(q, s, w1, base, start, tokens, *, sample=False, seeds=None, temps
                         f"{where}: bf16 draft logits differ at {bad.tolist()} "
                         f"(oracle {bf16_bits_to_f32(lb_o[bad])}, test {bf16_bits_to_f32(lb_t[bad])},"
                         f" l {l_o[bad]})")
-            if got != tok:
+            if got != tok and sample == 2:
+                u = oracle_icdf_uniform(seed, P)
+                row = lb_t if lb_t is not None else lb_o
+                lo = oracle_icdf_draw(row, temp, max(u - TOL_ICDF_U, 2.0 ** -24))
+                hi = oracle_icdf_draw(row, temp, min(u + TOL_ICDF_U, 1.0 - 2.0 ** -24))
+                if lo <= got <= hi:
+                    rep.near_ties.append((b, t, tok, got, 0.0))
+                else:
+                    rep.failures.append(f"{where}: token {got} vs oracle {tok} (draws of the "
+                                        f"stored row for u +- {TOL_ICDF_U}: {lo}..{hi})")
+            elif got != tok:
                 qty = sc_o if sample else l_o
                 gap = float(qty[tok]) - float(qty[got])
                 allow = tol

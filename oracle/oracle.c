@@ -208,6 +208,9 @@ int oracle_topk(const float* row, int64_t V, int64_t k, int32_t* cand) {
     return ORACLE_OK;
 }
 
+double oracle_icdf_uniform(uint64_t seed, uint64_t P);
+int64_t oracle_icdf_draw(const uint16_t* lb, int64_t V, float temp, double u);
+
 /* ---------------------------------------------------------------------------------------- */
 /* One draft step of one request (PR #62958, Overview; PR #64476, Claims; PR #49969, Purpose). */
 /*   l[v] = fp32( base[v] + sum_k s[v] * q[v,k] * W1[prev,k] )   for every v (dense), or for    */
@@ -215,6 +218,8 @@ int oracle_topk(const float* row, int64_t V, int64_t k, int32_t* cand) {
 /*   greedy:  token = argmax(l);                                                             */
 /*   sample:  lb = bf16(l); score = fp32(lb / temp + g(v)) (no divide at temp 1.0);           */
 /*            token = argmax(score).                                                          */
+/*   sample == 2 (inverse CDF): lb = bf16(l); token = oracle_icdf_draw(lb, temp, u(seed, P));  */
+/*            score receives float(lb).                                                        */
 /* logits receives l (fp32, dense). lb and score, if given, receive the bf16 row and the      */
 /* scores. Returns the token, or a negative status.                                           */
 /* ---------------------------------------------------------------------------------------- */
@@ -248,6 +253,14 @@ int64_t oracle_step(const int8_t* q, const float* s, const float* w1, int64_t V,
     }
 
     if (!sample) return oracle_argmax_f32(logits, V);
+    if (sample == 2) {
+        /* inverse-CDF sampling: the stored row, then one draw (see oracle_icdf_draw) */
+        for (int64_t v = 0; v < V; ++v) {
+            lb[v] = oracle_bf16_rne(logits[v]);
+            score[v] = oracle_bf16_to_f32(lb[v]);
+        }
+        return oracle_icdf_draw(lb, V, temp, oracle_icdf_uniform(seed, P));
+    }
 
 #pragma omp parallel for schedule(static)
     for (int64_t v = 0; v < V; ++v) {
@@ -525,4 +538,48 @@ float oracle_w2_l1_bound(const int8_t* q, const float* s, int64_t V, int64_t R) 
         if (c > best) best = c;
     }
     return best;
+}
+
+/* ======================================================================================== */
+/* Inverse-CDF sampling inside the walk (vLLM PR #62958 and #64476, Details, name a PR that    */
+/* fuses the Markov sampling loop by inverse CDF; the pages give no further detail).          */
+/* Reading: the step rounds its logits to bf16 and stores them (as the Gumbel walk does, so    */
+/* that verification works on the distribution drawn from), then draws the token from         */
+/* softmax(float(lb) / temp) by inverting its CDF in vocabulary order with one uniform per     */
+/* (request, step): the first index v whose running mass sum_{x<=v} exp(z_x - m) exceeds      */
+/* u * sum_x exp(z_x - m), z = float(lb) / temp, m = max z (fp64). The uniform comes from the  */
+/* same generator as the Gumbel noise on a disjoint counter: word 0 of Philox4x32-10 with     */
+/* counter (0, lo32(P), hi32(P), 1) and key (lo32(seed), hi32(seed)) (the Gumbel counters     */
+/* have 0 in their last word), mapped by oracle_uniform.                                      */
+/* ======================================================================================== */
+double oracle_icdf_uniform(uint64_t seed, uint64_t P) {
+    uint32_t ctr[4] = {0u, (uint32_t)P, (uint32_t)(P >> 32), 1u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return oracle_uniform(out[0]);
+}
+
+/* The inverse-CDF draw from the stored bf16 row lb with uniform u (see above). Rows must hold a */
+/* finite entry and no NaN or +inf. Returns the index, or -1 for such a row.                     */
+int64_t oracle_icdf_draw(const uint16_t* lb, int64_t V, float temp, double u) {
+    double m = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) {
+        const double z = (double)oracle_bf16_to_f32(lb[v]) / (double)temp;
+        if (isnan(z) || z == INFINITY) return -1;
+        if (z > m) m = z;
+    }
+    if (m == -INFINITY) return -1;
+    double total = 0.0;
+    for (int64_t v = 0; v < V; ++v) total += exp((double)oracle_bf16_to_f32(lb[v]) / (double)temp - m);
+    const double target = u * total;
+    double c = 0.0;
+    int64_t last = -1;
+    for (int64_t v = 0; v < V; ++v) {
+        const double e = exp((double)oracle_bf16_to_f32(lb[v]) / (double)temp - m);
+        c += e;
+        if (e > 0.0) last = v;
+        if (c > target) return v;
+    }
+    return last;
 }
