@@ -119,7 +119,7 @@ class Walk:
         self.ws = dm.new_workspace(bs, T, V, self.k)
         self.tokens = torch.empty((bs, T), dtype=torch.int32, device=dev)
         self.draft_logits = (torch.empty((bs, T, V), dtype=torch.bfloat16, device=dev)
-                             if mode == "sample" else None)
+                             if mode in ("sample", "sample_icdf") else None)
 
     def launch(self):
         if self.k:
@@ -130,6 +130,10 @@ class Walk:
         elif self.mode == "greedy":
             dm.dspark_walk_greedy(self.q, self.s, self.w1, self.base, self.start, self.ws,
                                   draft_tokens=self.tokens)
+        elif self.mode == "sample_icdf":
+            dm.dspark_walk_sample_icdf(self.q, self.s, self.w1, self.base, self.start, self.seeds,
+                                       self.temps, self.ws, draft_tokens=self.tokens,
+                                       draft_logits=self.draft_logits)
         else:
             dm.dspark_walk_sample(self.q, self.s, self.w1, self.base, self.start, self.seeds,
                                   self.temps, self.ws, draft_tokens=self.tokens,
@@ -145,7 +149,7 @@ class Walk:
             n += bs * T * k * (256 + 4)               # gathered candidate rows and scales
         else:
             n += V * 256 + V * 4
-        if self.mode == "sample":
+        if self.mode in ("sample", "sample_icdf"):
             n += bs * T * V * 2
         return n
 
@@ -413,6 +417,8 @@ SWEEP = [("v151936_t7_bs1", "sample"), ("v151936_t7_bs16", "greedy"),
          ("v129280_t5_bs64", "sample"), ("v248320_t16_bs1", "greedy"),
          ("v248320_t16_bs1", "sample"),
          ("topk512_v151936_t7_bs64", "greedy"), ("topk512_v151936_t7_bs64", "sample"),
+         ("v151936_t7_bs1", "sample_icdf"), ("v151936_t7_bs16", "sample_icdf"),
+         ("v151936_t16_bs1", "sample_icdf"),
          ("pruned:512:v151936_t7_bs1", "greedy"), ("pruned:512:v151936_t7_bs16", "greedy"),
          ("pruned:512:v151936_t7_bs64", "greedy"),
          ("verify:64:7:151936", "token"), ("verify:64:7:151936", "block"),

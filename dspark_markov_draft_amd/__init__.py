@@ -7,5 +7,5 @@ from .binding import (  # noqa: F401
     dspark_walk_greedy_noalloc, dspark_walk_plan_query, dspark_walk_sample, dspark_walk_topk,
     dspark_walk_workspace_bytes, dspark_workspace_status, new_workspace, dspark_verify,
     dspark_verify_workspace_bytes, VERIFY_TOKEN, VERIFY_BLOCK, dspark_w2_prune_bound,
-    dspark_walk_greedy_pruned,
+    dspark_walk_greedy_pruned, dspark_walk_sample_icdf,
 )

@@ -76,6 +76,8 @@ def lib():
                                                  vp, vp, vp]
         L.dspark_walk_sample.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, vp, vp, vp,
                                          vp, vp, vp, ctypes.c_size_t, vp]
+        L.dspark_walk_sample_icdf.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, vp, vp,
+                                              vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dspark_walk_topk.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i64, i32, vp,
                                        vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dspark_walk_plan_for.argtypes = [ctypes.c_int32, i64, i64, i64, i64,
@@ -96,7 +98,8 @@ def lib():
                      "dspark_walk_greedy", "dspark_walk_greedy_noalloc",
                      "dspark_walk_sample", "dspark_walk_topk", "dspark_workspace_status",
                      "dspark_philox_words", "dspark_debug_set", "dspark_kernel_times",
-                     "dspark_verify", "dspark_w2_prune_bound", "dspark_walk_greedy_pruned"]:
+                     "dspark_verify", "dspark_w2_prune_bound", "dspark_walk_greedy_pruned",
+                     "dspark_walk_sample_icdf"]:
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -296,6 +299,32 @@ def dspark_walk_sample(q, s, w1, base, start, seeds, temperature, workspace, pos
                                     _p(temperature), _p(draft_tokens), _p(draft_logits),
                                     _p(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
+    return draft_tokens, draft_logits
+
+
+def dspark_walk_sample_icdf(q, s, w1, base, start, seeds, temperature, workspace,
+                            positions=None, draft_tokens=None, draft_logits=None, stream=None):
+    """Probabilistic walk drawing each token by inverse CDF (arguments and outputs as
+    dspark_walk_sample). Returns (draft_tokens [bs, T] int32, draft_logits [bs, T, V] bf16)."""
+    _expect(base, "base", torch.float32, None)
+    if base.dim() == 3:
+        bs, T, V = base.shape
+        if draft_tokens is None:
+            draft_tokens = torch.empty((bs, T), dtype=torch.int32, device=base.device)
+        if draft_logits is None:
+            draft_logits = torch.empty((bs, T, V), dtype=torch.bfloat16, device=base.device)
+    bs, T, V = _check_walk_args(q, s, w1, base, start, workspace, draft_tokens)
+    _check_sample_args(bs, seeds, temperature, positions)
+    _expect(draft_logits, "draft_logits", torch.bfloat16, (bs, T, V))
+    _same_device(q=q, s=s, w1=w1, base=base, start=start, workspace=workspace,
+                 draft_tokens=draft_tokens, draft_logits=draft_logits, seeds=seeds,
+                 temperature=temperature, positions=positions)
+    _check(lib().dspark_walk_sample_icdf(_p(q), _p(s), _p(w1), _dtype_code(w1), _p(base),
+                                         _p(start), bs, T, V, q.shape[1], _p(seeds),
+                                         _p(positions), _p(temperature), _p(draft_tokens),
+                                         _p(draft_logits), _p(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(stream)))
     return draft_tokens, draft_logits
 
 

@@ -303,6 +303,36 @@ int dspark_walk_sample(const int8_t* w2_q, const float* w2_scale, const void* w1
     return dense_walk(a, rank, workspace_bytes, stream);
 }
 
+int dspark_walk_sample_icdf(const int8_t* w2_q, const float* w2_scale, const void* w1,
+                            int w1_dtype, const float* base_logits, const int32_t* start_tokens,
+                            int64_t bs, int64_t T, int64_t V, int64_t rank,
+                            const uint64_t* seeds, const int64_t* positions,
+                            const float* temperature, int32_t* draft_tokens,
+                            uint16_t* draft_logits, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    WalkLaunch a = {};
+    a.q = w2_q;
+    a.scale = w2_scale;
+    a.w1 = w1;
+    a.w1_dtype = w1_dtype;
+    a.base = base_logits;
+    a.start = start_tokens;
+    a.tokens = draft_tokens;
+    a.draft_logits = draft_logits;
+    a.seeds = seeds;
+    a.positions = positions;
+    a.temps = temperature;
+    a.workspace = workspace;
+    a.sample = 2;
+    if (bs > DSPARK_MAX_BS || T > DSPARK_MAX_STEPS || V > DSPARK_MAX_V) {
+        return (bs < 1 || T < 1 || V < 1) ? DSPARK_ERR_INVALID_ARG : DSPARK_ERR_UNSUPPORTED;
+    }
+    a.bs = (int)bs;
+    a.T = (int)T;
+    a.V = (int)V;
+    return dense_walk(a, rank, workspace_bytes, stream);
+}
+
 int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
                      const float* base_logits, const int32_t* start_tokens, int64_t bs,
                      int64_t T, int64_t V, int64_t rank, int64_t k, int sample,

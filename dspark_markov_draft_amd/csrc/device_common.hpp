@@ -179,6 +179,57 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t x) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Inverse-CDF sampling (the walk's second sampler). The uniform of a request at draft position P
+// is word 0 of Philox4x32-10 at counter (0, lo32 P, hi32 P, 1) under the request's seed, a
+// counter space disjoint from the Gumbel noise's (whose last counter word is 0), mapped to
+// (2 (x >> 9) + 1) 2^-24 like the noise. The step's distribution is softmax(lb / temp), handled
+// in the base-2 domain: z = lb * (log2(e) / temp), probabilities 2^(z - m) / s.
+// ---------------------------------------------------------------------------------------------
+constexpr float LOG2E_F = 1.4426950408889634f;
+
+__device__ __forceinline__ float icdf_uniform(uint64_t seed, uint64_t P) {
+    const uint4 r = philox4x32_10(0u, (uint32_t)P, (uint32_t)(P >> 32), 1u, (uint32_t)seed,
+                                  (uint32_t)(seed >> 32));
+    return (float)(2u * (r.x >> 9) + 1u) * 0x1p-24f;
+}
+
+// Running maximum m and sum s of 2^(z - m) over the values offered (m = -inf, s = 0: none, or
+// only -inf values). merge() combines two such pairs.
+struct RunningSoftmax {
+    float m = -INFINITY, s = 0.0f;
+    __device__ __forceinline__ void merge(float m2, float s2) {
+        const float M = fmaxf(m, m2);
+        const float a = m == -INFINITY ? 0.0f : s * exp2f(m - M);
+        const float b = m2 == -INFINITY ? 0.0f : s2 * exp2f(m2 - M);
+        m = M;
+        s = a + b;
+    }
+    __device__ __forceinline__ void offer(float z, bool ok) {
+        if (ok) merge(z, 1.0f);
+    }
+};
+// A pair as one 64-bit word (m's bits high, s's low). A real pair is never 0: s >= 1 when m is
+// finite, and m = -inf has non-zero bits.
+__device__ __forceinline__ uint64_t pack_softmax(float m, float s) {
+    return ((uint64_t)__float_as_uint(m) << 32) | __float_as_uint(s);
+}
+__device__ __forceinline__ float packed_m(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+__device__ __forceinline__ float packed_s(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// Wave-wide merge of (m, s) pairs; every lane ends with the whole wave's pair.
+__device__ __forceinline__ void wave_softmax(float& m, float& s) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        RunningSoftmax r;
+        r.m = m;
+        r.s = s;
+        r.merge(__shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+        m = r.m;
+        s = r.s;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Wave-wide maxima over the 64 lanes with DPP lane moves (a few cycles each, against ~100 for
 // an LDS-routed shuffle): swap within pairs and quads, mirror within 8 and 16 lanes, then
 // broadcast lane 15 of each 16-lane row into the next row and lane 31 into the upper half;

@@ -12,6 +12,7 @@ namespace dspark {
 // Workspace layout of a walk call (bytes from the start of the caller's workspace). A walk
 // leaves every word it uses at zero when it exits, so the caller zeroes the workspace once.
 constexpr size_t WS_ERR = 0;          // u32 error word (DSPARK_ERR_TIMEOUT / INVALID_ARG)
+constexpr size_t WS_ICDF_DONE = 2048; // u64 [256]: inverse-CDF walks' end-of-walk flags
 constexpr int RESULT_REPLICAS = 16;   // copies of the result words, read by disjoint workgroups
 constexpr size_t WS_RESULT = 4096;    // u64 [8 copies][16 steps][64 requests]: each step's winner
 constexpr size_t WS_SLOTS = WS_RESULT + (size_t)RESULT_REPLICAS * 16 * 64 * 8;  // then
@@ -68,7 +69,7 @@ struct WalkLaunch {
     void* workspace;
     uint32_t* error_word;     // where errors are recorded; NULL: the workspace's error word
     int bs, T, V;
-    int sample;
+    int sample;               // 0 greedy, 1 Gumbel-max, 2 inverse CDF
 };
 int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan, hipStream_t stream);
 

@@ -136,8 +136,10 @@ int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, int sampl
     int path = (bs >= min_bs && V % 4 == 0) ? DSPARK_PATH_MFMA
                : bs == 1                      ? DSPARK_PATH_MFMA1
                                               : DSPARK_PATH_DOT4;
+    // the inverse-CDF sampler runs on the one-request MFMA and lane-per-row kernels only
+    if (sample == 2 && path == DSPARK_PATH_MFMA) path = DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_DOT4) path = DSPARK_PATH_DOT4;
-    if (dbg.force_path == DSPARK_PATH_MFMA && V % 4 == 0) path = DSPARK_PATH_MFMA;
+    if (dbg.force_path == DSPARK_PATH_MFMA && V % 4 == 0 && sample != 2) path = DSPARK_PATH_MFMA;
     if (dbg.force_path == DSPARK_PATH_MFMA1 && bs == 1) path = DSPARK_PATH_MFMA1;
     if (path != DSPARK_PATH_DOT4 && plan_path(dev, cap, bs, V, path, sample, plan) == DSPARK_OK)
         return DSPARK_OK;
@@ -179,6 +181,7 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     p.result = reinterpret_cast<uint64_t*>(ws + WS_RESULT);
     p.slots = reinterpret_cast<uint64_t*>(ws + WS_SLOTS);
     p.err = a.error_word ? a.error_word : reinterpret_cast<uint32_t*>(ws + WS_ERR);
+    p.done = reinterpret_cast<uint64_t*>(ws + WS_ICDF_DONE);
     p.never = reinterpret_cast<const uint32_t*>(ws + WS_ERR + 4);
     p.bs = a.bs;
     p.T = a.T;
@@ -195,7 +198,7 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     p.spin_ticks = dbg.spin_ticks ? dbg.spin_ticks : DEFAULT_SPIN_TICKS;
     p.wait_unset = dbg.wait_unset ? 1 : 0;
     p.stamps = reinterpret_cast<uint64_t*>(dbg.stamps);
-    const bool timed = p.stamps != nullptr && a.w1_dtype == DSPARK_BF16;
+    const bool timed = p.stamps != nullptr && a.w1_dtype == DSPARK_BF16 && a.sample != 2;
 
     const int w1t = a.w1_dtype == DSPARK_F32 ? DT_F32 : a.w1_dtype == DSPARK_BF16 ? DT_BF16 : DT_F16;
     // the MFMA kernel for small slices keeps all its LDS in static arrays (no dynamic LDS)

@@ -70,6 +70,7 @@ struct WalkParams {
     uint32_t* err;
     const uint32_t* never;  // a workspace word nothing writes (test hook)
     uint64_t* stamps;       // instrumented builds: [num workgroups][STAMPS_PER_WG]
+    uint64_t* done;         // inverse-CDF walks: [256] end-of-walk flags (workspace)
     int bs, T, V;
     int rows_per_wg;        // contiguous W2 rows per workgroup (the last may own fewer)
     int reg_units;          // register-resident row sets (dot4) or tiles per wave (MFMA)
@@ -551,7 +552,317 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
     stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 4);
 }
 
-// Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0/1; w1t: DT_*).
+// ---- inverse-CDF combine (sample == 2) ---------------------------------------------------------
+// Each workgroup holds, per request, the pair (m, s) of its slice: the maximum m of z =
+// lb * log2(e) / temp over its rows and s = sum 2^(z - m). The token is the first row whose
+// running mass passes u * (total mass), which takes three hops per step (wave 0, lanes =
+// requests, all waits bounded in time):
+//  1. every workgroup stores its pair of request b in the step's slots ([b][workgroup], as the
+//     argmax keys); the reducer of b (workgroup b % num workgroups) reads them all, merges them in
+//     workgroup order (the vocabulary order of the slices), finds the workgroup w* whose slice
+//     holds the point u * S and the remaining mass lt inside it (in units of 2^(z - m_w*)),
+//     clears the slots, and publishes (w* + 1, lt) in ICDF_REPL copies of the step's selection
+//     word; having seen every pair of step t it also clears request b's selection and token
+//     words of step t - 1 (every workgroup read them before storing a pair of step t);
+//  2. every workgroup reads the selection words; for each request that selects it, it scans its
+//     own slice of the stored bf16 row (its own stores, visible after the workgroup barrier that
+//     precedes the combine) in vocabulary order for the first row whose running mass passes lt
+//     (the slice's last row with mass if rounding leaves none), writes the token and, unless the
+//     step is the last, publishes it (+1) in ICDF_REPL copies of the step's token word;
+//  3. every workgroup reads the token words (not after the last step).
+// After the last step every workgroup raises its done flag, and workgroup 0 waits for all of
+// them and clears the last step's selection words and the flags: the workspace is zero again.
+constexpr int ICDF_REPL = RESULT_REPLICAS / 2;   // copies of each selection / token word
+constexpr int ICDF_SCAN_ROWS = 8;                // rows per lane per pass of the slice scan
+
+__device__ __forceinline__ uint64_t* icdf_sel_word(const WalkParams& p, int rep, int t, int b) {
+    return result_word(p, rep, t, b);
+}
+__device__ __forceinline__ uint64_t* icdf_tok_word(const WalkParams& p, int rep, int t, int b) {
+    return result_word(p, ICDF_REPL + rep, t, b);
+}
+
+// Run by one whole wave: the first row of this workgroup's slice whose running mass
+// sum 2^(z - m) passes lt, z = lb * kz over the stored row of request b at step t.
+__device__ __forceinline__ uint32_t icdf_scan_slice(const WalkParams& p, int b, int t, float m,
+                                                    float kz, float lt, int lane) {
+    const int row0 = blockIdx.x * p.rows_per_wg;
+    const int nrows = min(p.rows_per_wg, p.V - row0);
+    const uint16_t* lb = p.draft_logits + ((int64_t)b * p.T + t) * p.V + row0;
+    float run = 0.0f;       // mass of the passes before
+    int last = -1;          // last row with mass (the rounding fallback)
+    for (int r0 = 0; r0 < nrows; r0 += WAVE * ICDF_SCAN_ROWS) {
+        const int rb = r0 + lane * ICDF_SCAN_ROWS;
+        float e[ICDF_SCAN_ROWS];
+        float mine = 0.0f;
+#pragma unroll
+        for (int i = 0; i < ICDF_SCAN_ROWS; ++i) {
+            const int r = rb + i;
+            const float x = r < nrows ? bf16_value(lb[r]) : -INFINITY;
+            e[i] = x == -INFINITY ? 0.0f : exp2f(x * kz - m);
+            mine += e[i];
+            if (e[i] > 0.0f) last = max(last, r);
+        }
+        float incl = mine;
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const float v = __shfl_up(incl, o, WAVE);
+            if (lane >= o) incl += v;
+        }
+        const float before = run + (incl - mine);
+        const uint64_t cross = __ballot(mine > 0.0f && before + mine > lt);
+        if (cross) {
+            const int L = __builtin_ctzll(cross);
+            int tok = -1;
+            if (lane == L) {
+                float c = before;
+#pragma unroll
+                for (int i = 0; i < ICDF_SCAN_ROWS; ++i) {
+                    c += e[i];
+                    if (tok < 0 && e[i] > 0.0f && c > lt) tok = rb + i;
+                }
+                if (tok < 0) {       // rounding inside the lane: its last row with mass
+#pragma unroll
+                    for (int i = 0; i < ICDF_SCAN_ROWS; ++i)
+                        if (e[i] > 0.0f) tok = rb + i;
+                }
+            }
+            return (uint32_t)(row0 + __shfl(tok, L, WAVE));
+        }
+        run += __shfl(incl, WAVE - 1, WAVE);
+    }
+    // the running mass never passed lt (rounding): the slice's last row with mass
+    int l = last;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l = max(l, __shfl_xor(l, o, WAVE));
+    return (uint32_t)(row0 + max(l, 0));
+}
+
+template <int TIMED>
+__device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, uint64_t pair,
+                                                  int32_t* tok, int lane) {
+    const int nwg = gridDim.x;
+    const int wg = blockIdx.x;
+    const bool last_step = t + 1 == p.T;
+    uint64_t* step_slots = p.slots + (size_t)t * nwg * p.stride;
+    if (lane < p.bs) st_dev(step_slots + (size_t)lane * nwg + wg, pair);
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 2);
+
+    // ---- 1. reducers: merge the pairs, select the slice ----------------------------------------
+    constexpr int NL = MAX_WORKGROUPS / WAVE;
+    for (int b = wg; b < p.bs; b += nwg) {
+        const uint64_t* col = step_slots + (size_t)b * nwg;
+        auto issue = [&](uint64_t (&v)[NL]) {
+#pragma unroll
+            for (int k = 0; k < NL; ++k) v[k] = ld_dev(col + min(lane + k * WAVE, nwg - 1));
+        };
+        auto complete = [&](const uint64_t (&v)[NL]) {
+            bool all = true;
+#pragma unroll
+            for (int k = 0; k < NL; ++k) all = all && v[k] != 0;
+            if (p.wait_unset)
+                all = all && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) != 0;
+            return __all(all);
+        };
+        uint64_t va[NL], vb[NL];
+        const WaitBound wait;
+        bool ok = true;
+        issue(va);
+        while (true) {
+            const uint64_t now = WaitBound::now();
+            issue(vb);
+            if (complete(va)) break;
+            issue(va);
+            if (complete(vb)) {
+#pragma unroll
+                for (int k = 0; k < NL; ++k) va[k] = vb[k];
+                break;
+            }
+            if (wait.expired(now, p.spin_ticks)) {
+                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                ok = false;
+                break;
+            }
+        }
+        // the slice pairs in workgroup order: k-major (workgroup k * 64 + lane)
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NL; ++k)
+            if (lane + k * WAVE < nwg && va[k] != 0) M = fmaxf(M, packed_m(va[k]));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, WAVE));
+        float mass[NL];
+        float S = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const bool in = lane + k * WAVE < nwg && va[k] != 0;
+            const float m = packed_m(va[k]);
+            mass[k] = (in && m != -INFINITY) ? packed_s(va[k]) * exp2f(m - M) : 0.0f;
+        }
+        // running mass in workgroup order, and the first workgroup whose interval passes u * S
+        float tot[NL], before[NL];
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            float incl = mass[k];
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const float v = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += v;
+            }
+            tot[k] = __shfl(incl, WAVE - 1, WAVE);
+            before[k] = incl - mass[k];
+        }
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            before[k] += S;
+            S += tot[k];
+        }
+        const uint64_t seed = p.seeds[b];
+        const uint64_t P = (uint64_t)(p.positions ? p.positions[b] : 0) + (uint64_t)t;
+        const float target = icdf_uniform(seed, P) * S;
+        int wsel = -1;
+        float lt = INFINITY;
+        int lastw = 0;
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const uint64_t has = __ballot(mass[k] > 0.0f);
+            if (has) lastw = k * WAVE + 63 - __builtin_clzll(has);
+            const uint64_t cross = __ballot(mass[k] > 0.0f && before[k] + mass[k] > target);
+            if (wsel < 0 && cross) {
+                const int L = __builtin_ctzll(cross);
+                wsel = k * WAVE + L;
+                // remaining mass inside the selected slice, in units of its own 2^(z - m_w*)
+                const float rem = target - __shfl(before[k], L, WAVE);
+                const float mw = __shfl(packed_m(va[k]), L, WAVE);
+                lt = rem * exp2f(M - mw);
+            }
+        }
+        if (wsel < 0) wsel = lastw;        // rounding: the last slice with mass, its last row
+        if (!ok) wsel = 0;
+        // clear the pairs read, and request b's words of step t - 1
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int w = lane + k * WAVE;
+            if (w < nwg) st_dev(step_slots + (size_t)b * nwg + w, 0);
+        }
+        if (lane < ICDF_REPL) {
+            if (t > 0) {
+                st_dev(icdf_sel_word(p, lane, t - 1, b), 0);
+                st_dev(icdf_tok_word(p, lane, t - 1, b), 0);
+            }
+            st_dev(icdf_sel_word(p, lane, t, b),
+                   ((uint64_t)(uint32_t)(wsel + 1) << 32) | __float_as_uint(lt));
+        }
+    }
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 3);
+
+    // ---- 2. every workgroup: the selection words; scan own slice for the requests it holds ----
+    {
+        const uint64_t* mine = icdf_sel_word(p, wg % ICDF_REPL, t, lane < p.bs ? lane : 0);
+        auto seen = [&](uint64_t k) {
+            bool okk = lane >= p.bs || k != 0;
+            if (p.wait_unset)
+                okk = okk && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) != 0;
+            return __all(okk);
+        };
+        uint64_t ka = ld_dev(mine), kb, sel = 0;
+        const WaitBound wait;
+        while (true) {
+            const uint64_t now = WaitBound::now();
+            kb = ld_dev(mine);
+            if (seen(ka)) { sel = ka; break; }
+            ka = ld_dev(mine);
+            if (seen(kb)) { sel = kb; break; }
+            if (wait.expired(now, p.spin_ticks)) {
+                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                sel = kb;
+                break;
+            }
+        }
+        uint64_t todo = __ballot(lane < p.bs && sel != 0 && (int)(sel >> 32) - 1 == wg);
+        while (todo) {
+            const int b = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const uint64_t sb = __shfl(sel, b, WAVE);
+            const float lt = __uint_as_float((uint32_t)sb);
+            const float kz = LOG2E_F * inv_temperature(p.temps[b]);
+            // this slice's own pair of request b: the one it stored (lane b holds it)
+            const float m_own = packed_m(__shfl(pair, b, WAVE));
+            uint32_t token = icdf_scan_slice(p, b, t, m_own, kz, lt, lane);
+            if (token >= (uint32_t)p.V) token = 0;
+            if (lane == 0) p.tokens[b * p.T + t] = (int32_t)token;
+            if (!last_step && lane < ICDF_REPL)
+                st_dev(icdf_tok_word(p, lane, t, b), (uint64_t)token + 1);
+        }
+    }
+    stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 4);
+
+    if (!last_step) {
+        // ---- 3. the tokens ----------------------------------------------------------------------
+        const uint64_t* mine = icdf_tok_word(p, wg % ICDF_REPL, t, lane < p.bs ? lane : 0);
+        auto seen = [&](uint64_t k) {
+            bool okk = lane >= p.bs || k != 0;
+            if (p.wait_unset)
+                okk = okk && __hip_atomic_load(p.never, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) != 0;
+            return __all(okk);
+        };
+        uint64_t ka = ld_dev(mine), kb, k = 0;
+        const WaitBound wait;
+        while (true) {
+            const uint64_t now = WaitBound::now();
+            kb = ld_dev(mine);
+            if (seen(ka)) { k = ka; break; }
+            ka = ld_dev(mine);
+            if (seen(kb)) { k = kb; break; }
+            if (wait.expired(now, p.spin_ticks)) {
+                if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                k = kb;
+                break;
+            }
+        }
+        if (lane < p.bs) {
+            uint32_t token = k == 0 ? 0u : (uint32_t)(k - 1);
+            if (token >= (uint32_t)p.V) token = 0;
+            tok[lane] = (int32_t)token;
+        }
+    } else {
+        // ---- end of walk: done flags; workgroup 0 clears the last step's selection words ----
+        if (lane == 0) st_dev(p.done + wg, 1);
+        if (wg == 0) {
+            auto all_done = [&]() {
+                bool a = true;
+#pragma unroll
+                for (int k = 0; k < NL; ++k) {
+                    const int w = lane + k * WAVE;
+                    if (w < nwg) a = a && ld_dev(p.done + w) != 0;
+                }
+                return __all(a);
+            };
+            const WaitBound wait;
+            while (true) {
+                const uint64_t now = WaitBound::now();
+                if (all_done()) break;
+                if (wait.expired(now, p.spin_ticks)) {
+                    if (lane == 0) flag_error(p.err, DSPARK_ERR_TIMEOUT);
+                    break;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NL; ++k) {
+                const int w = lane + k * WAVE;
+                if (w < nwg) st_dev(p.done + w, 0);
+            }
+            for (int i = lane; i < ICDF_REPL * p.bs; i += WAVE)
+                st_dev(icdf_sel_word(p, i / p.bs, t, i % p.bs), 0);
+        }
+    }
+}
+
+// Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0 greedy, 1 Gumbel,
+// 2 inverse CDF (one-request MFMA and lane-per-row kernels only); w1t: DT_*).
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
 const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles);
 const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits);

@@ -129,19 +129,26 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                         rtemp = inv_temperature(p.temps[b]);
                     }
                     // logit of row v -> output store, offered to this lane's running argmax (its
-                    // rows come in increasing index order)
+                    // rows come in increasing index order), or (inverse CDF) to its running
+                    // softmax pair
                     RunningArgmax run;
+                    RunningSoftmax soft;
+                    const float kz = rtemp * LOG2E_F;
                     auto finish = [&](int v, float base_v, float scale_v, int acc) {
                         const float l = walk_logit(base_v, scale_v, sb, acc);
                         if constexpr (!SAMPLE) {
                             if (p.out_logits) p.out_logits[orow + v] = l;
                             run.offer(l, (uint32_t)v, true);
-                        } else {
+                        } else if constexpr (SAMPLE == 1) {
                             const uint32_t h = bf16_bits(l);
                             p.draft_logits[orow + v] = (uint16_t)h;
                             const float x = bf16_value(h) * rtemp;
                             const float g = gumbel_from_word(noise_word(seed, P, (uint32_t)v));
                             run.offer(x + g, (uint32_t)v, true);
+                        } else {
+                            const uint32_t h = bf16_bits(l);
+                            p.draft_logits[orow + v] = (uint16_t)h;
+                            soft.offer(bf16_value(h) * kz, true);
                         }
                     };
 
@@ -203,8 +210,13 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                             finish(row0 + r, bv, sv, a);
                         }
                     }
-                    const uint64_t best = wave_max_u64(run.key());
-                    if (lane == 0) wkeys[wave * MAX_BS + b] = best;
+                    if constexpr (SAMPLE == 2) {
+                        wave_softmax(soft.m, soft.s);
+                        if (lane == 0) wkeys[wave * MAX_BS + b] = pack_softmax(soft.m, soft.s);
+                    } else {
+                        const uint64_t best = wave_max_u64(run.key());
+                        if (lane == 0) wkeys[wave * MAX_BS + b] = best;
+                    }
                 }
             }
         }
@@ -219,17 +231,30 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
         }
         if (wave == 0) {
             uint64_t k = 0;
-            if (lane < p.bs) {
-                // the four waves' keys: all read before any compare (one LDS round trip)
-                uint64_t o[WALK_WAVES];
+            if constexpr (SAMPLE == 2) {
+                if (lane < p.bs) {
+                    RunningSoftmax a;
 #pragma unroll
-                for (int w = 0; w < WALK_WAVES; ++w) o[w] = wkeys[w * MAX_BS + lane];
-                asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
-                const uint64_t k01 = o[1] > o[0] ? o[1] : o[0];
-                const uint64_t k23 = o[3] > o[2] ? o[3] : o[2];
-                k = k23 > k01 ? k23 : k01;
+                    for (int w = 0; w < WALK_WAVES; ++w) {
+                        const uint64_t o = wkeys[w * MAX_BS + lane];
+                        a.merge(packed_m(o), packed_s(o));
+                    }
+                    k = pack_softmax(a.m, a.s);
+                }
+                combine_icdf_step<TIMED>(p, t, k, tok, lane);
+            } else {
+                if (lane < p.bs) {
+                    // the four waves' keys: all read before any compare (one LDS round trip)
+                    uint64_t o[WALK_WAVES];
+#pragma unroll
+                    for (int w = 0; w < WALK_WAVES; ++w) o[w] = wkeys[w * MAX_BS + lane];
+                    asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+                    const uint64_t k01 = o[1] > o[0] ? o[1] : o[0];
+                    const uint64_t k23 = o[3] > o[2] ? o[3] : o[2];
+                    k = k23 > k01 ? k23 : k01;
+                }
+                combine_step<TIMED>(p, t, k, tok, lane);
             }
-            combine_step<TIMED>(p, t, k, tok, lane);
         }
         __syncthreads();
     }
@@ -237,6 +262,13 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
 
 const void* dot4_walk_kernel(int sample, int w1t, bool timed) {
 #define DSPARK_DOT4(S, W, TI) reinterpret_cast<const void*>(&dense_walk_dot4_kernel<S, W, TI>)
+    if (sample == 2) {
+        switch (w1t) {
+            case DT_F32: return DSPARK_DOT4(2, DT_F32, 0);
+            case DT_BF16: return DSPARK_DOT4(2, DT_BF16, 0);
+            default: return DSPARK_DOT4(2, DT_F16, 0);
+        }
+    }
     if (timed) return sample ? DSPARK_DOT4(1, DT_BF16, 1) : DSPARK_DOT4(0, DT_BF16, 1);
     if (sample) {
         switch (w1t) {

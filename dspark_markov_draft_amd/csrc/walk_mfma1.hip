@@ -134,6 +134,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         pos0 = (uint64_t)(p.positions ? p.positions[0] : 0);
         rtemp = inv_temperature(p.temps[0]);
     }
+    const float kz = rtemp * LOG2E_F;   // inverse CDF: z = lb * log2(e) / temp
 
     for (int t = 0; t < p.T; ++t) {
         // every wave's base logits of this step were issued before the previous combine: the
@@ -178,6 +179,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         const int64_t orow = (int64_t)t * p.V;
         const uint64_t P = pos0 + (uint64_t)t;
         RunningArgmax run;
+        RunningSoftmax soft;
 #pragma unroll
         for (int gi = 0; gi < M1_GROUPS; ++gi) {
             // this lane's row of tile slot 4 gi + ts: component ri of that slot's result
@@ -201,16 +203,25 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
             if constexpr (!SAMPLE) {
                 if (p.out_logits && vok[gi]) p.out_logits[orow + v] = l;
                 run.offer(l, (uint32_t)v, vok[gi]);
-            } else {
+            } else if constexpr (SAMPLE == 1) {
                 const uint32_t h = bf16_bits(l);
                 if (vok[gi]) p.draft_logits[orow + v] = (uint16_t)h;
                 const float x = bf16_value(h) * rtemp;
                 const float gn = gumbel_from_word(noise_word(seed, P, (uint32_t)v));
                 run.offer(x + gn, (uint32_t)v, vok[gi]);
+            } else {
+                const uint32_t h = bf16_bits(l);
+                if (vok[gi]) p.draft_logits[orow + v] = (uint16_t)h;
+                soft.offer(bf16_value(h) * kz, vok[gi]);
             }
         }
-        const uint64_t best = wave_max_u64(run.key());
-        if (lane == 0) wkeys[wave * MAX_BS] = best;
+        if constexpr (SAMPLE == 2) {
+            wave_softmax(soft.m, soft.s);
+            if (lane == 0) wkeys[wave * MAX_BS] = pack_softmax(soft.m, soft.s);
+        } else {
+            const uint64_t best = wave_max_u64(run.key());
+            if (lane == 0) wkeys[wave * MAX_BS] = best;
+        }
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
 
@@ -218,15 +229,26 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         if (t + 1 < p.T) load_base(t + 1);
         if (wave == 0) {
             uint64_t k = 0;
-            if (lane == 0) {
-                uint64_t o[WALK_WAVES];
+            if constexpr (SAMPLE == 2) {
+                RunningSoftmax a;
 #pragma unroll
-                for (int w = 0; w < WALK_WAVES; ++w) o[w] = wkeys[w * MAX_BS];
-                const uint64_t k01 = o[1] > o[0] ? o[1] : o[0];
-                const uint64_t k23 = o[3] > o[2] ? o[3] : o[2];
-                k = k23 > k01 ? k23 : k01;
+                for (int w = 0; w < WALK_WAVES; ++w) {
+                    const uint64_t o = wkeys[w * MAX_BS];
+                    a.merge(packed_m(o), packed_s(o));
+                }
+                k = pack_softmax(a.m, a.s);
+                combine_icdf_step<TIMED>(p, t, k, tok, lane);
+            } else {
+                if (lane == 0) {
+                    uint64_t o[WALK_WAVES];
+#pragma unroll
+                    for (int w = 0; w < WALK_WAVES; ++w) o[w] = wkeys[w * MAX_BS];
+                    const uint64_t k01 = o[1] > o[0] ? o[1] : o[0];
+                    const uint64_t k23 = o[3] > o[2] ? o[3] : o[2];
+                    k = k23 > k01 ? k23 : k01;
+                }
+                combine_step<TIMED>(p, t, k, tok, lane);
             }
-            combine_step<TIMED>(p, t, k, tok, lane);
         }
         __syncthreads();
     }
@@ -235,6 +257,13 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
 template <int LDS>
 static const void* mfma1_kernel_for(int sample, int w1t, bool timed) {
 #define DSPARK_MFMA1(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma1_kernel<S, W, TI, LDS>)
+    if (sample == 2) {
+        switch (w1t) {
+            case DT_F32: return DSPARK_MFMA1(2, DT_F32, 0);
+            case DT_BF16: return DSPARK_MFMA1(2, DT_BF16, 0);
+            default: return DSPARK_MFMA1(2, DT_F16, 0);
+        }
+    }
     if (timed) return sample ? DSPARK_MFMA1(1, DT_BF16, 1) : DSPARK_MFMA1(0, DT_BF16, 1);
     if (sample) {
         switch (w1t) {

@@ -181,6 +181,28 @@ int dspark_walk_sample(const int8_t* w2_q, const float* w2_scale, const void* w1
                        size_t workspace_bytes, void* stream);
 
 /*
+ * Probabilistic walk drawing each token by inverse CDF instead of Gumbel-max (vLLM PR #62958
+ * and #64476, Details, name a PR that fuses the Markov sampling loop by inverse CDF; the pages
+ * give no further detail). Arguments and outputs as dspark_walk_sample: the same bf16 row lb is
+ * stored in draft_logits, and the token is drawn from softmax(lb / temperature) by inverting its
+ * CDF in vocabulary order with one uniform per (request, step): the first index whose running
+ * mass exceeds u times the total, u = (2 (x >> 9) + 1) 2^-24 with x word 0 of Philox4x32-10 at
+ * counter (0, lo32 P, hi32 P, 1), key the request's seed, P = positions[b] + t (the Gumbel
+ * noise uses counters whose last word is 0). Base logits must hold no NaN or +inf, and each
+ * step a finite logit. One request runs on the one-request matrix-core kernel, more on the
+ * lane-per-row kernel. Each step takes three grid-wide exchanges: the slices' softmax pairs to
+ * one reducer per request, its choice of slice to every workgroup, the chosen slice's token
+ * to every workgroup.
+ */
+int dspark_walk_sample_icdf(const int8_t* w2_q, const float* w2_scale, const void* w1,
+                            int w1_dtype, const float* base_logits, const int32_t* start_tokens,
+                            int64_t bs, int64_t T, int64_t V, int64_t rank,
+                            const uint64_t* seeds, const int64_t* positions,
+                            const float* temperature, int32_t* draft_tokens,
+                            uint16_t* draft_logits, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * Top-k walk (PR #49969, Purpose). For each (request, step) the k largest base logits are the
  * candidates (at equal values the lower index ranks first); the Markov bias is evaluated for
  * candidates only; every other entry of the row is -inf; then greedy (sample = 0) or Gumbel
