@@ -54,11 +54,15 @@ struct RunningArgmax {
 };
 
 // The drafted logit of one vocabulary row: base + (s[v] * s1) * acc, where acc is the exact
-// int32 dot product of the row's int8 codes with the request's int8 W1 codes and s1 the W1
-// row's scale. Written as one explicit fused multiply-add so that every kernel (dense dot4,
+// int32 dot product of the row's int8 codes with the request's integer W1 codes and s1 the W1
+// row's code step. Written as one explicit fused multiply-add so that every kernel (dense dot4,
 // MFMA, top-k) rounds it identically.
 __device__ __forceinline__ float walk_logit(float base, float s_row, float s1, int32_t acc) {
     return __builtin_fmaf(s_row * s1, (float)acc, base);
+}
+// The dot product with the W1 codes C = 16 hi + lo from its two int8 parts (exact in int32).
+__device__ __forceinline__ int32_t join_digits(int32_t dot_hi, int32_t dot_lo) {
+    return (int32_t)((uint32_t)dot_hi << 4) + dot_lo;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -261,6 +265,7 @@ constexpr int DPP_HALF_MIRROR = 0x141; // row_half_mirror
 constexpr int DPP_MIRROR = 0x140;      // row_mirror
 constexpr int DPP_BCAST15 = 0x142;     // row_bcast:15
 constexpr int DPP_BCAST31 = 0x143;     // row_bcast:31
+constexpr int DPP_ROW_ROR8 = 0x128;    // row_ror:8 (lane l reads lane l ^ 8 of its 16-lane row)
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     v = dpp_max_u64<DPP_SWAP1>(v);

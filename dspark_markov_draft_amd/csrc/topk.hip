@@ -657,7 +657,8 @@ __device__ __forceinline__ int row16_sum_i32(int x) {
 // step is computed over every row, as the dense walk does, with the same rounding.
 template <int SAMPLE, int W1T, bool MULTI, bool TIMED, bool PRUNE = false>
 __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkParams p) {
-    __shared__ __align__(16) uint32_t w1q[TKW_WAVES][RANK / 4];  // one copy per wave
+    __shared__ __align__(16) uint32_t w1q[TKW_WAVES][RANK / 4];  // one copy per wave: high
+    __shared__ __align__(16) uint32_t w1l[TKW_WAVES][RANK / 4];  // and low W1 digits
     __shared__ uint64_t wkeys[2][TKW_WAVES];                      // by step parity
     __shared__ float wmin[2][TKW_WAVES];                          // PRUNE: smallest candidate base
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
@@ -735,20 +736,28 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
         a = wave_max_nonneg_f32(a);
         const float inv = w1_code_scale(a);
-        const float sb = a * (1.0f / 127.0f);
-        w1q[wave][lane] = pack_codes(w, inv);
+        const float sb = w1_code_step(a);
+        uint32_t lo, nib;
+        w1q[wave][lane] = pack_codes(w, inv, lo, nib);
+        w1l[wave][lane] = lo;
         tk_stamp<TIMED>(p.stamps, st0 + 1 + 2 * t);
         const int4 wc = reinterpret_cast<const int4*>(w1q[wave])[lane & 15];
+        const int4 wl = reinterpret_cast<const int4*>(w1l[wave])[lane & 15];
         uint64_t best = 0;
         float min_base = INFINITY;
         auto score = [&](const CandBlock& blk, bool has) {
             int acc = 0;
 #pragma unroll
             for (int i = 0; i < RANK / 16; ++i) {
+                // 16 * (high digits' products) + (low digits' products), summed over the row
                 int d = __builtin_amdgcn_sdot4(blk.q[i].x, wc.x, 0, false);
                 d = __builtin_amdgcn_sdot4(blk.q[i].y, wc.y, d, false);
                 d = __builtin_amdgcn_sdot4(blk.q[i].z, wc.z, d, false);
                 d = __builtin_amdgcn_sdot4(blk.q[i].w, wc.w, d, false);
+                d = __builtin_amdgcn_sdot4(blk.q[i].x, wl.x, d << 4, false);
+                d = __builtin_amdgcn_sdot4(blk.q[i].y, wl.y, d, false);
+                d = __builtin_amdgcn_sdot4(blk.q[i].z, wl.z, d, false);
+                d = __builtin_amdgcn_sdot4(blk.q[i].w, wl.w, d, false);
                 d = row16_sum_i32(d);
                 acc = (lane & 15) == i ? d : acc;
             }

@@ -14,7 +14,11 @@
 namespace dspark {
 
 constexpr int DOT4_LDS_SETS_MAX = 2;    // row sets in LDS
-constexpr int DOT4_FIXED_LDS = W1Q_BYTES + MAX_BS * 4 + WALK_WAVES * MAX_BS * 8 + MAX_BS * 4;
+// LDS besides the W2 rows: W1 high digits, their steps, wave keys, tokens; then the low digits
+// (all requests' in the lane-per-row kernel, the one request's in the one-request MFMA kernel)
+constexpr int WALK_FIXED_LDS = W1Q_BYTES + MAX_BS * 4 + WALK_WAVES * MAX_BS * 8 + MAX_BS * 4;
+constexpr int DOT4_FIXED_LDS = WALK_FIXED_LDS + W1L_BYTES;
+constexpr int MFMA1_FIXED_LDS = WALK_FIXED_LDS + RANK;
 constexpr int MFMA_REG_TILES = 8;       // 16-row tiles per wave in VGPRs
 constexpr int MFMA_TILE_LDS = 4 * WAVE * 16;
 // Smallest batch run on the MFMA kernel: below it the lane-per-row kernel is faster (measured at
@@ -45,12 +49,14 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         reg_rows = rpw < reg_units * WALK_WAVES * 16 ? rpw : reg_units * WALK_WAVES * 16;
         lds_rows = rpw - reg_rows;
         // (the variant with LDS slots always has MFMA1_LDS_TILES of them)
-        lds_bytes = (lds_units ? MFMA1_LDS_TILES : 0) * WALK_WAVES * MFMA_TILE_LDS + DOT4_FIXED_LDS;
+        lds_bytes = (lds_units ? MFMA1_LDS_TILES : 0) * WALK_WAVES * MFMA_TILE_LDS + MFMA1_FIXED_LDS;
     } else if (path == DSPARK_PATH_DOT4) {
         units = (rpw + WALK_THREADS - 1) / WALK_THREADS;            // row sets
         reg_units = units < DOT4_REG_SETS ? units : DOT4_REG_SETS;
         lds_units = units - reg_units;
         if (lds_units > DOT4_LDS_SETS_MAX) lds_units = DOT4_LDS_SETS_MAX;
+        const int64_t room = ((int64_t)dev.max_lds - DOT4_FIXED_LDS) / (WALK_THREADS * RANK);
+        if (lds_units > room) lds_units = room > 0 ? room : 0;
         reg_rows = rpw < reg_units * WALK_THREADS ? rpw : reg_units * WALK_THREADS;
         lds_rows = rpw - reg_rows;
         if (lds_rows > lds_units * WALK_THREADS) lds_rows = lds_units * WALK_THREADS;

@@ -11,7 +11,9 @@ namespace dspark {
 
 constexpr int WALK_THREADS = 256;
 constexpr int WALK_WAVES = WALK_THREADS / WAVE;  // 4: one wave per SIMD
-constexpr int W1Q_BYTES = MAX_BS * RANK;         // int8 codes of the gathered W1 rows (LDS)
+constexpr int W1Q_BYTES = MAX_BS * RANK;         // high digits of the gathered W1 rows (LDS)
+constexpr int W1L_BYTES = MAX_BS * RANK;         // their low digits, one byte each
+constexpr int W1N_BYTES = MAX_BS * RANK / 2;     // or two per byte (the multi-request MFMA kernel)
 constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workgroup per CU
 // Bound of every grid-wide wait, in ticks of the 100 MHz constant clock: 10 ms, some thousand
 // times the longest healthy wait (the first step's, behind the W2 fill). A walk whose
@@ -44,7 +46,7 @@ constexpr int MFMA_STATIC_STAGE_FLOATS =
 constexpr int MFMA_REQ_CONST_BYTES = MAX_BS * (8 + 8 + 4);
 __host__ __device__ constexpr int mfma_static_lds_bytes(int sample) {
     return 2 * MFMA_STATIC_STAGE_FLOATS * 4 + mfma_static_lds_slots(sample) * WALK_WAVES * 4 * WAVE * 16 +
-           W1Q_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 + WALK_WAVES * (MAX_BS / 16) * WAVE * 8 +
+           W1Q_BYTES + W1N_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 + MAX_BS * 8 +
            MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
 }
 static_assert(mfma_static_lds_bytes(1) <= 160 * 1024, "static LDS fits a CU");
@@ -123,41 +125,77 @@ __device__ __forceinline__ void flag_error(uint32_t* err, int status) {
     __hip_atomic_store(err, (uint32_t)(-status), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The gathered W1 row of request b as int8 codes in LDS: 256 bytes, whose 16-byte chunk ch
-// sits at position ch ^ (b & 15). A broadcast read of one chunk is unaffected; a read of chunk
-// ch for 16 consecutive requests (the MFMA B operand) spreads over all LDS banks.
-__device__ __forceinline__ int w1q_chunk_dword(int b, int ch) { return b * (RANK / 4) + ((ch ^ (b & 15)) << 2); }
+// W1 codes. The gathered row is coded per step as C[k] = rint(w[k] * 2032 / absmax), an integer
+// in [-2032, 2032] (2032 = 16 * 127), with the step s1 = absmax / 2032. C is held as two int8
+// digits, C = 16 * hi + lo with hi in [-127, 127] and lo in [-8, 7], so that the int8 dot
+// products give the exact int32 sum_k q[v,k] C[k] = 16 * sum q hi + sum q lo (at most
+// 256 * 127 * 2032 < 2^27 in magnitude). Every kernel forms the same integer and hence the same
+// logit. The coding error of a W1 element is at most s1 / 2 = absmax / 4064, 1/16 of that of a
+// plain int8 code, so a row with a few large entries still meets the logit tolerance.
+constexpr float W1_CODE_RANGE = 2032.0f;
 
-// 127 / absmax, the factor that maps a W1 row onto int8 codes; 0 for rows whose absmax is at
-// most 2^-100 (zero rows, and denormal ones whose 127 / absmax would overflow): their codes are
+// The digits of request b's row in LDS: 256 bytes per request (high digits, and low digits in
+// the byte form), whose 16-byte chunk ch sits at position ch ^ (b & 15). A broadcast read of one
+// chunk is unaffected; a read of chunk ch for 16 consecutive requests (the MFMA B operand)
+// spreads over all LDS banks.
+__device__ __forceinline__ int w1q_chunk_dword(int b, int ch) { return b * (RANK / 4) + ((ch ^ (b & 15)) << 2); }
+// The nibble form of the low digits (lo + 8 in 4 bits): 128 bytes per request, whose 8-byte
+// chunk ch (16 elements) sits at position ch ^ (b & 15).
+__device__ __forceinline__ int w1n_chunk_dword(int b, int ch) { return b * (RANK / 8) + ((ch ^ (b & 15)) << 1); }
+
+// 2032 / absmax, the factor that maps a W1 row onto its codes; 0 for rows whose absmax is at
+// most 2^-100 (zero rows, and denormal ones whose 2032 / absmax would overflow): their codes are
 // 0, dropping a bias below 2^-90.
 __device__ __forceinline__ float w1_code_scale(float absmax) {
-    return absmax > 0x1p-100f ? 127.0f / absmax : 0.0f;
+    return absmax > 0x1p-100f ? W1_CODE_RANGE / absmax : 0.0f;
 }
+// the code step s1 of a row with this absmax
+__device__ __forceinline__ float w1_code_step(float absmax) { return absmax * (1.0f / W1_CODE_RANGE); }
 
-// Four int8 codes rint(w * inv) (round half to even) in one dword. With inv = 127 / absmax of
-// the row, |w * inv| <= 127 * (1 + 2^-23)^2 < 127.5, so every code lies in [-127, 127] without
-// a clamp. The rounding: for |x| < 2^22, the fp32 sum x + 1.5 * 2^23 is rounded to an integer
-// (its unit in the last place is 1) half to even, and as 1.5 * 2^23 is even that integer is
-// 1.5 * 2^23 + rint(x); its bit pattern is 0x4B400000 + rint(x), whose low byte is the code in
-// two's complement. Three byte permutes pack the four low bytes. The product is rounded before
-// the sum: the empty asm makes it a value of its own, so the compiler cannot contract the two
-// into one fused multiply-add, which would round w * inv + 1.5 * 2^23 once and could differ
-// from rint of the rounded product.
-__device__ __forceinline__ uint32_t rne_code_bits(float w, float inv) {
+// The code of one element, offset: D = C + 8 (round half to even). With inv = 2032 / absmax,
+// |w * inv| <= 2032 * (1 + 2^-23)^2 < 2032.5, so C lies in [-2032, 2032] without a clamp. The
+// rounding: for |x| < 2^22, the fp32 sum x + 1.5 * 2^23 is rounded to an integer (its unit in
+// the last place is 1) half to even, and as 1.5 * 2^23 is even that integer is
+// 1.5 * 2^23 + rint(x), with bit pattern 0x4B400000 + rint(x). The product is rounded before the
+// sum: the empty asm makes it a value of its own, so the compiler cannot contract the two into
+// one fused multiply-add, which would round w * inv + 1.5 * 2^23 once and could differ from rint
+// of the rounded product. From D: hi = D >> 4 (arithmetic; bits 4..11 of D are its two's
+// complement byte) and lo = (D & 15) - 8.
+__device__ __forceinline__ uint32_t code_plus8(float w, float inv) {
     float x = w * inv;
     asm volatile("" : "+v"(x));
-    return __float_as_uint(x + 12582912.0f);   // + 1.5 * 2^23
+    return __float_as_uint(x + 12582912.0f) - (0x4B400000u - 8u);   // + 1.5 * 2^23
 }
-__device__ __forceinline__ uint32_t pack_codes(const float4 w, float inv) {
-    const uint32_t b0 = rne_code_bits(w.x, inv), b1 = rne_code_bits(w.y, inv);
-    const uint32_t b2 = rne_code_bits(w.z, inv), b3 = rne_code_bits(w.w, inv);
-    // v_perm_b32(hi, lo, sel): byte i of the result is byte sel_i of {hi, lo} (lo = 0..3)
+// Four low digits held as lo + 8 in the low nibble of each byte -> four int8 (lo in [-8, 7]):
+// n ^ 8 is lo in 4-bit two's complement, and its sign bit (bit 3) copied into bits 4..7 of the
+// same byte (shifts by 1..4 stay inside the byte) makes the int8.
+__device__ __forceinline__ uint32_t low_digit_bytes(uint32_t nib) {
+    const uint32_t x = nib ^ 0x08080808u;
+    const uint32_t m = x & 0x08080808u;
+    return x | (m << 1) | (m << 2) | (m << 3) | (m << 4);
+}
+// The 16 low digits of one chunk from its nibble form, as the four dwords of int8 the dot
+// products take: dword 0 of the pair holds elements 0..3 in its low nibbles and 4..7 in its
+// high nibbles, dword 1 elements 8..15 alike.
+__device__ __forceinline__ uint4 unpack_low_digits(const uint2 n) {
+    return make_uint4(low_digit_bytes(n.x & 0x0F0F0F0Fu), low_digit_bytes((n.x >> 4) & 0x0F0F0F0Fu),
+                      low_digit_bytes(n.y & 0x0F0F0F0Fu), low_digit_bytes((n.y >> 4) & 0x0F0F0F0Fu));
+}
+// v_perm_b32(hi, lo, sel): byte i of the result is byte sel_i of {hi, lo} (lo = 0..3)
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
     const uint32_t p01 = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);   // b0.byte0, b1.byte0
     const uint32_t p23 = __builtin_amdgcn_perm(b3, b2, 0x0C0C0400u);
     return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
-
+// Four elements: their high digits as four int8 in one dword (returned); their low digits as
+// four int8 in `lo`, or, offset by 8, as 4-bit values in `nib` (byte i holds element i's).
+__device__ __forceinline__ uint32_t pack_codes(const float4 w, float inv, uint32_t& lo, uint32_t& nib) {
+    const uint32_t d0 = code_plus8(w.x, inv), d1 = code_plus8(w.y, inv);
+    const uint32_t d2 = code_plus8(w.z, inv), d3 = code_plus8(w.w, inv);
+    nib = pack_low_bytes(d0, d1, d2, d3) & 0x0F0F0F0Fu;
+    lo = low_digit_bytes(nib);
+    return pack_low_bytes(d0 >> 4, d1 >> 4, d2 >> 4, d3 >> 4);
+}
 // maximum of non-negative floats over each 16-lane row of the wave (all 16 lanes get it)
 __device__ __forceinline__ float row16_max_nonneg_f32(float x) {
     uint32_t v = __float_as_uint(x);
@@ -177,31 +215,36 @@ __device__ __forceinline__ void dot16x4(const int4 a, const int4 b, int4& acc) {
 }
 __device__ __forceinline__ int hsum(const int4 a) { return (a.x + a.y) + (a.z + a.w); }
 
-// One W1 row quantised by one wave (lane l holds elements 4l .. 4l+3): returns lane l's four
-// codes and sets s1 = absmax / 127 (codes = rint(w * 127 / absmax), zero for a zero row).
-__device__ __forceinline__ uint32_t w1_row_quantise(const float4 w, float& s1) {
+// One W1 row coded by one wave (lane l holds elements 4l .. 4l+3): returns lane l's four high
+// digits, sets `lo` to its four low digits (int8) and s1 to the row's code step.
+__device__ __forceinline__ uint32_t w1_row_quantise(const float4 w, float& s1, uint32_t& lo) {
     float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
     a = wave_max_nonneg_f32(a);
     const float inv = w1_code_scale(a);
-    s1 = a * (1.0f / 127.0f);
-    return pack_codes(w, inv);
+    s1 = w1_code_step(a);
+    uint32_t nib;
+    return pack_codes(w, inv, lo, nib);
 }
 
-// Per step: W1[prev_b] for every request, as int8 codes with one absmax scale per row
-// (s1[b] = absmax / 127, codes = rint(w * 127 / absmax)). Up to 4 requests: one per wave, 64
-// lanes on the row. More: sixteen lanes share a row: lane
-// (quarter q, ql) holds elements 16 ql .. 16 ql + 15 of request 4 (iteration * 4 + wave) + q,
-// so one wave instruction serves 4 requests; all of a wave's rows are loaded before any is used.
+// Where the low digits go: one int8 each (the layout of the high digits), or two per byte.
+constexpr int LOW_BYTES = 1;
+constexpr int LOW_NIBBLES = 2;
+
+// Per step: W1[prev_b] for every request, coded as above: high digits into w1q, low digits into
+// w1l (LOW form), the step into s1[b]. Up to 4 requests (byte form): one per wave, 64 lanes on
+// the row. More, or the nibble form: sixteen lanes share a row: lane (quarter q, ql) holds
+// elements 16 ql .. 16 ql + 15 of request 4 (iteration * 4 + wave) + q, so one wave instruction
+// serves 4 requests; all of a wave's rows are loaded before any is used.
 // after_issue() runs once the wave's loads are issued and before their values are used: loads
 // it issues complete after the W1 rows (vector memory returns in issue order) without delaying
 // them.
 constexpr int GATHER_ITERS = MAX_BS / (WALK_WAVES * 4);   // 4 request groups per wave at bs 64
 
-template <int W1T, int MAX_NIT = 2, typename AfterIssue>
+template <int W1T, int LOW, int MAX_NIT = 2, typename AfterIssue>
 __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32_t* tok,
-                                                uint32_t* w1q, float* s1, int wave, int lane,
-                                                AfterIssue&& after_issue) {
-    if (p.bs <= WALK_WAVES) {
+                                                uint32_t* w1q, uint32_t* w1l, float* s1, int wave,
+                                                int lane, AfterIssue&& after_issue) {
+    if (LOW == LOW_BYTES && p.bs <= WALK_WAVES) {
         // at most one request per wave: all 64 lanes on one row (elements 4l .. 4l+3)
         const int b = wave;
         float4 w = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -209,7 +252,10 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
         after_issue();
         if (b < p.bs) {
             float sb;
-            w1q[w1q_chunk_dword(b, lane >> 2) + (lane & 3)] = w1_row_quantise(w, sb);
+            uint32_t lo;
+            const int d = w1q_chunk_dword(b, lane >> 2) + (lane & 3);
+            w1q[d] = w1_row_quantise(w, sb, lo);
+            w1l[d] = lo;
             if (lane == 0) s1[b] = sb;
         }
         return;
@@ -256,14 +302,19 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
                                    fmaxf(fabsf(wv[i][k].z), fabsf(wv[i][k].w))));
             a = row16_max_nonneg_f32(a);
             const float inv = w1_code_scale(a);
-            uint4 codes;
-            codes.x = pack_codes(wv[i][0], inv);
-            codes.y = pack_codes(wv[i][1], inv);
-            codes.z = pack_codes(wv[i][2], inv);
-            codes.w = pack_codes(wv[i][3], inv);
+            uint4 codes, lo, nib;
+            codes.x = pack_codes(wv[i][0], inv, lo.x, nib.x);
+            codes.y = pack_codes(wv[i][1], inv, lo.y, nib.y);
+            codes.z = pack_codes(wv[i][2], inv, lo.z, nib.z);
+            codes.w = pack_codes(wv[i][3], inv, lo.w, nib.w);
             if (b < p.bs) {
                 *reinterpret_cast<uint4*>(w1q + w1q_chunk_dword(b, ql)) = codes;
-                if (ql == 0) s1[b] = a * (1.0f / 127.0f);
+                if constexpr (LOW == LOW_BYTES)
+                    *reinterpret_cast<uint4*>(w1l + w1q_chunk_dword(b, ql)) = lo;
+                else
+                    *reinterpret_cast<uint2*>(w1l + w1n_chunk_dword(b, ql)) =
+                        make_uint2(nib.x | (nib.y << 4), nib.z | (nib.w << 4));
+                if (ql == 0) s1[b] = w1_code_step(a);
             }
         }
     };

@@ -3,7 +3,7 @@
 //
 // What it computes (vLLM PR #62958, int8 DSpark Markov walk, Overview and Details; vLLM PR
 // #64476, Claims): for every request b and step t,
-//     l[v]  = base[b,t,v] + s[v] * s1 * sum_k q[v,k] * q1[k],   q1/s1 = int8 codes of W1[prev_b]
+//     l[v]  = base[b,t,v] + s[v] * s1 * sum_k q[v,k] * C[k],   C/s1 = the codes of W1[prev_b]
 //     greedy: token = argmax_v l[v];
 //     sample: lb = bf16(l), token = argmax_v (lb[v] / temp_b + Gumbel(Philox(seed_b, P, v)))
 // with torch.argmax order, and token becomes prev_b for step t+1.
@@ -15,8 +15,9 @@
 //   * the next up to 2 x 256 rows live in LDS (16-byte chunks XOR-swizzled by row, so the
 //     lanes of a wave reading one chunk index hit different banks),
 //   * rows beyond are re-read from memory at every step.
-// The W1 codes are LDS broadcasts; v_dot4_i32_i8 accumulates exact int32 sums in four
-// independent chains per row (its latency is ~20 cycles, its issue ~4); scale, base logit and
+// The W1 codes (two int8 digits per element) are LDS broadcasts; v_dot4_i32_i8 accumulates
+// exact int32 sums in four independent chains per row and digit (its latency is ~20 cycles, its
+// issue ~4), joined as 16 * high + low; scale, base logit and
 // sampler finish each row; wave-wide and workgroup-wide maxima of 64-bit argmax keys give the
 // slice's best, and combine_step() combines the slices across the grid.
 #include "walk_common.hpp"
@@ -44,7 +45,8 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
 
     unsigned char* lds_rows = smem;
     uint32_t* w1q = reinterpret_cast<uint32_t*>(smem + (size_t)lds_j * WALK_THREADS * RANK);
-    float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
+    uint32_t* w1l = w1q + W1Q_BYTES / 4;
+    float* s1 = reinterpret_cast<float*>(w1l + W1L_BYTES / 4);
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
     int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
 
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
         // wave 0 runs the combine, whose polls would wait behind any load it has in flight
         // (vector memory returns in issue order): its share of this step's first base logits is
         // issued here, behind the W1 row loads, instead of before the previous combine
-        gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {
+        gather_w1_codes<W1T, LOW_BYTES>(p, tok, w1q, w1l, s1, wave, lane, [&] {
             if (wave == 0 && t > 0) {
 #pragma unroll
                 for (int u = 0; u < PF_DEPTH; ++u)
@@ -153,10 +155,15 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                     };
 
                     const int4* wq = reinterpret_cast<const int4*>(w1q + b * (RANK / 4));
-                    const int sw = b & 15;  // chunk c of this request's codes is at c ^ sw
-                    int4 acc[REG_J];
+                    const int4* wl = reinterpret_cast<const int4*>(w1l + b * (RANK / 4));
+                    const int sw = b & 15;  // chunk c of this request's digits is at c ^ sw
+                    // each row chunk (moved out of its AGPRs once) into a high and a low chain
+                    int4 acc[REG_J], acl[REG_J];
 #pragma unroll
-                    for (int j = 0; j < REG_J; ++j) acc[j] = make_int4(0, 0, 0, 0);
+                    for (int j = 0; j < REG_J; ++j) {
+                        acc[j] = make_int4(0, 0, 0, 0);
+                        acl[j] = make_int4(0, 0, 0, 0);
+                    }
 #pragma unroll
                     for (int c = 0; c < ROW_CHUNKS; ++c) {
                         // a compiler-only barrier every 4 chunks: the W1 chunks are read from
@@ -164,37 +171,44 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_dot4_kernel(const 
                         // rows in VGPRs
                         if (c % 4 == 0) asm volatile("" ::: "memory");
                         const int4 w = wq[c ^ sw];
+                        const int4 wlo = wl[c ^ sw];
 #pragma unroll
-                        for (int j = 0; j < REG_J; ++j) dot16x4(qr[j][c], w, acc[j]);
+                        for (int j = 0; j < REG_J; ++j) {
+                            dot16x4(qr[j][c], w, acc[j]);
+                            dot16x4(qr[j][c], wlo, acl[j]);
+                        }
                     }
 #pragma unroll
                     for (int j = 0; j < REG_J; ++j) {
                         const int r = j * WALK_THREADS + tid;
-                        if (r < nrows) finish(row0 + r, cur[j], sc[j], hsum(acc[j]));
+                        if (r < nrows) finish(row0 + r, cur[j], sc[j], join_digits(hsum(acc[j]), hsum(acl[j])));
                     }
                     // row sets beyond the registers: LDS-resident, then streamed from memory
                     for (int j = REG_J; j < nj; ++j) {
                         const int r = j * WALK_THREADS + tid;
                         if (r < nrows) {
+                            // each row chunk read once, into a high and a low chain
                             int4 a4 = make_int4(0, 0, 0, 0), b4 = make_int4(0, 0, 0, 0);
                             if (j < REG_J + lds_j) {
                                 const int4* src = reinterpret_cast<const int4*>(
                                     lds_rows + (size_t)((j - REG_J) * WALK_THREADS + tid) * RANK);
 #pragma unroll
-                                for (int c = 0; c < ROW_CHUNKS; c += 2) {
-                                    dot16x4(src[c ^ (tid & 15)], wq[c ^ sw], a4);
-                                    dot16x4(src[(c + 1) ^ (tid & 15)], wq[(c + 1) ^ sw], b4);
+                                for (int c = 0; c < ROW_CHUNKS; ++c) {
+                                    const int4 x = src[c ^ (tid & 15)];
+                                    dot16x4(x, wq[c ^ sw], a4);
+                                    dot16x4(x, wl[c ^ sw], b4);
                                 }
                             } else {
                                 const int4* src = reinterpret_cast<const int4*>(
                                     p.q + (int64_t)(row0 + r) * RANK);
 #pragma unroll 4
-                                for (int c = 0; c < ROW_CHUNKS; c += 2) {
-                                    dot16x4(src[c], wq[c ^ sw], a4);
-                                    dot16x4(src[c + 1], wq[(c + 1) ^ sw], b4);
+                                for (int c = 0; c < ROW_CHUNKS; ++c) {
+                                    const int4 x = src[c];
+                                    dot16x4(x, wq[c ^ sw], a4);
+                                    dot16x4(x, wl[c ^ sw], b4);
                                 }
                             }
-                            const int a = hsum(a4) + hsum(b4);
+                            const int a = join_digits(hsum(a4), hsum(b4));
                             float bv = 0.0f, sv = 0.0f;
                             if (j < PF_J) {
 #pragma unroll

@@ -2,21 +2,26 @@
 // W2 [V x 256] with the requests' W1 codes [256 x bs]).
 //
 // What it computes: as the v_dot4 kernel (vLLM PR #62958, int8 DSpark Markov walk, Overview
-// and Details; vLLM PR #64476, Claims): l[v] = base[b,t,v] + s[v] * s1_b * sum_k q[v,k] q1_b[k],
-// then the first-maximum argmax (greedy) or the Gumbel-max of bf16(l) / temp + noise (sample).
+// and Details; vLLM PR #64476, Claims): l[v] = base[b,t,v] + s[v] * s1_b * sum_k q[v,k] C_b[k]
+// (C = 16 hi + lo, the two-digit W1 codes), then the first-maximum argmax (greedy) or the
+// Gumbel-max of bf16(l) / temp + noise (sample).
 //
 // v_mfma_i32_16x16x64_i8 multiplies a 16 x 64 int8 tile by a 64 x 16 int8 tile into 16 x 16
 // int32. Lane l supplies row l % 16 of A and column l % 16 of B, each for the k-chunk of lane
 // group l / 16, and receives D[(l / 16) * 4 + i][l % 16], i < 4. Here A = 16 rows of W2 and
-// B = the W1 codes of 16 requests; lane group g carries bytes g*64 + kb*16 .. +15 of the row in
+// B = the W1 digits of 16 requests; lane group g carries bytes g*64 + kb*16 .. +15 of the row in
 // K-block kb, so over the four K-blocks a lane holds one contiguous 64-byte quarter of its row.
+// Each tile's accumulator takes the high digits' 4 MFMAs, is shifted left by 4, and takes the
+// low digits' 4 MFMAs: 16 * (high sum) + (low sum), the exact integer of the other kernels. The
+// low digits sit in LDS as nibbles (8 KB for 64 requests) and are widened to int8 when read.
 //
 // The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves: each wave keeps up
 // to 8 tiles (128 rows) in VGPRs as ready A operands, further tiles in LDS (laid out so a
 // K-block read is 64 consecutive 16-byte lane slots), and streams any rest from memory. Per
-// step and 16-request tile: 4 MFMAs per W2 tile; each lane then finishes 4 consecutive rows of
+// step and 16-request tile: 8 MFMAs per W2 tile; each lane then finishes 4 consecutive rows of
 // one request (one float4 of base logits, one Philox call for the 4 noise words), keeps its
-// best key, and the workgroup's best per request goes to combine_step().
+// best key, the four lanes of a request in a wave merge theirs with two lane swaps, and the
+// workgroup's best per request goes to combine_step().
 //
 // The base logits of a 16-request tile (16 rows of the workgroup's slice) are copied into LDS
 // by global_load_lds DMA before the tile is used (one latency per request tile instead of one
@@ -45,11 +50,12 @@ static_assert(NT_STAT * WALK_WAVES * TILE_ROWS == MFMA_STATIC_SLOT_ROWS, "STAT s
 constexpr int STAT_COPY_SLOTS = MFMA_STATIC_COPY_UNITS / WAVE / WALK_WAVES;
 static_assert(MFMA_STATIC_COPY_UNITS % (WAVE * WALK_WAVES) == 0 && STAT_COPY_SLOTS <= NT_STAT,
               "STAT copy slots");
-constexpr int LKEY_BYTES = WALK_WAVES * MAX_RT * WAVE * 8;
+constexpr int LKEY_BYTES = MAX_BS * 8;   // the workgroup's best key per request
 
-// dynamic LDS besides the W2 tiles: W1 codes, their scales, row scales, lane keys, tokens
+// dynamic LDS besides the W2 tiles: W1 digits, their steps, row scales, wave keys, tokens
 __host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
-    return W1Q_BYTES + MAX_BS * 4 + ((rows_per_wg * 4 + 15) / 16) * 16 + LKEY_BYTES + MAX_BS * 4;
+    return W1Q_BYTES + W1N_BYTES + MAX_BS * 4 + ((rows_per_wg * 4 + 15) / 16) * 16 + LKEY_BYTES +
+           MAX_BS * 4;
 }
 
 // STAT (slices of up to MFMA_STATIC_ROWS rows): every LDS buffer is a static array of its own
@@ -71,9 +77,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     __shared__ __align__(16) unsigned char tiles_s[STAT ? mfma_static_lds_slots(SAMPLE) * WALK_WAVES *
                                                               TILE_LDS_BYTES : 16];
     __shared__ __align__(16) uint32_t w1q_s[STAT ? W1Q_BYTES / 4 : 4];
+    __shared__ __align__(16) uint32_t w1n_s[STAT ? W1N_BYTES / 4 : 4];
     __shared__ __align__(16) float s1_s[STAT ? MAX_BS : 4];
     __shared__ __align__(16) float scl_s[STAT ? MFMA_STATIC_SLOT_ROWS : 4];
-    __shared__ __align__(16) uint64_t lkeys_s[STAT ? WALK_WAVES * MAX_RT * WAVE : 2];
+    __shared__ __align__(16) uint64_t lkeys_s[STAT ? MAX_BS : 2];
     __shared__ __align__(16) int32_t tok_s[STAT ? MAX_BS : 4];
     __shared__ __align__(16) uint64_t rq_seed[SAMPLE ? MAX_BS : 2];
     __shared__ __align__(16) uint64_t rq_pos[SAMPLE ? MAX_BS : 2];
@@ -90,24 +97,26 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     const int ntw = p.total_units;                             // tile slots per wave
     const int lds_tw = p.lds_units;
 
-    // dynamic layout (without STAT): LDS tiles, staging buffers, W1 codes, their scales, row
-    // scales, lane keys, tokens
+    // dynamic layout (without STAT): LDS tiles, staging buffers, W1 high digits, low digits,
+    // their steps, row scales, wave keys, tokens
     unsigned char* const d_tiles = smem;
     float* const d_stage = reinterpret_cast<float*>(smem + (size_t)lds_tw * WALK_WAVES * TILE_LDS_BYTES);
     const int ss = p.stage_stride;
     const int nbuf = p.stage_bufs;   // 1 or 2 (the host guarantees at least one)
     uint32_t* const d_w1q = reinterpret_cast<uint32_t*>(d_stage + (size_t)p.stage_bufs * 16 * ss);
-    float* const d_s1 = reinterpret_cast<float*>(d_w1q + W1Q_BYTES / 4);
+    uint32_t* const d_w1n = d_w1q + W1Q_BYTES / 4;
+    float* const d_s1 = reinterpret_cast<float*>(d_w1n + W1N_BYTES / 4);
     float* const d_scl = d_s1 + MAX_BS;
     uint64_t* const d_lkeys = reinterpret_cast<uint64_t*>(d_scl + ((p.rows_per_wg * 4 + 15) / 16) * 4);
     unsigned char* lds_tiles = STAT ? tiles_s : d_tiles;
     float* const buf0 = STAT ? stage_a : d_stage;
     float* const buf1 = STAT ? stage_b : d_stage + (size_t)16 * ss;
     uint32_t* w1q = STAT ? w1q_s : d_w1q;
+    uint32_t* w1n = STAT ? w1n_s : d_w1n;
     float* s1 = STAT ? s1_s : d_s1;
     float* scl = STAT ? scl_s : d_scl;
     uint64_t* lkeys = STAT ? lkeys_s : d_lkeys;
-    int32_t* tok = STAT ? tok_s : reinterpret_cast<int32_t*>(d_lkeys + WALK_WAVES * MAX_RT * WAVE);
+    int32_t* tok = STAT ? tok_s : reinterpret_cast<int32_t*>(d_lkeys + MAX_BS);
 
     // ---- fill: W2 tiles as A operands (VGPRs, then LDS), row scales into LDS ---------------
     auto load_a = [&](int tl, int kb) -> v4i {
@@ -138,6 +147,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     for (int i = tid; i < (STAT ? MFMA_STATIC_SLOT_ROWS : ntiles * TILE_ROWS); i += WALK_THREADS)
         scl[i] = i < nrows ? p.scale[row0 + i] : 0.0f;
     load_start_tokens(p, tok);
+    if (tid < MAX_BS) lkeys[tid] = 0;   // the per-request key words start empty
     if constexpr (SAMPLE) {
         // read once here rather than at every request tile, where each read was a round trip
         if (tid < p.bs) {
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     };
 
     for (int t = 0; t < p.T; ++t) {
-        gather_w1_codes<W1T, STAT ? 4 : 2>(p, tok, w1q, s1, wave, lane, [] {});
+        gather_w1_codes<W1T, LOW_NIBBLES, STAT ? 4 : 2>(p, tok, w1q, w1n, s1, wave, lane, [] {});
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
@@ -231,18 +241,40 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 __syncthreads();   // every wave is done with the previous request tile
                 stage_base(rt, t, cur);
             }
-            __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed ...
-            __syncthreads();                  // ... and every other wave's
+            // This tile's base logits have landed: this wave's copies, then (barrier) every other
+            // wave's; past the barrier every wave is also done with the buffer that the next
+            // copy overwrites. With STAT the tile's MFMAs, which need no base logit, are issued
+            // before this wait and run while the copy lands; the next tile's copy is issued
+            // after it (the wait counts every load in flight).
+            auto landed = [&]() {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            };
+            if constexpr (!STAT) landed();
             const bool prefetch = nbuf == 2 && rt + 1 < nrt;
             if (!STAT && prefetch) stage_base(rt + 1, t, nxt);
             const float* sbase = cur + (size_t)c * ss;
             const int b = rt * 16 + c;
             const bool vb = b < p.bs;
-            v4i bop[4];
+            // Column c of the result depends only on column c of B, and the columns of requests
+            // past bs are dropped: their digits are read (in bounds: the arrays hold 64
+            // requests) without a branch, whatever the LDS holds there.
+            auto high_op = [&](int kb) -> v4i {
+                return *reinterpret_cast<const v4i*>(w1q + w1q_chunk_dword(b, g * 4 + kb));
+            };
+            // low digits, widened from their nibbles
+            auto low_op = [&](int kb) -> v4i {
+                const uint4 x = unpack_low_digits(
+                    *reinterpret_cast<const uint2*>(w1n + w1n_chunk_dword(b, g * 4 + kb)));
+                return (v4i){(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+            };
+            // both digits' B operands of the request tile, read together (one LDS wait)
+            v4i bop[4], bol[4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                bop[kb] = vb ? *reinterpret_cast<const v4i*>(w1q + w1q_chunk_dword(b, g * 4 + kb))
-                             : (v4i){0, 0, 0, 0};
+            for (int kb = 0; kb < 4; ++kb) {
+                bop[kb] = high_op(kb);
+                bol[kb] = low_op(kb);
+            }
             const float sb = vb ? s1[b] : 0.0f;
             const int64_t orow = ((int64_t)(vb ? b : 0) * p.T + t) * p.V;
             uint64_t seed = 0, P = 0;
@@ -309,33 +341,73 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             // Every tile of this wave in increasing row order: register tiles (all their MFMAs
             // first, each into its own accumulator, so the matrix core runs ahead while the VALU
             // finishes tile after tile), then LDS tiles, then streamed ones.
-            auto for_tiles = [&](auto&& fin, auto&& after) {
+            auto for_tiles = [&](auto&& fin, auto&& after, auto&& half_end) {
                 if constexpr (STAT) {
                     // At most NT_STAT tile slots per wave, all on chip: every slot's MFMAs are
                     // issued first and every slot is finished, with no branch on the tile, so
                     // the compiler can overlap one tile's LDS reads with another's arithmetic.
                     // Slots past the slice's tiles hold zero codes and their rows are past vend.
-                    v4i accs[NT_STAT];
+                    auto a_op = [&](int tw, int kb) -> v4i {
+                        if (tw < NTR) return qa[tw][kb];
+                        return reinterpret_cast<const v4i*>(
+                            lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) *
+                                            TILE_LDS_BYTES)[kb * WAVE + lane];
+                    };
+                    // The sampling kernel takes the slots in two halves (half the accumulators
+                    // live at a time), the greedy kernel in one pass. A pass: the high digits'
+                    // MFMAs, every accumulator times 16, the low digits' MFMAs (K-block by
+                    // K-block, so that consecutive MFMAs feed different accumulators), then the
+                    // finish. The first pass's MFMAs run before the wait for this tile's base
+                    // logits. The next tile's copy instructions are spread: one behind each
+                    // finished slot of the first pass, and in a later pass one behind each
+                    // group of its MFMAs (a copy whose issue stalls while HBM is busy then stalls
+                    // the wave only while the matrix core works through the group before it).
+                    constexpr int HALF = SAMPLE ? (NT_STAT + 1) / 2 : NT_STAT;
 #pragma unroll
-                    for (int tw = 0; tw < NT_STAT; ++tw) {
-                        accs[tw] = (v4i){0, 0, 0, 0};
+                    for (int h0 = 0; h0 < NT_STAT; h0 += HALF) {
+                        constexpr int n = HALF;
+                        const bool first = h0 == 0;
+                        v4i accs[n];
+#pragma unroll
+                        for (int i = 0; i < n; ++i) accs[i] = (v4i){0, 0, 0, 0};
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) {
-                            v4i a;
-                            if (tw < NTR)
-                                a = qa[tw][kb];
-                            else
-                                a = reinterpret_cast<const v4i*>(
-                                    lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) *
-                                                    TILE_LDS_BYTES)[kb * WAVE + lane];
-                            accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop[kb], accs[tw],
-                                                                             0, 0, 0);
-                        }
-                    }
+                            const v4i bh = bop[kb];
 #pragma unroll
-                    for (int tw = 0; tw < NT_STAT; ++tw) {
-                        fin(accs[tw], row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4, tw);
-                        after(tw);
+                            for (int i = 0; i < n; ++i)
+                                if (h0 + i < NT_STAT)
+                                    accs[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                        a_op(h0 + i, kb), bh, accs[i], 0, 0, 0);
+                            if (!first && kb < n && h0 + kb < NT_STAT) after(h0 + kb);
+                        }
+#pragma unroll
+                        for (int i = 0; i < n; ++i) accs[i] = accs[i] << 4;
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
+                            const v4i bl = bol[kb];
+#pragma unroll
+                            for (int i = 0; i < n; ++i)
+                                if (h0 + i < NT_STAT)
+                                    accs[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                        a_op(h0 + i, kb), bl, accs[i], 0, 0, 0);
+                            if (!first && 4 + kb < n && h0 + 4 + kb < NT_STAT) after(h0 + 4 + kb);
+                        }
+                        if (!first) {
+                            // a pass of more than 8 slots: its last copy instructions
+#pragma unroll
+                            for (int i = 8; i < n; ++i)
+                                if (h0 + i < NT_STAT) after(h0 + i);
+                        }
+                        if (first) landed();
+#pragma unroll
+                        for (int i = 0; i < n; ++i) {
+                            const int tw = h0 + i;
+                            if (tw < NT_STAT) {
+                                fin(accs[i], row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4, tw);
+                                if (first) after(tw);
+                            }
+                        }
+                        half_end(h0);
                     }
                     return;
                 }
@@ -352,26 +424,41 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 }
 #pragma unroll
                 for (int tw = 0; tw < NTR; ++tw) {
+                    if (tw * WALK_WAVES + wave < ntiles) {
+                        accs[tw] = accs[tw] << 4;
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+                            accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bol[kb],
+                                                                             accs[tw], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int tw = 0; tw < NTR; ++tw) {
                     const int tl = tw * WALK_WAVES + wave;
                     if (tl < ntiles) fin(accs[tw], row0 + tl * TILE_ROWS + g * 4, tw);
                 }
                 for (int tw = NTR; tw < ntw; ++tw) {
                     const int tl = tw * WALK_WAVES + wave;
                     if (tl < ntiles) {
-                        v4i acc = {0, 0, 0, 0};
+                        // the tile's A operands read once (from LDS or memory) for both digits
+                        v4i a4[4];
                         if (tw < NTR + lds_tw) {
                             const v4i* src = reinterpret_cast<const v4i*>(
                                 lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) * TILE_LDS_BYTES);
 #pragma unroll
-                            for (int kb = 0; kb < 4; ++kb)
-                                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane],
-                                                                            bop[kb], acc, 0, 0, 0);
+                            for (int kb = 0; kb < 4; ++kb) a4[kb] = src[kb * WAVE + lane];
                         } else {
 #pragma unroll
-                            for (int kb = 0; kb < 4; ++kb)
-                                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(load_a(tl, kb), bop[kb],
-                                                                            acc, 0, 0, 0);
+                            for (int kb = 0; kb < 4; ++kb) a4[kb] = load_a(tl, kb);
                         }
+                        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+                            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a4[kb], bop[kb], acc, 0, 0, 0);
+                        acc = acc << 4;
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+                            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a4[kb], bol[kb], acc, 0, 0, 0);
                         fin(acc, row0 + tl * TILE_ROWS + g * 4, tw);
                     }
                 }
@@ -386,20 +473,21 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             // Four running maxima, one per row of the group, so that the compare-and-select
             // chains are independent; merged afterwards by value, then lowest row. The check sum
             // of all scores is NaN if any score is (or on an inf - inf false alarm). With STAT
-            // the stores wait until every slot is scored (stores in between would split the
-            // code into blocks the compiler schedules one at a time).
+            // the stores wait until every slot of a half is scored (stores in between would
+            // split the code into blocks the compiler schedules one at a time).
             float run_v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             uint32_t run_i[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
             float chk = 0.0f;
-            constexpr bool HOLD = STAT && (SAMPLE || OUTL);   // outputs held until all slots
-            uint32_t held[HOLD ? NT_STAT : 1][4];
+            constexpr bool HOLD = STAT && (SAMPLE || OUTL);   // outputs held for a half
+            constexpr int HALF_SLOTS = SAMPLE ? (NT_STAT + 1) / 2 : NT_STAT;
+            uint32_t held[HOLD ? HALF_SLOTS : 1][4];
             for_tiles([&](const v4i acc, int vt, int tw) {
                 float sc[4];
                 uint32_t out[4];
                 const bool ok = scores4(acc, vt, sc, out);
                 if constexpr (HOLD) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) held[tw][i] = out[i];
+                    for (int i = 0; i < 4; ++i) held[tw % HALF_SLOTS][i] = out[i];
                 } else if constexpr (!STAT) {
                     store4(vt, ok, out);
                 }
@@ -417,16 +505,18 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 if constexpr (STAT) {
                     if (prefetch && tw < STAT_COPY_SLOTS) copy_job(rt + 1, t, nxt, tw * WALK_WAVES + wave);
                 }
-            });
-            if constexpr (HOLD) {
-                if (SAMPLE || p.out_logits != nullptr) {
+            }, [&](int h0) {
+                if constexpr (HOLD) {
+                    if (SAMPLE || p.out_logits != nullptr) {
 #pragma unroll
-                    for (int tw = 0; tw < NT_STAT; ++tw) {
-                        const int vt = row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4;
-                        store4(vt, vb && vt < vend, held[tw]);
+                        for (int i = 0; i < HALF_SLOTS; ++i) {
+                            const int tw = h0 + i;
+                            const int vt = row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4;
+                            if (tw < NT_STAT) store4(vt, vb && vt < vend, held[i]);
+                        }
                     }
                 }
-            }
+            });
             const bool nan_seen = chk != chk;
             float bv = run_v[0];
             uint32_t bi = run_i[0];
@@ -447,8 +537,23 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 best = (vb && wave < ntiles && vt0 < vend) ? argmax_key(-INFINITY, (uint32_t)vt0) : 0ull;
             }
             if (__any(nan_seen)) {
+                // The exact pass, rare (a NaN score): every tile once more, its W2 rows read
+                // from memory (the same codes as the on-chip copies) in a loop that is not
+                // unrolled, so that it adds little code.
                 best = 0;
-                for_tiles([&](const v4i acc, int vt, int) {
+#pragma unroll 1
+                for (int tw = 0; tw < ntw; ++tw) {
+                    const int tl = tw * WALK_WAVES + wave;
+                    if (tl >= ntiles) break;
+                    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(load_a(tl, kb), bop[kb], acc, 0, 0, 0);
+                    acc = acc << 4;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(load_a(tl, kb), bol[kb], acc, 0, 0, 0);
+                    const int vt = row0 + tl * TILE_ROWS + g * 4;
                     float sc[4];
                     uint32_t out[4];
                     const bool ok = scores4(acc, vt, sc, out);
@@ -458,9 +563,14 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                         const uint64_t k = argmax_key(sc[i], (uint32_t)(vt + i)) & keep;
                         best = k > best ? k : best;
                     }
-                }, [](int) {});
+                }
             }
-            lkeys[(wave * MAX_RT + rt) * WAVE + lane] = best;
+            // the workgroup's best per request: every lane's key into one LDS word per request
+            // by an atomic maximum (keys order as the values they carry; 0 is no row). Merging
+            // the four lanes of a request in registers first put a dependent cross-lane chain
+            // at the end of every request tile, ~5 us per walk at 64 requests.
+            __hip_atomic_fetch_max(&lkeys[rt * 16 + c], best, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
         };
         for (int rt = 0; rt < nrt; ++rt) {
             // the buffer each tile reads is named in the code (not picked by an index), so that
@@ -477,27 +587,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 
         if (wave == 0) {
             uint64_t k = 0;
-            if (lane < p.bs) {
-                // the 16 lane keys of request `lane` (4 waves x 4 row groups): all reads are
-                // issued before any compare (read one at a time, each was a separate LDS round
-                // trip on the combine's critical path), then reduced as a tree
-                const int rt = lane >> 4, cc = lane & 15;
-                uint64_t o[16];
-#pragma unroll
-                for (int w = 0; w < WALK_WAVES; ++w)
-#pragma unroll
-                    for (int gg = 0; gg < 4; ++gg)
-                        o[w * 4 + gg] = lkeys[(w * MAX_RT + rt) * WAVE + gg * 16 + cc];
-                asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]),
-                             "+v"(o[5]), "+v"(o[6]), "+v"(o[7]), "+v"(o[8]), "+v"(o[9]),
-                             "+v"(o[10]), "+v"(o[11]), "+v"(o[12]), "+v"(o[13]), "+v"(o[14]),
-                             "+v"(o[15]));
-#pragma unroll
-                for (int n = 8; n >= 1; n /= 2)
-#pragma unroll
-                    for (int i = 0; i < n; ++i) o[i] = o[i + n] > o[i] ? o[i + n] : o[i];
-                k = o[0];
-            }
+            // the workgroup's key of request `lane`, cleared for the next step (whose first
+            // update follows the barrier after the combine)
+            k = lkeys[lane];
+            lkeys[lane] = 0;
+            if (lane >= p.bs) k = 0;
             combine_step<TIMED>(p, t, k, tok, lane);
         }
         __syncthreads();

@@ -2,18 +2,21 @@
 //
 // What it computes: as the other dense-walk kernels (vLLM PR #62958, int8 DSpark Markov walk,
 // Overview and Details; vLLM PR #64476, Claims): l[v] = base[0,t,v] + s[v] * s1 * sum_k q[v,k]
-// q1[k], then the first-maximum argmax (greedy) or the Gumbel-max of bf16(l) / temp + noise.
+// C[k] (C = 16 hi + lo, the two-digit W1 codes), then the first-maximum argmax (greedy) or the
+// Gumbel-max of bf16(l) / temp + noise.
 //
 // One request makes each step a GEMV, and the lane-per-row v_dot4 kernel spends most of its
 // step issuing VALU work: 64 v_dot4 per row plus a move per W2 word held in AGPRs. Here the
 // workgroup's W2 rows sit in registers as the A operands of v_mfma_i32_16x16x64_i8 (which reads
-// them from AGPRs directly), and the request's W1 codes are the B operand of all 16 columns:
-// every column of the 16 x 16 result holds the same 16 dot products. Lane l receives rows
-// 4 (l / 16) .. 4 (l / 16) + 3 of the tile, so among four tiles it finishes one row of its own
-// choosing (tile (l / 4) % 4, row 4 (l / 16) + l % 4), and the 64 lanes finish 64 distinct rows
-// with no data movement between lanes. The matrix core does 16 times the MACs the method needs
-// (the 16 columns hold 16 copies of one), which at 16 cycles per MFMA is 40 MFMAs, ~0.3 us per
-// step for a 640-row slice; the VALU only finishes three rows per lane.
+// them from AGPRs directly), and the request's W1 digits are the B operand: the high digits in
+// columns 0..7, the low digits in columns 8..15, so every column of the 16 x 16 result holds one
+// of the two dot products of each of the tile's 16 rows. Lane l receives rows
+// 4 (l / 16) .. 4 (l / 16) + 3 of the tile in column l % 16, so among four tiles it finishes one
+// row of its own choosing (tile (l / 4) % 4, row 4 (l / 16) + l % 4); lane l ^ 8 holds the same
+// rows in the other kind of column and sends it the other dot product with one DPP move. The
+// matrix core does 8 times the MACs the method needs (each column holds one of 8 copies), which
+// at 16 cycles per MFMA is 40 MFMAs, ~0.3 us per step for a 640-row slice; the VALU only
+// finishes three rows per lane.
 //
 // The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves (tile tw * 4 + wave):
 // the first MFMA1_TILES slots of each wave in registers, up to MFMA1_LDS_TILES more in LDS (a
@@ -62,6 +65,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     float* s1 = reinterpret_cast<float*>(w1q + W1Q_BYTES / 4);
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
     int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
+    uint32_t* w1l = reinterpret_cast<uint32_t*>(tok + MAX_BS);   // the request's low digits
 
     // ---- step 0's W1 codes, by the last wave before its share of the fill ----------------
     // The start token is known at launch, so its row is gathered while the other waves' fill
@@ -72,8 +76,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         int s0 = p.start[0];
         if (s0 < 0 || s0 >= p.V) s0 = 0;
         float sb;
-        const uint32_t codes = w1_row_quantise(load4_as_f32<W1T>(p.w1, (int64_t)s0 * RANK + lane * 4), sb);
+        uint32_t lo;
+        const uint32_t codes =
+            w1_row_quantise(load4_as_f32<W1T>(p.w1, (int64_t)s0 * RANK + lane * 4), sb, lo);
         w1q[w1q_chunk_dword(0, lane >> 2) + (lane & 3)] = codes;
+        w1l[w1q_chunk_dword(0, lane >> 2) + (lane & 3)] = lo;
         if (lane == 0) s1[0] = sb;
     }
     // ---- fill: this wave's tiles as A operands; zero past the slice -----------------------
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         // little, as the combine waits for the last workgroup anyway, while the W1 row of wave 0's
         // gather has nothing queued ahead of it
         if (t > 0) {
-            gather_w1_codes<W1T>(p, tok, w1q, s1, wave, lane, [&] {});
+            gather_w1_codes<W1T, LOW_BYTES>(p, tok, w1q, w1l, s1, wave, lane, [&] {});
             __syncthreads();
         }
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
@@ -151,9 +158,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
 #pragma unroll
         for (int gi = 0; gi < M1_GROUPS; ++gi) cur[gi] = pf[gi];
         v4i1 bop[4];
+        const uint32_t* wd = c < 8 ? w1q : w1l;   // column c: high digits, or low from 8 on
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            bop[kb] = *reinterpret_cast<const v4i1*>(w1q + w1q_chunk_dword(0, kb * 4 + g));
+            bop[kb] = *reinterpret_cast<const v4i1*>(wd + w1q_chunk_dword(0, kb * 4 + g));
         const float sb = s1[0];
 
         // every register slot's MFMAs first (slots past the slice hold zero codes), then the LDS
@@ -194,10 +202,18 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
                 s = ri == 3 ? x[3] : s;
                 a[j] = s;
             }
-            int dot = a[0];
-            dot = ts == 1 ? a[1] : dot;
-            dot = ts == 2 ? a[2] : dot;
-            dot = ts == 3 ? a[3] : dot;
+            // this lane's product (column l % 16: high digits for ts < 2) and, for lane l ^ 8,
+            // the product of the row that lane finishes (tile slot 4 gi + (ts ^ 2), the other
+            // kind of column), exchanged by a rotation of each 16-lane row by 8
+            int mine = a[0], theirs = a[2];
+            mine = ts == 1 ? a[1] : mine;
+            theirs = ts == 1 ? a[3] : theirs;
+            mine = ts == 2 ? a[2] : mine;
+            theirs = ts == 2 ? a[0] : theirs;
+            mine = ts == 3 ? a[3] : mine;
+            theirs = ts == 3 ? a[1] : theirs;
+            const int other = __builtin_amdgcn_update_dpp(theirs, theirs, DPP_ROW_ROR8, 0xF, 0xF, false);
+            const int dot = ts < 2 ? join_digits(mine, other) : join_digits(other, mine);
             const int v = vrow[gi];
             const float l = walk_logit(cur[gi], sc[gi], sb, dot);
             if constexpr (!SAMPLE) {

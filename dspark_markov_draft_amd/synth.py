@@ -100,6 +100,20 @@ def make_inputs(case: Case, bs: Optional[int] = None, V: Optional[int] = None,
     return Inputs(case, w1, w2, base, start, seeds, temperature)
 
 
+def with_heavy_entries(w: torch.Tensor, per_row: int, mult: float, std: float,
+                       seed: int) -> torch.Tensor:
+    """A copy of ``w`` [V, 256] in which ``per_row`` entries of every row, at seeded random
+    columns, are replaced by +-``mult`` * ``std`` (random signs): rows whose largest entries are
+    far above the rest, as some trained rows have. Same dtype as ``w``."""
+    g = torch.Generator().manual_seed(seed)
+    V, K = w.shape
+    cols = torch.argsort(torch.rand(V, K, generator=g), dim=1)[:, :per_row]
+    signs = torch.where(torch.rand(V, per_row, generator=g) < 0.5, -1.0, 1.0)
+    out = w.float().clone()
+    out.scatter_(1, cols, signs * (mult * std))
+    return out.to(w.dtype)
+
+
 def seeds_as_int64(seeds: np.ndarray) -> torch.Tensor:
     """uint64 request seeds as a same-bits int64 tensor (torch has no uint64 arithmetic)."""
     return torch.from_numpy(np.ascontiguousarray(seeds, dtype=np.uint64).view(np.int64))

@@ -64,8 +64,8 @@ enum dspark_dtype { DSPARK_F32 = 0, DSPARK_BF16 = 1, DSPARK_F16 = 2 };
 const char* dspark_status_string(int status);
 
 /*
- * Quantise W2 to int8 with one fp32 scale per row (PR #62958, Overview: "int8 with one fp32
- * scale per row"). Reading of the unstated recipe: symmetric absmax, per row
+ * Quantise W2 to int8 codes and one fp32 scale per row (PR #62958, Overview). Reading of the
+ * unstated recipe: symmetric absmax, per row
  *     s[v] = max_k |W2[v,k]| / 127            (IEEE fp32 division)
  *     q[v,k] = clamp(rint(W2[v,k] / s[v]), -127, 127)   (IEEE division, round half to even)
  * and an all-zero row gets s = 0, q = 0.
@@ -109,8 +109,8 @@ typedef struct dspark_walk_plan {
 /* Which kernel runs a dense walk: a few requests are GEMVs, more make every step a GEMM (int8
  * matrix cores, 16 requests per tile: DSPARK_PATH_MFMA, from 3 requests greedy and 4 sampling).
  * One request runs on the matrix cores too when each workgroup's slice is at most 1152 rows
- * (every supported V on a 256-CU device), with its W1 codes in all 16 columns
- * (DSPARK_PATH_MFMA1); otherwise, and for 2 (greedy) or 2-3 (sampling) requests, the
+ * (every supported V on a 256-CU device), with the two digits of its W1 codes in the two halves
+ * of the 16 columns (DSPARK_PATH_MFMA1); otherwise, and for 2 (greedy) or 2-3 (sampling) requests, the
  * lane-per-row v_dot4 kernel runs (DSPARK_PATH_DOT4).
  * The plan queries below report the greedy walk's plan. */
 enum dspark_path { DSPARK_PATH_DOT4 = 1, DSPARK_PATH_MFMA = 2, DSPARK_PATH_MFMA1 = 3 };
@@ -131,8 +131,11 @@ int dspark_walk_plan_for(int32_t cus, int64_t max_lds, int64_t bs, int64_t T, in
  *   draft_tokens [bs, T] int32 out
  *   out_logits [bs, T, V] fp32 out, or NULL: the logits the argmax ran on
  *   workspace of dspark_walk_workspace_bytes(bs, T, V, 0) bytes, zeroed once at allocation
- * Numerics: the bias is (s[v] * s1) * sum_k q[v,k] * q1[k] with q1 = int8 codes of the gathered
- * W1 row under its own absmax scale s1 (exact int32 sum); logits are fp32.
+ * Numerics: the bias is (s[v] * s1) * sum_k q[v,k] * C[k], where the gathered W1 row is coded
+ * per step as C = rint(W1[prev] * 2032 / absmax), integers in [-2032, 2032] with step
+ * s1 = absmax / 2032 (each element within s1 / 2 of W1), held as two int8 digits
+ * C = 16 hi + lo; the sum is exact in int32 and every kernel computes the same one. Logits are
+ * fp32.
  */
 int dspark_walk_greedy(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
                        const float* base_logits, const int32_t* start_tokens, int64_t bs,
