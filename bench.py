@@ -418,7 +418,7 @@ SWEEP = [("v151936_t7_bs1", "sample"), ("v151936_t7_bs16", "greedy"),
          ("v248320_t16_bs1", "sample"),
          ("topk512_v151936_t7_bs64", "greedy"), ("topk512_v151936_t7_bs64", "sample"),
          ("v151936_t7_bs1", "sample_icdf"), ("v151936_t7_bs16", "sample_icdf"),
-         ("v151936_t16_bs1", "sample_icdf"),
+         ("v151936_t7_bs64", "sample_icdf"), ("v151936_t16_bs1", "sample_icdf"),
          ("pruned:512:v151936_t7_bs1", "greedy"), ("pruned:512:v151936_t7_bs16", "greedy"),
          ("pruned:512:v151936_t7_bs64", "greedy"),
          ("verify:64:7:151936", "token"), ("verify:64:7:151936", "block"),

@@ -142,10 +142,8 @@ int plan_walk(const DeviceInfo& dev, int64_t bs, int64_t T, int64_t V, int sampl
     int path = (bs >= min_bs && V % 4 == 0) ? DSPARK_PATH_MFMA
                : bs == 1                      ? DSPARK_PATH_MFMA1
                                               : DSPARK_PATH_DOT4;
-    // the inverse-CDF sampler runs on the one-request MFMA and lane-per-row kernels only
-    if (sample == 2 && path == DSPARK_PATH_MFMA) path = DSPARK_PATH_DOT4;
     if (dbg.force_path == DSPARK_PATH_DOT4) path = DSPARK_PATH_DOT4;
-    if (dbg.force_path == DSPARK_PATH_MFMA && V % 4 == 0 && sample != 2) path = DSPARK_PATH_MFMA;
+    if (dbg.force_path == DSPARK_PATH_MFMA && V % 4 == 0) path = DSPARK_PATH_MFMA;
     if (dbg.force_path == DSPARK_PATH_MFMA1 && bs == 1) path = DSPARK_PATH_MFMA1;
     if (path != DSPARK_PATH_DOT4 && plan_path(dev, cap, bs, V, path, sample, plan) == DSPARK_OK)
         return DSPARK_OK;

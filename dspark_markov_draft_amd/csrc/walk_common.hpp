@@ -33,9 +33,9 @@ constexpr int MFMA1_MAX_ROWS = (MFMA1_TILES + MFMA1_LDS_TILES) * WALK_WAVES * 16
 constexpr int MFMA_STATIC_ROWS = 624;
 constexpr int MFMA_STATIC_STRIDE = 628;
 constexpr int MFMA_STATIC_TILE_SLOTS = 10;
-// tile slots per wave held in LDS (the rest in registers): the sampling kernel holds one more in
-// LDS, which leaves its Philox sampler the registers it would otherwise take from spills
-__host__ __device__ constexpr int mfma_static_lds_slots(int sample) { return sample ? 3 : 2; }
+// tile slots per wave held in LDS (the rest in registers): the Gumbel sampling kernel holds one
+// more in LDS, which leaves its Philox sampler the registers it would otherwise take from spills
+__host__ __device__ constexpr int mfma_static_lds_slots(int sample) { return sample == 1 ? 3 : 2; }
 constexpr int MFMA_STATIC_SLOT_ROWS = MFMA_STATIC_TILE_SLOTS * WALK_WAVES * 16;
 constexpr int MFMA_STATIC_COPY_UNITS = (16 * MFMA_STATIC_STRIDE / 4 + WAVE - 1) / WAVE * WAVE;
 constexpr int MFMA_STATIC_STAGE_FLOATS =
@@ -46,10 +46,12 @@ constexpr int MFMA_STATIC_STAGE_FLOATS =
 constexpr int MFMA_REQ_CONST_BYTES = MAX_BS * (8 + 8 + 4);
 __host__ __device__ constexpr int mfma_static_lds_bytes(int sample) {
     return 2 * MFMA_STATIC_STAGE_FLOATS * 4 + mfma_static_lds_slots(sample) * WALK_WAVES * 4 * WAVE * 16 +
-           W1Q_BYTES + W1N_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 + MAX_BS * 8 +
-           MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
+           W1Q_BYTES + W1N_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 +
+           (sample == 2 ? WALK_WAVES : 1) * MAX_BS * 8 + MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
 }
-static_assert(mfma_static_lds_bytes(1) <= 160 * 1024, "static LDS fits a CU");
+static_assert(mfma_static_lds_bytes(0) <= 160 * 1024 && mfma_static_lds_bytes(1) <= 160 * 1024 &&
+                  mfma_static_lds_bytes(2) <= 160 * 1024,
+              "static LDS fits a CU");
 // The kernel with dynamic LDS has small static arrays too (the request constants and the
 // unused forms of the static buffers): its dynamic LDS leaves this much of the CU's LDS free.
 constexpr int MFMA_DYN_STATIC_RESERVE = 2048;

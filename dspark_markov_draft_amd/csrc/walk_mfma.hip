@@ -3,8 +3,9 @@
 //
 // What it computes: as the v_dot4 kernel (vLLM PR #62958, int8 DSpark Markov walk, Overview
 // and Details; vLLM PR #64476, Claims): l[v] = base[b,t,v] + s[v] * s1_b * sum_k q[v,k] C_b[k]
-// (C = 16 hi + lo, the two-digit W1 codes), then the first-maximum argmax (greedy) or the
-// Gumbel-max of bf16(l) / temp + noise (sample).
+// (C = 16 hi + lo, the two-digit W1 codes), then the first-maximum argmax (greedy), the
+// Gumbel-max of bf16(l) / temp + noise (sample), or (inverse CDF) each lane's running softmax
+// pair of z = bf16(l) * log2(e) / temp, merged per request and handed to combine_icdf_step().
 //
 // v_mfma_i32_16x16x64_i8 multiplies a 16 x 64 int8 tile by a 64 x 16 int8 tile into 16 x 16
 // int32. Lane l supplies row l % 16 of A and column l % 16 of B, each for the k-chunk of lane
@@ -50,7 +51,12 @@ static_assert(NT_STAT * WALK_WAVES * TILE_ROWS == MFMA_STATIC_SLOT_ROWS, "STAT s
 constexpr int STAT_COPY_SLOTS = MFMA_STATIC_COPY_UNITS / WAVE / WALK_WAVES;
 static_assert(MFMA_STATIC_COPY_UNITS % (WAVE * WALK_WAVES) == 0 && STAT_COPY_SLOTS <= NT_STAT,
               "STAT copy slots");
-constexpr int LKEY_BYTES = MAX_BS * 8;   // the workgroup's best key per request
+// the workgroup's best key per request (argmax), or each wave's softmax pair per request
+// (inverse CDF)
+__host__ __device__ constexpr int lkey_bytes(int sample) {
+    return (sample == 2 ? WALK_WAVES : 1) * MAX_BS * 8;
+}
+constexpr int LKEY_BYTES = lkey_bytes(2);   // the dynamic layout reserves the larger
 
 // dynamic LDS besides the W2 tiles: W1 digits, their steps, row scales, wave keys, tokens
 __host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
@@ -80,10 +86,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     __shared__ __align__(16) uint32_t w1n_s[STAT ? W1N_BYTES / 4 : 4];
     __shared__ __align__(16) float s1_s[STAT ? MAX_BS : 4];
     __shared__ __align__(16) float scl_s[STAT ? MFMA_STATIC_SLOT_ROWS : 4];
-    __shared__ __align__(16) uint64_t lkeys_s[STAT ? MAX_BS : 2];
+    __shared__ __align__(16) uint64_t lkeys_s[STAT ? lkey_bytes(SAMPLE) / 8 : 2];
     __shared__ __align__(16) int32_t tok_s[STAT ? MAX_BS : 4];
-    __shared__ __align__(16) uint64_t rq_seed[SAMPLE ? MAX_BS : 2];
-    __shared__ __align__(16) uint64_t rq_pos[SAMPLE ? MAX_BS : 2];
+    __shared__ __align__(16) uint64_t rq_seed[SAMPLE == 1 ? MAX_BS : 2];
+    __shared__ __align__(16) uint64_t rq_pos[SAMPLE == 1 ? MAX_BS : 2];
     __shared__ __align__(16) float rq_rtemp[SAMPLE ? MAX_BS : 4];
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     float* s1 = STAT ? s1_s : d_s1;
     float* scl = STAT ? scl_s : d_scl;
     uint64_t* lkeys = STAT ? lkeys_s : d_lkeys;
-    int32_t* tok = STAT ? tok_s : reinterpret_cast<int32_t*>(d_lkeys + MAX_BS);
+    int32_t* tok = STAT ? tok_s : reinterpret_cast<int32_t*>(d_lkeys + LKEY_BYTES / 8);
 
     // ---- fill: W2 tiles as A operands (VGPRs, then LDS), row scales into LDS ---------------
     auto load_a = [&](int tl, int kb) -> v4i {
@@ -151,8 +157,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     if constexpr (SAMPLE) {
         // read once here rather than at every request tile, where each read was a round trip
         if (tid < p.bs) {
-            rq_seed[tid] = p.seeds[tid];
-            rq_pos[tid] = (uint64_t)(p.positions ? p.positions[tid] : 0);
+            if constexpr (SAMPLE == 1) {
+                rq_seed[tid] = p.seeds[tid];
+                rq_pos[tid] = (uint64_t)(p.positions ? p.positions[tid] : 0);
+            }
             rq_rtemp[tid] = inv_temperature(p.temps[tid]);
         }
     }
@@ -283,12 +291,15 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 if (vb) {
                     // volatile: read here, not hoisted out of the step loop, where every request
                     // tile's values would hold registers through the whole walk
-                    seed = *reinterpret_cast<volatile uint64_t*>(&rq_seed[b]);
-                    P = *reinterpret_cast<volatile uint64_t*>(&rq_pos[b]) + (uint64_t)t;
+                    if constexpr (SAMPLE == 1) {
+                        seed = *reinterpret_cast<volatile uint64_t*>(&rq_seed[b]);
+                        P = *reinterpret_cast<volatile uint64_t*>(&rq_pos[b]) + (uint64_t)t;
+                    }
                     rtemp = *reinterpret_cast<volatile float*>(&rq_rtemp[b]);
                 }
             }
             const PhiloxRun prun = philox_run(seed, P);
+            const float kz = rtemp * LOG2E_F;   // inverse CDF: z = lb * log2(e) / temp
             // Rows vt .. vt+3 of request b from the accumulator of one tile: their logits (and
             // bf16 rows and noise when sampling), the quantity the argmax compares, and in `out`
             // the bits store4 writes (fp32 logits, or two words of bf16 pairs). The group is
@@ -311,6 +322,14 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                         sc[i] = l[i];
                         out[i] = __float_as_uint(l[i]);
                     }
+                } else if constexpr (SAMPLE == 2) {
+                    out[0] = bf16x2_bits(l[0], l[1]);
+                    out[1] = bf16x2_bits(l[2], l[3]);
+                    out[2] = out[3] = 0;
+                    sc[0] = bf16_lo(out[0]) * kz;
+                    sc[1] = bf16_hi(out[0]) * kz;
+                    sc[2] = bf16_lo(out[1]) * kz;
+                    sc[3] = bf16_hi(out[1]) * kz;
                 } else {
                     out[0] = bf16x2_bits(l[0], l[1]);
                     out[1] = bf16x2_bits(l[2], l[3]);
@@ -362,7 +381,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     // finished slot of the first pass, and in a later pass one behind each
                     // group of its MFMAs (a copy whose issue stalls while HBM is busy then stalls
                     // the wave only while the matrix core works through the group before it).
-                    constexpr int HALF = SAMPLE ? (NT_STAT + 1) / 2 : NT_STAT;
+                    constexpr int HALF = SAMPLE == 1 ? (NT_STAT + 1) / 2 : NT_STAT;
 #pragma unroll
                     for (int h0 = 0; h0 < NT_STAT; h0 += HALF) {
                         constexpr int n = HALF;
@@ -478,8 +497,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             float run_v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             uint32_t run_i[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
             float chk = 0.0f;
+            RunningSoftmax soft;   // inverse CDF: this lane's pair of request b
             constexpr bool HOLD = STAT && (SAMPLE || OUTL);   // outputs held for a half
-            constexpr int HALF_SLOTS = SAMPLE ? (NT_STAT + 1) / 2 : NT_STAT;
+            constexpr int HALF_SLOTS = SAMPLE == 1 ? (NT_STAT + 1) / 2 : NT_STAT;
             uint32_t held[HOLD ? HALF_SLOTS : 1][4];
             for_tiles([&](const v4i acc, int vt, int tw) {
                 float sc[4];
@@ -491,13 +511,18 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 } else if constexpr (!STAT) {
                     store4(vt, ok, out);
                 }
-                chk += ok ? (sc[0] + sc[1]) + (sc[2] + sc[3]) : 0.0f;
+                if constexpr (SAMPLE == 2) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = ok ? sc[i] : -INFINITY;
-                    if (x > run_v[i]) {
-                        run_v[i] = x;
-                        run_i[i] = (uint32_t)(vt + i);
+                    for (int i = 0; i < 4; ++i) soft.offer(sc[i], ok);
+                } else {
+                    chk += ok ? (sc[0] + sc[1]) + (sc[2] + sc[3]) : 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = ok ? sc[i] : -INFINITY;
+                        if (x > run_v[i]) {
+                            run_v[i] = x;
+                            run_i[i] = (uint32_t)(vt + i);
+                        }
                     }
                 }
             }, [&](int tw) {
@@ -517,6 +542,15 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     }
                 }
             });
+            if constexpr (SAMPLE == 2) {
+                // request c's pair over this wave's rows: the four lanes of the request (row
+                // groups g at lanes c + 16 g) merged by two lane exchanges, stored by g = 0
+#pragma unroll
+                for (int o = 32; o >= 16; o >>= 1)
+                    soft.merge(__shfl_xor(soft.m, o, WAVE), __shfl_xor(soft.s, o, WAVE));
+                if (g == 0) lkeys[wave * MAX_BS + rt * 16 + c] = pack_softmax(soft.m, soft.s);
+                return;
+            }
             const bool nan_seen = chk != chk;
             float bv = run_v[0];
             uint32_t bi = run_i[0];
@@ -587,12 +621,26 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 
         if (wave == 0) {
             uint64_t k = 0;
-            // the workgroup's key of request `lane`, cleared for the next step (whose first
-            // update follows the barrier after the combine)
-            k = lkeys[lane];
-            lkeys[lane] = 0;
-            if (lane >= p.bs) k = 0;
-            combine_step<TIMED>(p, t, k, tok, lane);
+            if constexpr (SAMPLE == 2) {
+                // request `lane`'s pair over the whole slice: the four waves' merged
+                RunningSoftmax a;
+#pragma unroll
+                for (int w = 0; w < WALK_WAVES; ++w) {
+                    const uint64_t o = lkeys[w * MAX_BS + lane];
+                    a.merge(packed_m(o), packed_s(o));
+                }
+                k = lane < p.bs ? pack_softmax(a.m, a.s) : 0ull;
+            } else {
+                // the workgroup's key of request `lane`, cleared for the next step (whose first
+                // update follows the barrier after the combine)
+                k = lkeys[lane];
+                lkeys[lane] = 0;
+                if (lane >= p.bs) k = 0;
+            }
+            if constexpr (SAMPLE == 2)
+                combine_icdf_step<TIMED>(p, t, k, tok, lane);
+            else
+                combine_step<TIMED>(p, t, k, tok, lane);
         }
         __syncthreads();
     }
@@ -604,6 +652,13 @@ template <int STAT, int OUTL>
 static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
 #define DSPARK_MFMA(S, W, TI) \
     reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT, (S ? 1 : OUTL)>)
+    if (sample == 2) {   // inverse CDF (no instrumented build)
+        switch (w1t) {
+            case DT_F32: return DSPARK_MFMA(2, DT_F32, 0);
+            case DT_BF16: return DSPARK_MFMA(2, DT_BF16, 0);
+            default: return DSPARK_MFMA(2, DT_F16, 0);
+        }
+    }
     if (timed) return sample ? DSPARK_MFMA(1, DT_BF16, 1) : DSPARK_MFMA(0, DT_BF16, 1);
     if (sample) {
         switch (w1t) {

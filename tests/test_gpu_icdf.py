@@ -1,7 +1,8 @@
 """The inverse-CDF walk (dspark_walk_sample_icdf) against the CPU oracle, through the C ABI:
 bf16 rows by the interval rule, tokens teacher-forced (a token differing from the oracle's must
 be a draw of the walk's own stored row for a uniform within 1e-5 of the step's); oracle-sized
-shapes over both kernels, ragged slices, grid caps and single steps; the benchmarked shapes;
+shapes over all three kernels (one-request MFMA, lane-per-row, batched MFMA with static and
+dynamic LDS), ragged slices, grid caps and single steps; the benchmarked shapes;
 token frequencies against softmax (chi-squared); the token-feedback walk; timeouts and a
 workspace left zeroed."""
 import numpy as np
@@ -48,7 +49,10 @@ SMALL = [  # V, T, bs, dtype, grid cap, path (0: chosen)
     (5000, 3, 1, torch.bfloat16, 0, B.PATH_DOT4),
     (5001, 3, 2, torch.bfloat16, 0, 0),       # odd V
     (20000, 3, 3, torch.float16, 16, 0),      # large slices: LDS row sets, several scan passes
-    (30000, 2, 17, torch.bfloat16, 0, 0),     # 17 requests on the lane-per-row kernel
+    (30000, 2, 17, torch.bfloat16, 0, B.PATH_DOT4),   # 17 requests on the lane-per-row kernel
+    (30000, 2, 17, torch.bfloat16, 0, 0),     # the same on the batched MFMA kernel (2 tiles)
+    (4096, 3, 5, torch.float32, 0, 0),        # batched: one partial request tile
+    (20000, 3, 20, torch.float16, 24, 0),     # batched, 848-row slices: dynamic LDS variant
     (3000, 5, 64, torch.bfloat16, 0, 0),      # full batch, 12 workgroups: several reducers each
     (20000, 3, 1, torch.bfloat16, 20, 0),     # one request, 1000-row slices (LDS tiles)
     (30000, 1, 1, torch.bfloat16, 0, 0),      # a single step
@@ -85,10 +89,13 @@ def test_icdf_full_size(name, parity_log):
     assert int(ws.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("path", [0, B.PATH_DOT4])
 @pytest.mark.parametrize("temp", [1.0, 0.6])
-def test_icdf_frequencies_are_softmax(temp):
+def test_icdf_frequencies_are_softmax(temp, path):
     """W2 = 0 and bf16-exact base logits: each step draws from softmax(base / temp). 64 requests
-    x 2 steps x 600 calls with fresh seeds: the token counts match it (chi-squared)."""
+    x 2 steps x 600 calls with fresh seeds: the token counts match it (chi-squared). On the
+    batched MFMA kernel (chosen) and the lane-per-row kernel."""
+    dm.dspark_debug_set(B.DEBUG_FORCE_PATH, path)
     V, T, bs, calls = 8, 2, 64, 600
     row = np.array([0.0, 0.5, -1.0, 1.25, 2.0, -0.75, 0.25, 1.0], np.float32)
     w = torch.zeros(V, 256, dtype=torch.bfloat16)
