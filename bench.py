@@ -64,7 +64,8 @@ VERIFY_KERNELS = "verify_*_kernel"
 LDS_PEAK_GBS = 128 * 256 * 2.4
 DOT4_MACS = 157.3e12          # int8 v_dot4 multiply-adds per second (256 CUs, 2.4 GHz)
 MFMA_I8_MACS = 2.5e15         # dense int8 matrix-core multiply-adds per second (5.0 POP/s)
-STAMPS_PER_WG = 82
+STAMPS_PER_WG = 210
+STAMP_TILE0 = 82   # per-request-tile words of the multi-request MFMA kernel
 
 
 def log(*a):
@@ -315,6 +316,21 @@ def stamp_split(w, flush, calls=5):
             "compute_to_last_store": np.mean(cc[1:] if T > 1 else cc) * tick,
             "last_store_to_all_hold_token": np.mean(ce) * tick}
         r["barrier_stall_share"] = float(np.median(waits / (end - start)))
+        if plan["path"] == 2:
+            # multi-request MFMA kernel: per 16-request tile, from the previous tile's end (the
+            # first tile: from the W1 codes) to its base logits landed, and from there to done
+            nrt = (w.bs + 15) // 16
+            land, fin = [[] for _ in range(nrt)], [[] for _ in range(nrt)]
+            for t in range(T):
+                prev_end = s[:, 2 + 5 * t]
+                for rt in range(nrt):
+                    k = STAMP_TILE0 + 2 * (4 * t + rt)
+                    land[rt].append(np.median(s[:, k] - prev_end))
+                    fin[rt].append(np.median(s[:, k + 1] - s[:, k]))
+                    prev_end = s[:, k + 1]
+            r["request_tile_median_us"] = {
+                f"tile{rt}": {"to_landed": np.mean(land[rt]) * tick, "finish": np.mean(fin[rt]) * tick}
+                for rt in range(nrt)}
         return r
 
     rs = [one(s) for s in runs]
@@ -334,6 +350,10 @@ def stamp_split(w, flush, calls=5):
            "per_step_median_us": {k: med(["per_step_median_us", k]) for k in rs[0]["per_step_median_us"]},
            "critical_path_per_step_us": {k: med(["critical_path_per_step_us", k])
                                          for k in rs[0]["critical_path_per_step_us"]}}
+    if "request_tile_median_us" in rs[0]:
+        out["request_tile_median_us"] = {
+            tile: {k: med(["request_tile_median_us", tile, k]) for k in v}
+            for tile, v in rs[0]["request_tile_median_us"].items()}
     return out
 
 

@@ -24,7 +24,7 @@ DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG, DEBUG_STAMPS = 1,
 DEBUG_FORCE_PATH = 5
 DEBUG_KERNEL_TIMING = 6
 PATH_DOT4, PATH_MFMA, PATH_MFMA1 = 1, 2, 3
-STAMPS_PER_WG = 82
+STAMPS_PER_WG = 210
 
 OK = 0
 ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NO_DEVICE = -1, -2, -3, -4

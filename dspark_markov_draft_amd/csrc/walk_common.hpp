@@ -107,7 +107,11 @@ struct WaitBound {
 // slot stored, reductions done, result words seen.
 constexpr int STAMP_STEP0 = 2;
 constexpr int STAMPS_PER_STEP = 5;
-constexpr int STAMPS_PER_WG = STAMP_STEP0 + MAX_STEPS * STAMPS_PER_STEP;
+// the multi-request MFMA kernel adds two words per step and 16-request tile: the tile's base
+// logits landed (every wave past the barrier), the tile finished
+constexpr int STAMP_TILE0 = STAMP_STEP0 + MAX_STEPS * STAMPS_PER_STEP;   // 82
+constexpr int STAMP_TILES = MAX_BS / 16;
+constexpr int STAMPS_PER_WG = STAMP_TILE0 + MAX_STEPS * STAMP_TILES * 2;   // 210
 
 template <int TIMED>
 __device__ __forceinline__ void stamp(const WalkParams& p, int slot) {

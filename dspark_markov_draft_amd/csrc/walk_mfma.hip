@@ -257,6 +257,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             auto landed = [&]() {
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
+                stamp<TIMED>(p, STAMP_TILE0 + (t * STAMP_TILES + rt) * 2);
             };
             if constexpr (!STAT) landed();
             const bool prefetch = nbuf == 2 && rt + 1 < nrt;
@@ -605,6 +606,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             // at the end of every request tile, ~5 us per walk at 64 requests.
             __hip_atomic_fetch_max(&lkeys[rt * 16 + c], best, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+            stamp<TIMED>(p, STAMP_TILE0 + (t * STAMP_TILES + rt) * 2 + 1);
         };
         for (int rt = 0; rt < nrt; ++rt) {
             // the buffer each tile reads is named in the code (not picked by an index), so that

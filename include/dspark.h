@@ -325,11 +325,12 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *   DSPARK_DEBUG_FORCE_PATH: 0 chooses by batch size; DSPARK_PATH_DOT4 / DSPARK_PATH_MFMA force
  *       that kernel for every batch size, DSPARK_PATH_MFMA1 for one request whose slices fit it
  *       (all compute the same results);
- *   DSPARK_DEBUG_STAMPS: a device address (8-byte aligned) of 256 x 82 uint64 words, or 0.
+ *   DSPARK_DEBUG_STAMPS: a device address (8-byte aligned) of 256 x 210 uint64 words, or 0.
  *       When set, dense walks with bf16 W1 run an instrumented build of the same kernel that
  *       stores the 100 MHz device clock per workgroup: [0] start, [1] W2 resident, then per step
  *       t at 2 + 5t: W1 codes ready, slice argmax done, own slot stored, reductions done,
- *       result words seen. Top-k walks with bf16 W1 (k <= 512, V % 4 == 0) use words
+ *       result words seen; the multi-request MFMA kernel also, per step t and 16-request tile
+ *       r, at 82 + 2 (4t + r): the tile's base logits landed, the tile done. Top-k walks with bf16 W1 (k <= 512, V % 4 == 0) use words
  *       row * 8 + (0 start, 1 first bound, 2 row scanned, 3 k-th key, 4 done) for each
  *       (request, step) row of the candidate select, and 8192 + request * 40 + (0 start, then
  *       per step t: 1 + 2t W1 codes ready, 2 + 2t token known) for the walk. For profiling only;
