@@ -922,7 +922,7 @@ __device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, ui
 }
 
 // Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0 greedy, 1 Gumbel,
-// 2 inverse CDF (one-request MFMA and lane-per-row kernels only); w1t: DT_*).
+// 2 inverse CDF; w1t: DT_*).
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
 const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles);
 const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits);
