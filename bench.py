@@ -21,8 +21,8 @@ Bounds reported beside the measured time (`bounds`):
     B_W2 = V x 256 read once; `frac` = R_W2 / kernel time. For the top-k walk the W2 traffic is
     the gathered candidate rows, bs T k 256 bytes, at HBM peak;
   * R_full: every algorithmic byte of the call at HBM peak;
-  * F_ALU: bs T V 256 int8 multiply-adds at the full v_dot4 rate (157.3 T/s), F_MFMA at the
-    dense int8 matrix-core rate (2.5 P/s);
+  * F_ALU: the walk's int8 multiply-adds (bs T V 256, twice: one per digit of the W1 codes) at
+    the full v_dot4 rate (157.3 T/s), F_MFMA at the dense int8 matrix-core rate (2.5 P/s);
   * `stamps`: an instrumented build of the same kernel records the device's 100 MHz clock per
     workgroup at each phase of each step (cold calls): the median W2 fill, per step the W1
     gather, the slice dot products + argmax, the key store, and the wait from a workgroup's own
@@ -92,7 +92,7 @@ def bounds(w, kernel_us):
     r_full = w.algorithmic_bytes() / (HBM_PEAK_GBS * 1e3)
     out = {"r_full_us": round(r_full, 3), "r_full_frac": round(r_full / kernel_us, 4)}
     if isinstance(w, Walk):
-        macs = w.bs * w.T * (w.k if w.k else w.V) * 256
+        macs = w.bs * w.T * (w.k if w.k else w.V) * 256 * 2   # two int8 digits per W1 code
         out["f_alu_us"] = round(macs / DOT4_MACS * 1e6, 3)
         out["f_mfma_us"] = round(macs / MFMA_I8_MACS * 1e6, 3)
     return out
