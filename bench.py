@@ -29,9 +29,10 @@ Bounds reported beside the measured time (`bounds`):
     key store until it holds the step's token; along the critical path, the time from the last
     workgroup's key store until every workgroup holds the token; the barrier stall share is a
     workgroup's summed waits over its whole span (median over workgroups);
-  * `exchange_floor`: per-step time of the same greedy kernel at V = 65536 (256 workgroups of
-    256 rows: a quarter of the headline's slice), from 16- and 7-step walks, beside the
-    headline's own per-step time.
+  * `exchange_floor`: per-step time of the greedy one-request kernel at V = 65536 (256
+    workgroups of 256 rows, which run its 4-tile-slot build: the headline's gather and
+    exchange with 4 of its 10 slots of products per wave), from 16- and 7-step walks, beside
+    the headline's own per-step time.
 
 `roofline.traffic` is the HBM traffic per launch measured by the FETCH_SIZE / WRITE_SIZE
 counters (profiles/traffic.json, calibrated against a plain copy of known size); it is reported
@@ -359,7 +360,8 @@ def stamp_split(w, flush, calls=5):
 
 def exchange_floor(dev, flush, stream, steps):
     """Per-step time of the greedy one-request kernel with small slices (V = 65536: 256
-    workgroups of 256 rows), from kernel times of 16- and 7-step walks."""
+    workgroups of 256 rows, its 4-tile-slot build), from kernel times of 16- and 7-step
+    walks."""
     res = {}
     for V in (65536,):
         k = {}

@@ -214,7 +214,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
                          ? mfma_walk_kernel(a.sample, w1t, timed, static_stage,
                                             a.out_logits != nullptr)
                      : plan.path == DSPARK_PATH_MFMA1
-                         ? mfma1_walk_kernel(a.sample, w1t, timed, plan.lds_units > 0)
+                         ? mfma1_walk_kernel(a.sample, w1t, timed, plan.lds_units > 0,
+                                             mfma1_reg_slots(plan.total_units))
                                                        : dot4_walk_kernel(a.sample, w1t, timed);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dyn_lds) !=
         hipSuccess) {

@@ -22,6 +22,12 @@ constexpr int LDS_MIN_BYTES = 96 * 1024;         // > half a CU's LDS: one workg
 constexpr uint32_t DEFAULT_SPIN_TICKS = 1000000u;
 constexpr int DOT4_REG_SETS = 3;  // lane-per-row kernel: row sets of 256 rows held in registers
 constexpr int MFMA1_TILES = 10;      // one-request MFMA kernel: 16-row tiles per wave in registers
+// Smaller register-slot counts for smaller slices: the kernel multiplies and finishes every slot
+// it has (no branch per tile), so a slice of at most 4 or 8 tiles per wave runs an instantiation
+// with that many slots.
+__host__ __device__ constexpr int mfma1_reg_slots(int tiles_per_wave) {
+    return tiles_per_wave <= 4 ? 4 : tiles_per_wave <= 8 ? 8 : MFMA1_TILES;
+}
 constexpr int MFMA1_LDS_TILES = 8;   // and at most this many more in LDS (4 KB each)
 constexpr int MFMA1_MAX_ROWS = (MFMA1_TILES + MFMA1_LDS_TILES) * WALK_WAVES * 16;   // 1152
 // MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
@@ -924,7 +930,7 @@ __device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, ui
 // Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0 greedy, 1 Gumbel,
 // 2 inverse CDF; w1t: DT_*).
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
-const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles);
+const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles, int reg_slots);
 const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits);
 int mfma_fixed_lds_bytes(int rows_per_wg);
 

@@ -19,7 +19,8 @@
 // finishes three rows per lane.
 //
 // The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves (tile tw * 4 + wave):
-// the first MFMA1_TILES slots of each wave in registers, up to MFMA1_LDS_TILES more in LDS (a
+// the first NREG slots of each wave in registers (NREG = 4, 8 or MFMA1_TILES, the fewest that
+// hold the slice: every slot is multiplied and finished), up to MFMA1_LDS_TILES more in LDS (a
 // K-block of a tile is 64 consecutive 16-byte lane slots there, read without bank conflicts).
 // A lane holds, for tile slot tw and K-block kb, bytes kb * 64 + g * 16 .. +15 of its row
 // (g = lane / 16), and the W1 codes are read from LDS in the same order: any order of K serves
@@ -36,10 +37,11 @@ typedef int v4i1 __attribute__((ext_vector_type(4)));
 constexpr int M1_TILE_LDS_BYTES = 4 * WAVE * 16;
 
 // LDS: slices of more than MFMA1_TILES tiles per wave (the LDS tile slots exist); without it the
-// kernel has only the register slots, and no code or registers for the others.
-template <int SAMPLE, int W1T, int TIMED, int LDS>
+// kernel has only its NREG register slots, and no code or registers for the others.
+template <int SAMPLE, int W1T, int TIMED, int LDS, int NREG>
 __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const WalkParams p) {
-    constexpr int M1_SLOTS = MFMA1_TILES + (LDS ? MFMA1_LDS_TILES : 0);   // tile slots per wave
+    static_assert(NREG == MFMA1_TILES || !LDS, "LDS slots follow a full set of register slots");
+    constexpr int M1_SLOTS = NREG + (LDS ? MFMA1_LDS_TILES : 0);   // tile slots per wave
     constexpr int M1_GROUPS = (M1_SLOTS + 3) / 4;   // rows each lane finishes per step, at most
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     // tile slots per wave holding rows; the LDS variant multiplies all its MFMA1_LDS_TILES LDS
     // slots (branch-free), those past nslots hold copies of the slice's first row, not finished
     const int ntl = LDS ? p.lds_units : 0;
-    const int nslots = MFMA1_TILES + ntl;
+    const int nslots = NREG + ntl;
 
     unsigned char* lds_tiles = smem;
     uint32_t* w1q = reinterpret_cast<uint32_t*>(
@@ -84,9 +86,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         if (lane == 0) s1[0] = sb;
     }
     // ---- fill: this wave's tiles as A operands; zero past the slice -----------------------
-    v4i1 qa[MFMA1_TILES][4];
+    v4i1 qa[NREG][4];
 #pragma unroll
-    for (int tw = 0; tw < MFMA1_TILES; ++tw) {
+    for (int tw = 0; tw < NREG; ++tw) {
         const int tl = tw * WALK_WAVES + wave;
         const int row = row0 + tl * 16 + c;
         const bool have = tl < ntiles && row < vend;
@@ -98,11 +100,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     // LDS slots, copied by DMA straight from memory (a K-block is the 64 consecutive 16-byte lane
     // slots one global_load_lds writes). Rows past the slice copy the slice's first row: their
     // products are never finished.
-    for (int tw = MFMA1_TILES; tw < M1_SLOTS; ++tw) {
+    for (int tw = NREG; tw < M1_SLOTS; ++tw) {
         const int tl = tw * WALK_WAVES + wave;
         int row = row0 + tl * 16 + c;
         if (!(tw < nslots && tl < ntiles && row < vend)) row = row0;
-        unsigned char* dst = lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES;
+        unsigned char* dst = lds_tiles + (size_t)((tw - NREG) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
             __builtin_amdgcn_global_load_lds(
@@ -168,17 +170,17 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         // slots', then the finish
         v4i1 acc[M1_SLOTS];
 #pragma unroll
-        for (int tw = 0; tw < MFMA1_TILES; ++tw) {
+        for (int tw = 0; tw < NREG; ++tw) {
             acc[tw] = (v4i1){0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 acc[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb], acc[tw], 0, 0, 0);
         }
 #pragma unroll
-        for (int tw = MFMA1_TILES; tw < M1_SLOTS; ++tw) {
+        for (int tw = NREG; tw < M1_SLOTS; ++tw) {
             acc[tw] = (v4i1){0, 0, 0, 0};
             const v4i1* src = reinterpret_cast<const v4i1*>(
-                lds_tiles + (size_t)((tw - MFMA1_TILES) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES);
+                lds_tiles + (size_t)((tw - NREG) * WALK_WAVES + wave) * M1_TILE_LDS_BYTES);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 acc[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(src[kb * WAVE + lane], bop[kb],
@@ -270,9 +272,9 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     }
 }
 
-template <int LDS>
+template <int LDS, int NREG>
 static const void* mfma1_kernel_for(int sample, int w1t, bool timed) {
-#define DSPARK_MFMA1(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma1_kernel<S, W, TI, LDS>)
+#define DSPARK_MFMA1(S, W, TI) reinterpret_cast<const void*>(&dense_walk_mfma1_kernel<S, W, TI, LDS, NREG>)
     if (sample == 2) {
         switch (w1t) {
             case DT_F32: return DSPARK_MFMA1(2, DT_F32, 0);
@@ -296,8 +298,11 @@ static const void* mfma1_kernel_for(int sample, int w1t, bool timed) {
 #undef DSPARK_MFMA1
 }
 
-const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles) {
-    return lds_tiles ? mfma1_kernel_for<1>(sample, w1t, timed) : mfma1_kernel_for<0>(sample, w1t, timed);
+const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles, int reg_slots) {
+    if (lds_tiles) return mfma1_kernel_for<1, MFMA1_TILES>(sample, w1t, timed);
+    if (reg_slots <= 4) return mfma1_kernel_for<0, 4>(sample, w1t, timed);
+    if (reg_slots <= 8) return mfma1_kernel_for<0, 8>(sample, w1t, timed);
+    return mfma1_kernel_for<0, MFMA1_TILES>(sample, w1t, timed);
 }
 
 }  // namespace dspark

@@ -76,8 +76,8 @@ def test_icdf_parity_small(V, T, bs, dtype, cap, path):
     assert dm.dspark_workspace_status(ws) == 0
 
 
-@pytest.mark.parametrize("name", ["v151936_t7_bs1", "v151936_t7_bs16", "v151936_t16_bs1",
-                                  "v129280_t5_bs1"])
+@pytest.mark.parametrize("name", ["v151936_t7_bs1", "v151936_t7_bs16", "v151936_t7_bs64",
+                                  "v151936_t16_bs1", "v129280_t5_bs1"])
 def test_icdf_full_size(name, parity_log):
     inp = make_inputs(CASES[name])
     p = Problem(inp.w1, inp.w2, inp.base, inp.start, seeds=inp.seeds,

@@ -120,8 +120,8 @@ def test_infinities_fall_back():
     assert dense_steps.tolist() == [1, 2]
 
 
-@pytest.mark.parametrize("name,k", [("v151936_t7_bs1", 512), ("v151936_t7_bs64", 512),
-                                    ("v151936_t7_bs16", 2048)])
+@pytest.mark.parametrize("name,k", [("v151936_t7_bs1", 512), ("v151936_t7_bs16", 512),
+                                    ("v151936_t7_bs64", 512), ("v151936_t7_bs16", 2048)])
 def test_pruned_full_size(name, k, parity_log):
     inp = make_inputs(CASES[name])
     p = Problem(inp.w1, inp.w2, inp.base, inp.start)
