@@ -72,22 +72,22 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         const int64_t want = bs > 16 ? 2 : 1;
         const bool stat = rpw <= MFMA_STATIC_ROWS && stage_stride <= MFMA_STATIC_STRIDE;
         const int64_t dyn_max = (int64_t)dev.max_lds - MFMA_DYN_STATIC_RESERVE;   // without STAT
+        const int64_t tiles = rpw / 16;
+        units = (tiles + WALK_WAVES - 1) / WALK_WAVES;              // tile slots per wave
+        const int slots = mfma_static_slots((int)units);            // of the static build
         if (stat) {
             // all LDS is static and of fixed size (both staging buffers exist for any batch)
             stage_bufs = want;
-            if (mfma_static_lds_bytes(sample) > (int64_t)dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
+            if (mfma_static_lds_bytes(sample, slots) > (int64_t)dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
         } else {
             stage_bufs = (dyn_max - fixed) / buf_bytes;
             if (stage_bufs > want) stage_bufs = want;
             if (stage_bufs < 1) return DSPARK_ERR_UNSUPPORTED;    // the caller falls back
         }
         const int64_t stage_lds = stage_bufs * buf_bytes;
-        const int64_t tiles = rpw / 16;
-        units = (tiles + WALK_WAVES - 1) / WALK_WAVES;              // tile slots per wave
-        const int64_t reg_tiles =
-            stat ? MFMA_STATIC_TILE_SLOTS - mfma_static_lds_slots(sample) : MFMA_REG_TILES;
+        const int64_t reg_tiles = stat ? slots - mfma_static_lds_slots(sample, slots) : MFMA_REG_TILES;
         reg_units = units < reg_tiles ? units : reg_tiles;
-        int64_t room = stat ? mfma_static_lds_slots(sample)
+        int64_t room = stat ? mfma_static_lds_slots(sample, slots)
                             : (dyn_max - fixed - stage_lds) / (WALK_WAVES * MFMA_TILE_LDS);
         if (room < 0) room = 0;
         lds_units = units - reg_units;
@@ -95,7 +95,7 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         reg_rows = rpw < reg_units * WALK_WAVES * 16 ? rpw : reg_units * WALK_WAVES * 16;
         lds_rows = rpw - reg_rows;
         if (lds_rows > lds_units * WALK_WAVES * 16) lds_rows = lds_units * WALK_WAVES * 16;
-        lds_bytes = stat ? mfma_static_lds_bytes(sample)
+        lds_bytes = stat ? mfma_static_lds_bytes(sample, slots)
                          : lds_units * WALK_WAVES * MFMA_TILE_LDS + fixed + stage_lds;
         if (!stat && lds_bytes > dyn_max) return DSPARK_ERR_UNSUPPORTED;
     }
@@ -212,7 +212,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     const int dyn_lds = static_stage ? 0 : plan.lds_bytes;
     const void* fn = plan.path == DSPARK_PATH_MFMA
                          ? mfma_walk_kernel(a.sample, w1t, timed, static_stage,
-                                            a.out_logits != nullptr)
+                                            a.out_logits != nullptr,
+                                            mfma_static_slots(plan.total_units))
                      : plan.path == DSPARK_PATH_MFMA1
                          ? mfma1_walk_kernel(a.sample, w1t, timed, plan.lds_units > 0,
                                              mfma1_reg_slots(plan.total_units))

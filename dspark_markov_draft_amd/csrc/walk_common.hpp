@@ -33,15 +33,24 @@ constexpr int MFMA1_MAX_ROWS = (MFMA1_TILES + MFMA1_LDS_TILES) * WALK_WAVES * 16
 // MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
 // two staging buffers for 16 rows of at most MFMA_STATIC_STRIDE floats (157 odd 16-byte units),
 // up to mfma_static_lds_slots() LDS tiles per wave, W1 codes and scales, row scales, lane keys,
-// tokens. Every wave has MFMA_STATIC_TILE_SLOTS tile slots (8 in registers, then LDS), covering
+// tokens. Every wave has MFMA_STATIC_TILE_SLOTS tile slots (registers first, then LDS), covering
 // MFMA_STATIC_SLOT_ROWS rows; the row-scale array and the staging buffers are sized for reads of
 // all of them. A staging buffer also holds whole 64-lane copy instructions (64 units each).
+// Slices of at most MFMA_STATIC_SMALL_SLOTS tiles per wave run a build with that many slots:
+// every slot is multiplied and finished, with no branch per tile.
 constexpr int MFMA_STATIC_ROWS = 624;
 constexpr int MFMA_STATIC_STRIDE = 628;
 constexpr int MFMA_STATIC_TILE_SLOTS = 10;
-// tile slots per wave held in LDS (the rest in registers): the Gumbel sampling kernel holds one
-// more in LDS, which leaves its Philox sampler the registers it would otherwise take from spills
-__host__ __device__ constexpr int mfma_static_lds_slots(int sample) { return sample == 1 ? 3 : 2; }
+constexpr int MFMA_STATIC_SMALL_SLOTS = 8;
+__host__ __device__ constexpr int mfma_static_slots(int tiles_per_wave) {
+    return tiles_per_wave <= MFMA_STATIC_SMALL_SLOTS ? MFMA_STATIC_SMALL_SLOTS : MFMA_STATIC_TILE_SLOTS;
+}
+// tile slots per wave held in LDS (the rest in registers) of the build with `slots` slots: 8 in
+// registers, or 7 in the Gumbel sampling kernel, which leaves its Philox sampler the registers
+// it would otherwise take from spills
+__host__ __device__ constexpr int mfma_static_lds_slots(int sample, int slots) {
+    return slots - (sample == 1 ? 7 : 8);
+}
 constexpr int MFMA_STATIC_SLOT_ROWS = MFMA_STATIC_TILE_SLOTS * WALK_WAVES * 16;
 constexpr int MFMA_STATIC_COPY_UNITS = (16 * MFMA_STATIC_STRIDE / 4 + WAVE - 1) / WAVE * WAVE;
 constexpr int MFMA_STATIC_STAGE_FLOATS =
@@ -50,14 +59,22 @@ constexpr int MFMA_STATIC_STAGE_FLOATS =
         : 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS;
 // per-request sampling constants, loaded once per call: seed, position offset, 1 / temperature
 constexpr int MFMA_REQ_CONST_BYTES = MAX_BS * (8 + 8 + 4);
-__host__ __device__ constexpr int mfma_static_lds_bytes(int sample) {
-    return 2 * MFMA_STATIC_STAGE_FLOATS * 4 + mfma_static_lds_slots(sample) * WALK_WAVES * 4 * WAVE * 16 +
+__host__ __device__ constexpr int mfma_static_lds_bytes(int sample, int slots) {
+    return 2 * MFMA_STATIC_STAGE_FLOATS * 4 + mfma_static_lds_slots(sample, slots) * WALK_WAVES * 4 * WAVE * 16 +
            W1Q_BYTES + W1N_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 +
            (sample == 2 ? WALK_WAVES : 1) * MAX_BS * 8 + MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
 }
-static_assert(mfma_static_lds_bytes(0) <= 160 * 1024 && mfma_static_lds_bytes(1) <= 160 * 1024 &&
-                  mfma_static_lds_bytes(2) <= 160 * 1024,
+static_assert(mfma_static_lds_bytes(0, MFMA_STATIC_TILE_SLOTS) <= 160 * 1024 &&
+                  mfma_static_lds_bytes(1, MFMA_STATIC_TILE_SLOTS) <= 160 * 1024 &&
+                  mfma_static_lds_bytes(2, MFMA_STATIC_TILE_SLOTS) <= 160 * 1024,
               "static LDS fits a CU");
+// more than half a CU's LDS, so that one workgroup runs per CU with the small build too
+static_assert(mfma_static_lds_bytes(0, MFMA_STATIC_SMALL_SLOTS) > 80 * 1024 &&
+                  mfma_static_lds_bytes(2, MFMA_STATIC_SMALL_SLOTS) > 80 * 1024,
+              "one workgroup per CU");
+static_assert(mfma_static_lds_slots(1, MFMA_STATIC_SMALL_SLOTS) >= 0 &&
+                  mfma_static_lds_slots(0, MFMA_STATIC_SMALL_SLOTS) >= 0,
+              "register slots");
 // The kernel with dynamic LDS has small static arrays too (the request constants and the
 // unused forms of the static buffers): its dynamic LDS leaves this much of the CU's LDS free.
 constexpr int MFMA_DYN_STATIC_RESERVE = 2048;
@@ -931,7 +948,8 @@ __device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, ui
 // 2 inverse CDF; w1t: DT_*).
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
 const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles, int reg_slots);
-const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits);
+const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits,
+                             int slots);
 int mfma_fixed_lds_bytes(int rows_per_wg);
 
 }  // namespace dspark

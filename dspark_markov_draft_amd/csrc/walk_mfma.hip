@@ -44,12 +44,14 @@ constexpr int TILE_ROWS = 16;
 constexpr int NT_REG = 8;                       // W2 tiles per wave held in VGPRs
 constexpr int TILE_LDS_BYTES = 4 * WAVE * 16;   // one tile: 4 K-blocks x 64 lanes x 16 bytes
 constexpr int MAX_RT = MAX_BS / 16;             // 16-request tiles
-constexpr int NT_STAT = MFMA_STATIC_TILE_SLOTS;   // tile slots per wave with STAT
-static_assert(NT_STAT == NT_REG + mfma_static_lds_slots(0), "STAT tile slots");
-static_assert(NT_STAT * WALK_WAVES * TILE_ROWS == MFMA_STATIC_SLOT_ROWS, "STAT slot rows");
-// copy instructions per wave for one request tile with STAT: at most one after each tile slot
+static_assert(MFMA_STATIC_TILE_SLOTS == NT_REG + mfma_static_lds_slots(0, MFMA_STATIC_TILE_SLOTS),
+              "STAT tile slots");
+static_assert(MFMA_STATIC_TILE_SLOTS * WALK_WAVES * TILE_ROWS == MFMA_STATIC_SLOT_ROWS, "STAT slot rows");
+// copy instructions per wave for one request tile with STAT: one after each tile slot, and the
+// rest (a build with fewer slots) after the last
 constexpr int STAT_COPY_SLOTS = MFMA_STATIC_COPY_UNITS / WAVE / WALK_WAVES;
-static_assert(MFMA_STATIC_COPY_UNITS % (WAVE * WALK_WAVES) == 0 && STAT_COPY_SLOTS <= NT_STAT,
+static_assert(MFMA_STATIC_COPY_UNITS % (WAVE * WALK_WAVES) == 0 &&
+                  STAT_COPY_SLOTS <= MFMA_STATIC_TILE_SLOTS && STAT_COPY_SLOTS >= MFMA_STATIC_SMALL_SLOTS,
               "STAT copy slots");
 // the workgroup's best key per request (argmax), or each wave's softmax pair per request
 // (inverse CDF)
@@ -70,18 +72,20 @@ __host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
 // other one or any other LDS data, and reads them while the DMA runs. With dynamic LDS it has
 // to assume that any LDS read may alias the DMA's target, and waits for every DMA in flight
 // before each LDS read, which serialises the next request tile's copy with the current tile's
-// compute.
-template <int SAMPLE, int W1T, int TIMED, int STAT, int OUTL>
+// compute. NT: the tile slots per wave with STAT (MFMA_STATIC_TILE_SLOTS, or
+// MFMA_STATIC_SMALL_SLOTS for slices that need no more).
+template <int SAMPLE, int W1T, int TIMED, int STAT, int OUTL, int NT>
 __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const WalkParams p) {
+    constexpr int NT_STAT = NT;
+    constexpr int LDS_SLOTS = STAT ? mfma_static_lds_slots(SAMPLE, NT) : 0;   // of the NT
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
     // the staging buffers and row scales are padded for the past-the-end tile slots (below)
     __shared__ __align__(16) float stage_a[STAT ? MFMA_STATIC_STAGE_FLOATS : 4];
     __shared__ __align__(16) float stage_b[STAT ? MFMA_STATIC_STAGE_FLOATS : 4];
     // W2 tile slots per wave in registers (the rest of the NT_STAT slots with STAT are in LDS)
-    constexpr int NTR = STAT ? NT_STAT - mfma_static_lds_slots(SAMPLE) : NT_REG;
-    __shared__ __align__(16) unsigned char tiles_s[STAT ? mfma_static_lds_slots(SAMPLE) * WALK_WAVES *
-                                                              TILE_LDS_BYTES : 16];
+    constexpr int NTR = STAT ? NT_STAT - LDS_SLOTS : NT_REG;
+    __shared__ __align__(16) unsigned char tiles_s[LDS_SLOTS ? LDS_SLOTS * WALK_WAVES * TILE_LDS_BYTES : 16];
     __shared__ __align__(16) uint32_t w1q_s[STAT ? W1Q_BYTES / 4 : 4];
     __shared__ __align__(16) uint32_t w1n_s[STAT ? W1N_BYTES / 4 : 4];
     __shared__ __align__(16) float s1_s[STAT ? MAX_BS : 4];
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     }
     // with STAT every LDS slot is written (zero codes past the slice's tiles): the tile loop
     // multiplies all of them
-    for (int tw = NTR; tw < NTR + (STAT ? mfma_static_lds_slots(SAMPLE) : lds_tw); ++tw) {
+    for (int tw = NTR; tw < NTR + (STAT ? LDS_SLOTS : lds_tw); ++tw) {
         const int tl = tw * WALK_WAVES + wave;
         const bool have = tl < ntiles && tw < NTR + lds_tw;
         if (have || STAT) {
@@ -529,7 +533,14 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             }, [&](int tw) {
                 // this wave's share of the next request tile's copy, spread over the slots
                 if constexpr (STAT) {
-                    if (prefetch && tw < STAT_COPY_SLOTS) copy_job(rt + 1, t, nxt, tw * WALK_WAVES + wave);
+                    if (prefetch) {
+                        copy_job(rt + 1, t, nxt, tw * WALK_WAVES + wave);
+                        if (tw == NT_STAT - 1) {
+#pragma unroll
+                            for (int s = NT_STAT; s < STAT_COPY_SLOTS; ++s)
+                                copy_job(rt + 1, t, nxt, s * WALK_WAVES + wave);
+                        }
+                    }
                 }
             }, [&](int h0) {
                 if constexpr (HOLD) {
@@ -650,10 +661,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 
 // OUTL: a greedy kernel with STAT holds its logits for the optional fp32 output (every other
 // kernel writes its outputs as before); one without (OUTL = 0) is used when none is asked for
-template <int STAT, int OUTL>
+template <int STAT, int OUTL, int NT>
 static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
 #define DSPARK_MFMA(S, W, TI) \
-    reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT, (S ? 1 : OUTL)>)
+    reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT, (S ? 1 : OUTL), NT>)
     if (sample == 2) {   // inverse CDF (no instrumented build)
         switch (w1t) {
             case DT_F32: return DSPARK_MFMA(2, DT_F32, 0);
@@ -677,10 +688,15 @@ static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
 #undef DSPARK_MFMA
 }
 
-const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits) {
-    if (!static_stage) return mfma_kernel_for<0, 1>(sample, w1t, timed);
-    return out_logits ? mfma_kernel_for<1, 1>(sample, w1t, timed)
-                      : mfma_kernel_for<1, 0>(sample, w1t, timed);
+const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits,
+                             int slots) {
+    constexpr int F = MFMA_STATIC_TILE_SLOTS, S = MFMA_STATIC_SMALL_SLOTS;
+    if (!static_stage) return mfma_kernel_for<0, 1, F>(sample, w1t, timed);
+    if (slots <= S)
+        return out_logits ? mfma_kernel_for<1, 1, S>(sample, w1t, timed)
+                          : mfma_kernel_for<1, 0, S>(sample, w1t, timed);
+    return out_logits ? mfma_kernel_for<1, 1, F>(sample, w1t, timed)
+                      : mfma_kernel_for<1, 0, F>(sample, w1t, timed);
 }
 
 int mfma_fixed_lds_bytes(int rows_per_wg) { return mfma_fixed_lds(rows_per_wg); }

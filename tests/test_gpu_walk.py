@@ -114,6 +114,10 @@ SMALL = [  # V, T, bs, dtype, grid cap (0 = one workgroup per CU)
                                             # second), W1 gather of four groups with idle ones
     (8192, 2, 40, torch.float16, 0),        # MFMA, static LDS: three request tiles
     (12480, 2, 24, torch.float32, 20),      # MFMA, static LDS: 624-row slices (the largest)
+    (10000, 3, 19, torch.bfloat16, 20),     # MFMA, static LDS, 8-slot build: 512-row slices (its
+                                            # largest, with the sampling kernel's LDS slot), ragged
+    (12000, 3, 1, torch.float16, 24),       # one request, 500-row slices: the 8-slot build
+    (15000, 2, 1, torch.bfloat16, 24),      # one request, 628-row slices: the 10-slot build
     (20000, 3, 1, torch.bfloat16, 20),      # one request, 1000-row slices: LDS tiles (MFMA1)
     (9000, 2, 1, torch.float16, 8),         # one request, 1128-row slices: 8 LDS tiles, ragged
     (30000, 1, 1, torch.bfloat16, 0),       # a single step: the first step is also the last
