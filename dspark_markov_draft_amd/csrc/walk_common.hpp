@@ -45,11 +45,10 @@ constexpr int MFMA_STATIC_SMALL_SLOTS = 8;
 __host__ __device__ constexpr int mfma_static_slots(int tiles_per_wave) {
     return tiles_per_wave <= MFMA_STATIC_SMALL_SLOTS ? MFMA_STATIC_SMALL_SLOTS : MFMA_STATIC_TILE_SLOTS;
 }
-// tile slots per wave held in LDS (the rest in registers) of the build with `slots` slots: 8 in
-// registers, or 7 in the Gumbel sampling kernel, which leaves its Philox sampler the registers
-// it would otherwise take from spills
+// tile slots per wave held in LDS (the rest, 8, in registers) of the build with `slots` slots
+// (the sampling kernels finish their slots in two halves, which leaves them the registers)
 __host__ __device__ constexpr int mfma_static_lds_slots(int sample, int slots) {
-    return slots - (sample == 1 ? 7 : 8);
+    return (void)sample, slots - 8;
 }
 constexpr int MFMA_STATIC_SLOT_ROWS = MFMA_STATIC_TILE_SLOTS * WALK_WAVES * 16;
 constexpr int MFMA_STATIC_COPY_UNITS = (16 * MFMA_STATIC_STRIDE / 4 + WAVE - 1) / WAVE * WAVE;
