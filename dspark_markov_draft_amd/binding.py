@@ -23,6 +23,7 @@ MAX_STEPS, MAX_BS, MAX_V, MAX_TOPK = 16, 64, 270336, 2048
 DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG, DEBUG_STAMPS = 1, 2, 3, 4
 DEBUG_FORCE_PATH = 5
 DEBUG_KERNEL_TIMING = 6
+DEBUG_MFMA_WAVES = 7
 PATH_DOT4, PATH_MFMA, PATH_MFMA1 = 1, 2, 3
 STAMPS_PER_WG = 210
 
@@ -47,7 +48,7 @@ class WalkPlan(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("reg_units", ctypes.c_int32), ("lds_units", ctypes.c_int32),
                 ("total_units", ctypes.c_int32), ("stage_bufs", ctypes.c_int32),
-                ("stage_stride", ctypes.c_int32)]
+                ("stage_stride", ctypes.c_int32), ("waves_per_workgroup", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

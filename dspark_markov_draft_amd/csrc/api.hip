@@ -525,6 +525,10 @@ int dspark_debug_set(int key, int64_t value) {
             k.force_path = (int)value;
             return DSPARK_OK;
         case DSPARK_DEBUG_KERNEL_TIMING: return set_kernel_timing(value);
+        case DSPARK_DEBUG_MFMA_WAVES:
+            if (value != 0 && value != 4 && value != 8) return DSPARK_ERR_INVALID_ARG;
+            k.mfma_waves = (int)value;
+            return DSPARK_OK;
         case DSPARK_DEBUG_STAMPS:
             if (value & 7) return DSPARK_ERR_INVALID_ARG;
             k.stamps = (uintptr_t)value;

@@ -38,6 +38,7 @@ struct DebugKnobs {
     uint32_t wait_unset = 0;
     uintptr_t stamps = 0;
     int force_path = 0;
+    int mfma_waves = 0;
 };
 DebugKnobs& debug_knobs();
 

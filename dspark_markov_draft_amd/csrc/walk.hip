@@ -26,11 +26,15 @@ constexpr int MFMA_TILE_LDS = 4 * WAVE * 16;
 // moves the crossover up by one request, its finish costing more per MFMA tile).
 constexpr int MFMA_MIN_BS_GREEDY = 3;
 constexpr int MFMA_MIN_BS_SAMPLE = 4;
+// Waves per workgroup of the MFMA kernel with static LDS (4 or 8; the test hook
+// DSPARK_DEBUG_MFMA_WAVES forces either); the kernel with dynamic LDS has 4.
+constexpr int MFMA_STATIC_WAVES = 8;
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int path, int sample,
                      dspark_walk_plan* plan) {
+    int waves = WALK_WAVES;
     const int64_t quantum = path == DSPARK_PATH_MFMA ? 16 : 4;   // (MFMA1 handles partial tiles)
     int64_t rpw = (V + cap - 1) / cap;
     if (rpw < WALK_THREADS) rpw = V < WALK_THREADS ? V : WALK_THREADS;
@@ -72,30 +76,33 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
         const int64_t want = bs > 16 ? 2 : 1;
         const bool stat = rpw <= MFMA_STATIC_ROWS && stage_stride <= MFMA_STATIC_STRIDE;
         const int64_t dyn_max = (int64_t)dev.max_lds - MFMA_DYN_STATIC_RESERVE;   // without STAT
+        const int forced = debug_knobs().mfma_waves;
+        if (stat) waves = forced ? forced : MFMA_STATIC_WAVES;
         const int64_t tiles = rpw / 16;
-        units = (tiles + WALK_WAVES - 1) / WALK_WAVES;              // tile slots per wave
-        const int slots = mfma_static_slots((int)units);            // of the static build
+        units = (tiles + waves - 1) / waves;                        // tile slots per wave
+        const int slots = mfma_static_slots((int)units, waves);     // of the static build
         if (stat) {
             // all LDS is static and of fixed size (both staging buffers exist for any batch)
             stage_bufs = want;
-            if (mfma_static_lds_bytes(sample, slots) > (int64_t)dev.max_lds) return DSPARK_ERR_UNSUPPORTED;
+            if (mfma_static_lds_bytes(sample, slots, waves) > (int64_t)dev.max_lds)
+                return DSPARK_ERR_UNSUPPORTED;
         } else {
             stage_bufs = (dyn_max - fixed) / buf_bytes;
             if (stage_bufs > want) stage_bufs = want;
             if (stage_bufs < 1) return DSPARK_ERR_UNSUPPORTED;    // the caller falls back
         }
         const int64_t stage_lds = stage_bufs * buf_bytes;
-        const int64_t reg_tiles = stat ? slots - mfma_static_lds_slots(sample, slots) : MFMA_REG_TILES;
+        const int64_t reg_tiles = stat ? slots - mfma_static_lds_slots(slots, waves) : MFMA_REG_TILES;
         reg_units = units < reg_tiles ? units : reg_tiles;
-        int64_t room = stat ? mfma_static_lds_slots(sample, slots)
+        int64_t room = stat ? mfma_static_lds_slots(slots, waves)
                             : (dyn_max - fixed - stage_lds) / (WALK_WAVES * MFMA_TILE_LDS);
         if (room < 0) room = 0;
         lds_units = units - reg_units;
         if (lds_units > room) lds_units = room;
-        reg_rows = rpw < reg_units * WALK_WAVES * 16 ? rpw : reg_units * WALK_WAVES * 16;
+        reg_rows = rpw < reg_units * waves * 16 ? rpw : reg_units * waves * 16;
         lds_rows = rpw - reg_rows;
-        if (lds_rows > lds_units * WALK_WAVES * 16) lds_rows = lds_units * WALK_WAVES * 16;
-        lds_bytes = stat ? mfma_static_lds_bytes(sample, slots)
+        if (lds_rows > lds_units * waves * 16) lds_rows = lds_units * waves * 16;
+        lds_bytes = stat ? mfma_static_lds_bytes(sample, slots, waves)
                          : lds_units * WALK_WAVES * MFMA_TILE_LDS + fixed + stage_lds;
         if (!stat && lds_bytes > dyn_max) return DSPARK_ERR_UNSUPPORTED;
     }
@@ -125,6 +132,7 @@ static int plan_path(const DeviceInfo& dev, int cap, int64_t bs, int64_t V, int 
     plan->total_units = (int32_t)units;
     plan->stage_bufs = (int32_t)stage_bufs;
     plan->stage_stride = (int32_t)stage_stride;
+    plan->waves_per_workgroup = waves;
     return DSPARK_OK;
 }
 
@@ -213,7 +221,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     const void* fn = plan.path == DSPARK_PATH_MFMA
                          ? mfma_walk_kernel(a.sample, w1t, timed, static_stage,
                                             a.out_logits != nullptr,
-                                            mfma_static_slots(plan.total_units))
+                                            mfma_static_slots(plan.total_units, plan.waves_per_workgroup),
+                                            plan.waves_per_workgroup)
                      : plan.path == DSPARK_PATH_MFMA1
                          ? mfma1_walk_kernel(a.sample, w1t, timed, plan.lds_units > 0,
                                              mfma1_reg_slots(plan.total_units))
@@ -223,7 +232,8 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
         (void)hipGetLastError();
     }
     void* args[] = {&p};
-    const hipError_t e = launch_walk_kernel(fn, dim3(plan.num_workgroups), dim3(WALK_THREADS),
+    const int threads = plan.path == DSPARK_PATH_MFMA ? plan.waves_per_workgroup * WAVE : WALK_THREADS;
+    const hipError_t e = launch_walk_kernel(fn, dim3(plan.num_workgroups), dim3(threads),
                                             args, (size_t)dyn_lds, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();

@@ -33,24 +33,32 @@ constexpr int MFMA1_MAX_ROWS = (MFMA1_TILES + MFMA1_LDS_TILES) * WALK_WAVES * 16
 // MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
 // two staging buffers for 16 rows of at most MFMA_STATIC_STRIDE floats (157 odd 16-byte units),
 // up to mfma_static_lds_slots() LDS tiles per wave, W1 codes and scales, row scales, lane keys,
-// tokens. Every wave has MFMA_STATIC_TILE_SLOTS tile slots (registers first, then LDS), covering
-// MFMA_STATIC_SLOT_ROWS rows; the row-scale array and the staging buffers are sized for reads of
-// all of them. A staging buffer also holds whole 64-lane copy instructions (64 units each).
-// Slices of at most MFMA_STATIC_SMALL_SLOTS tiles per wave run a build with that many slots:
-// every slot is multiplied and finished, with no branch per tile.
+// tokens. Its workgroup has 4 waves (one per SIMD) or 8 (two per SIMD, half the registers
+// each). Every wave has mfma_static_slots() tile slots (registers first, then LDS), at most
+// MFMA_STATIC_SLOT_ROWS rows per workgroup; the row-scale array and the staging buffers are
+// sized for reads of all of them. A staging buffer also holds whole 64-lane copy instructions
+// (64 units each). The kernel multiplies and finishes every slot it has, with no branch per
+// tile, so a slice that needs fewer slots runs a build with fewer.
 constexpr int MFMA_STATIC_ROWS = 624;
 constexpr int MFMA_STATIC_STRIDE = 628;
-constexpr int MFMA_STATIC_TILE_SLOTS = 10;
-constexpr int MFMA_STATIC_SMALL_SLOTS = 8;
-__host__ __device__ constexpr int mfma_static_slots(int tiles_per_wave) {
-    return tiles_per_wave <= MFMA_STATIC_SMALL_SLOTS ? MFMA_STATIC_SMALL_SLOTS : MFMA_STATIC_TILE_SLOTS;
+constexpr int MFMA_STATIC_SLOT_ROWS = 640;
+// tile slots per wave of the builds with `waves` waves: the most a wave has (MFMA_STATIC_SLOT_ROWS
+// rows), or, for slices of at most 512 rows, the fewer that hold them
+__host__ __device__ constexpr int mfma_static_max_slots(int waves) {
+    return MFMA_STATIC_SLOT_ROWS / (16 * waves);
 }
-// tile slots per wave held in LDS (the rest, 8, in registers) of the build with `slots` slots
-// (the sampling kernels finish their slots in two halves, which leaves them the registers)
-__host__ __device__ constexpr int mfma_static_lds_slots(int sample, int slots) {
-    return (void)sample, slots - 8;
+__host__ __device__ constexpr int mfma_static_small_slots(int waves) { return 512 / (16 * waves); }
+__host__ __device__ constexpr int mfma_static_slots(int tiles_per_wave, int waves) {
+    return tiles_per_wave <= mfma_static_small_slots(waves) ? mfma_static_small_slots(waves)
+                                                            : mfma_static_max_slots(waves);
 }
-constexpr int MFMA_STATIC_SLOT_ROWS = MFMA_STATIC_TILE_SLOTS * WALK_WAVES * 16;
+// tile slots per wave held in registers: 8 with 4 waves, 5 with 8 (the sampling kernels finish
+// their slots in two halves, which leaves them the registers); the rest of a build's slots are
+// in LDS
+__host__ __device__ constexpr int mfma_static_reg_slots(int waves) { return waves == 4 ? 8 : 4; }
+__host__ __device__ constexpr int mfma_static_lds_slots(int slots, int waves) {
+    return slots > mfma_static_reg_slots(waves) ? slots - mfma_static_reg_slots(waves) : 0;
+}
 constexpr int MFMA_STATIC_COPY_UNITS = (16 * MFMA_STATIC_STRIDE / 4 + WAVE - 1) / WAVE * WAVE;
 constexpr int MFMA_STATIC_STAGE_FLOATS =
     MFMA_STATIC_COPY_UNITS * 4 > 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS
@@ -58,22 +66,20 @@ constexpr int MFMA_STATIC_STAGE_FLOATS =
         : 15 * MFMA_STATIC_STRIDE + MFMA_STATIC_SLOT_ROWS;
 // per-request sampling constants, loaded once per call: seed, position offset, 1 / temperature
 constexpr int MFMA_REQ_CONST_BYTES = MAX_BS * (8 + 8 + 4);
-__host__ __device__ constexpr int mfma_static_lds_bytes(int sample, int slots) {
-    return 2 * MFMA_STATIC_STAGE_FLOATS * 4 + mfma_static_lds_slots(sample, slots) * WALK_WAVES * 4 * WAVE * 16 +
+__host__ __device__ constexpr int mfma_static_lds_bytes(int sample, int slots, int waves) {
+    return 2 * MFMA_STATIC_STAGE_FLOATS * 4 + mfma_static_lds_slots(slots, waves) * waves * 4 * WAVE * 16 +
            W1Q_BYTES + W1N_BYTES + MAX_BS * 4 + MFMA_STATIC_SLOT_ROWS * 4 +
-           (sample == 2 ? WALK_WAVES : 1) * MAX_BS * 8 + MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
+           (sample == 2 ? waves : 1) * MAX_BS * 8 + MAX_BS * 4 + MFMA_REQ_CONST_BYTES;
 }
-static_assert(mfma_static_lds_bytes(0, MFMA_STATIC_TILE_SLOTS) <= 160 * 1024 &&
-                  mfma_static_lds_bytes(1, MFMA_STATIC_TILE_SLOTS) <= 160 * 1024 &&
-                  mfma_static_lds_bytes(2, MFMA_STATIC_TILE_SLOTS) <= 160 * 1024,
+static_assert(mfma_static_lds_bytes(0, 10, 4) <= 160 * 1024 && mfma_static_lds_bytes(1, 10, 4) <= 160 * 1024 &&
+                  mfma_static_lds_bytes(2, 10, 4) <= 160 * 1024 && mfma_static_lds_bytes(2, 5, 8) <= 160 * 1024,
               "static LDS fits a CU");
-// more than half a CU's LDS, so that one workgroup runs per CU with the small build too
-static_assert(mfma_static_lds_bytes(0, MFMA_STATIC_SMALL_SLOTS) > 80 * 1024 &&
-                  mfma_static_lds_bytes(2, MFMA_STATIC_SMALL_SLOTS) > 80 * 1024,
+// more than half a CU's LDS, so that one workgroup runs per CU with every build
+static_assert(mfma_static_lds_bytes(0, 8, 4) > 80 * 1024 && mfma_static_lds_bytes(0, 4, 8) > 80 * 1024,
               "one workgroup per CU");
-static_assert(mfma_static_lds_slots(1, MFMA_STATIC_SMALL_SLOTS) >= 0 &&
-                  mfma_static_lds_slots(0, MFMA_STATIC_SMALL_SLOTS) >= 0,
-              "register slots");
+static_assert(mfma_static_max_slots(4) == 10 && mfma_static_small_slots(4) == 8 &&
+                  mfma_static_max_slots(8) == 5 && mfma_static_small_slots(8) == 4,
+              "slot builds");
 // The kernel with dynamic LDS has small static arrays too (the request constants and the
 // unused forms of the static buffers): its dynamic LDS leaves this much of the CU's LDS free.
 constexpr int MFMA_DYN_STATIC_RESERVE = 2048;
@@ -266,13 +272,14 @@ constexpr int LOW_NIBBLES = 2;
 // after_issue() runs once the wave's loads are issued and before their values are used: loads
 // it issues complete after the W1 rows (vector memory returns in issue order) without delaying
 // them.
-constexpr int GATHER_ITERS = MAX_BS / (WALK_WAVES * 4);   // 4 request groups per wave at bs 64
+// NW: the workgroup's waves (4, or 8 in the nibble form); iterations take 4 NW requests each
 
-template <int W1T, int LOW, int MAX_NIT = 2, typename AfterIssue>
+template <int W1T, int LOW, int MAX_NIT = 2, int NW = WALK_WAVES, typename AfterIssue>
 __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32_t* tok,
                                                 uint32_t* w1q, uint32_t* w1l, float* s1, int wave,
                                                 int lane, AfterIssue&& after_issue) {
-    if (LOW == LOW_BYTES && p.bs <= WALK_WAVES) {
+    static_assert(NW == WALK_WAVES || (NW == 8 && LOW == LOW_NIBBLES), "gather waves");
+    if (LOW == LOW_BYTES && p.bs <= NW) {
         // at most one request per wave: all 64 lanes on one row (elements 4l .. 4l+3)
         const int b = wave;
         float4 w = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -303,7 +310,7 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
         for (int ii = 0; ii < NIT; ++ii) {
             const int i = NIT - 1 - ii;
             const int it = it0 + i;
-            const int b = (it * WALK_WAVES + wave) * 4 + q;
+            const int b = (it * NW + wave) * 4 + q;
             const int64_t e = (int64_t)tok[b < p.bs ? b : 0] * RANK + ql * 16;
 #pragma unroll
             for (int k = 0; k < 4; ++k) raw[i][k] = load4_raw<W1T>(p.w1, e + 4 * k);
@@ -322,7 +329,7 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
             const int it = it0 + i;
-            const int b = (it * WALK_WAVES + wave) * 4 + q;
+            const int b = (it * NW + wave) * 4 + q;
             float a = 0.0f;
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -346,9 +353,18 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
             }
         }
     };
+    static_assert(MAX_NIT == 1 || MAX_NIT == 2 || MAX_NIT == 4, "gather passes");
+    if constexpr (NW == 8) {
+        // 32 requests per iteration: one, or two in one pass
+        if (p.bs <= 32 || MAX_NIT == 1) {
+            gather(std::integral_constant<int, 1>{}, 0, true);
+            if (p.bs > 32) gather(std::integral_constant<int, 1>{}, 1, false);
+        } else {
+            gather(std::integral_constant<int, 2>{}, 0, true);
+        }
+        return;
+    }
     // iterations with a request for some wave: 16 requests per iteration
-    static_assert(GATHER_ITERS == 4 && (MAX_NIT == 1 || MAX_NIT == 2 || MAX_NIT == 4),
-                  "gather passes");
     if (p.bs <= 16) {
         gather(std::integral_constant<int, 1>{}, 0, true);
     } else if constexpr (MAX_NIT == 4) {
@@ -948,7 +964,7 @@ __device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, ui
 const void* dot4_walk_kernel(int sample, int w1t, bool timed);
 const void* mfma1_walk_kernel(int sample, int w1t, bool timed, bool lds_tiles, int reg_slots);
 const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits,
-                             int slots);
+                             int slots, int waves);
 int mfma_fixed_lds_bytes(int rows_per_wg);
 
 }  // namespace dspark

@@ -44,21 +44,22 @@ constexpr int TILE_ROWS = 16;
 constexpr int NT_REG = 8;                       // W2 tiles per wave held in VGPRs
 constexpr int TILE_LDS_BYTES = 4 * WAVE * 16;   // one tile: 4 K-blocks x 64 lanes x 16 bytes
 constexpr int MAX_RT = MAX_BS / 16;             // 16-request tiles
-static_assert(MFMA_STATIC_TILE_SLOTS == NT_REG + mfma_static_lds_slots(0, MFMA_STATIC_TILE_SLOTS),
+static_assert(mfma_static_max_slots(4) == NT_REG + mfma_static_lds_slots(mfma_static_max_slots(4), 4),
               "STAT tile slots");
-static_assert(MFMA_STATIC_TILE_SLOTS * WALK_WAVES * TILE_ROWS == MFMA_STATIC_SLOT_ROWS, "STAT slot rows");
 // copy instructions per wave for one request tile with STAT: one after each tile slot, and the
 // rest (a build with fewer slots) after the last
-constexpr int STAT_COPY_SLOTS = MFMA_STATIC_COPY_UNITS / WAVE / WALK_WAVES;
-static_assert(MFMA_STATIC_COPY_UNITS % (WAVE * WALK_WAVES) == 0 &&
-                  STAT_COPY_SLOTS <= MFMA_STATIC_TILE_SLOTS && STAT_COPY_SLOTS >= MFMA_STATIC_SMALL_SLOTS,
+__host__ __device__ constexpr int stat_copy_slots(int waves) {
+    return MFMA_STATIC_COPY_UNITS / WAVE / waves;
+}
+static_assert(MFMA_STATIC_COPY_UNITS % (WAVE * 8) == 0 && stat_copy_slots(4) == mfma_static_max_slots(4) &&
+                  stat_copy_slots(8) == mfma_static_max_slots(8),
               "STAT copy slots");
 // the workgroup's best key per request (argmax), or each wave's softmax pair per request
 // (inverse CDF)
-__host__ __device__ constexpr int lkey_bytes(int sample) {
-    return (sample == 2 ? WALK_WAVES : 1) * MAX_BS * 8;
+__host__ __device__ constexpr int lkey_bytes(int sample, int waves) {
+    return (sample == 2 ? waves : 1) * MAX_BS * 8;
 }
-constexpr int LKEY_BYTES = lkey_bytes(2);   // the dynamic layout reserves the larger
+constexpr int LKEY_BYTES = lkey_bytes(2, WALK_WAVES);   // the dynamic layout reserves the larger
 
 // dynamic LDS besides the W2 tiles: W1 digits, their steps, row scales, wave keys, tokens
 __host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
@@ -72,12 +73,16 @@ __host__ __device__ constexpr int mfma_fixed_lds(int rows_per_wg) {
 // other one or any other LDS data, and reads them while the DMA runs. With dynamic LDS it has
 // to assume that any LDS read may alias the DMA's target, and waits for every DMA in flight
 // before each LDS read, which serialises the next request tile's copy with the current tile's
-// compute. NT: the tile slots per wave with STAT (MFMA_STATIC_TILE_SLOTS, or
-// MFMA_STATIC_SMALL_SLOTS for slices that need no more).
-template <int SAMPLE, int W1T, int TIMED, int STAT, int OUTL, int NT>
-__global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const WalkParams p) {
+// compute. NT: the tile slots per wave with STAT (mfma_static_slots()). NW: the waves, 4 (one
+// per SIMD), or 8 with STAT (two per SIMD, half the registers each: while one waits, for its
+// memory or in the issue of a copy, the other computes).
+template <int SAMPLE, int W1T, int TIMED, int STAT, int OUTL, int NT, int NW>
+__global__ __launch_bounds__(NW * WAVE, 1) void dense_walk_mfma_kernel(const WalkParams p) {
+    static_assert(NW == 4 || (NW == 8 && STAT), "waves");
+    constexpr int NTHREADS = NW * WAVE;
     constexpr int NT_STAT = NT;
-    constexpr int LDS_SLOTS = STAT ? mfma_static_lds_slots(SAMPLE, NT) : 0;   // of the NT
+    constexpr int LDS_SLOTS = STAT ? mfma_static_lds_slots(NT, NW) : 0;   // of the NT
+    constexpr int STAT_COPY_SLOTS = stat_copy_slots(NW);
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
     // the staging buffers and row scales are padded for the past-the-end tile slots (below)
@@ -85,12 +90,12 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     __shared__ __align__(16) float stage_b[STAT ? MFMA_STATIC_STAGE_FLOATS : 4];
     // W2 tile slots per wave in registers (the rest of the NT_STAT slots with STAT are in LDS)
     constexpr int NTR = STAT ? NT_STAT - LDS_SLOTS : NT_REG;
-    __shared__ __align__(16) unsigned char tiles_s[LDS_SLOTS ? LDS_SLOTS * WALK_WAVES * TILE_LDS_BYTES : 16];
+    __shared__ __align__(16) unsigned char tiles_s[LDS_SLOTS ? LDS_SLOTS * NW * TILE_LDS_BYTES : 16];
     __shared__ __align__(16) uint32_t w1q_s[STAT ? W1Q_BYTES / 4 : 4];
     __shared__ __align__(16) uint32_t w1n_s[STAT ? W1N_BYTES / 4 : 4];
     __shared__ __align__(16) float s1_s[STAT ? MAX_BS : 4];
     __shared__ __align__(16) float scl_s[STAT ? MFMA_STATIC_SLOT_ROWS : 4];
-    __shared__ __align__(16) uint64_t lkeys_s[STAT ? lkey_bytes(SAMPLE) / 8 : 2];
+    __shared__ __align__(16) uint64_t lkeys_s[STAT ? lkey_bytes(SAMPLE, NW) / 8 : 2];
     __shared__ __align__(16) int32_t tok_s[STAT ? MAX_BS : 4];
     __shared__ __align__(16) uint64_t rq_seed[SAMPLE == 1 ? MAX_BS : 2];
     __shared__ __align__(16) uint64_t rq_pos[SAMPLE == 1 ? MAX_BS : 2];
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     // dynamic layout (without STAT): LDS tiles, staging buffers, W1 high digits, low digits,
     // their steps, row scales, wave keys, tokens
     unsigned char* const d_tiles = smem;
-    float* const d_stage = reinterpret_cast<float*>(smem + (size_t)lds_tw * WALK_WAVES * TILE_LDS_BYTES);
+    float* const d_stage = reinterpret_cast<float*>(smem + (size_t)lds_tw * NW * TILE_LDS_BYTES);
     const int ss = p.stage_stride;
     const int nbuf = p.stage_bufs;   // 1 or 2 (the host guarantees at least one)
     uint32_t* const d_w1q = reinterpret_cast<uint32_t*>(d_stage + (size_t)p.stage_bufs * 16 * ss);
@@ -137,24 +142,24 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     v4i qa[NTR][4];
 #pragma unroll
     for (int tw = 0; tw < NTR; ++tw) {
-        const int tl = tw * WALK_WAVES + wave;
+        const int tl = tw * NW + wave;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qa[tw][kb] = tl < ntiles ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
     }
     // with STAT every LDS slot is written (zero codes past the slice's tiles): the tile loop
     // multiplies all of them
     for (int tw = NTR; tw < NTR + (STAT ? LDS_SLOTS : lds_tw); ++tw) {
-        const int tl = tw * WALK_WAVES + wave;
+        const int tl = tw * NW + wave;
         const bool have = tl < ntiles && tw < NTR + lds_tw;
         if (have || STAT) {
             v4i* dst = reinterpret_cast<v4i*>(
-                lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) * TILE_LDS_BYTES);
+                lds_tiles + (size_t)((tw - NTR) * NW + wave) * TILE_LDS_BYTES);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 dst[kb * WAVE + lane] = have ? load_a(tl, kb) : (v4i){0, 0, 0, 0};
         }
     }
-    for (int i = tid; i < (STAT ? MFMA_STATIC_SLOT_ROWS : ntiles * TILE_ROWS); i += WALK_THREADS)
+    for (int i = tid; i < (STAT ? MFMA_STATIC_SLOT_ROWS : ntiles * TILE_ROWS); i += NTHREADS)
         scl[i] = i < nrows ? p.scale[row0 + i] : 0.0f;
     load_start_tokens(p, tok);
     if (tid < MAX_BS) lkeys[tid] = 0;   // the per-request key words start empty
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     const int units = nrows / 4;
     // STAT: the copy of a request tile is one flat list of full instructions over the buffer's
     // 16-byte units. Unit L is unit L % upr of row L / upr (upr: units per padded row), and
-    // instruction j (units 64j .. 64j+63) belongs to wave j % 4, so each wave has at most
+    // instruction j (units 64j .. 64j+63) belongs to wave j % NW, so each wave has at most
     // STAT_COPY_SLOTS of them and can issue them one at a time between its tile slots: a wave
     // that issues many copies back to back while HBM is busy stalls in the issue itself. Pad
     // units, and units past the tile's last valid request (last instruction only), copy an
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     };
     auto stage_base = [&](int rt, int t, float* dst_buf) {
         if constexpr (STAT) {
-            for (int s = 0; s < STAT_COPY_SLOTS; ++s) copy_job(rt, t, dst_buf, s * WALK_WAVES + wave);
+            for (int s = 0; s < STAT_COPY_SLOTS; ++s) copy_job(rt, t, dst_buf, s * NW + wave);
             return;
         }
         for (int r = 0; r < 16; ++r) {
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             if (b >= p.bs) break;
             const float* src = p.base + ((int64_t)b * p.T + t) * p.V + row0;
             float* dst = dst_buf + (size_t)r * ss;
-            for (int u0 = wave * WAVE; u0 < units; u0 += WALK_THREADS) {
+            for (int u0 = wave * WAVE; u0 < units; u0 += NTHREADS) {
                 if (u0 + lane < units)
                     __builtin_amdgcn_global_load_lds((global_void_ptr)(src + 4 * (u0 + lane)),
                                                      (lds_void_ptr)(dst + 4 * u0), 16, 0, 0);
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     auto stage_base_w123 = [&](int rt, int t, float* dst_buf) {
         if (wave == 0) return;
         if constexpr (STAT) {
-            for (int j = wave - 1; j < STAT_COPY_SLOTS * WALK_WAVES; j += WALK_WAVES - 1)
+            for (int j = wave - 1; j < STAT_COPY_SLOTS * NW; j += NW - 1)
                 copy_job(rt, t, dst_buf, j);
             return;
         }
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
             if (b >= p.bs) break;
             const float* src = p.base + ((int64_t)b * p.T + t) * p.V + row0;
             float* dst = dst_buf + (size_t)r * ss;
-            for (int u0 = (wave - 1) * WAVE; u0 < units; u0 += WALK_THREADS - WAVE) {
+            for (int u0 = (wave - 1) * WAVE; u0 < units; u0 += NTHREADS - WAVE) {
                 if (u0 + lane < units)
                     __builtin_amdgcn_global_load_lds((global_void_ptr)(src + 4 * (u0 + lane)),
                                                      (lds_void_ptr)(dst + 4 * u0), 16, 0, 0);
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
     };
 
     for (int t = 0; t < p.T; ++t) {
-        gather_w1_codes<W1T, LOW_NIBBLES, STAT ? 4 : 2>(p, tok, w1q, w1n, s1, wave, lane, [] {});
+        gather_w1_codes<W1T, LOW_NIBBLES, STAT ? 4 : 2, NW>(p, tok, w1q, w1n, s1, wave, lane, [] {});
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                     auto a_op = [&](int tw, int kb) -> v4i {
                         if (tw < NTR) return qa[tw][kb];
                         return reinterpret_cast<const v4i*>(
-                            lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) *
+                            lds_tiles + (size_t)((tw - NTR) * NW + wave) *
                                             TILE_LDS_BYTES)[kb * WAVE + lane];
                     };
                     // The sampling kernel takes the slots in two halves (half the accumulators
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                         for (int i = 0; i < n; ++i) {
                             const int tw = h0 + i;
                             if (tw < NT_STAT) {
-                                fin(accs[i], row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4, tw);
+                                fin(accs[i], row0 + (tw * NW + wave) * TILE_ROWS + g * 4, tw);
                                 if (first) after(tw);
                             }
                         }
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 #pragma unroll
                 for (int tw = 0; tw < NTR; ++tw) {
                     accs[tw] = (v4i){0, 0, 0, 0};
-                    if (tw * WALK_WAVES + wave < ntiles) {
+                    if (tw * NW + wave < ntiles) {
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb)
                             accs[tw] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[tw][kb], bop[kb],
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 }
 #pragma unroll
                 for (int tw = 0; tw < NTR; ++tw) {
-                    if (tw * WALK_WAVES + wave < ntiles) {
+                    if (tw * NW + wave < ntiles) {
                         accs[tw] = accs[tw] << 4;
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb)
@@ -458,17 +463,17 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 }
 #pragma unroll
                 for (int tw = 0; tw < NTR; ++tw) {
-                    const int tl = tw * WALK_WAVES + wave;
+                    const int tl = tw * NW + wave;
                     if (tl < ntiles) fin(accs[tw], row0 + tl * TILE_ROWS + g * 4, tw);
                 }
                 for (int tw = NTR; tw < ntw; ++tw) {
-                    const int tl = tw * WALK_WAVES + wave;
+                    const int tl = tw * NW + wave;
                     if (tl < ntiles) {
                         // the tile's A operands read once (from LDS or memory) for both digits
                         v4i a4[4];
                         if (tw < NTR + lds_tw) {
                             const v4i* src = reinterpret_cast<const v4i*>(
-                                lds_tiles + (size_t)((tw - NTR) * WALK_WAVES + wave) * TILE_LDS_BYTES);
+                                lds_tiles + (size_t)((tw - NTR) * NW + wave) * TILE_LDS_BYTES);
 #pragma unroll
                             for (int kb = 0; kb < 4; ++kb) a4[kb] = src[kb * WAVE + lane];
                         } else {
@@ -534,11 +539,11 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 // this wave's share of the next request tile's copy, spread over the slots
                 if constexpr (STAT) {
                     if (prefetch) {
-                        copy_job(rt + 1, t, nxt, tw * WALK_WAVES + wave);
+                        copy_job(rt + 1, t, nxt, tw * NW + wave);
                         if (tw == NT_STAT - 1) {
 #pragma unroll
                             for (int s = NT_STAT; s < STAT_COPY_SLOTS; ++s)
-                                copy_job(rt + 1, t, nxt, s * WALK_WAVES + wave);
+                                copy_job(rt + 1, t, nxt, s * NW + wave);
                         }
                     }
                 }
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 #pragma unroll
                         for (int i = 0; i < HALF_SLOTS; ++i) {
                             const int tw = h0 + i;
-                            const int vt = row0 + (tw * WALK_WAVES + wave) * TILE_ROWS + g * 4;
+                            const int vt = row0 + (tw * NW + wave) * TILE_ROWS + g * 4;
                             if (tw < NT_STAT) store4(vt, vb && vt < vend, held[i]);
                         }
                     }
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 best = 0;
 #pragma unroll 1
                 for (int tw = 0; tw < ntw; ++tw) {
-                    const int tl = tw * WALK_WAVES + wave;
+                    const int tl = tw * NW + wave;
                     if (tl >= ntiles) break;
                     v4i acc = {0, 0, 0, 0};
 #pragma unroll
@@ -638,7 +643,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
                 // request `lane`'s pair over the whole slice: the four waves' merged
                 RunningSoftmax a;
 #pragma unroll
-                for (int w = 0; w < WALK_WAVES; ++w) {
+                for (int w = 0; w < NW; ++w) {
                     const uint64_t o = lkeys[w * MAX_BS + lane];
                     a.merge(packed_m(o), packed_s(o));
                 }
@@ -661,10 +666,10 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma_kernel(const 
 
 // OUTL: a greedy kernel with STAT holds its logits for the optional fp32 output (every other
 // kernel writes its outputs as before); one without (OUTL = 0) is used when none is asked for
-template <int STAT, int OUTL, int NT>
+template <int STAT, int OUTL, int NT, int NW>
 static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
 #define DSPARK_MFMA(S, W, TI) \
-    reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT, (S ? 1 : OUTL), NT>)
+    reinterpret_cast<const void*>(&dense_walk_mfma_kernel<S, W, TI, STAT, (S ? 1 : OUTL), NT, NW>)
     if (sample == 2) {   // inverse CDF (no instrumented build)
         switch (w1t) {
             case DT_F32: return DSPARK_MFMA(2, DT_F32, 0);
@@ -688,15 +693,21 @@ static const void* mfma_kernel_for(int sample, int w1t, bool timed) {
 #undef DSPARK_MFMA
 }
 
-const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits,
-                             int slots) {
-    constexpr int F = MFMA_STATIC_TILE_SLOTS, S = MFMA_STATIC_SMALL_SLOTS;
-    if (!static_stage) return mfma_kernel_for<0, 1, F>(sample, w1t, timed);
+template <int NW>
+static const void* mfma_static_kernel(int sample, int w1t, bool timed, bool out_logits, int slots) {
+    constexpr int F = mfma_static_max_slots(NW), S = mfma_static_small_slots(NW);
     if (slots <= S)
-        return out_logits ? mfma_kernel_for<1, 1, S>(sample, w1t, timed)
-                          : mfma_kernel_for<1, 0, S>(sample, w1t, timed);
-    return out_logits ? mfma_kernel_for<1, 1, F>(sample, w1t, timed)
-                      : mfma_kernel_for<1, 0, F>(sample, w1t, timed);
+        return out_logits ? mfma_kernel_for<1, 1, S, NW>(sample, w1t, timed)
+                          : mfma_kernel_for<1, 0, S, NW>(sample, w1t, timed);
+    return out_logits ? mfma_kernel_for<1, 1, F, NW>(sample, w1t, timed)
+                      : mfma_kernel_for<1, 0, F, NW>(sample, w1t, timed);
+}
+
+const void* mfma_walk_kernel(int sample, int w1t, bool timed, bool static_stage, bool out_logits,
+                             int slots, int waves) {
+    if (!static_stage) return mfma_kernel_for<0, 1, 10, WALK_WAVES>(sample, w1t, timed);
+    return waves == 8 ? mfma_static_kernel<8>(sample, w1t, timed, out_logits, slots)
+                      : mfma_static_kernel<WALK_WAVES>(sample, w1t, timed, out_logits, slots);
 }
 
 int mfma_fixed_lds_bytes(int rows_per_wg) { return mfma_fixed_lds(rows_per_wg); }

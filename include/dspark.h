@@ -104,6 +104,7 @@ typedef struct dspark_walk_plan {
     int32_t total_units;         /* all row sets / tiles per wave (the rest are streamed) */
     int32_t stage_bufs;          /* MFMA: LDS buffers staging a 16-request tile's base logits */
     int32_t stage_stride;        /* MFMA: floats per request row in such a buffer */
+    int32_t waves_per_workgroup; /* 4 (one per SIMD), or 8 for the MFMA kernel with static LDS */
 } dspark_walk_plan;
 
 /* Which kernel runs a dense walk: a few requests are GEMVs, more make every step a GEMM (int8
@@ -337,7 +338,9 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *   DSPARK_DEBUG_KERNEL_TIMING: n in 1..4096 launches every later walk and verification kernel
  *       on the current device with hipExtLaunchKernel and one of a ring of n HIP event pairs,
  *       which the dispatch records at the kernel's start and end (read them with
- *       dspark_kernel_times); 0 frees the ring. For benchmarks; not around graph capture.
+ *       dspark_kernel_times); 0 frees the ring. For benchmarks; not around graph capture;
+ *   DSPARK_DEBUG_MFMA_WAVES: 0 = the library's choice; 4 or 8 forces the waves per workgroup of
+ *       the multi-request MFMA kernel for slices of at most 624 rows (the same results).
  */
 enum dspark_debug_key {
     DSPARK_DEBUG_MAX_WORKGROUPS = 1,
@@ -345,7 +348,8 @@ enum dspark_debug_key {
     DSPARK_DEBUG_WAIT_UNSET_FLAG = 3,
     DSPARK_DEBUG_STAMPS = 4,
     DSPARK_DEBUG_FORCE_PATH = 5,
-    DSPARK_DEBUG_KERNEL_TIMING = 6
+    DSPARK_DEBUG_KERNEL_TIMING = 6,
+    DSPARK_DEBUG_MFMA_WAVES = 7
 };
 int dspark_debug_set(int key, int64_t value);
 

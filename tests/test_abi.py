@@ -93,15 +93,38 @@ def test_plan_partition(bs, cus, V):
         assert p["rows_in_registers"] <= 3 * 256 and p["rows_in_lds"] <= 512
         assert p["total_units"] == -(-rpw // 256)
     else:
-        assert p["rows_in_registers"] <= 512         # 8 tiles x 16 rows x 4 waves
-        assert p["total_units"] == -(-(rpw // 16) // 4)
+        # 4 waves, or 8 (5 register tiles each) for slices with static LDS
+        w = p["waves_per_workgroup"]
+        stat = rpw <= 624 and p["stage_stride"] <= 628
+        assert w == 4 or (w == 8 and stat)
+        assert p["rows_in_registers"] <= (8 if w == 4 else 5) * 16 * w
+        assert p["total_units"] == -(-(rpw // 16) // w)
         assert p["stage_bufs"] == (2 if bs > 16 else 1) or p["stage_bufs"] >= 1
         assert p["stage_stride"] >= rpw and (p["stage_stride"] // 4) % 2 == 1
+    if not mfma:
+        assert p["waves_per_workgroup"] == 4
     assert p["reg_units"] + p["lds_units"] <= p["total_units"]
     assert 96 * 1024 <= p["lds_bytes"] <= 163840
     if V >= 256 * cus:
         # big vocabularies: the smallest multiple of the quantum that covers V with every CU
         assert (rpw - quantum) * cus < V <= rpw * cus
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+def test_plan_mfma_waves_hook(waves):
+    """The test hook forces the waves per workgroup of the static-LDS MFMA kernel; the tiles per
+    wave follow, and the kernel with dynamic LDS keeps 4."""
+    try:
+        assert B.lib().dspark_debug_set(B.DEBUG_MFMA_WAVES, waves) == 0
+        p = B.dspark_walk_plan_for(256, 163840, 64, 7, 151936)   # 608-row slices: static
+        assert p["path"] == B.PATH_MFMA and p["waves_per_workgroup"] == waves
+        assert p["total_units"] == -(-38 // waves)
+        assert p["rows_in_registers"] + p["rows_in_lds"] == 608
+        p = B.dspark_walk_plan_for(256, 163840, 64, 7, 200000)   # 784-row slices: dynamic
+        assert p["path"] == B.PATH_MFMA and p["waves_per_workgroup"] == 4
+        assert B.lib().dspark_debug_set(B.DEBUG_MFMA_WAVES, 5) == B.ERR_INVALID_ARG
+    finally:
+        B.lib().dspark_debug_set(B.DEBUG_MFMA_WAVES, 0)
 
 
 @pytest.mark.parametrize("bs", [1, 16, 64])
