@@ -295,6 +295,9 @@ __device__ __forceinline__ void gather_w1_codes(const WalkParams& p, const int32
         }
         return;
     }
+    // (the per-lane LDS addresses of the codes are computed at every call: hoisted out of the
+    // caller's step loop, they were spilled and reloaded before each write)
+    asm volatile("" : "+v"(lane));
     // Iterations it0 .. it0 + NIT - 1, NIT a template argument so that the code is
     // straight-line: all their loads are issued before any is used. (With a branch per iteration
     // the compiler moved each iteration's loads next to their use, one memory round trip per
@@ -545,6 +548,10 @@ __device__ __forceinline__ void combine_step(const WalkParams& p, int t, uint64_
         combine_step_small<TIMED, 2>(p, t, key, tok, lane);
         return;
     }
+    // the per-lane addresses below are computed here at every step: the compiler would
+    // otherwise hoist them out of the caller's step loop and hold (or spill) them for the whole
+    // walk
+    asm volatile("" : "+v"(lane));
     const int nwg = gridDim.x;
     const int wg = blockIdx.x;
     uint64_t* step_slots = p.slots + (size_t)t * nwg * p.stride;

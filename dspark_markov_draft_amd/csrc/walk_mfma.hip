@@ -294,7 +294,6 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dense_walk_mfma_kernel(const Wal
                 bol[kb] = low_op(kb);
             }
             const float sb = vb ? s1[b] : 0.0f;
-            const int64_t orow = ((int64_t)(vb ? b : 0) * p.T + t) * p.V;
             uint64_t seed = 0, P = 0;
             float rtemp = 1.0f;
             if constexpr (SAMPLE) {
@@ -354,8 +353,13 @@ __global__ __launch_bounds__(NW * WAVE, 1) void dense_walk_mfma_kernel(const Wal
                 }
                 return ok;
             };
-            // writes what scores4 left in `out` (greedy: only when the caller asked for logits)
+            // writes what scores4 left in `out` (greedy: only when the caller asked for logits).
+            // The row offset is computed here, not once per request tile: held through the tile,
+            // its two registers were spilled.
             auto store4 = [&](int vt, bool ok, const uint32_t (&out)[4]) {
+                int bo = vb ? b : 0;
+                asm volatile("" : "+v"(bo));
+                const int64_t orow = ((int64_t)bo * p.T + t) * p.V;
                 if constexpr (!SAMPLE) {
                     if (p.out_logits != nullptr && ok)
                         *reinterpret_cast<uint4*>(p.out_logits + orow + vt) =
