@@ -55,7 +55,7 @@ __host__ __device__ constexpr int mfma_static_slots(int tiles_per_wave, int wave
 // tile slots per wave held in registers: 8 with 4 waves, 5 with 8 (the sampling kernels finish
 // their slots in two halves, which leaves them the registers); the rest of a build's slots are
 // in LDS
-__host__ __device__ constexpr int mfma_static_reg_slots(int waves) { return waves == 4 ? 8 : 4; }
+__host__ __device__ constexpr int mfma_static_reg_slots(int waves) { return waves == 4 ? 8 : 5; }
 __host__ __device__ constexpr int mfma_static_lds_slots(int slots, int waves) {
     return slots > mfma_static_reg_slots(waves) ? slots - mfma_static_reg_slots(waves) : 0;
 }
