@@ -206,6 +206,7 @@ int launch_dense_walk(const WalkLaunch& a, const dspark_walk_plan& plan_in, hipS
     p.stage_bufs = plan.stage_bufs;
     p.stage_stride = plan.stage_stride;
     p.vec_ok = vec_ok ? 1 : 0;
+    p.w1_row_bytes = RANK * (a.w1_dtype == DSPARK_F32 ? 4 : 2);
     const DebugKnobs& dbg = debug_knobs();
     p.spin_ticks = dbg.spin_ticks ? dbg.spin_ticks : DEFAULT_SPIN_TICKS;
     p.wait_unset = dbg.wait_unset ? 1 : 0;
