@@ -42,11 +42,11 @@ struct RunningArgmax {
     float v = 0.0f;
     uint32_t i = 0xFFFFFFFFu;
     __device__ __forceinline__ void offer(float x, uint32_t idx, bool ok) {
-        const bool better = x > v || i == 0xFFFFFFFFu || (x != x && v == v);
-        if (ok && better) {
-            v = x;
-            i = idx;
-        }
+        // bitwise, not short-circuit, operators: selects rather than branches
+        const bool better = (x > v) | (i == 0xFFFFFFFFu) | ((x != x) & (v == v));
+        const bool take = ok & better;
+        v = take ? x : v;
+        i = take ? idx : i;
     }
     __device__ __forceinline__ uint64_t key() const {
         return i == 0xFFFFFFFFu ? 0ull : argmax_key(v, i);
@@ -246,14 +246,6 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 }
 
 template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)v);
-    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > v ? o : v;
-}
-
-template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
     const uint32_t o = dpp_u32<CTRL, ROW_MASK>(v);
     return o > v ? o : v;
@@ -267,28 +259,29 @@ constexpr int DPP_BCAST15 = 0x142;     // row_bcast:15
 constexpr int DPP_BCAST31 = 0x143;     // row_bcast:31
 constexpr int DPP_ROW_ROR8 = 0x128;    // row_ror:8 (lane l reads lane l ^ 8 of its 16-lane row)
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = dpp_max_u64<DPP_SWAP1>(v);
-    v = dpp_max_u64<DPP_SWAP2>(v);
-    v = dpp_max_u64<DPP_HALF_MIRROR>(v);
-    v = dpp_max_u64<DPP_MIRROR>(v);
-    v = dpp_max_u64<DPP_BCAST15, 0xA>(v);
-    v = dpp_max_u64<DPP_BCAST31, 0xC>(v);
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// maximum of non-negative floats (ordered like their bit patterns)
-__device__ __forceinline__ float wave_max_nonneg_f32(float x) {
-    uint32_t v = __float_as_uint(x);
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = dpp_max_u32<DPP_SWAP1>(v);
     v = dpp_max_u32<DPP_SWAP2>(v);
     v = dpp_max_u32<DPP_HALF_MIRROR>(v);
     v = dpp_max_u32<DPP_MIRROR>(v);
     v = dpp_max_u32<DPP_BCAST15, 0xA>(v);
     v = dpp_max_u32<DPP_BCAST31, 0xC>(v);
-    return __uint_as_float(__builtin_amdgcn_readlane(v, 63));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// The lexicographic maximum in two 32-bit passes: the largest high word, then the largest low
+// word among the lanes that hold it (a 64-bit pass needs a 64-bit compare and two selects per
+// step).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+    return ((uint64_t)mh << 32) | ml;
+}
+
+// maximum of non-negative floats (ordered like their bit patterns)
+__device__ __forceinline__ float wave_max_nonneg_f32(float x) {
+    return __uint_as_float(wave_max_u32(__float_as_uint(x)));
 }
 
 // ---------------------------------------------------------------------------------------------
