@@ -18,7 +18,7 @@ constexpr int DOT4_LDS_SETS_MAX = 2;    // row sets in LDS
 // (all requests' in the lane-per-row kernel, the one request's in the one-request MFMA kernel)
 constexpr int WALK_FIXED_LDS = W1Q_BYTES + MAX_BS * 4 + WALK_WAVES * MAX_BS * 8 + MAX_BS * 4;
 constexpr int DOT4_FIXED_LDS = WALK_FIXED_LDS + W1L_BYTES;
-constexpr int MFMA1_FIXED_LDS = WALK_FIXED_LDS + RANK;
+constexpr int MFMA1_FIXED_LDS = WALK_FIXED_LDS + RANK + MFMA1_MAX_GROUPS * WAVE * 4;
 constexpr int MFMA_REG_TILES = 8;       // 16-row tiles per wave in VGPRs
 constexpr int MFMA_TILE_LDS = 4 * WAVE * 16;
 // Smallest batch run on the MFMA kernel: below it the lane-per-row kernel is faster (measured at

@@ -30,6 +30,8 @@ __host__ __device__ constexpr int mfma1_reg_slots(int tiles_per_wave) {
 }
 constexpr int MFMA1_LDS_TILES = 8;   // and at most this many more in LDS (4 KB each)
 constexpr int MFMA1_MAX_ROWS = (MFMA1_TILES + MFMA1_LDS_TILES) * WALK_WAVES * 16;   // 1152
+// rows each lane of the one-request kernel finishes per step, at most (4 tile slots per row)
+constexpr int MFMA1_MAX_GROUPS = (MFMA1_TILES + MFMA1_LDS_TILES + 3) / 4;
 // MFMA kernel, slices of up to MFMA_STATIC_ROWS rows: all LDS in static arrays (see the kernel):
 // two staging buffers for 16 rows of at most MFMA_STATIC_STRIDE floats (157 odd 16-byte units),
 // up to mfma_static_lds_slots() LDS tiles per wave, W1 codes and scales, row scales, lane keys,

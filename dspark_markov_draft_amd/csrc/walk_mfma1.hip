@@ -43,6 +43,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     static_assert(NREG == MFMA1_TILES || !LDS, "LDS slots follow a full set of register slots");
     constexpr int M1_SLOTS = NREG + (LDS ? MFMA1_LDS_TILES : 0);   // tile slots per wave
     constexpr int M1_GROUPS = (M1_SLOTS + 3) / 4;   // rows each lane finishes per step, at most
+    static_assert(M1_GROUPS <= MFMA1_MAX_GROUPS, "LDS for wave 0's base logits");
     stamp<TIMED>(p, 0);
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -68,6 +69,8 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
     int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
     uint32_t* w1l = reinterpret_cast<uint32_t*>(tok + MAX_BS);   // the request's low digits
+    // wave 0's base logits of the next step, copied by wave 1 (argmax walks)
+    float* pf0 = reinterpret_cast<float*>(w1l + RANK / 4);
 
     // ---- step 0's W1 codes, by the last wave before its share of the fill ----------------
     // The start token is known at launch, so its row is gathered while the other waves' fill
@@ -130,6 +133,24 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
 #pragma unroll
         for (int gi = 0; gi < M1_GROUPS; ++gi) pf[gi] = vok[gi] ? br[vrow[gi]] : 0.0f;
     };
+    // Wave 0 runs the combine, and loads it issues before would delay its key store and polls
+    // (vector memory completes in issue order), so in the argmax walks without LDS tiles wave 1
+    // copies wave 0's base logits of the next step into LDS by DMA and waits for them before the
+    // step's barrier. (Measured: 32.0 -> 31.7 us at T = 7, 61.5 -> 60.6 at T = 16; with LDS
+    // tiles, where wave 1 has more to copy, 1 us slower at T = 16, so not there.)
+    constexpr bool W0_LDS = SAMPLE != 2 && !LDS;
+    auto copy_base_w0 = [&](int t) {
+        const float* br = p.base + (int64_t)t * p.V;
+#pragma unroll
+        for (int gi = 0; gi < M1_GROUPS; ++gi) {
+            const int tw = 4 * gi + ts;
+            const int r = row0 + tw * WALK_WAVES * 16 + 4 * g + ri;   // wave 0's row
+            const bool ok = tw < nslots && r < vend;
+            __builtin_amdgcn_global_load_lds(
+                (__attribute__((address_space(1))) void*)(br + (ok ? r : row0)),
+                (__attribute__((address_space(3))) void*)(pf0 + gi * WAVE), 4, 0, 0);
+        }
+    };
     load_base(0);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's tile copies have landed, and every wave's
     __syncthreads();                  // after the barrier
@@ -157,8 +178,13 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 0);
 
         float cur[M1_GROUPS];
+        if (W0_LDS && wave == 0 && t > 0) {
 #pragma unroll
-        for (int gi = 0; gi < M1_GROUPS; ++gi) cur[gi] = pf[gi];
+            for (int gi = 0; gi < M1_GROUPS; ++gi) cur[gi] = vok[gi] ? pf0[gi * WAVE + lane] : 0.0f;
+        } else {
+#pragma unroll
+            for (int gi = 0; gi < M1_GROUPS; ++gi) cur[gi] = pf[gi];
+        }
         v4i1 bop[4];
         const uint32_t* wd = c < 8 ? w1q : w1l;   // column c: high digits, or low from 8 on
 #pragma unroll
@@ -243,8 +269,14 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         __syncthreads();
         stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 1);
 
-        // the next step's base logits load while the combine waits
-        if (t + 1 < p.T) load_base(t + 1);
+        // the next step's base logits load while the combine waits (wave 0's: above)
+        if (t + 1 < p.T) {
+            if (!W0_LDS || wave != 0) load_base(t + 1);
+            if (W0_LDS && wave == 1) {
+                copy_base_w0(t + 1);
+                __builtin_amdgcn_s_waitcnt(0);   // landed before the step's last barrier
+            }
+        }
         if (wave == 0) {
             uint64_t k = 0;
             if constexpr (SAMPLE == 2) {
