@@ -71,6 +71,13 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// 2^x by the hardware instruction alone (exp2f adds a range reduction that keeps results
+// below 2^-126 as denormals; this flushes them to 0). Used only for terms that are added to a
+// sum that holds the maximum's own term 1, or compared with terms of their own size, where
+// such values change nothing; the per-entry masses that decide which tokens can be drawn use
+// exp2f.
+__device__ __forceinline__ float exp2_sum_term(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // (m, s) pairs: s = sum of 2^(z - m) over the entries seen, m their maximum (-inf, 0: none).
 __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
     const float M = fmaxf(m, m2);
@@ -167,13 +174,15 @@ __global__ __launch_bounds__(VT) void verify_stats_kernel(const VerifyParams p) 
             mp = fmaxf(mp, zp[j][e]);
             mq = fmaxf(mq, zq[j][e]);
         }
+    // (a row part with no finite entry subtracts 0: its -inf entries give exactly 0)
+    const float mpc = mp == -INFINITY ? 0.0f : mp, mqc = mq == -INFINITY ? 0.0f : mq;
     float sp = 0.0f, sq = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sp += mp == -INFINITY ? 0.0f : exp2f(zp[j][e] - mp);
-            sq += mq == -INFINITY ? 0.0f : exp2f(zq[j][e] - mq);
+            sp += exp2_sum_term(zp[j][e] - mpc);
+            sq += exp2_sum_term(zq[j][e] - mqc);
         }
     block_ms(mp, sp, lds);
     block_ms(mq, sq, lds);
@@ -276,7 +285,8 @@ __global__ __launch_bounds__(VT) void verify_residual_kernel(const VerifyParams 
     for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float d = w * prob_of(zp[j][e] * k, mp, ip) - prob_of(zq[j][e] * k, mq, iq);
+            const float d = w * (exp2_sum_term(zp[j][e] * k - mp) * ip) -
+                            exp2_sum_term(zq[j][e] * k - mq) * iq;
             R += d > 0.0f ? d : 0.0f;
         }
     R = block_sum(R, lds);

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(s1 + MAX_BS);
     int32_t* tok = reinterpret_cast<int32_t*>(wkeys + WALK_WAVES * MAX_BS);
     uint32_t* w1l = reinterpret_cast<uint32_t*>(tok + MAX_BS);   // the request's low digits
-    // wave 0's base logits of the next step, copied by wave 1 (argmax walks)
+    // wave 0's base logits of the next step, copied by wave 1 (argmax walks without LDS tiles)
     float* pf0 = reinterpret_cast<float*>(w1l + RANK / 4);
 
     // ---- step 0's W1 codes, by the last wave before its share of the fill ----------------
