@@ -61,9 +61,17 @@ struct VerifyParams {
     VerifyState* state;        // [bs]
     float4* stats;             // [bs][T + 1][C]: (mp, sp, mq, sq) per chunk
     float* resid;              // [bs][T][C]
-    float2* mass;              // [bs][C]: (mass of r, mass of p_tau)
-    int bs, T, V, mode, C;
+    float2* mass;              // [bs][CM]: (mass of r, mass of p_tau) per chunk of MASS_J * 1024
+    int bs, T, V, mode, C, CM;
 };
+
+// The next token's pass (masses per chunk, then the draw's in-order scan of one chunk) uses
+// chunks of MASS_J * 1024 entries: more workgroups for the one row per request it reads, and a
+// short scan. Up to MASS_MAX_CHUNKS chunks per row.
+constexpr int MASS_J = 2;
+constexpr int MASS_GROUPS = 4;                       // the draw's selection: chunks per lane
+constexpr int MASS_MAX_CHUNKS = MASS_GROUPS * WAVE;
+static_assert((int64_t)MASS_MAX_CHUNKS * MASS_J * 1024 >= DSPARK_MAX_V, "chunks of the largest V");
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(VT) void verify_mass_kernel(const VerifyParams p) {
         }
     mr = block_sum(mr, lds);
     mpt = block_sum(mpt, lds);
-    if (threadIdx.x == 0) p.mass[(int64_t)b * p.C + c] = make_float2(mr, mpt);
+    if (threadIdx.x == 0) p.mass[(int64_t)b * p.CM + c] = make_float2(mr, mpt);
 }
 
 // ---- 6. the draw, the outputs, and the request's workspace words cleared -------------------
@@ -396,39 +404,69 @@ __global__ __launch_bounds__(VT) void verify_draw_kernel(const VerifyParams p) {
     const VerifyState& s = p.state[b];
     const int tau = s.tau;
     const NextDist d = next_dist(p, b);
-    const float2* mass = p.mass + (int64_t)b * p.C;
-    if (threadIdx.x == 0) {
-        // total mass (r; p_tau if r has none), the chunk where the running mass passes u * total
-        float tot = 0.0f;
-        for (int c = 0; c < p.C; ++c) tot += mass[c].x;
+    const float2* mass = p.mass + (int64_t)b * p.CM;
+    if (wave == 0) {
+        // total mass (r; p_tau if r has none), then the first chunk with mass where the running
+        // mass passes u * total: wave 0, chunk g * 64 + lane in lane `lane` of group g, running
+        // masses by a scan of each group over the lanes, in chunk order
+        float mr[MASS_GROUPS], mpt[MASS_GROUPS];
+        float tr = 0.0f, tp = 0.0f;
+#pragma unroll
+        for (int g = 0; g < MASS_GROUPS; ++g) {
+            const int c = g * WAVE + lane;
+            const float2 v = c < p.CM ? mass[c] : make_float2(0.0f, 0.0f);
+            mr[g] = v.x;
+            mpt[g] = v.y;
+            tr += v.x;
+            tp += v.y;
+        }
+        float tot = wave_sum(tr);
         const int up = tot > 0.0f ? 0 : 1;
-        if (up) {
-            tot = 0.0f;
-            for (int c = 0; c < p.C; ++c) tot += mass[c].y;
-        }
+        if (up) tot = wave_sum(tp);
         const float target = p.uniforms[(int64_t)b * (p.T + 1) + p.T] * tot;
-        float run = 0.0f;
+        float mg[MASS_GROUPS];   // the masses in use, chosen value by value (no array select)
+#pragma unroll
+        for (int g = 0; g < MASS_GROUPS; ++g) mg[g] = up ? mpt[g] : mr[g];
+        float run = 0.0f;          // mass of the groups before
         int sel = -1, last = 0;
-        float before = 0.0f;
-        for (int c = 0; c < p.C; ++c) {
-            const float m = up ? mass[c].y : mass[c].x;
-            if (m > 0.0f) {
-                last = c;
-                if (sel < 0 && run + m > target) {
-                    sel = c;
-                    before = run;
-                }
+        float before = 0.0f, before_last = 0.0f;
+        auto group = [&](int g, float m) {
+            float incl = m;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const float v = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += v;
             }
-            run += m;
-        }
+            const float excl = run + (incl - m);   // running mass before this lane's chunk
+            const uint64_t cross = __ballot(m > 0.0f && excl + m > target);
+            if (sel < 0 && cross != 0) {
+                const int f = __builtin_ctzll(cross);
+                sel = g * WAVE + f;
+                before = __shfl(excl, f, WAVE);
+            }
+            const uint64_t has = __ballot(m > 0.0f);
+            if (has != 0) {
+                const int l = 63 - __builtin_clzll(has);
+                last = g * WAVE + l;
+                before_last = __shfl(excl, l, WAVE);
+            }
+            run += __shfl(incl, WAVE - 1, WAVE);
+        };
+        static_assert(MASS_GROUPS == 4, "groups");
+        group(0, mg[0]);
+        group(1, mg[1]);
+        group(2, mg[2]);
+        group(3, mg[3]);
         if (sel < 0) {   // rounding: the running mass never passed the target
             sel = last;
-            before = run - (up ? mass[last].y : mass[last].x);
+            before = before_last;
         }
-        chunk_sel = sel;
-        local_target = target - before;
-        use_p = up;
-        found = 0x7FFFFFFF;
+        if (lane == 0) {
+            chunk_sel = sel;
+            local_target = target - before;
+            use_p = up;
+            found = 0x7FFFFFFF;
+        }
     }
     __syncthreads();
     const int c = chunk_sel;
@@ -518,8 +556,8 @@ __global__ __launch_bounds__(VT) void verify_draw_kernel(const VerifyParams p) {
         for (int i = threadIdx.x; i < (p.T + 1) * p.C; i += VT) st[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         float* rs = p.resid + (int64_t)b * p.T * p.C;
         for (int i = threadIdx.x; i < p.T * p.C; i += VT) rs[i] = 0.0f;
-        float2* ms = p.mass + (int64_t)b * p.C;
-        for (int i = threadIdx.x; i < p.C; i += VT) ms[i] = make_float2(0.f, 0.f);
+        float2* ms = p.mass + (int64_t)b * p.CM;
+        for (int i = threadIdx.x; i < p.CM; i += VT) ms[i] = make_float2(0.f, 0.f);
         uint32_t* sw = reinterpret_cast<uint32_t*>(&p.state[b]);
         for (int i = threadIdx.x; i < (int)(VERIFY_STATE_BYTES / 4); i += VT) sw[i] = 0u;
     }
@@ -549,8 +587,8 @@ int launch_verify_j(const VerifyParams& p_in, hipStream_t s) {
         ok = ok && go(reinterpret_cast<const void*>(&verify_residual_kernel<J, VEC>),
                       dim3(p.C, p.bs * (p.T - 1)));
     if (p.mode == 1) ok = ok && go(reinterpret_cast<const void*>(&verify_choose_kernel), dim3(p.bs));
-    ok = ok && go(reinterpret_cast<const void*>(&verify_mass_kernel<J, VEC>), dim3(p.C, p.bs));
-    ok = ok && go(reinterpret_cast<const void*>(&verify_draw_kernel<J, VEC>), dim3(p.bs));
+    ok = ok && go(reinterpret_cast<const void*>(&verify_mass_kernel<MASS_J, VEC>), dim3(p.CM, p.bs));
+    ok = ok && go(reinterpret_cast<const void*>(&verify_draw_kernel<MASS_J, VEC>), dim3(p.bs));
     if (!ok) {
         (void)hipGetLastError();
         return DSPARK_ERR_LAUNCH;
@@ -563,20 +601,21 @@ int launch_verify_j(const VerifyParams& p_in, hipStream_t s) {
 static size_t up16(size_t n) { return (n + 15) / 16 * 16; }
 
 // workspace regions after the error word: states [bs], chunk statistics [bs][T + 1][C] (float4),
-// residual sums [bs][T][C], next-token masses [bs][C] (float2), each 16-byte aligned
+// residual sums [bs][T][C], next-token masses [bs][CM] (float2), each 16-byte aligned
 struct VerifyLayout {
     size_t state, stats, resid, mass, end;
-    VerifyLayout(int64_t bs, int64_t T, int64_t C) {
+    VerifyLayout(int64_t bs, int64_t T, int64_t C, int64_t CM) {
         state = VERIFY_WS_STATE;
         stats = state + (size_t)bs * VERIFY_STATE_BYTES;
         resid = stats + up16((size_t)bs * (T + 1) * C * 16);
         mass = resid + up16((size_t)bs * T * C * 4);
-        end = mass + up16((size_t)bs * C * 8);
+        end = mass + up16((size_t)bs * CM * 8);
     }
 };
 
 size_t verify_workspace_bytes(int64_t bs, int64_t T, int64_t V) {
-    const VerifyLayout L(bs, T, (V + 2047) / 2048);   // the smallest chunk: the most chunks
+    const int64_t most = (V + 2047) / 2048;   // the smallest chunk: the most chunks
+    const VerifyLayout L(bs, T, most, most);
     return (L.end + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN;
 }
 
@@ -596,8 +635,10 @@ int launch_verify(const VerifyLaunch& a, hipStream_t stream) {
     p.mode = a.mode;
     const int J = verify_groups(a.bs, a.T, a.V);
     p.C = (a.V + J * 1024 - 1) / (J * 1024);
+    p.CM = (a.V + MASS_J * 1024 - 1) / (MASS_J * 1024);
+    if (p.CM > MASS_MAX_CHUNKS) return DSPARK_ERR_UNSUPPORTED;
     char* ws = static_cast<char*>(a.workspace);
-    const VerifyLayout L(a.bs, a.T, p.C);
+    const VerifyLayout L(a.bs, a.T, p.C, p.CM);
     p.err = reinterpret_cast<uint32_t*>(ws + WS_ERR);
     p.state = reinterpret_cast<VerifyState*>(ws + L.state);
     p.stats = reinterpret_cast<float4*>(ws + L.stats);
