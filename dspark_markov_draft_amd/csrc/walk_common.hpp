@@ -762,6 +762,7 @@ __device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, ui
     const int nwg = gridDim.x;
     const int wg = blockIdx.x;
     const bool last_step = t + 1 == p.T;
+    uint32_t touch = 0;
     uint64_t* step_slots = p.slots + (size_t)t * nwg * p.stride;
     if (lane < p.bs) st_dev(step_slots + (size_t)lane * nwg + wg, pair);
     stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 2);
@@ -913,6 +914,11 @@ __device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, ui
             if (lane == 0) p.tokens[b * p.T + t] = (int32_t)token;
             if (!last_step && lane < ICDF_REPL)
                 st_dev(icdf_tok_word(p, lane, t, b), (uint64_t)token + 1);
+            // as in combine_step: the token's W1 row is read here, one hop before every
+            // workgroup gathers it, so that it is in the memory-side cache by then
+            if (!last_step && p.bs > 16 && lane * 64 < p.w1_row_bytes)
+                touch ^= *reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.w1) +
+                                                             (int64_t)token * p.w1_row_bytes + lane * 64);
         }
     }
     stamp<TIMED>(p, STAMP_STEP0 + t * STAMPS_PER_STEP + 4);
@@ -977,6 +983,7 @@ __device__ __forceinline__ void combine_icdf_step(const WalkParams& p, int t, ui
                 st_dev(icdf_sel_word(p, i / p.bs, t, i % p.bs), 0);
         }
     }
+    asm volatile("" ::"v"(touch));
 }
 
 // Kernel entry points, as host-side stubs for hipLaunchKernel (sample: 0 greedy, 1 Gumbel,
