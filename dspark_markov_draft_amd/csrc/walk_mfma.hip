@@ -16,9 +16,10 @@
 // low digits' 4 MFMAs: 16 * (high sum) + (low sum), the exact integer of the other kernels. The
 // low digits sit in LDS as nibbles (8 KB for 64 requests) and are widened to int8 when read.
 //
-// The workgroup's rows form 16-row tiles dealt round-robin to its 4 waves: each wave keeps up
-// to 8 tiles (128 rows) in VGPRs as ready A operands, further tiles in LDS (laid out so a
-// K-block read is 64 consecutive 16-byte lane slots), and streams any rest from memory. Per
+// The workgroup's rows form 16-row tiles dealt round-robin to its waves: 8 waves (two per SIMD)
+// with 5 or 4 tiles each in registers for slices of up to 624 rows, otherwise 4 waves that keep
+// up to 8 tiles (128 rows) in VGPRs as ready A operands, further tiles in LDS (laid out so a
+// K-block read is 64 consecutive 16-byte lane slots), and stream any rest from memory. Per
 // step and 16-request tile: 8 MFMAs per W2 tile; each lane then finishes 4 consecutive rows of
 // one request (one float4 of base logits, one Philox call for the 4 noise words), keeps its
 // best key, the four lanes of a request in a wave merge theirs with two lane swaps, and the
