@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 def _reset_knobs():
     yield
     for key in (B.DEBUG_MAX_WORKGROUPS, B.DEBUG_SPIN_LIMIT, B.DEBUG_WAIT_UNSET_FLAG,
-                B.DEBUG_FORCE_PATH):
+                B.DEBUG_FORCE_PATH, B.DEBUG_MFMA_WAVES):
         dm.dspark_debug_set(key, 0)
 
 
@@ -323,6 +323,37 @@ def test_full_size_without_out_logits_same_tokens(name):
     a, _ = p.greedy(want_logits=True, qs=qs)
     b, _ = p.greedy(want_logits=False, qs=qs)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("case", [(10000, 3, 19, 20), (12480, 2, 24, 20), "v151936_t7_bs64"])
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_mfma_wave_layouts_agree_bitwise(case, mode):
+    """The batched kernel's static-LDS builds with 8 waves (two per SIMD, the default) and with 4
+    (forced by the test hook) form every logit with the same exact sums and fp32 operations: the
+    same tokens and bit-identical logits or bf16 rows. Slices of 512 rows (the builds with 8 and
+    4 slots per wave), of 624 rows (10 and 5) and the full-size 64-request walk; the 4-wave run is
+    also checked against the oracle."""
+    if isinstance(case, str):
+        inp = make_inputs(CASES[case])
+        p = Problem(inp.w1, inp.w2, inp.base, inp.start, seeds=inp.seeds,
+                    temps=inp.temperature.numpy())
+    else:
+        V, T, bs, cap = case
+        dm.dspark_debug_set(B.DEBUG_MAX_WORKGROUPS, cap)
+        temps = np.linspace(0.5, 2.0, bs).astype(np.float32)
+        p = random_problem(V, T, bs, dtype=torch.bfloat16, seed=V + bs, temps=temps)
+    qs = p.quantize()
+    outs = []
+    for waves in (8, 4):
+        dm.dspark_debug_set(B.DEBUG_MFMA_WAVES, waves)
+        plan = dm.dspark_walk_plan_query(*p.shape)
+        assert plan["path"] == B.PATH_MFMA and plan["waves_per_workgroup"] == waves
+        outs.append(p.greedy(qs=qs) if mode == "greedy" else p.sample(qs=qs))
+    view = np.uint32 if mode == "greedy" else np.uint16
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(view), outs[1][1].view(view))
+    rep = p.check_greedy(*outs[1]) if mode == "greedy" else p.check_sample(*outs[1])
+    assert rep.ok, rep.summary()
 
 
 # ----------------------------------------------------------------------------------------------
