@@ -214,6 +214,36 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
         }
         const int64_t orow = (int64_t)t * p.V;
         const uint64_t P = pos0 + (uint64_t)t;
+        // Gumbel noise: the four lanes of a quad (ri = 0..3) finish the four rows of one 4-row
+        // group in each row group gi, and one Philox call yields those four words. So lane ri
+        // draws the call of group ri + 4k alone, and the quad shares the words below, instead of
+        // every lane drawing every group's call for one word of it.
+        constexpr int NCALL = (M1_GROUPS + 3) / 4;
+        uint4 nw[SAMPLE == 1 ? NCALL : 1];
+        if constexpr (SAMPLE == 1) {
+#pragma unroll
+            for (int k = 0; k < NCALL; ++k) {
+                int vr = vrow[0];   // (a lane past the last group draws group 0's call, unused)
+#pragma unroll
+                for (int gi = 1; gi < M1_GROUPS; ++gi) vr = ri + 4 * k == gi ? vrow[gi] : vr;
+                nw[k] = philox4x32_10((uint32_t)vr >> 2, (uint32_t)P, (uint32_t)(P >> 32), 0u,
+                                      (uint32_t)seed, (uint32_t)(seed >> 32));
+            }
+        }
+        // word ri of the call that quad lane s drew: broadcast within the quad, then chosen
+        auto quad_word = [&](const uint4 w, int s) -> uint32_t {
+            uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                switch (s) {
+                    case 0: x[i] = dpp_u32<0x00>(x[i]); break;
+                    case 1: x[i] = dpp_u32<0x55>(x[i]); break;
+                    case 2: x[i] = dpp_u32<0xAA>(x[i]); break;
+                    default: x[i] = dpp_u32<0xFF>(x[i]); break;
+                }
+            }
+            return ri == 0 ? x[0] : ri == 1 ? x[1] : ri == 2 ? x[2] : x[3];
+        };
         RunningArgmax run;
         RunningSoftmax soft;
 #pragma unroll
@@ -251,7 +281,7 @@ __global__ __launch_bounds__(WALK_THREADS, 1) void dense_walk_mfma1_kernel(const
                 const uint32_t h = bf16_bits(l);
                 if (vok[gi]) p.draft_logits[orow + v] = (uint16_t)h;
                 const float x = bf16_value(h) * rtemp;
-                const float gn = gumbel_from_word(noise_word(seed, P, (uint32_t)v));
+                const float gn = gumbel_from_word(quad_word(nw[gi / 4], gi % 4));
                 run.offer(x + gn, (uint32_t)v, vok[gi]);
             } else {
                 const uint32_t h = bf16_bits(l);
