@@ -390,11 +390,14 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     }
     // and the first batch of the main pass, so that it is in flight while the chunk's histogram
     // and bound are computed (every workgroup starts at once, so HBM would idle meanwhile)
-    constexpr int BATCH = MAIN_UNROLL * SEL_THREADS;
+    // (rows without float4 loads take half batches: their scalar loads need more address
+    // registers)
+    constexpr int MU = VEC ? MAIN_UNROLL : MAIN_UNROLL / 2;
+    constexpr int BATCH = MU * SEL_THREADS;
     int g0 = STASH_GROUPS * SEL_THREADS;
-    float4 cur[MAIN_UNROLL];
+    float4 cur[MU];
 #pragma unroll
-    for (int u = 0; u < MAIN_UNROLL; ++u) {
+    for (int u = 0; u < MU; ++u) {
         const int g = g0 + u * SEL_THREADS + tid;
         cur[u] = load_group_clamped<VEC>(p, x, g, ngroups);
     }
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
     __syncthreads();
 
     // Every key in a bin >= bin_lo goes into this wave's LDS region (wave-uniform count, no
-    // atomics for the position) and into the histogram. Membership is one float compare per
+    // atomics for the position). Membership is one float compare per
     // element: the keys order values as IEEE comparison does (-0 with +0), with NaN above +inf,
     // so "key >= the bin's lowest key B" is "not (x < t)" for t the value whose key is B (NaN
     // passes, as it should). The bins below -inf's key hold no value (t = -inf admits all).
@@ -448,51 +451,71 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
                                                : __uint_as_float(~kB);
     uint64_t* region = buf + wave * REGION_CAP;
     uint32_t n_region = 0;
-    // A group's members are appended in one pass: each lane counts its members c (0..4), its
-    // position is the members of the lanes below it, read from three ballots of c's bits.
+    // The scan stores each member as its raw (index, value bits) pair: element u of the group
+    // goes to the position given by the members of element u in the lanes below (one ballot per
+    // element). Order keys and the histogram are made after the scan, over the region only, so
+    // that the streaming loop does the least work per element.
     auto offer = [&](const float4 a, int g, bool present) {
         const float e[4] = {a.x, a.y, a.z, a.w};
         bool in[4];
-        uint32_t c = 0;
+        uint64_t m[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             in[u] = present && (VEC || 4 * g + u < p.V) && !(e[u] < t_lo);
-            c += in[u] ? 1u : 0u;
+            m[u] = __ballot(in[u]);
         }
-        if (__ballot(c != 0) == 0) return;
-        const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
-        uint32_t pos = n_region + lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2);
+        if ((m[0] | m[1] | m[2] | m[3]) == 0) return;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (in[u]) {
-                atomicAdd(&hist[top_bin(e[u])], 1u);
-                if (pos < (uint32_t)REGION_CAP) region[pos] = composite_key(e[u], (uint32_t)(4 * g + u));
-                ++pos;
-            }
+            if (m[u] == 0) continue;
+            const uint32_t pos = n_region + lanes_below(m[u]);
+            if (in[u] && pos < (uint32_t)REGION_CAP)
+                region[pos] = ((uint64_t)(uint32_t)(4 * g + u) << 32) | __float_as_uint(e[u]);
+            n_region += (uint32_t)__popcll(m[u]);
         }
-        n_region += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
     };
 #pragma unroll
     for (int s = 0; s < STASH_GROUPS; ++s) {
         const int g = s * SEL_THREADS + tid;
         offer(stash[s], g, g < ngroups);
     }
-    // the rest of the row, one batch in flight while the previous one is examined
-    for (; g0 < ngroups; g0 += BATCH) {
-        float4 nxt[MAIN_UNROLL];
+    // The rest of the row in two register sets used in turn, so that one batch is in flight
+    // while the other is examined and no loaded value is ever copied between registers (a copy
+    // would wait for its load).
+    for (; g0 < ngroups; g0 += 2 * BATCH) {
+        float4 nxt[MU];
 #pragma unroll
-        for (int u = 0; u < MAIN_UNROLL; ++u) {
+        for (int u = 0; u < MU; ++u) {
             const int g = g0 + BATCH + u * SEL_THREADS + tid;
             nxt[u] = load_group_clamped<VEC>(p, x, g, ngroups);
         }
 #pragma unroll
-        for (int u = 0; u < MAIN_UNROLL; ++u) {
+        for (int u = 0; u < MU; ++u) {
             const int g = g0 + u * SEL_THREADS + tid;
             offer(cur[u], g, g < ngroups);
             if (g < ngroups) fill_group<VEC>(p, row, g);
         }
 #pragma unroll
-        for (int u = 0; u < MAIN_UNROLL; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < MU; ++u) {
+            const int g = g0 + 2 * BATCH + u * SEL_THREADS + tid;
+            cur[u] = load_group_clamped<VEC>(p, x, g, ngroups);
+        }
+#pragma unroll
+        for (int u = 0; u < MU; ++u) {
+            const int g = g0 + BATCH + u * SEL_THREADS + tid;
+            offer(nxt[u], g, g < ngroups);
+            if (g < ngroups) fill_group<VEC>(p, row, g);
+        }
+    }
+    // the region's pairs to order keys, counted in the histogram of the offered keys
+    {
+        const uint32_t n = n_region < (uint32_t)REGION_CAP ? n_region : (uint32_t)REGION_CAP;
+        for (uint32_t e = lane; e < n; e += WAVE) {
+            const uint64_t r = region[e];
+            const float v = __uint_as_float((uint32_t)r);
+            atomicAdd(&hist[top_bin(v)], 1u);
+            region[e] = composite_key(v, (uint32_t)(r >> 32));
+        }
     }
     if (lane == 0) cnt[wave] = n_region;
     __syncthreads();
