@@ -59,7 +59,7 @@ from dspark_markov_draft_amd.synth import (CASES, Case, make_inputs, make_verify
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
 KERNEL_NAMES = {1: "dense_walk_dot4_kernel", 2: "dense_walk_mfma_kernel", 3: "dense_walk_mfma1_kernel"}
-TOPK_KERNELS = "topk_select_kernel+topk_walk_kernel"
+TOPK_KERNELS = "topk_fused_kernel"   # k <= 512: select and walk in one launch
 VERIFY_KERNELS = "verify_*_kernel"
 # LDS read peak: 128 bytes per clock per compute unit x 256 units x 2.4 GHz
 LDS_PEAK_GBS = 128 * 256 * 2.4
@@ -381,7 +381,7 @@ KERNEL_SOURCES = {
     "dense_walk_dot4_kernel": COMMON_SOURCES + ["walk_dot4.hip"],
     "dense_walk_mfma_kernel": COMMON_SOURCES + ["walk_mfma.hip"],
     "dense_walk_mfma1_kernel": COMMON_SOURCES + ["walk_mfma1.hip"],
-    "topk_select_kernel+topk_walk_kernel": COMMON_SOURCES + ["topk.hip"],
+    TOPK_KERNELS: COMMON_SOURCES + ["topk.hip"],
     VERIFY_KERNELS: ["device_common.hpp", "internal.hpp", "api.hip", "verify.hip"],
 }
 

@@ -24,6 +24,7 @@ DEBUG_MAX_WORKGROUPS, DEBUG_SPIN_LIMIT, DEBUG_WAIT_UNSET_FLAG, DEBUG_STAMPS = 1,
 DEBUG_FORCE_PATH = 5
 DEBUG_KERNEL_TIMING = 6
 DEBUG_MFMA_WAVES = 7
+DEBUG_TOPK_SPLIT = 8
 PATH_DOT4, PATH_MFMA, PATH_MFMA1 = 1, 2, 3
 STAMPS_PER_WG = 210
 

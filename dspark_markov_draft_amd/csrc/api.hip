@@ -529,6 +529,7 @@ int dspark_debug_set(int key, int64_t value) {
             if (value != 0 && value != 4 && value != 8) return DSPARK_ERR_INVALID_ARG;
             k.mfma_waves = (int)value;
             return DSPARK_OK;
+        case DSPARK_DEBUG_TOPK_SPLIT: k.topk_split = value != 0; return DSPARK_OK;
         case DSPARK_DEBUG_STAMPS:
             if (value & 7) return DSPARK_ERR_INVALID_ARG;
             k.stamps = (uintptr_t)value;

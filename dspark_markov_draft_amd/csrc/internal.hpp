@@ -39,6 +39,7 @@ struct DebugKnobs {
     uintptr_t stamps = 0;
     int force_path = 0;
     int mfma_waves = 0;
+    int topk_split = 0;
 };
 DebugKnobs& debug_knobs();
 

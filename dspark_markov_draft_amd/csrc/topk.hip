@@ -163,12 +163,28 @@ __device__ __forceinline__ float4 load_group_clamped(const SelectParams& p, cons
     }
 }
 
-template <bool VEC>
+// A candidate list entry holds its vocabulary index + 1: the lists are zero between calls, so a
+// non-zero entry is a written one. Entries are written once per call with device-scope stores
+// (write-through, seen by device-scope loads from any XCD), so the walk of the same launch can
+// read each entry as soon as it is non-zero.
+__device__ __forceinline__ void put_cand(int32_t* out, uint32_t pos, uint32_t v) {
+    __hip_atomic_store(out + pos, (int32_t)(v + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// -inf over group g of the dense output row. COH: device-scope 8-byte stores, complete at the
+// device's coherence point when they are acknowledged, so that a walk of the same launch on
+// another XCD can then overwrite the candidates' entries without a cache write-back between.
+template <bool VEC, bool COH = false>
 __device__ __forceinline__ void fill_group(const SelectParams& p, int64_t row, int g) {
     const int i = 4 * g;
+    constexpr uint64_t NEG_INF_BF16X4 = 0xFF80FF80FF80FF80ull;
+    constexpr uint64_t NEG_INF_F32X2 = 0xFF800000FF800000ull;
     if (p.fill_bf16) {
         uint16_t* o = p.fill_bf16 + row * p.V + i;
-        if constexpr (VEC) {
+        if constexpr (VEC && COH) {
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(o), NEG_INF_BF16X4, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        } else if constexpr (VEC) {
             *reinterpret_cast<uint2*>(o) = make_uint2(0xFF80FF80u, 0xFF80FF80u);
         } else {
             for (int u = 0; u < 4; ++u)
@@ -177,7 +193,11 @@ __device__ __forceinline__ void fill_group(const SelectParams& p, int64_t row, i
     }
     if (p.fill_f32) {
         float* o = p.fill_f32 + row * p.V + i;
-        if constexpr (VEC) {
+        if constexpr (VEC && COH) {
+            uint64_t* o2 = reinterpret_cast<uint64_t*>(o);
+            __hip_atomic_store(o2, NEG_INF_F32X2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(o2 + 1, NEG_INF_F32X2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if constexpr (VEC) {
             *reinterpret_cast<float4*>(o) = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         } else {
             for (int u = 0; u < 4; ++u)
@@ -243,7 +263,7 @@ __device__ __forceinline__ void emit_from_buffer(const uint64_t* buf, const uint
         const bool in = e < (uint32_t)BUF_CAP && buf_slot(cnt, e) && buf[e] >= kth &&
                         (buf[e] >> L1_SHIFT) == bin;
         const uint32_t po = wave_append(n_out, in, lane);
-        if (in && po < (uint32_t)k) out[po] = (int32_t)composite_index(buf[e]);
+        if (in && po < (uint32_t)k) put_cand(out, po, composite_index(buf[e]));
     }
 }
 
@@ -293,7 +313,7 @@ __device__ __forceinline__ void select_fallback(const SelectParams& p, const flo
             const uint32_t bin = top_bin(e[u]);
             const bool hi = valid && bin > d1, eq = valid && bin == d1;
             const uint32_t po = wave_append(n_out, hi, lane);
-            if (hi && po < (uint32_t)p.k) out[po] = i;
+            if (hi && po < (uint32_t)p.k) put_cand(out, po, (uint32_t)i);
             const uint32_t pb = wave_append(n_buf, eq, lane);
             if (eq && pb < (uint32_t)BUF_CAP) buf[pb] = composite_key(e[u], (uint32_t)i);
         }
@@ -354,15 +374,17 @@ __device__ __forceinline__ void select_fallback(const SelectParams& p, const flo
             const uint64_t ck = composite_key(e[u], (uint32_t)i);
             const bool in = g < ngroups && i < p.V && (ck >> L1_SHIFT) == d1 && ck >= kth;
             const uint32_t po = wave_append(n_out, in, lane);
-            if (in && po < (uint32_t)p.k) out[po] = i;
+            if (in && po < (uint32_t)p.k) put_cand(out, po, (uint32_t)i);
         }
     }
 }
 
 // (2 workgroups per CU: at most 128 VGPRs, i.e. 4 waves per SIMD)
-template <bool VEC, bool TIMED>
-__global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const SelectParams p) {
-    extern __shared__ __align__(16) unsigned char smem[];
+// The k best keys of one base row (all threads of a workgroup of SEL_THREADS), with the row's
+// -inf fill when asked for; smem holds SEL_LDS_BYTES.
+template <bool VEC, bool TIMED, bool COH = false>
+__device__ __forceinline__ void select_row(const SelectParams& p, const int64_t row,
+                                           unsigned char* smem) {
     uint64_t* buf = reinterpret_cast<uint64_t*>(smem);
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + BUF_CAP * 8);
     uint32_t* sh = hist + L1_BINS;  // [0] digit, [1] count above, [2] n_out, [3] n_buf,
@@ -370,7 +392,6 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
                                     // counts of the compaction
     uint32_t* cnt = sh + 8;         // [8 .. 15] keys per wave region
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-    const int64_t row = blockIdx.x;
     const float* x = p.base + row * p.V;
     int32_t* out = p.cand + row * p.k;
     const int ngroups = (p.V + 3) / 4;
@@ -411,7 +432,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 if (VEC || 4 * g + u < p.V) atomicAdd(&hist[top_bin(e[u])], 1u);
-            fill_group<VEC>(p, row, g);
+            fill_group<VEC, COH>(p, row, g);
         }
     }
     __syncthreads();
@@ -493,7 +514,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         for (int u = 0; u < MU; ++u) {
             const int g = g0 + u * SEL_THREADS + tid;
             offer(cur[u], g, g < ngroups);
-            if (g < ngroups) fill_group<VEC>(p, row, g);
+            if (g < ngroups) fill_group<VEC, COH>(p, row, g);
         }
 #pragma unroll
         for (int u = 0; u < MU; ++u) {
@@ -504,7 +525,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         for (int u = 0; u < MU; ++u) {
             const int g = g0 + BATCH + u * SEL_THREADS + tid;
             offer(nxt[u], g, g < ngroups);
-            if (g < ngroups) fill_group<VEC>(p, row, g);
+            if (g < ngroups) fill_group<VEC, COH>(p, row, g);
         }
     }
     // the region's pairs to order keys, counted in the histogram of the offered keys
@@ -517,6 +538,9 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
             region[e] = composite_key(v, (uint32_t)(r >> 32));
         }
     }
+    // COH: every -inf fill store of the row is acknowledged before any candidate entry is
+    // written (those come after this barrier), so a reader that sees an entry also sees the fill
+    if constexpr (COH) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0) cnt[wave] = n_region;
     __syncthreads();
     tk_stamp<TIMED>(p.stamps, row * 8 + 2);
@@ -595,7 +619,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         const bool hi = e < n_mine && bin > d1, eq = e < n_mine && bin == d1;
         const uint64_t mh = __ballot(hi), me = __ballot(eq);
         const uint32_t ph = off_hi + lanes_below(mh), pe = off_eq + lanes_below(me);
-        if (hi && ph < (uint32_t)p.k) out[ph] = (int32_t)composite_index(ck);
+        if (hi && ph < (uint32_t)p.k) put_cand(out, ph, composite_index(ck));
         if (eq && pe < SMALL_CAP) small[pe] = ck;
         off_hi += (uint32_t)__popcll(mh);
         off_eq += (uint32_t)__popcll(me);
@@ -611,7 +635,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
             const uint32_t e = e0 + tid;
             const bool in = e < m && small[e] >= kth;
             const uint32_t po = wave_append(sh + 2, in, lane);
-            if (in && po < (uint32_t)p.k) out[po] = (int32_t)composite_index(small[e]);
+            if (in && po < (uint32_t)p.k) put_cand(out, po, composite_index(small[e]));
         }
     } else {
         // radix levels over the whole buffer (still intact)
@@ -620,6 +644,12 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const Selec
         emit_from_buffer(buf, cnt, kth, d1, out, sh + 2, p.k, tid, lane);
     }
     tk_stamp<TIMED>(p.stamps, row * 8 + 4);
+}
+
+template <bool VEC, bool TIMED>
+__global__ __launch_bounds__(SEL_THREADS, 4) void topk_select_kernel(const SelectParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    select_row<VEC, TIMED>(p, blockIdx.x, smem);
 }
 
 struct TopkWalkParams {
@@ -668,6 +698,28 @@ __device__ __forceinline__ int row16_sum_i32(int x) {
     return x;
 }
 
+// The exact int32 dot of W1 codes with the W2 row of this lane's candidate: lane group r's 16
+// lanes hold the rows of candidates 4i + r in load i, each lane one 16-byte chunk; lane 16r + i
+// ends with candidate 4i + r's sum, 16 * (high digits' products) + (low digits' products).
+__device__ __forceinline__ int cand_dot(const CandBlock& blk, const int4 wc, const int4 wl,
+                                        int lane) {
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < RANK / 16; ++i) {
+        int d = __builtin_amdgcn_sdot4(blk.q[i].x, wc.x, 0, false);
+        d = __builtin_amdgcn_sdot4(blk.q[i].y, wc.y, d, false);
+        d = __builtin_amdgcn_sdot4(blk.q[i].z, wc.z, d, false);
+        d = __builtin_amdgcn_sdot4(blk.q[i].w, wc.w, d, false);
+        d = __builtin_amdgcn_sdot4(blk.q[i].x, wl.x, d << 4, false);
+        d = __builtin_amdgcn_sdot4(blk.q[i].y, wl.y, d, false);
+        d = __builtin_amdgcn_sdot4(blk.q[i].z, wl.z, d, false);
+        d = __builtin_amdgcn_sdot4(blk.q[i].w, wl.w, d, false);
+        d = row16_sum_i32(d);
+        acc = (lane & 15) == i ? d : acc;
+    }
+    return acc;
+}
+
 // MULTI: k > TKW_THREADS, candidates in several chunks per step, loaded as they are scored;
 // otherwise one candidate per thread, the next step's loaded while this step is scored.
 // PRUNE (greedy only): the lossless top-k pruned walk. Its result is the dense greedy walk's:
@@ -707,7 +759,7 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
     const int own = (lane & 15) * 4 + (lane >> 4);  // this lane's candidate within the wave's 64
     // raw index of candidate j of step t (j clamped into the list; load_block bounds the value)
     auto cand_index = [&](int t, int j) -> uint32_t {
-        return (uint32_t)req_cand[(int64_t)t * p.k + min(j, p.k - 1)];
+        return (uint32_t)req_cand[(int64_t)t * p.k + min(j, p.k - 1)] - 1u;
     };
     auto load_block = [&](int t, uint32_t own_idx, CandBlock& blk) {
         const uint32_t v = own_idx < (uint32_t)p.V ? own_idx : 0u;  // always: select emits rows
@@ -769,21 +821,7 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
         uint64_t best = 0;
         float min_base = INFINITY;
         auto score = [&](const CandBlock& blk, bool has) {
-            int acc = 0;
-#pragma unroll
-            for (int i = 0; i < RANK / 16; ++i) {
-                // 16 * (high digits' products) + (low digits' products), summed over the row
-                int d = __builtin_amdgcn_sdot4(blk.q[i].x, wc.x, 0, false);
-                d = __builtin_amdgcn_sdot4(blk.q[i].y, wc.y, d, false);
-                d = __builtin_amdgcn_sdot4(blk.q[i].z, wc.z, d, false);
-                d = __builtin_amdgcn_sdot4(blk.q[i].w, wc.w, d, false);
-                d = __builtin_amdgcn_sdot4(blk.q[i].x, wl.x, d << 4, false);
-                d = __builtin_amdgcn_sdot4(blk.q[i].y, wl.y, d, false);
-                d = __builtin_amdgcn_sdot4(blk.q[i].z, wl.z, d, false);
-                d = __builtin_amdgcn_sdot4(blk.q[i].w, wl.w, d, false);
-                d = row16_sum_i32(d);
-                acc = (lane & 15) == i ? d : acc;
-            }
+            const int acc = cand_dot(blk, wc, wl, lane);
             const float l = walk_logit(blk.base, blk.s, sb, acc);
             uint64_t key;
             const int64_t off = row * p.V + blk.v;
@@ -882,6 +920,177 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
     for (int i = tid; i < p.T * p.k; i += TKW_THREADS) clr[i] = 0;
 }
 
+// ---- select and walk in one launch (k <= TKW_THREADS, rows that allow float4 loads) ----------
+// Rows are listed in step-major order (every request's step 0 first), and the workgroups of step 0
+// then walk their request. The dispatcher places the first F = min(rows, CUs) workgroups one per
+// CU and the rest second on CUs in the same order, so the last of the first F hold a CU alone.
+// Those take the step-0 rows (their rows finish soonest, and the walks run without a select on
+// their CU); the others among the first F take steps 1, 2, ... in order; the workgroups placed
+// second take the remaining rows in reverse, so that the rows finishing last belong to the last
+// steps. Any order is correct; this one makes the walks wait least. A step reads its row's candidate entries as soon
+// as they are written (non-zero, see put_cand), and the row's -inf fill is complete by then (the
+// fill stores are acknowledged before the first entry is written). The walk of a request thus
+// starts as soon as its first row is selected, while the rows of later steps are still being read:
+// in the two-launch form every walk waits for the last row of the whole batch. Workgroups are
+// dispatched in index order and only the bs walkers wait, so a row's workgroup is always resident
+// or dispatched once another finishes; each wait is still bounded in time (it then flags
+// DSPARK_ERR_TIMEOUT and goes on).
+struct FusedParams {
+    SelectParams s;
+    TopkWalkParams w;
+    const uint32_t* never;  // a word that stays zero (test hook: waits that cannot end)
+    uint32_t spin_ticks;
+    int wait_unset;
+    int first_slots;        // the device's compute units (at least bs)
+};
+
+// A candidate entry of step `row`: a device-scope load (no stale line of another call serves it).
+__device__ __forceinline__ uint32_t load_entry(const TopkWalkParams& p, int64_t row, int j) {
+    return (uint32_t)__hip_atomic_load(p.cand + row * p.k + min(j, p.k - 1), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-wide wait until every lane's entry `e` (loaded earlier) is written; reloads it meanwhile.
+// The compiler barrier keeps the loads that use the entry below the loop.
+__device__ __forceinline__ uint32_t wait_entry(const FusedParams& fp, uint32_t e, int64_t row,
+                                               int j, int lane) {
+    const WaitBound wait;
+    while (true) {
+        const uint64_t now = WaitBound::now();
+        bool ok = e != 0;
+        if (fp.wait_unset)
+            ok = ok && __hip_atomic_load(fp.never, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+        if (__all(ok)) break;
+        if (wait.expired(now, fp.spin_ticks)) {
+            if (lane == 0) flag_error(fp.w.err, DSPARK_ERR_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        e = load_entry(fp.w, row, j);
+    }
+    asm volatile("" ::: "memory");
+    return e;
+}
+
+template <int SAMPLE, int W1T, bool TIMED>
+__global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedParams fp) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const TopkWalkParams& p = fp.w;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+    const int i = blockIdx.x, n = p.bs * p.T;
+    const int F = n < fp.first_slots ? n : fp.first_slots;   // >= bs
+    const int lin = i < F - p.bs ? i + p.bs : i < F ? i - (F - p.bs) : F + (n - 1 - i);
+    const int t0 = lin / p.bs, b = lin - t0 * p.bs;
+    select_row<true, TIMED, true>(fp.s, (int64_t)b * p.T + t0, smem);
+    if (t0 != 0) return;
+    __syncthreads();  // the select's LDS is free from here on
+
+    // the walk of request b
+    uint32_t* w1q = reinterpret_cast<uint32_t*>(smem) + wave * (RANK / 4);   // high digits
+    uint32_t* w1l = w1q + SEL_WAVES * (RANK / 4);                            // low digits
+    uint64_t* wkeys = reinterpret_cast<uint64_t*>(smem + 2 * SEL_WAVES * RANK);  // [2][waves]
+    const int64_t st0 = TK_WALK_STAMPS0 + (int64_t)b * 40;
+    tk_stamp<TIMED>(p.stamps, st0);
+    int prev = p.start[b];
+    if (prev < 0 || prev >= p.V) {
+        if (tid == 0) flag_error(p.err, DSPARK_ERR_INVALID_ARG);
+        prev = 0;
+    }
+    uint64_t seed = 0, P0 = 0;
+    float rtemp = 1.0f;
+    if constexpr (SAMPLE) {
+        seed = p.seeds[b];
+        P0 = p.positions ? (uint64_t)p.positions[b] : 0;
+        rtemp = inv_temperature(p.temps[b]);
+    }
+    const int own = (lane & 15) * 4 + (lane >> 4);  // this lane's candidate within the wave's 64
+    const int j = wave * WAVE + own;
+    const bool has = j < p.k;
+    const int64_t row0 = (int64_t)b * p.T;
+    // Step t's candidate rows from its entry e (written): W2 row (whole lines per load, as in the
+    // two-launch walk), scale and base logit.
+    CandBlock blk;
+    auto load_rows = [&](int t, uint32_t e) {
+        const uint32_t ci = e - 1u;
+        const uint32_t v = ci < (uint32_t)p.V ? ci : 0u;
+        blk.v = v;
+        blk.s = p.scale[v];
+        blk.base = p.base[(row0 + t) * p.V + v];
+        const int c = lane & 15;
+#pragma unroll
+        for (int r = 0; r < RANK / 16; ++r) {
+            const uint32_t vi = (uint32_t)__shfl((int)v, (lane & 48) | r);
+            blk.q[r] = reinterpret_cast<const int4*>(p.q + (int64_t)vi * RANK)[c];
+        }
+    };
+    // The entry of the next step is loaded a step ahead, without waiting: when its step comes it
+    // has usually been written already, and then the rows load without a dependent entry load.
+    uint32_t e_next = 0;
+    load_rows(0, wait_entry(fp, load_entry(p, row0, j), row0, j, lane));
+    if (p.T > 1) e_next = load_entry(p, row0 + 1, j);
+    for (int t = 0; t < p.T; ++t) {
+        const int64_t row = row0 + t;
+        const float4 w = load4_as_f32<W1T>(p.w1, (int64_t)prev * RANK + lane * 4);
+        float a = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+        a = wave_max_nonneg_f32(a);
+        const float inv = w1_code_scale(a);
+        const float sb = w1_code_step(a);
+        uint32_t lo, nib;
+        w1q[lane] = pack_codes(w, inv, lo, nib);
+        w1l[lane] = lo;
+        tk_stamp<TIMED>(p.stamps, st0 + 1 + 2 * t);
+        const int4 wc = reinterpret_cast<const int4*>(w1q)[lane & 15];
+        const int4 wl = reinterpret_cast<const int4*>(w1l)[lane & 15];
+        const int acc = cand_dot(blk, wc, wl, lane);
+        const float l = walk_logit(blk.base, blk.s, sb, acc);
+        const int64_t off = row * p.V + blk.v;
+        uint64_t key;
+        if constexpr (!SAMPLE) {
+            if (has && p.out_f32) p.out_f32[off] = l;
+            key = argmax_key(l, blk.v);
+        } else {
+            const uint32_t h = bf16_bits(l);
+            if (has) p.out_bf16[off] = (uint16_t)h;
+            const float xs = bf16_value(h) * rtemp;
+            const float g = gumbel_from_word(noise_word(seed, P0 + (uint64_t)t, blk.v));
+            key = argmax_key(xs + g, blk.v);
+        }
+        // the next step's rows load while this step's argmax is combined
+        if (t + 1 < p.T) {
+            load_rows(t + 1, wait_entry(fp, e_next, row + 1, j, lane));
+            if (t + 2 < p.T) e_next = load_entry(p, row + 2, j);
+        }
+        const uint64_t best = wave_max_u64(has ? key : 0ull);
+        if (lane == 0) wkeys[(t & 1) * SEL_WAVES + wave] = best;
+        __syncthreads();
+        uint64_t m = wkeys[(t & 1) * SEL_WAVES];
+#pragma unroll
+        for (int w2 = 1; w2 < SEL_WAVES; ++w2) {
+            const uint64_t o = wkeys[(t & 1) * SEL_WAVES + w2];
+            m = o > m ? o : m;
+        }
+        // every candidate at -inf: the dense row is -inf throughout, whose first max is 0
+        uint32_t token = (uint32_t)(m >> 32) <= ORDER_KEY_NEG_INF ? 0u : key_index(m);
+        if (token >= (uint32_t)p.V) token = 0;
+        if (tid == 0) p.tokens[b * p.T + t] = (int32_t)token;
+        prev = (int)token;
+        tk_stamp<TIMED>(p.stamps, st0 + 2 + 2 * t);
+    }
+    // Every entry of this request has been read before the last barrier: clear them, so that the
+    // workspace is all zero again.
+    __syncthreads();
+    int32_t* clr = p.cand + row0 * p.k;
+    for (int e = tid; e < p.T * p.k; e += SEL_THREADS) clr[e] = 0;
+}
+
+template <int SAMPLE>
+static const void* topk_fused_fn(int w1t, bool timed) {
+    if (timed && w1t == DT_BF16) return reinterpret_cast<const void*>(&topk_fused_kernel<SAMPLE, DT_BF16, true>);
+    if (w1t == DT_F32) return reinterpret_cast<const void*>(&topk_fused_kernel<SAMPLE, DT_F32, false>);
+    if (w1t == DT_BF16) return reinterpret_cast<const void*>(&topk_fused_kernel<SAMPLE, DT_BF16, false>);
+    return reinterpret_cast<const void*>(&topk_fused_kernel<SAMPLE, DT_F16, false>);
+}
+
 template <bool MULTI>
 static const void* pruned_walk_fn(int w1t) {
     if (w1t == DT_F32) return reinterpret_cast<const void*>(&topk_walk_kernel<0, DT_F32, MULTI, false, true>);
@@ -919,20 +1128,7 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
     const bool vec = (w.V % 4 == 0) && ((uintptr_t)w.base % 16 == 0);
     sp.stamps = reinterpret_cast<uint64_t*>(debug_knobs().stamps);
     const bool timed = sp.stamps != nullptr;
-    void* sargs[] = {&sp};
-    const void* sel = vec ? (timed ? reinterpret_cast<const void*>(&topk_select_kernel<true, true>)
-                                   : reinterpret_cast<const void*>(&topk_select_kernel<true, false>))
-                          : reinterpret_cast<const void*>(&topk_select_kernel<false, false>);
-    if (hipFuncSetAttribute(sel, hipFuncAttributeMaxDynamicSharedMemorySize, SEL_LDS_BYTES) !=
-        hipSuccess) {
-        (void)hipGetLastError();
-    }
-    hipError_t e = launch_walk_kernel(sel, dim3((unsigned)(w.bs * w.T)), dim3(SEL_THREADS), sargs,
-                                      (size_t)SEL_LDS_BYTES, stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return DSPARK_ERR_LAUNCH;
-    }
+    const int w1t = w.w1_dtype == DSPARK_F32 ? DT_F32 : w.w1_dtype == DSPARK_BF16 ? DT_BF16 : DT_F16;
 
     TopkWalkParams kp = {};
     kp.q = w.q;
@@ -955,7 +1151,50 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
     kp.T = w.T;
     kp.V = w.V;
     kp.k = a.k;
-    const int w1t = w.w1_dtype == DSPARK_F32 ? DT_F32 : w.w1_dtype == DSPARK_BF16 ? DT_BF16 : DT_F16;
+
+    if (vec && !a.w2_bound && a.k <= TKW_THREADS && !debug_knobs().topk_split) {
+        // select and walk in one launch
+        FusedParams fp = {};
+        fp.s = sp;
+        fp.w = kp;
+        fp.never = reinterpret_cast<const uint32_t*>(ws + WS_ERR + 4);
+        const DebugKnobs& dbg = debug_knobs();
+        fp.spin_ticks = dbg.spin_ticks ? dbg.spin_ticks : DEFAULT_SPIN_TICKS;
+        fp.wait_unset = dbg.wait_unset ? 1 : 0;
+        DeviceInfo dev;
+        if (current_device_info(&dev) != DSPARK_OK) return DSPARK_ERR_NO_DEVICE;
+        fp.first_slots = dev.cus > w.bs ? dev.cus : w.bs;
+        const void* fn = w.sample ? topk_fused_fn<1>(w1t, timed) : topk_fused_fn<0>(w1t, timed);
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SEL_LDS_BYTES) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+        }
+        void* fargs[] = {&fp};
+        const hipError_t fe = launch_walk_kernel(fn, dim3((unsigned)(w.bs * w.T)),
+                                                 dim3(SEL_THREADS), fargs,
+                                                 (size_t)SEL_LDS_BYTES, stream);
+        if (fe != hipSuccess) {
+            (void)hipGetLastError();
+            return DSPARK_ERR_LAUNCH;
+        }
+        return DSPARK_OK;
+    }
+
+    void* sargs[] = {&sp};
+    const void* sel = vec ? (timed ? reinterpret_cast<const void*>(&topk_select_kernel<true, true>)
+                                   : reinterpret_cast<const void*>(&topk_select_kernel<true, false>))
+                          : reinterpret_cast<const void*>(&topk_select_kernel<false, false>);
+    if (hipFuncSetAttribute(sel, hipFuncAttributeMaxDynamicSharedMemorySize, SEL_LDS_BYTES) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+    }
+    hipError_t e = launch_walk_kernel(sel, dim3((unsigned)(w.bs * w.T)), dim3(SEL_THREADS), sargs,
+                                      (size_t)SEL_LDS_BYTES, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return DSPARK_ERR_LAUNCH;
+    }
+
     void* kargs[] = {&kp};
     const void* fn = a.w2_bound ? (a.k > TKW_THREADS ? pruned_walk_fn<true>(w1t)
                                                      : pruned_walk_fn<false>(w1t))

@@ -214,6 +214,10 @@ int dspark_walk_sample_icdf(const int8_t* w2_q, const float* w2_scale, const voi
  * vocabulary index.
  *   draft_logits: sample = 1: bf16 [bs, T, V] (required); sample = 0: fp32 [bs, T, V] or NULL
  *   1 <= k <= min(V, DSPARK_MAX_TOPK); base logits must not hold NaN (result undefined)
+ * With k <= 512 and V % 4 == 0 (16-byte aligned base rows) the select and the walk run in one
+ * launch: each request's walk starts once its first row is selected and waits (bounded in time,
+ * as the dense walks' waits) for the rows of later steps. Otherwise two launches: every row's
+ * select, then the walks. Both forms give the same results.
  */
 int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
                      const float* base_logits, const int32_t* start_tokens, int64_t bs,
@@ -319,10 +323,11 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
 /*
  * Test hooks (process-wide, not thread-safe):
  *   DSPARK_DEBUG_MAX_WORKGROUPS: cap the dense walk's grid (0 = one per compute unit);
- *   DSPARK_DEBUG_SPIN_LIMIT: bound of each grid-wide wait, in ticks of the 100 MHz device clock,
- *       before DSPARK_ERR_TIMEOUT is recorded (0 = the default, 10 ms; at most 2^32 - 1);
- *   DSPARK_DEBUG_WAIT_UNSET_FLAG: non-zero makes the grid-wide waits also wait for a workspace
- *       flag that nothing sets, so each runs into its time bound (for the timeout test);
+ *   DSPARK_DEBUG_SPIN_LIMIT: bound of each grid-wide wait (and of the one-launch top-k walk's
+ *       waits for its rows), in ticks of the 100 MHz device clock, before DSPARK_ERR_TIMEOUT is
+ *       recorded (0 = the default, 10 ms; at most 2^32 - 1);
+ *   DSPARK_DEBUG_WAIT_UNSET_FLAG: non-zero makes those waits also wait for a workspace flag
+ *       that nothing sets, so each runs into its time bound (for the timeout tests);
  *   DSPARK_DEBUG_FORCE_PATH: 0 chooses by batch size; DSPARK_PATH_DOT4 / DSPARK_PATH_MFMA force
  *       that kernel for every batch size, DSPARK_PATH_MFMA1 for one request whose slices fit it
  *       (all compute the same results);
@@ -340,7 +345,9 @@ int dspark_philox_words(uint64_t seed, uint64_t position, int64_t v0, int64_t n,
  *       which the dispatch records at the kernel's start and end (read them with
  *       dspark_kernel_times); 0 frees the ring. For benchmarks; not around graph capture;
  *   DSPARK_DEBUG_MFMA_WAVES: 0 = the library's choice; 4 or 8 forces the waves per workgroup of
- *       the multi-request MFMA kernel for slices of at most 624 rows (the same results).
+ *       the multi-request MFMA kernel for slices of at most 624 rows (the same results);
+ *   DSPARK_DEBUG_TOPK_SPLIT: non-zero runs top-k walks in two launches also where one would
+ *       serve (the same results).
  */
 enum dspark_debug_key {
     DSPARK_DEBUG_MAX_WORKGROUPS = 1,
@@ -349,7 +356,8 @@ enum dspark_debug_key {
     DSPARK_DEBUG_STAMPS = 4,
     DSPARK_DEBUG_FORCE_PATH = 5,
     DSPARK_DEBUG_KERNEL_TIMING = 6,
-    DSPARK_DEBUG_MFMA_WAVES = 7
+    DSPARK_DEBUG_MFMA_WAVES = 7,
+    DSPARK_DEBUG_TOPK_SPLIT = 8
 };
 int dspark_debug_set(int key, int64_t value);
 

@@ -348,6 +348,9 @@ def test_misc_validation():
     assert L.dspark_debug_set(B.DEBUG_FORCE_PATH, 4) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_STAMPS, 12) == B.ERR_INVALID_ARG
     assert L.dspark_debug_set(B.DEBUG_KERNEL_TIMING, 4097) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(B.DEBUG_TOPK_SPLIT, -1) == B.ERR_INVALID_ARG
+    assert L.dspark_debug_set(B.DEBUG_TOPK_SPLIT, 1) == B.OK
+    assert L.dspark_debug_set(B.DEBUG_TOPK_SPLIT, 0) == B.OK
     n = ctypes.c_int32(-1)
     buf = (ctypes.c_float * 4)()
     assert L.dspark_kernel_times(None, 4, ctypes.byref(n)) == B.ERR_INVALID_ARG

@@ -213,6 +213,55 @@ def test_topk_leaves_workspace_zeroed_for_dense_walks():
     assert dm.dspark_workspace_status(ws) == 0
 
 
+@pytest.fixture
+def split_knob_reset():
+    yield
+    dm.dspark_debug_set(B.DEBUG_TOPK_SPLIT, 0)
+    dm.dspark_debug_set(B.DEBUG_WAIT_UNSET_FLAG, 0)
+    dm.dspark_debug_set(B.DEBUG_SPIN_LIMIT, 0)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+@pytest.mark.parametrize("V,T,bs,k", [(20000, 3, 5, 512), (9000, 16, 3, 100), (6000, 1, 4, 300),
+                                      (151936, 7, 64, 512)])
+def test_topk_one_launch_equals_two_launches(V, T, bs, k, mode, split_knob_reset):
+    """The one-launch form (select and walk together, walks waiting for their rows) gives the
+    two-launch form's tokens and dense rows bit for bit, and leaves the workspace zeroed."""
+    sample = mode == "sample"
+    p = random_problem(V, T, bs, seed=V + T + k, temps=np.linspace(0.6, 1.4, bs).astype(np.float32),
+                       positions=np.arange(bs, dtype=np.int64) * 5)
+    qs = p.quantize()
+    ws = dm.new_workspace(bs, T, V, k)
+    one = p.topk(k, sample=sample, ws=ws, qs=qs)
+    assert int(ws.count_nonzero()) == 0
+    dm.dspark_debug_set(B.DEBUG_TOPK_SPLIT, 1)
+    two = p.topk(k, sample=sample, ws=ws, qs=qs)
+    assert dm.dspark_workspace_status(ws) == 0
+    assert np.array_equal(one[0], two[0])
+    assert np.array_equal(one[1].view(np.uint8), two[1].view(np.uint8))
+
+
+def test_topk_one_launch_wait_timeout_is_reported_and_recovers(split_knob_reset):
+    """The walks' waits for their rows are bounded: forced never to end, each runs into its
+    (small) bound, the kernel completes and records DSPARK_ERR_TIMEOUT (check_workspace raises
+    it and zeroes the workspace); the next call is exact."""
+    p = random_problem(8192, 3, 2, seed=23)
+    qs = p.quantize()
+    ws = dm.new_workspace(2, 3, 8192, 64)
+    dm.dspark_debug_set(B.DEBUG_SPIN_LIMIT, 200)
+    dm.dspark_debug_set(B.DEBUG_WAIT_UNSET_FLAG, 1)
+    p.topk(64, ws=ws, qs=qs)
+    dm.dspark_debug_set(B.DEBUG_WAIT_UNSET_FLAG, 0)
+    dm.dspark_debug_set(B.DEBUG_SPIN_LIMIT, 0)
+    with pytest.raises(B.DsparkError) as e:
+        dm.check_workspace(ws)
+    assert e.value.status == B.ERR_TIMEOUT
+    assert int(ws.count_nonzero()) == 0
+    tok, out = p.topk(64, ws=ws, qs=qs)
+    assert dm.dspark_workspace_status(ws) == 0
+    assert p.check_topk(64, tok, out).ok
+
+
 def test_topk_out_of_range_start_is_contained():
     p = random_problem(5000, 2, 2, seed=19)
     p.start = torch.tensor([3, 5000], dtype=torch.int32, device=DEV)
