@@ -618,11 +618,29 @@ def main():
                      "kernel": kernel},
         "w2_roofline": w2,
         "bounds": head_bounds,
+        "design": design_notes(plan),
         "evidence": evidence,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
     print(json.dumps(out), flush=True)
+
+
+def design_notes(plan):
+    """How the measured kernel departs from a packed-dot, LDS-resident, atomic-combine design
+    (each choice is backed by a measurement in the design notes)."""
+    if not plan:
+        return None
+    path = plan["path"]
+    return {
+        "int8_gemv": {1: "v_dot4 (lane per row)", 2: "v_mfma_i32_16x16x64_i8, 16-request tiles",
+                      3: "v_mfma_i32_16x16x64_i8, one request"}.get(path, "?"),
+        "w2_residency": (f"{plan['rows_in_registers']} rows per workgroup in registers "
+                         f"(MFMA / dot operands), {plan['rows_in_lds']} in LDS, "
+                         f"{plan['rows_streamed']} streamed"),
+        "combine": "per-workgroup u64 key slots polled with device-scope loads; no atomics",
+        "launch": "plain launch, one workgroup per CU, every wait bounded by 10 ms of device clock",
+    }
 
 
 def _case_dims(name):
