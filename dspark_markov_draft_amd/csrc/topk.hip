@@ -923,11 +923,13 @@ __global__ __launch_bounds__(TKW_THREADS) void topk_walk_kernel(const TopkWalkPa
 // ---- select and walk in one launch (k <= TKW_THREADS, rows that allow float4 loads) ----------
 // Rows are listed in step-major order (every request's step 0 first), and the workgroups of step 0
 // then walk their request. The dispatcher places the first F = min(rows, CUs) workgroups one per
-// CU and the rest second on CUs in the same order, so the last of the first F hold a CU alone.
-// Those take the step-0 rows (their rows finish soonest, and the walks run without a select on
-// their CU); the others among the first F take steps 1, 2, ... in order; the workgroups placed
-// second take the remaining rows in reverse, so that the rows finishing last belong to the last
-// steps. Any order is correct; this one makes the walks wait least. A step reads its row's candidate entries as soon
+// CU and the rest second on CUs in the same order, so the last of the first F hold a CU alone
+// when the rows fit two per CU. Those take the step-0 rows (their rows finish soonest, and the
+// walks run without a select on their CU); the others among the first F take steps 1, 2, ... in
+// order. When all rows fit two per CU, the workgroups placed second take the remaining rows in
+// reverse, so that the rows finishing last belong to the last steps. With more rows, the rest
+// keep step order: the workgroups dispatched as others finish then take the latest steps. Any
+// order is correct; this one makes the walks wait least. A step reads its row's candidate entries as soon
 // as they are written (non-zero, see put_cand), and the row's -inf fill is complete by then (the
 // fill stores are acknowledged before the first entry is written). The walk of a request thus
 // starts as soon as its first row is selected, while the rows of later steps are still being read:
@@ -979,7 +981,10 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedP
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
     const int i = blockIdx.x, n = p.bs * p.T;
     const int F = n < fp.first_slots ? n : fp.first_slots;   // >= bs
-    const int lin = i < F - p.bs ? i + p.bs : i < F ? i - (F - p.bs) : F + (n - 1 - i);
+    const int lin = i < F - p.bs ? i + p.bs
+                    : i < F      ? i - (F - p.bs)
+                    : n <= 2 * F ? F + (n - 1 - i)
+                                 : i;
     const int t0 = lin / p.bs, b = lin - t0 * p.bs;
     select_row<true, TIMED, true>(fp.s, (int64_t)b * p.T + t0, smem);
     if (t0 != 0) return;
@@ -1152,7 +1157,13 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
     kp.V = w.V;
     kp.k = a.k;
 
-    if (vec && !a.w2_bound && a.k <= TKW_THREADS && !debug_knobs().topk_split) {
+    // One launch pays when some rows are placed second on a CU: the walks then overlap their
+    // select. With at most one row per CU every row finishes at about the same time and the walk
+    // kernel alone, which loads each step's rows a step ahead, is faster.
+    DeviceInfo dev;
+    if (current_device_info(&dev) != DSPARK_OK) return DSPARK_ERR_NO_DEVICE;
+    if (vec && !a.w2_bound && a.k <= TKW_THREADS && (int64_t)w.bs * w.T > dev.cus &&
+        !debug_knobs().topk_split) {
         // select and walk in one launch
         FusedParams fp = {};
         fp.s = sp;
@@ -1161,8 +1172,6 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
         const DebugKnobs& dbg = debug_knobs();
         fp.spin_ticks = dbg.spin_ticks ? dbg.spin_ticks : DEFAULT_SPIN_TICKS;
         fp.wait_unset = dbg.wait_unset ? 1 : 0;
-        DeviceInfo dev;
-        if (current_device_info(&dev) != DSPARK_OK) return DSPARK_ERR_NO_DEVICE;
         fp.first_slots = dev.cus > w.bs ? dev.cus : w.bs;
         const void* fn = w.sample ? topk_fused_fn<1>(w1t, timed) : topk_fused_fn<0>(w1t, timed);
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SEL_LDS_BYTES) !=

@@ -214,10 +214,11 @@ int dspark_walk_sample_icdf(const int8_t* w2_q, const float* w2_scale, const voi
  * vocabulary index.
  *   draft_logits: sample = 1: bf16 [bs, T, V] (required); sample = 0: fp32 [bs, T, V] or NULL
  *   1 <= k <= min(V, DSPARK_MAX_TOPK); base logits must not hold NaN (result undefined)
- * With k <= 512 and V % 4 == 0 (16-byte aligned base rows) the select and the walk run in one
- * launch: each request's walk starts once its first row is selected and waits (bounded in time,
- * as the dense walks' waits) for the rows of later steps. Otherwise two launches: every row's
- * select, then the walks. Both forms give the same results.
+ * With k <= 512, V % 4 == 0 (16-byte aligned base rows) and more (request, step) rows than the
+ * device has compute units, the select and the walk run in one launch: each request's walk
+ * starts once its first row is selected and waits (bounded in time, as the dense walks' waits)
+ * for the rows of later steps. Otherwise two launches: every row's select, then the walks. Both
+ * forms give the same results.
  */
 int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, int w1_dtype,
                      const float* base_logits, const int32_t* start_tokens, int64_t bs,

@@ -222,11 +222,12 @@ def split_knob_reset():
 
 
 @pytest.mark.parametrize("mode", ["greedy", "sample"])
-@pytest.mark.parametrize("V,T,bs,k", [(20000, 3, 5, 512), (9000, 16, 3, 100), (6000, 1, 4, 300),
-                                      (151936, 7, 64, 512)])
+@pytest.mark.parametrize("V,T,bs,k", [(20000, 5, 60, 512), (9000, 16, 20, 100), (6000, 9, 32, 300),
+                                      (151936, 7, 64, 512), (12000, 16, 40, 256)])
 def test_topk_one_launch_equals_two_launches(V, T, bs, k, mode, split_knob_reset):
-    """The one-launch form (select and walk together, walks waiting for their rows) gives the
-    two-launch form's tokens and dense rows bit for bit, and leaves the workspace zeroed."""
+    """The one-launch form (select and walk together, walks waiting for their rows; used for more
+    (request, step) rows than compute units: all shapes here) gives the two-launch form's tokens
+    and dense rows bit for bit, and leaves the workspace zeroed."""
     sample = mode == "sample"
     p = random_problem(V, T, bs, seed=V + T + k, temps=np.linspace(0.6, 1.4, bs).astype(np.float32),
                        positions=np.arange(bs, dtype=np.int64) * 5)
@@ -245,9 +246,9 @@ def test_topk_one_launch_wait_timeout_is_reported_and_recovers(split_knob_reset)
     """The walks' waits for their rows are bounded: forced never to end, each runs into its
     (small) bound, the kernel completes and records DSPARK_ERR_TIMEOUT (check_workspace raises
     it and zeroes the workspace); the next call is exact."""
-    p = random_problem(8192, 3, 2, seed=23)
+    p = random_problem(4096, 5, 64, seed=23)      # 320 rows: the one-launch form
     qs = p.quantize()
-    ws = dm.new_workspace(2, 3, 8192, 64)
+    ws = dm.new_workspace(64, 5, 4096, 64)
     dm.dspark_debug_set(B.DEBUG_SPIN_LIMIT, 200)
     dm.dspark_debug_set(B.DEBUG_WAIT_UNSET_FLAG, 1)
     p.topk(64, ws=ws, qs=qs)
