@@ -158,6 +158,39 @@ __device__ __forceinline__ void load_entries(const float* trow, const uint16_t* 
     }
 }
 
+// The J groups of four entries a thread reads from a chunk (group j at x0 + 4 (j VT + thread)).
+// A chunk wholly inside the row takes the vector loads with no per-group branch, so that all of
+// them are in flight together; a per-group choice between vector and element loads made the
+// compiled code wait for each group's loads before issuing the next.
+template <int J, int VEC>
+__device__ __forceinline__ void load_chunk(const float* trow, const uint16_t* drow, int64_t base,
+                                           int V, float (&zp)[J][4], float (&zq)[J][4]) {
+    if (VEC && base + (int64_t)J * VT * 4 <= V) {
+        float4 a[J];
+        uint2 d[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int64_t x0 = base + (int64_t)(j * VT + threadIdx.x) * 4;
+            a[j] = *reinterpret_cast<const float4*>(trow + x0);
+            if (drow) d[j] = *reinterpret_cast<const uint2*>(drow + x0);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            zp[j][0] = a[j].x; zp[j][1] = a[j].y; zp[j][2] = a[j].z; zp[j][3] = a[j].w;
+            if (drow) {
+                zq[j][0] = bf16_lo(d[j].x); zq[j][1] = bf16_hi(d[j].x);
+                zq[j][2] = bf16_lo(d[j].y); zq[j][3] = bf16_hi(d[j].y);
+            } else {
+                zq[j][0] = zq[j][1] = zq[j][2] = zq[j][3] = -INFINITY;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        load_entries<VEC>(trow, drow, base + (int64_t)(j * VT + threadIdx.x) * 4, V, zp[j], zq[j]);
+}
+
 // ---- 1. row statistics ------------------------------------------------------------------
 template <int J, int VEC>
 __global__ __launch_bounds__(VT) void verify_stats_kernel(const VerifyParams p) {
@@ -169,9 +202,7 @@ __global__ __launch_bounds__(VT) void verify_stats_kernel(const VerifyParams p) 
     const uint16_t* drow = t < p.T ? p.draft + ((int64_t)b * p.T + t) * p.V : nullptr;
     const int64_t base = (int64_t)c * (J * VT * 4);
     float zp[J][4], zq[J][4];
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-        load_entries<VEC>(trow, drow, base + (int64_t)(j * VT + threadIdx.x) * 4, p.V, zp[j], zq[j]);
+    load_chunk<J, VEC>(trow, drow, base, p.V, zp, zq);
     float mp = -INFINITY, mq = -INFINITY;
 #pragma unroll
     for (int j = 0; j < J; ++j)
@@ -285,9 +316,7 @@ __global__ __launch_bounds__(VT) void verify_residual_kernel(const VerifyParams 
     const uint16_t* drow = p.draft + ((int64_t)b * p.T + i) * p.V;
     const int64_t base = (int64_t)c * (J * VT * 4);
     float zp[J][4], zq[J][4];
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-        load_entries<VEC>(trow, drow, base + (int64_t)(j * VT + threadIdx.x) * 4, p.V, zp[j], zq[j]);
+    load_chunk<J, VEC>(trow, drow, base, p.V, zp, zq);
     float R = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j)
@@ -373,9 +402,7 @@ __global__ __launch_bounds__(VT) void verify_mass_kernel(const VerifyParams p) {
     const uint16_t* drow = d.last ? nullptr : p.draft + ((int64_t)b * p.T + tau) * p.V;
     const int64_t base = (int64_t)c * (J * VT * 4);
     float zp[J][4], zq[J][4];
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-        load_entries<VEC>(trow, drow, base + (int64_t)(j * VT + threadIdx.x) * 4, p.V, zp[j], zq[j]);
+    load_chunk<J, VEC>(trow, drow, base, p.V, zp, zq);
     float mr = 0.0f, mpt = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j)
