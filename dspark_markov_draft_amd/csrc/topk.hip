@@ -1,28 +1,31 @@
 // The top-k Markov walk (vLLM PR #49969, Purpose: the drafter's logits restricted to the k
 // best candidates of the target's base logits and scattered into a dense -inf row; vLLM PR
-// #62958, Details: the unchanged sampler over that row). Two kernels on the caller's stream.
+// #62958, Details: the unchanged sampler over that row), on the caller's stream.
 //
-// topk_select_kernel, one workgroup per (request, step) row of base logits: the k largest base
-// logits, ties toward the lower vocabulary index. Every element gets a unique 51-bit key (the
-// 32-bit order key of its value above 19 bits of reversed index), so "the k largest keys" is
-// exactly the wanted set, and an MSB-first radix select finds the k-th key. The row is read
+// The select (select_row), one workgroup per (request, step) row of base logits: the k largest
+// base logits, ties toward the lower vocabulary index. Every element gets a unique 51-bit key
+// (the 32-bit order key of its value above 19 bits of reversed index), so "the k largest keys"
+// is exactly the wanted set, and an MSB-first radix select finds the k-th key. The row is read
 // from HBM once: its first 18432 elements stay in registers while their top-12-bit histogram
-// gives the bin L holding their k-th largest key; at least k keys of the row lie in bins >= L,
-// so the k-th key of the row does too. One pass over the rest of the row then appends every
-// element of a bin >= L to an LDS buffer, where 12- and 10-bit radix levels find the k-th key
-// and the winners are emitted. If the buffer overflows (rows sorted ascending, long plateaus),
-// an exact fallback takes two more passes: the histogram of the whole row, then the elements
-// above the k-th key's bin out directly and that bin to LDS (or, if that bin is itself too
-// large, its levels over the row in global memory). The first pass also writes -inf over the
-// dense output row when there is one.
+// gives a bound, the bin L of the chunk's ceil(2 k chunk / V)-th largest key (k itself when the
+// chunk is the whole row). One pass over the rest of the row then appends every element of a
+// bin >= L to an LDS buffer, where 12- and 10-bit radix levels find the k-th key and the winners
+// are emitted. If fewer than k keys reach L, or the buffer overflows (rows sorted ascending,
+// long plateaus, a chunk holding much of the top), an exact fallback takes two more passes: the
+// histogram of the whole row, then the elements above the k-th key's bin out directly and that
+// bin to LDS (or, if that bin is itself too large, its levels over the row in global memory).
+// The first pass also writes -inf over the dense output row when there is one.
 //
-// topk_walk_kernel, one workgroup per request, its steps in sequence (requests never wait for
-// each other): per step the wave-level int8 quantisation of W1[prev] used by the dense walk,
-// the v_dot4 logits of the step's k candidates with the dense walk's rounding, their values in
-// the dense output row, the sampler's noise keyed by vocabulary index, and the argmax over the
-// candidates, which equals the argmax of the dense row with -inf elsewhere. The candidates'
-// W2 rows, scales and base logits are loaded together with the step's W1 row, and the next
-// step's candidate indices one step ahead.
+// The walk, one workgroup per request, its steps in sequence (requests never wait for each
+// other): per step the wave-level int8 quantisation of W1[prev] used by the dense walk, the
+// v_dot4 logits of the step's k candidates with the dense walk's rounding, their values in the
+// dense output row, the sampler's noise keyed by vocabulary index, and the argmax over the
+// candidates, which equals the argmax of the dense row with -inf elsewhere.
+//
+// Two forms. topk_fused_kernel (k <= 512, float4 rows, more rows than compute units): one launch
+// in which the workgroups of step 0 walk their request once their own row is selected, reading
+// each later step's candidates as they are written. Otherwise topk_select_kernel, then
+// topk_walk_kernel, whose candidate rows for the next step load while the current step runs.
 #include "walk_common.hpp"
 
 namespace dspark {
