@@ -977,8 +977,12 @@ __device__ __forceinline__ uint32_t wait_entry(const FusedParams& fp, uint32_t e
     return e;
 }
 
-template <int SAMPLE, int W1T, bool TIMED>
+// PRUNE (greedy only): the lossless pruned walk, as in topk_walk_kernel. A step that is not
+// certified is computed over every row with few registers (the next step's candidate rows stay
+// where they are): each wave takes 8 rows per pass, two per 16-lane group.
+template <int SAMPLE, int W1T, bool TIMED, bool PRUNE = false>
 __global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedParams fp) {
+    static_assert(!(PRUNE && SAMPLE), "the pruned walk is greedy");
     extern __shared__ __align__(16) unsigned char smem[];
     const TopkWalkParams& p = fp.w;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
@@ -997,6 +1001,7 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedP
     uint32_t* w1q = reinterpret_cast<uint32_t*>(smem) + wave * (RANK / 4);   // high digits
     uint32_t* w1l = w1q + SEL_WAVES * (RANK / 4);                            // low digits
     uint64_t* wkeys = reinterpret_cast<uint64_t*>(smem + 2 * SEL_WAVES * RANK);  // [2][waves]
+    float* wmin = reinterpret_cast<float*>(wkeys + 2 * SEL_WAVES);              // [2][waves]
     const int64_t st0 = TK_WALK_STAMPS0 + (int64_t)b * 40;
     tk_stamp<TIMED>(p.stamps, st0);
     int prev = p.start[b];
@@ -1011,6 +1016,8 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedP
         P0 = p.positions ? (uint64_t)p.positions[b] : 0;
         rtemp = inv_temperature(p.temps[b]);
     }
+    const float w2_bound = PRUNE ? p.w2_bound[0] : 0.0f;
+    int dense_count = 0;
     const int own = (lane & 15) * 4 + (lane >> 4);  // this lane's candidate within the wave's 64
     const int j = wave * WAVE + own;
     const bool has = j < p.k;
@@ -1063,6 +1070,8 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedP
             const float g = gumbel_from_word(noise_word(seed, P0 + (uint64_t)t, blk.v));
             key = argmax_key(xs + g, blk.v);
         }
+        float min_base = INFINITY;
+        if constexpr (PRUNE) min_base = has ? blk.base : INFINITY;
         // the next step's rows load while this step's argmax is combined
         if (t + 1 < p.T) {
             load_rows(t + 1, wait_entry(fp, e_next, row + 1, j, lane));
@@ -1070,12 +1079,78 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedP
         }
         const uint64_t best = wave_max_u64(has ? key : 0ull);
         if (lane == 0) wkeys[(t & 1) * SEL_WAVES + wave] = best;
+        if constexpr (PRUNE) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) min_base = fminf(min_base, __shfl_xor(min_base, o, WAVE));
+            if (lane == 0) wmin[(t & 1) * SEL_WAVES + wave] = min_base;
+        }
         __syncthreads();
         uint64_t m = wkeys[(t & 1) * SEL_WAVES];
 #pragma unroll
         for (int w2 = 1; w2 < SEL_WAVES; ++w2) {
             const uint64_t o = wkeys[(t & 1) * SEL_WAVES + w2];
             m = o > m ? o : m;
+        }
+        if constexpr (PRUNE) {
+            float kth = wmin[(t & 1) * SEL_WAVES];
+#pragma unroll
+            for (int w2 = 1; w2 < SEL_WAVES; ++w2) kth = fminf(kth, wmin[(t & 1) * SEL_WAVES + w2]);
+            const float lstar = key_value(m);
+            const float reach = w2_bound * a;        // bound on any row's |bias| this step
+            const float margin = (fabsf(lstar) + fabsf(kth) + reach) * 0x1p-16f;
+            // false for any NaN or infinity (then the difference or the margin is not finite)
+            if (!(lstar - kth > reach + margin)) {
+                // Every row of the step, scored as the dense walk scores it: per pass, lane
+                // group g (lanes 16g .. 16g+15) takes rows r0 + 4i + g, i = 0..1, each lane one
+                // 16-byte chunk of W2; lane 16g + i then finishes row r0 + 4i + g.
+                const int g = lane >> 4, c = lane & 15;
+                const int4 wc2 = reinterpret_cast<const int4*>(w1q)[c];
+                const int4 wl2 = reinterpret_cast<const int4*>(w1l)[c];
+                uint64_t bestd = 0;
+#pragma unroll 1
+                for (int r0 = wave * 8; r0 < p.V; r0 += SEL_WAVES * 8) {
+                    int4 qv[2];
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int v = min(r0 + 4 * ii + g, p.V - 1);
+                        qv[ii] = reinterpret_cast<const int4*>(p.q + (int64_t)v * RANK)[c];
+                    }
+                    const int vr = r0 + 4 * (c & 1) + g;           // the row this lane finishes
+                    const int vc = min(vr, p.V - 1);
+                    const float sr = p.scale[vc], br = p.base[row * p.V + vc];
+                    int acc = 0;
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        int d = __builtin_amdgcn_sdot4(qv[ii].x, wc2.x, 0, false);
+                        d = __builtin_amdgcn_sdot4(qv[ii].y, wc2.y, d, false);
+                        d = __builtin_amdgcn_sdot4(qv[ii].z, wc2.z, d, false);
+                        d = __builtin_amdgcn_sdot4(qv[ii].w, wc2.w, d, false);
+                        d = __builtin_amdgcn_sdot4(qv[ii].x, wl2.x, d << 4, false);
+                        d = __builtin_amdgcn_sdot4(qv[ii].y, wl2.y, d, false);
+                        d = __builtin_amdgcn_sdot4(qv[ii].z, wl2.z, d, false);
+                        d = __builtin_amdgcn_sdot4(qv[ii].w, wl2.w, d, false);
+                        d = row16_sum_i32(d);
+                        acc = (c & 1) == ii ? d : acc;
+                    }
+                    if (c < 2 && vr < p.V) {
+                        const float l = walk_logit(br, sr, w1_code_step(a), acc);
+                        if (p.out_f32) p.out_f32[row * p.V + vr] = l;
+                        const uint64_t kd = argmax_key(l, (uint32_t)vr);
+                        bestd = kd > bestd ? kd : bestd;
+                    }
+                }
+                bestd = wave_max_u64(bestd);
+                __syncthreads();                     // every wave has read this step's keys
+                if (lane == 0) wkeys[(t & 1) * SEL_WAVES + wave] = bestd;
+                __syncthreads();
+                m = wkeys[(t & 1) * SEL_WAVES];
+#pragma unroll
+                for (int w2 = 1; w2 < SEL_WAVES; ++w2) {
+                    const uint64_t o = wkeys[(t & 1) * SEL_WAVES + w2];
+                    m = o > m ? o : m;
+                }
+                ++dense_count;
+            }
         }
         // every candidate at -inf: the dense row is -inf throughout, whose first max is 0
         uint32_t token = (uint32_t)(m >> 32) <= ORDER_KEY_NEG_INF ? 0u : key_index(m);
@@ -1084,11 +1159,19 @@ __global__ __launch_bounds__(SEL_THREADS, 4) void topk_fused_kernel(const FusedP
         prev = (int)token;
         tk_stamp<TIMED>(p.stamps, st0 + 2 + 2 * t);
     }
+    if constexpr (PRUNE)
+        if (tid == 0 && p.dense_steps) p.dense_steps[b] = dense_count;
     // Every entry of this request has been read before the last barrier: clear them, so that the
     // workspace is all zero again.
     __syncthreads();
     int32_t* clr = p.cand + row0 * p.k;
     for (int e = tid; e < p.T * p.k; e += SEL_THREADS) clr[e] = 0;
+}
+
+static const void* pruned_fused_fn(int w1t) {
+    if (w1t == DT_F32) return reinterpret_cast<const void*>(&topk_fused_kernel<0, DT_F32, false, true>);
+    if (w1t == DT_BF16) return reinterpret_cast<const void*>(&topk_fused_kernel<0, DT_BF16, false, true>);
+    return reinterpret_cast<const void*>(&topk_fused_kernel<0, DT_F16, false, true>);
 }
 
 template <int SAMPLE>
@@ -1165,7 +1248,7 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
     // kernel alone, which loads each step's rows a step ahead, is faster.
     DeviceInfo dev;
     if (current_device_info(&dev) != DSPARK_OK) return DSPARK_ERR_NO_DEVICE;
-    if (vec && !a.w2_bound && a.k <= TKW_THREADS && (int64_t)w.bs * w.T > dev.cus &&
+    if (vec && a.k <= TKW_THREADS && (int64_t)w.bs * w.T > dev.cus &&
         !debug_knobs().topk_split) {
         // select and walk in one launch
         FusedParams fp = {};
@@ -1176,7 +1259,9 @@ int launch_topk_walk(const TopkLaunch& a, hipStream_t stream) {
         fp.spin_ticks = dbg.spin_ticks ? dbg.spin_ticks : DEFAULT_SPIN_TICKS;
         fp.wait_unset = dbg.wait_unset ? 1 : 0;
         fp.first_slots = dev.cus > w.bs ? dev.cus : w.bs;
-        const void* fn = w.sample ? topk_fused_fn<1>(w1t, timed) : topk_fused_fn<0>(w1t, timed);
+        const void* fn = a.w2_bound ? pruned_fused_fn(w1t)
+                       : w.sample   ? topk_fused_fn<1>(w1t, timed)
+                                    : topk_fused_fn<0>(w1t, timed);
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, SEL_LDS_BYTES) !=
             hipSuccess) {
             (void)hipGetLastError();

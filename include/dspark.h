@@ -247,7 +247,8 @@ int dspark_walk_topk(const int8_t* w2_q, const float* w2_scale, const void* w1, 
  *               candidates, or every row of a step that was not certified), -inf elsewhere
  *   dense_steps [bs] int32 or NULL: per request, the number of steps computed over every row
  *   workspace of dspark_walk_workspace_bytes(bs, T, V, k) bytes (as dspark_walk_topk)
- * Base logits must not hold NaN (as dspark_walk_topk).
+ * Base logits must not hold NaN (as dspark_walk_topk). It runs on the top-k walk's kernels, in
+ * one launch or two under the same conditions as dspark_walk_topk.
  */
 int dspark_w2_prune_bound(const int8_t* w2_q, const float* w2_scale, int64_t V, int64_t rank,
                           float* bound, void* stream);

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import dspark_markov_draft_amd as dm
+import dspark_markov_draft_amd.binding as B
 import oracle
 from dspark_markov_draft_amd.synth import CASES, make_inputs
 from oracle.check import check_walk
@@ -118,6 +119,65 @@ def test_infinities_fall_back():
     assert np.array_equal(tok, dtok)
     assert tok[0, 0] == 10 and tok[1, 1] == 0 and tok[1, 2] == 77
     assert dense_steps.tolist() == [1, 2]
+
+
+@pytest.fixture
+def split_knob_reset():
+    yield
+    dm.dspark_debug_set(B.DEBUG_TOPK_SPLIT, 0)
+
+
+def _flat_odd_steps(p):
+    base = p.base_np.copy()
+    base[:, 1::2] *= 0.003                                # odd steps: flat rows
+    return Problem(p.w1_cpu, p.w2_cpu, base, p.start_np)
+
+
+@pytest.mark.parametrize("case", ["random", "flat", "flat_odd", "inf"])
+def test_pruned_one_launch(case, split_knob_reset):
+    """More (request, step) rows than compute units: the pruned walk runs in one launch with
+    the select. Against the dense walk and the oracle (as everywhere here), and bit for bit
+    against the two-launch form, dense_steps included; with steps that fall back to every row
+    (flat rows, infinities) as well as certified ones."""
+    if case == "random":
+        p, k = random_problem(20000, 5, 60, w_std=0.02, base_std=3.0, seed=61), 512
+    elif case == "flat":
+        p, k = random_problem(4096, 5, 64, w_std=0.05, base_std=0.01, seed=62), 64
+    elif case == "flat_odd":
+        p, k = _flat_odd_steps(random_problem(8000, 6, 48, w_std=0.05, seed=63)), 128
+    else:
+        p = random_problem(5000, 6, 50, seed=64)
+        base = p.base_np.copy()
+        base[0, 0, [10, 4000]] = np.inf
+        base[1, 1, :] = -np.inf
+        base[7, 2, 77] = np.inf
+        p, k = Problem(p.w1_cpu, p.w2_cpu, base, p.start_np), 32
+    qs = p.quantize()
+    bound = _bound(p, qs)
+    if case == "inf":
+        # (a -inf row has no finite logit to count, so the per-row count of _check_against_dense
+        # does not apply: tokens against the dense walk and the oracle)
+        tok, _, dense_steps = _pruned(p, k, qs, bound)
+        dtok, _ = p.greedy(qs=qs)
+        assert np.array_equal(tok, dtok)
+        q_o, s_o = p.oracle_q()
+        rep = check_walk(q_o, s_o, p.w1_np(), p.base_np, p.start_np, tok)
+        assert rep.ok, rep.summary()
+        assert tok[0, 0] == 10 and tok[1, 1] == 0 and tok[7, 2] == 77
+    else:
+        dense_steps, _ = _check_against_dense(p, k, qs, bound)
+    if case == "flat":
+        assert (dense_steps == p.shape[1]).all(), dense_steps
+    elif case == "flat_odd":
+        assert (dense_steps == 3).all(), dense_steps
+    elif case == "inf":
+        assert dense_steps[0] >= 1 and dense_steps[1] >= 1 and dense_steps[7] >= 1
+    one = _pruned(p, k, qs, bound)
+    dm.dspark_debug_set(B.DEBUG_TOPK_SPLIT, 1)
+    two = _pruned(p, k, qs, bound)
+    assert np.array_equal(one[0], two[0])
+    assert np.array_equal(one[1].view(np.uint32), two[1].view(np.uint32))
+    assert np.array_equal(one[2], two[2])
 
 
 @pytest.mark.parametrize("name,k", [("v151936_t7_bs1", 512), ("v151936_t7_bs16", 512),
