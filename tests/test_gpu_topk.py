@@ -223,7 +223,8 @@ def split_knob_reset():
 
 @pytest.mark.parametrize("mode", ["greedy", "sample"])
 @pytest.mark.parametrize("V,T,bs,k", [(20000, 5, 60, 512), (9000, 16, 20, 100), (6000, 9, 32, 300),
-                                      (151936, 7, 64, 512), (12000, 16, 40, 256)])
+                                      (151936, 7, 64, 512), (12000, 16, 40, 256),
+                                      (3000, 5, 64, 1), (512, 6, 60, 512)])
 def test_topk_one_launch_equals_two_launches(V, T, bs, k, mode, split_knob_reset):
     """The one-launch form (select and walk together, walks waiting for their rows; used for more
     (request, step) rows than compute units: all shapes here) gives the two-launch form's tokens
@@ -240,6 +241,16 @@ def test_topk_one_launch_equals_two_launches(V, T, bs, k, mode, split_knob_reset
     assert dm.dspark_workspace_status(ws) == 0
     assert np.array_equal(one[0], two[0])
     assert np.array_equal(one[1].view(np.uint8), two[1].view(np.uint8))
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+@pytest.mark.parametrize("V,T,bs,k", [(5000, 5, 64, 64), (512, 6, 60, 512)])
+def test_topk_one_launch_parity(V, T, bs, k, mode):
+    """The one-launch form (more rows than compute units) against the oracle, every request."""
+    p = random_problem(V, T, bs, seed=V + 3 * k, temps=np.linspace(0.5, 1.5, bs).astype(np.float32),
+                       positions=np.arange(bs, dtype=np.int64) * 7)
+    _, _, rep = _run_check(p, k, mode)
+    assert rep.ok, rep.summary()
 
 
 def test_topk_one_launch_wait_timeout_is_reported_and_recovers(split_knob_reset):
